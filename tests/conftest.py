@@ -1,0 +1,32 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def gpu_available():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.fixture(scope="session")
+def lib():
+    """The built C-ABI library, loaded through the Python binding (GPU tests only)."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import fp8_grouped_gemm_ragged_amd as g
+
+    g.load()  # raises if the shared library is missing: no fallback
+    return g

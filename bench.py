@@ -1,0 +1,221 @@
+"""Benchmark of the FP8 grouped (ragged) matmul hot path on one MI355X.
+
+One step is the whole path over one batch of the Mixtral-shaped merged gate|up expert
+layer (G=8 experts, K=4096, N=2x14336=28672, M=16384 rows = 8192 tokens x top-2, Zipf(1.1)
+routing), inputs resident in HBM:
+
+  1. block scales of lhs  (abs-max prepass, e4m3, 128 rows x K)
+  2. gmm_fwd   out[M, N]      = q(lhs) . rhs[g]        (bf16 lhs quantized in-kernel)
+  3. block scales of grad (abs-max prepass, e5m2, 128 rows x N)
+  4. gmm_dlhs  dlhs[M, K]     = q(grad) . rhs[g]^T
+  5. tgmm_drhs drhs[G, K, N]  = q(lhs)_g^T . q(grad)_g  (scales of steps 1 and 3 reused)
+
+value = 3 * 2*M*K*N / step time (TFLOP/s).  Each product call is a single kernel launch,
+timed with HIP events on the stream it runs on; the slowest one is reported against the
+dense FP8 MFMA peak (5.0 PFLOP/s).  The CPU oracle is timed on a bounded sample of the same
+workload (rank 0, N=1) for reference.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 GMM TFLOP/s (fwd/dlhs/drhs) and % of MI355X FP8 MFMA peak"
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mixtral_gate_up")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=1024)
+    p.add_argument("--cpu-sample-cols", type=int, default=2048, help="at most 4096")
+    return p.parse_args()
+
+
+class Step:
+    """Pre-allocated buffers and direct C-ABI calls for one pass of the path."""
+
+    def __init__(self, g, wl, seed):
+        import torch
+
+        from synth.workloads import normal_bf16
+
+        self.g, self.torch = g, torch
+        lib = g.load()
+        self.lib = lib
+        dev = "cuda"
+        G, M, K, N = wl.G, wl.M, wl.K, wl.N
+        self.G, self.M, self.K, self.N = G, M, K, N
+        self.sizes = wl.group_sizes()
+        self.gs = torch.tensor(self.sizes, dtype=torch.int32, device=dev)
+        self.lhs = normal_bf16((M, K), 1.0, seed, dev)
+        self.grad = normal_bf16((M, N), 1e-3, seed + 2, dev)
+        w = normal_bf16((G, K, N), 0.02, seed + 1, dev)
+        # weights arrive pre-quantized: forward copy per output channel n stored [G, N, K]
+        # (contraction contiguous), dlhs copy per output channel k stored [G, K, N]
+        self.w_fwd, self.s_fwd = g.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+        self.w_dlhs, self.s_dlhs = g.gmm_quantize_rhs(w, "e4m3", 1, "kn")
+        self.w_sample = w[:, :, :4096].to("cpu")  # for the CPU baseline sample only
+        del w
+        self.out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.dlhs = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.drhs = torch.empty((G, K, N), dtype=torch.bfloat16, device=dev)
+        nb = (M + 127) // 128
+        self.s_lhs = torch.empty(nb, dtype=torch.float32, device=dev)
+        self.s_grad = torch.empty(nb, dtype=torch.float32, device=dev)
+        op = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC, 0.0)
+        n = g._SZ()
+        self._chk(lib.gmm_workspace_size(g.OP_FWD, ctypes.byref(op), ctypes.byref(op), M,
+                                         max(K, N), 0, ctypes.byref(n)))
+        self.ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+        self.ws_n = n.value
+        self.op_lhs = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
+        self.op_grad = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC_GIVEN, 0.0)
+        self.r_lhs, self.r_grad = ctypes.byref(self.op_lhs), ctypes.byref(self.op_grad)
+        P = lambda t: t.data_ptr()
+        self.p = {k: P(getattr(self, k)) for k in
+                  ("lhs", "grad", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs", "drhs",
+                   "s_lhs", "s_grad", "ws", "gs")}
+        torch.cuda.synchronize()
+
+    def run(self, stream, ev=None):
+        """Enqueue one step; ev (6 events) brackets: scales, fwd, scales, dlhs, tgmm."""
+        lib, p, s = self.lib, self.p, stream
+        M, K, N, G = self.M, self.K, self.N, self.G
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        chk = self._chk
+        rec(0)
+        chk(lib.gmm_dynamic_scales(self.g.E4M3, M, K, p["lhs"], p["s_lhs"], p["ws"], self.ws_n, s))
+        rec(1)
+        chk(lib.gmm_fwd(self.r_lhs, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
+                        p["lhs"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"], None, 0, s))
+        rec(2)
+        chk(lib.gmm_dynamic_scales(self.g.E5M2, M, N, p["grad"], p["s_grad"], p["ws"], self.ws_n, s))
+        rec(3)
+        chk(lib.gmm_dlhs(self.r_grad, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
+                         p["grad"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, s))
+        rec(4)
+        chk(lib.tgmm_drhs(self.r_lhs, self.r_grad, self.g.OUT_BF16, M, K, N, G, p["lhs"], p["s_lhs"],
+                          p["grad"], p["s_grad"], p["gs"], p["drhs"], None, 0, s))
+        rec(5)
+
+    def _chk(self, status):
+        if status != 0:
+            raise RuntimeError(f"library call failed: {self.g.gmm_status_string(status)}")
+
+
+def cpu_baseline(step, rows, cols):
+    """Time the CPU oracle on a bounded sample: the first `rows` rows (with their group
+    split), all K, the first `cols` columns of the merged weight; fwd + dlhs + tgmm."""
+    import torch
+
+    import oracle.ops as ops
+    from oracle.quant import quantize_rhs_per_channel
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    M, K = rows, step.K
+    off = np.concatenate([[0], np.cumsum(step.sizes)])
+    sizes = np.clip(np.minimum(off[1:], M) - np.minimum(off[:-1], M), 0, None).astype(np.int32)
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    lhs = bits(step.lhs[:M].to("cpu"))
+    grad = bits(step.grad[:M, :cols].to("cpu"))
+    w = bits(step.w_sample[:, :, :cols].contiguous())
+    t0 = time.perf_counter()
+    wq_n, ws_n = quantize_rhs_per_channel(w, "e4m3", "n")
+    wq_k, ws_k = quantize_rhs_per_channel(w, "e4m3", "k")
+    ops.fwd(lhs, wq_n, ws_n, sizes, "e4m3", "dynamic", None, "e4m3", "bf16")
+    ops.dlhs(grad, wq_k, ws_k, sizes, "e5m2", "dynamic", None, "e4m3", "bf16")
+    ops.tgmm(lhs, grad, sizes, out_dtype="bf16")
+    dt = time.perf_counter() - t0
+    flops = 3 * 2.0 * M * K * cols
+    return {
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+        "kind": "oracle", "seconds": round(dt, 2),
+        "sample": f"first {M} rows (their group split), K={K}, first {cols} of N columns; "
+                  f"weight quantization + fwd + dlhs + tgmm, bf16 outputs; "
+                  f"{len(os.sched_getaffinity(0))} host cores visible",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path runs "
+              "on a single MI355X and this build has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import fp8_grouped_gemm_ragged_amd as g
+    from synth.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    step = Step(g, wl, seed=wl.seed * 100)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    for _ in range(args.warmup):
+        step.run(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run(s, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["scales_lhs", "gmm_fwd", "scales_grad", "gmm_dlhs", "tgmm_drhs"]
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+           for j, n in enumerate(names)}
+    ms_step = wall * 1000.0 / args.steps
+    flop_op = 2.0 * wl.M * wl.K * wl.N
+    value = 3 * flop_op / (ms_step / 1000.0) / 1e12
+    ops = {n: {"ms": round(per[n], 4), "TFLOP/s": round(flop_op / (per[n] / 1000) / 1e12, 1),
+               "frac_peak": round(flop_op / (per[n] / 1000) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+           for n in ("gmm_fwd", "gmm_dlhs", "tgmm_drhs")}
+    dom = max(ops, key=lambda n: per[n])
+    ach = flop_op / (per[dom] / 1000.0) / 1e12
+    kern = {"gmm_fwd": "gmm_kernel<e4m3,e4m3,bf16-A,K-contiguous B>",
+            "gmm_dlhs": "gmm_kernel<e5m2,e4m3,bf16-A,N-contiguous B>",
+            "tgmm_drhs": "tgmm_kernel<e4m3,e5m2>"}[dom]
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "G": wl.G, "M": wl.M, "K": wl.K, "N": wl.N,
+                   "routing": f"zipf{wl.zipf_s}", "group_sizes": [int(x) for x in wl.group_sizes()],
+                   "lhs": "bf16 -> e4m3 dynamic 128-row blocks", "grad": "bf16 -> e5m2 dynamic 128-row blocks",
+                   "rhs": "e4m3 per-channel", "out": "bf16", "step": "scales+fwd+scales+dlhs+tgmm"},
+        "ops": ops, "scales_ms": {"lhs": round(per["scales_lhs"], 4), "grad": round(per["scales_grad"], 4)},
+        "roofline": {"kernel": kern, "op": dom, "bound": "mfma", "achieved": round(ach, 1),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

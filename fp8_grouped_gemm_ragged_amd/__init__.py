@@ -1,0 +1,346 @@
+"""Python binding of the gfx950 FP8 grouped (ragged) matmul library ``libgmm_fp8.so``.
+
+Argument marshalling only: every computation runs in the HIP kernels behind the C ABI
+declared in ``include/gmm_fp8.h``.  PyTorch provides device memory and the current
+stream; outputs and workspaces are allocated here with ``torch.empty`` and filled by
+the library.  There is no fallback: if the shared library is missing, ``load()``
+raises, and so does every call.
+
+Functions (same names as the C ABI):
+  gmm_fwd, gmm_dlhs, tgmm_drhs, gmm_dynamic_scales, gmm_quantize, gmm_quantize_rhs,
+  gmm_static_scale_from_bound, gmm_workspace_size, gmm_status_string, gmm_version.
+
+fp8 codes travel as ``torch.uint8`` tensors; bf16 values as ``torch.bfloat16``.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "load", "library_path", "GmmError", "gmm_fwd", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
+    "gmm_dynamic_scales",
+    "gmm_quantize_rhs", "gmm_static_scale_from_bound", "gmm_workspace_size",
+    "gmm_status_string", "gmm_version", "E4M3", "E5M2", "STATIC", "DYNAMIC", "BLOCK_ROWS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgmm_fp8.so")
+_lib = None
+
+# enum values of include/gmm_fp8.h
+GMM_OK = 0
+E4M3, E5M2 = 0, 1
+STATIC, DYNAMIC, DYNAMIC_GIVEN = 0, 1, 2
+KIND_BF16, KIND_FP8 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+RHS_KN, RHS_NK = 0, 1
+OP_FWD, OP_DLHS, OP_TGMM = 0, 1, 2
+BLOCK_ROWS = 128
+
+_FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+_SCALING = {"static": STATIC, "dynamic": DYNAMIC, "dynamic_given": DYNAMIC_GIVEN,
+            STATIC: STATIC, DYNAMIC: DYNAMIC, DYNAMIC_GIVEN: DYNAMIC_GIVEN}
+_LAYOUT = {"kn": RHS_KN, "nk": RHS_NK, RHS_KN: RHS_KN, RHS_NK: RHS_NK}
+
+
+class GmmError(ValueError):
+    """A library call returned an error status."""
+
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {gmm_status_string(status)} (status {status})")
+        self.status = status
+
+
+class Operand(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("format", ctypes.c_int32),
+                ("scaling", ctypes.c_int32), ("static_scale", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _SZ, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_OPP = ctypes.POINTER(Operand)
+
+_SIGNATURES = {
+    "gmm_fwd": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_dlhs": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "tgmm_drhs": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_workspace_size": [_I32, _OPP, _OPP, _I64, _I64, _I64, ctypes.POINTER(_SZ)],
+    "gmm_dynamic_scales": [_I32, _I64, _I64, _P, _P, _P, _SZ, _P],
+    "gmm_quantize": [_OPP, _I64, _I64, _P, _P, _P, _P, _SZ, _P],
+    "gmm_quantize_rhs": [_I32, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _P],
+    "gmm_static_scale_from_bound": [_F, _F, _I32, ctypes.POINTER(_F)],
+    "gmm_status_string": [_I32],
+    "gmm_version": [],
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load(path=None):
+    """Load (once) and return the shared library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m fp8_grouped_gemm_ragged_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(p)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("gmm_status_string", "gmm_version") else ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def gmm_status_string(status):
+    return load().gmm_status_string(int(status)).decode()
+
+
+def gmm_version():
+    return load().gmm_version().decode()
+
+
+def _check(status, what):
+    if status != GMM_OK:
+        raise GmmError(status, what)
+
+
+def _operand(kind, fmt, scaling, static_scale):
+    return Operand(kind, _FMT[fmt], _SCALING[scaling],
+                   float(static_scale) if static_scale is not None else 0.0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def gmm_static_scale_from_bound(lo, hi, fmt="e4m3"):
+    """Per-tensor scale of a fixed symmetric range [lo, hi] = [-b, b]: RNE(b / qmax)."""
+    out = _F()
+    _check(load().gmm_static_scale_from_bound(float(lo), float(hi), _FMT[fmt], ctypes.byref(out)),
+           "gmm_static_scale_from_bound")
+    return out.value
+
+
+def gmm_workspace_size(op, a_fmt, a_scaling, rows, cols_a=0, cols_b=0, b_fmt="e5m2",
+                       b_scaling="dynamic", a_kind=KIND_BF16, static_scale=1.0):
+    a = _operand(a_kind, a_fmt, a_scaling, static_scale)
+    b = _operand(KIND_BF16, b_fmt, b_scaling, static_scale)
+    n = _SZ()
+    _check(load().gmm_workspace_size(int(op), ctypes.byref(a), ctypes.byref(b), int(rows),
+                                     int(cols_a), int(cols_b), ctypes.byref(n)), "gmm_workspace_size")
+    return n.value
+
+
+def _workspace(nbytes, device):
+    import torch
+
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device) if nbytes else None
+
+
+def _nblocks(rows):
+    return (rows + BLOCK_ROWS - 1) // BLOCK_ROWS
+
+
+def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_scales,
+          rhs_layout, out_dtype, out, contraction_dim, out_cols):
+    import torch
+
+    lib = load()
+    prequant = a.dtype == torch.uint8
+    _need(a, torch.uint8 if prequant else torch.bfloat16, "lhs/grad", 2)
+    _need(rhs, torch.uint8, "rhs", 3)
+    _need(rhs_scales, torch.float32, "rhs_scales", 2)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M = a.shape[0]
+    G = rhs.shape[0]
+    K_or_N = a.shape[1]
+    # logical (K, N) of the weight from its layout
+    if _LAYOUT[rhs_layout] == RHS_KN:
+        K, N = rhs.shape[1], rhs.shape[2]
+    else:
+        N, K = rhs.shape[1], rhs.shape[2]
+    if K_or_N != (K if contraction_dim == "K" else N):
+        raise ValueError("operand width does not match the rhs contraction dimension")
+    odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    n_out = N if out_cols == "N" else K
+    if out is None:
+        out = torch.empty((M, n_out), dtype=odt, device=a.device)
+    else:
+        _need(out, odt, "out", 2)
+    op = _operand(KIND_FP8 if prequant else KIND_BF16, fmt, scaling, static_scale)
+    mode = _SCALING[scaling]
+    if mode != STATIC and a_scales is None:
+        if prequant or mode == DYNAMIC_GIVEN:
+            raise ValueError("this recipe needs the operand's block scales as an input")
+        a_scales = torch.empty(_nblocks(M), dtype=torch.float32, device=a.device)
+    if a_scales is not None:
+        _need(a_scales, torch.float32, "scales", 1)
+    ws_n = _SZ()
+    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), M, K_or_N, 0,
+                                  ctypes.byref(ws_n)), "gmm_workspace_size")
+    ws = _workspace(ws_n.value, a.device)
+    fn = getattr(lib, cname)
+    _check(fn(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], OUT_F32 if odt == torch.float32 else OUT_BF16,
+              M, K, N, G, _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales), _ptr(group_sizes),
+              _ptr(out), _ptr(ws), ws_n.value, _stream()), cname)
+    return out, a_scales
+
+
+def gmm_fwd(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic",
+            static_scale=None, lhs_scales=None, rhs_layout="nk", out_dtype=None, out=None,
+            return_scales=False):
+    """Forward grouped matmul: out[M, N] = q(lhs)[rows of g] . rhs[g] (scales applied).
+
+    lhs: bf16 [M, K] (quantized in-kernel) or uint8 fp8 codes [M, K] (pre-quantized,
+    then ``lhs_scales`` holds its block scales when dynamic).  lhs_scaling "static",
+    "dynamic" (block scales computed by the call; returned with return_scales) or
+    "dynamic_given" (block scales from an earlier call in ``lhs_scales``).  rhs: uint8 codes,
+    [G, N, K] for rhs_layout "nk" or [G, K, N] for "kn"; rhs_scales f32 [G, N].
+    """
+    o, s = _gemm("gmm_fwd", lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
+                 static_scale, lhs_scales, rhs_layout, out_dtype, out, "K", "N")
+    return (o, s) if return_scales else o
+
+
+def gmm_dlhs(grad, rhs, rhs_scales, group_sizes, *, grad_format="e5m2", grad_scaling="dynamic",
+             static_scale=None, grad_scales=None, rhs_layout="kn", out_dtype=None, out=None,
+             return_scales=False):
+    """lhs gradient: dlhs[M, K] = q(grad)[rows of g] . rhs[g]^T; rhs_scales f32 [G, K]."""
+    o, s = _gemm("gmm_dlhs", grad, rhs, rhs_scales, group_sizes, grad_format, grad_scaling,
+                 static_scale, grad_scales, rhs_layout, out_dtype, out, "N", "K")
+    return (o, s) if return_scales else o
+
+
+def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic",
+              lhs_static_scale=None, lhs_scales=None, grad_format="e5m2",
+              grad_scaling="dynamic", grad_static_scale=None, grad_scales=None,
+              out_dtype=None, out=None, return_scales=False):
+    """Weight gradient: drhs[g] = q(lhs)_g^T . q(grad)_g, [G, K, N]; empty groups give zeros."""
+    import torch
+
+    lib = load()
+    _need(lhs, torch.bfloat16, "lhs", 2)
+    _need(grad, torch.bfloat16, "grad", 2)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = lhs.shape
+    if grad.shape[0] != M:
+        raise ValueError("lhs and grad must have the same number of rows")
+    N = grad.shape[1]
+    G = group_sizes.shape[0]
+    odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((G, K, N), dtype=odt, device=lhs.device)
+    else:
+        _need(out, odt, "out", 3)
+    aop = _operand(KIND_BF16, lhs_format, lhs_scaling, lhs_static_scale)
+    bop = _operand(KIND_BF16, grad_format, grad_scaling, grad_static_scale)
+    def scales_for(mode, given):
+        if _SCALING[mode] == DYNAMIC_GIVEN:
+            if given is None:
+                raise ValueError("dynamic_given needs the block scales")
+            _need(given, torch.float32, "scales", 1)
+            return given
+        if _SCALING[mode] == DYNAMIC:
+            return given if given is not None else torch.empty(_nblocks(M), dtype=torch.float32, device=lhs.device)
+        return None
+
+    sa = scales_for(lhs_scaling, lhs_scales)
+    sg = scales_for(grad_scaling, grad_scales)
+    ws_n = _SZ()
+    _check(lib.gmm_workspace_size(OP_TGMM, ctypes.byref(aop), ctypes.byref(bop), M, K, N,
+                                  ctypes.byref(ws_n)), "gmm_workspace_size")
+    ws = _workspace(ws_n.value, lhs.device)
+    _check(lib.tgmm_drhs(ctypes.byref(aop), ctypes.byref(bop), OUT_F32 if odt == torch.float32 else OUT_BF16,
+                         M, K, N, G, _ptr(lhs), _ptr(sa), _ptr(grad), _ptr(sg), _ptr(group_sizes),
+                         _ptr(out), _ptr(ws), ws_n.value, _stream()), "tgmm_drhs")
+    return (out, sa, sg) if return_scales else out
+
+
+def gmm_dynamic_scales(x, fmt="e4m3"):
+    """Per-128-row-block scales of a bf16 matrix [R, C] (the abs-max prepass alone)."""
+    import torch
+
+    lib = load()
+    _need(x, torch.bfloat16, "x", 2)
+    R, C = x.shape
+    scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
+    op = _operand(KIND_BF16, fmt, "dynamic", None)
+    ws_n = _SZ()
+    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0,
+                                  ctypes.byref(ws_n)), "gmm_workspace_size")
+    ws = _workspace(ws_n.value, x.device)
+    _check(lib.gmm_dynamic_scales(_FMT[fmt], R, C, _ptr(x), _ptr(scales), _ptr(ws), ws_n.value,
+                                  _stream()), "gmm_dynamic_scales")
+    return scales
+
+
+def gmm_quantize(x, fmt="e4m3", scaling="dynamic", static_scale=None, scales=None):
+    """Stand-alone quantization of bf16 [R, C] -> (uint8 codes [R, C], f32 scales or None).
+
+    scaling "dynamic_given" takes the block scales in ``scales``."""
+    import torch
+
+    lib = load()
+    _need(x, torch.bfloat16, "x", 2)
+    R, C = x.shape
+    op = _operand(KIND_BF16, fmt, scaling, static_scale)
+    codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    mode = _SCALING[scaling]
+    if mode == DYNAMIC_GIVEN and scales is None:
+        raise ValueError("dynamic_given needs the block scales")
+    if mode == DYNAMIC and scales is None:
+        scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
+    ws_n = _SZ()
+    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0,
+                                  ctypes.byref(ws_n)), "gmm_workspace_size")
+    ws = _workspace(ws_n.value, x.device)
+    _check(lib.gmm_quantize(ctypes.byref(op), R, C, _ptr(x), _ptr(codes), _ptr(scales), _ptr(ws),
+                            ws_n.value, _stream()), "gmm_quantize")
+    return codes, scales
+
+
+def gmm_quantize_rhs(w, fmt="e4m3", channel_axis=0, layout="kn"):
+    """Per-channel quantization of a bf16 weight [G, K, N].
+
+    channel_axis 0 -> scales [G, N] (forward); 1 -> scales [G, K] (dlhs).
+    layout "kn" -> codes [G, K, N]; "nk" -> codes [G, N, K].
+    """
+    import torch
+
+    lib = load()
+    _need(w, torch.bfloat16, "w", 3)
+    G, K, N = w.shape
+    shape = (G, K, N) if _LAYOUT[layout] == RHS_KN else (G, N, K)
+    codes = torch.empty(shape, dtype=torch.uint8, device=w.device)
+    scales = torch.empty((G, N) if channel_axis == 0 else (G, K), dtype=torch.float32, device=w.device)
+    _check(lib.gmm_quantize_rhs(_FMT[fmt], int(channel_axis), _LAYOUT[layout], G, K, N, _ptr(w),
+                                _ptr(codes), _ptr(scales), _stream()), "gmm_quantize_rhs")
+    return codes, scales

@@ -1,0 +1,391 @@
+// C-ABI entry points: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued.
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/gmm_fp8.h"
+#include "kernels.hpp"
+
+using namespace gmm;
+
+namespace {
+
+constexpr int64_t MAX_DIM = int64_t(1) << 22;  // K, N limit: keeps every tile offset 32-bit
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && v[0] != '0';
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int64_t nblocks(int64_t rows) { return (rows + BLOCK_ROWS - 1) / BLOCK_ROWS; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of one bf16 operand whose dynamic scales the call computes: abs-max
+// partials, plus room for the scales when the caller does not ask for them.
+size_t dyn_ws_bytes(int64_t rows) {
+  const size_t nb = (size_t)nblocks(rows);
+  return align256(nb * AMAX_SPLIT * 4) + align256(nb * 4);
+}
+
+struct DynWs {
+  uint32_t* partial;
+  float* scale;
+};
+
+DynWs carve(void* base, int64_t rows) {
+  const size_t nb = (size_t)nblocks(rows);
+  uint8_t* p = (uint8_t*)base;
+  DynWs w;
+  w.partial = (uint32_t*)p;
+  w.scale = (float*)(p + align256(nb * AMAX_SPLIT * 4));
+  return w;
+}
+
+// The call runs the abs-max prepass itself (and needs workspace) only for a bf16
+// operand with GMM_SCALE_DYNAMIC.
+bool needs_dyn_ws(const gmm_operand_t* op) {
+  return op && op->kind == GMM_OPERAND_BF16 && op->scaling == GMM_SCALE_DYNAMIC;
+}
+
+// Per-block scales are an input for DYNAMIC_GIVEN and for pre-quantized dynamic codes.
+bool scales_are_input(const gmm_operand_t* op) {
+  return op->scaling == GMM_SCALE_DYNAMIC_GIVEN ||
+         (op->kind == GMM_OPERAND_FP8 && op->scaling == GMM_SCALE_DYNAMIC);
+}
+
+// Resolve the scaling of one operand for the kernels: static scale and inverse, or a
+// pointer to per-block scales (running the prepass when the call computes them).
+struct Scaling {
+  const float* blk = nullptr;
+  float s = 0.0f, inv = 0.0f;
+};
+
+gmm_status_t resolve_scaling(const gmm_operand_t* op, const void* x, int64_t R, int64_t C,
+                             float* user_scales, void* ws, hipStream_t st, Scaling& out) {
+  if (op->scaling == GMM_SCALE_STATIC) {
+    out.s = op->static_scale;
+    out.inv = 1.0f / op->static_scale;  // IEEE division on the host: RNE(1/s)
+    return GMM_OK;
+  }
+  if (scales_are_input(op)) {
+    out.blk = user_scales;
+    return GMM_OK;
+  }
+  DynWs w = carve(ws, R);
+  float* dst = user_scales ? user_scales : w.scale;
+  if (R > 0 && launch_dynamic_scales(op->format, x, R, C, w.partial, dst, st) != hipSuccess)
+    return GMM_ERR_HIP;
+  out.blk = dst;
+  return GMM_OK;
+}
+
+gmm_status_t check_operand(const gmm_operand_t* op) {
+  if (!op) return GMM_ERR_NULL;
+  if (op->kind != GMM_OPERAND_BF16 && op->kind != GMM_OPERAND_FP8) return GMM_ERR_RECIPE;
+  if (op->format != GMM_FP8_E4M3 && op->format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (op->scaling != GMM_SCALE_STATIC && op->scaling != GMM_SCALE_DYNAMIC &&
+      op->scaling != GMM_SCALE_DYNAMIC_GIVEN)
+    return GMM_ERR_RECIPE;
+  if (op->scaling == GMM_SCALE_STATIC) {
+    const float s = op->static_scale;
+    // finite, positive, normal: guards against underflow and scales close to zero
+    if (!std::isfinite(s) || !(s >= FLT_MIN)) return GMM_ERR_SCALE;
+  }
+  return GMM_OK;
+}
+
+gmm_status_t check_shape(int64_t M, int64_t K, int64_t N, int32_t G) {
+  if (M < 0 || M >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  if (G < 1 || G > GMM_MAX_GROUPS) return GMM_ERR_SHAPE;
+  if (K <= 0 || N <= 0 || K % 128 || N % 128 || K > MAX_DIM || N > MAX_DIM) return GMM_ERR_SHAPE;
+  if (K * N >= (int64_t(1) << 32)) return GMM_ERR_SHAPE;
+  return GMM_OK;
+}
+
+// GMM_CHECK=1: synchronous validation of group_sizes (debug mode).
+gmm_status_t check_group_sizes(const int32_t* gs, int32_t G, int64_t M, hipStream_t st) {
+  if (!env_flag("GMM_CHECK")) return GMM_OK;
+  std::vector<int32_t> h(G);
+  if (hipMemcpyAsync(h.data(), gs, sizeof(int32_t) * G, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return GMM_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return GMM_ERR_HIP;
+  int64_t sum = 0;
+  for (int32_t v : h) {
+    if (v < 0) return GMM_ERR_GROUP_SIZES;
+    sum += v;
+  }
+  return sum == M ? GMM_OK : GMM_ERR_GROUP_SIZES;
+}
+
+void trace(const char* what, int64_t M, int64_t K, int64_t N, int32_t G) {
+  if (env_flag("GMM_TRACE"))
+    std::fprintf(stderr, "[gmm_fp8] %s M=%lld K=%lld N=%lld G=%d\n", what, (long long)M,
+                 (long long)K, (long long)N, G);
+}
+
+// Shared body of gmm_fwd / gmm_dlhs: out[M, Nout] = A[M, Kc] x B.
+gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rhs_format,
+                          bool b_trans, int32_t out_dtype, int64_t M, int64_t Kc,
+                          int64_t Nout, int32_t G, const void* a, float* a_scales,
+                          const uint8_t* rhs, const float* rhs_scales,
+                          const int32_t* group_sizes, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t st) {
+  gmm_status_t s = check_operand(aop);
+  if (s != GMM_OK) return s;
+  if (rhs_format != GMM_FP8_E4M3) return GMM_ERR_RECIPE;  // weights are e4m3 codes
+  if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
+  if ((s = check_shape(M, Kc, Nout, G)) != GMM_OK) return s;
+  if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
+  if (M > 0 && (!a || !out)) return GMM_ERR_NULL;
+  const bool a_fp8 = aop->kind == GMM_OPERAND_FP8;
+  const bool dyn = aop->scaling != GMM_SCALE_STATIC;
+  if (scales_are_input(aop) && M > 0 && !a_scales) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)a, (const void*)rhs, (const void*)rhs_scales,
+                          (const void*)group_sizes, (const void*)out, (const void*)a_scales,
+                          (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t ws_need = needs_dyn_ws(aop) ? dyn_ws_bytes(M) : 0;
+  if (ws_need && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
+  const size_t a_bytes = (size_t)M * Kc * (a_fp8 ? 1 : 2);
+  const size_t out_bytes = (size_t)M * Nout * (out_dtype == GMM_OUT_F32 ? 4 : 2);
+  const size_t b_bytes = (size_t)G * Kc * Nout;
+  const size_t as_bytes = (size_t)nblocks(M) * 4;
+  if (overlaps(out, out_bytes, a, a_bytes) || overlaps(out, out_bytes, rhs, b_bytes) ||
+      overlaps(out, out_bytes, rhs_scales, (size_t)G * Nout * 4) ||
+      overlaps(out, out_bytes, group_sizes, (size_t)G * 4) ||
+      (needs_dyn_ws(aop) && overlaps(a_scales, as_bytes, a, a_bytes)) ||
+      overlaps(workspace, ws_need, a, a_bytes) || overlaps(workspace, ws_need, out, out_bytes))
+    return GMM_ERR_ALIAS;
+  if ((s = check_group_sizes(group_sizes, G, M, st)) != GMM_OK) return s;
+  trace(name, M, Kc, Nout, G);
+  if (M == 0) return GMM_OK;
+
+  GemmParams p{};
+  p.a = a;
+  p.b = rhs;
+  p.b_scale = rhs_scales;
+  p.group_sizes = group_sizes;
+  p.out = out;
+  p.M = M;
+  p.Kc = (int32_t)Kc;
+  p.Nout = (int32_t)Nout;
+  p.G = G;
+  p.out_f32 = out_dtype == GMM_OUT_F32;
+  Scaling sc;
+  if ((s = resolve_scaling(aop, a, M, Kc, a_scales, workspace, st, sc)) != GMM_OK) return s;
+  p.a_scale_blk = sc.blk;
+  p.a_scale_static = sc.s;
+  p.a_inv_static = sc.inv;
+  if (launch_gemm(aop->format, FMT_E4M3, a_fp8, b_trans, p, st) != hipSuccess) return GMM_ERR_HIP;
+  return GMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gmm_status_t gmm_fwd(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                     int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                     const void* lhs, float* lhs_scales, const uint8_t* rhs,
+                     const float* rhs_scales, const int32_t* group_sizes, void* out,
+                     void* workspace, size_t workspace_bytes, gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  // forward contracts over K: contiguous when the codes are stored [G, N, K]
+  return grouped_gemm("gmm_fwd", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN, out_dtype, M, K,
+                      N, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes, out, workspace,
+                      workspace_bytes, (hipStream_t)stream);
+}
+
+gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
+                      int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                      const void* grad, float* grad_scales, const uint8_t* rhs,
+                      const float* rhs_scales, const int32_t* group_sizes, void* dlhs,
+                      void* workspace, size_t workspace_bytes, gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  // dlhs contracts over N: contiguous when the codes are stored [G, K, N]
+  return grouped_gemm("gmm_dlhs", grad_op, rhs_format, rhs_layout == GMM_RHS_NK, out_dtype, M,
+                      N, K, G, grad, grad_scales, rhs, rhs_scales, group_sizes, dlhs, workspace,
+                      workspace_bytes, (hipStream_t)stream);
+}
+
+gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
+                       int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                       const void* lhs, float* lhs_scales, const void* grad,
+                       float* grad_scales, const int32_t* group_sizes, void* drhs,
+                       void* workspace, size_t workspace_bytes, gmm_stream_t stream) {
+  gmm_status_t s;
+  if ((s = check_operand(lhs_op)) != GMM_OK) return s;
+  if ((s = check_operand(grad_op)) != GMM_OK) return s;
+  if (lhs_op->kind != GMM_OPERAND_BF16 || grad_op->kind != GMM_OPERAND_BF16) return GMM_ERR_RECIPE;
+  if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
+  if ((s = check_shape(M, K, N, G)) != GMM_OK) return s;
+  if (!group_sizes || !drhs) return GMM_ERR_NULL;
+  if (M > 0 && (!lhs || !grad)) return GMM_ERR_NULL;
+  if (M > 0 && ((scales_are_input(lhs_op) && !lhs_scales) || (scales_are_input(grad_op) && !grad_scales)))
+    return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)lhs, (const void*)grad, (const void*)group_sizes,
+                          (const void*)drhs, (const void*)lhs_scales, (const void*)grad_scales,
+                          (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t wa = needs_dyn_ws(lhs_op) ? dyn_ws_bytes(M) : 0;
+  const size_t wb = needs_dyn_ws(grad_op) ? dyn_ws_bytes(M) : 0;
+  if ((wa + wb) && (!workspace || workspace_bytes < wa + wb)) return GMM_ERR_WORKSPACE;
+  const size_t out_bytes = (size_t)G * K * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
+  if (overlaps(drhs, out_bytes, lhs, (size_t)M * K * 2) ||
+      overlaps(drhs, out_bytes, grad, (size_t)M * N * 2) ||
+      overlaps(drhs, out_bytes, group_sizes, (size_t)G * 4) ||
+      overlaps(workspace, wa + wb, drhs, out_bytes))
+    return GMM_ERR_ALIAS;
+  if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
+  trace("tgmm_drhs", M, K, N, G);
+  hipStream_t st = (hipStream_t)stream;
+
+  TgmmParams p{};
+  p.a = (const uint16_t*)lhs;
+  p.b = (const uint16_t*)grad;
+  p.group_sizes = group_sizes;
+  p.out = drhs;
+  p.M = M;
+  p.Kout = (int32_t)K;
+  p.Nout = (int32_t)N;
+  p.G = G;
+  p.out_f32 = out_dtype == GMM_OUT_F32;
+  if (M > 0) {
+    Scaling sa, sg;
+    if ((s = resolve_scaling(lhs_op, lhs, M, K, lhs_scales, workspace, st, sa)) != GMM_OK) return s;
+    if ((s = resolve_scaling(grad_op, grad, M, N, grad_scales, (uint8_t*)workspace + wa, st, sg)) !=
+        GMM_OK)
+      return s;
+    p.a_scale_blk = sa.blk;
+    p.a_scale_static = sa.s;
+    p.a_inv_static = sa.inv;
+    p.b_scale_blk = sg.blk;
+    p.b_scale_static = sg.s;
+    p.b_inv_static = sg.inv;
+  }
+  if (launch_tgmm(lhs_op->format, grad_op->format, p, st) != hipSuccess) return GMM_ERR_HIP;
+  return GMM_OK;
+}
+
+gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_operand_t* b,
+                                int64_t rows, int64_t cols_a, int64_t cols_b, size_t* bytes) {
+  (void)cols_a;
+  (void)cols_b;
+  if (!bytes || !a) return GMM_ERR_NULL;
+  if (rows < 0) return GMM_ERR_SHAPE;
+  gmm_status_t s = check_operand(a);
+  if (s != GMM_OK) return s;
+  size_t n = needs_dyn_ws(a) ? dyn_ws_bytes(rows) : 0;
+  if (op == GMM_OP_TGMM) {
+    if (!b) return GMM_ERR_NULL;
+    if ((s = check_operand(b)) != GMM_OK) return s;
+    n += needs_dyn_ws(b) ? dyn_ws_bytes(rows) : 0;
+  } else if (op != GMM_OP_FWD && op != GMM_OP_DLHS) {
+    return GMM_ERR_RECIPE;
+  }
+  *bytes = n;
+  return GMM_OK;
+}
+
+gmm_status_t gmm_quantize(const gmm_operand_t* op, int64_t R, int64_t C, const void* x,
+                          uint8_t* codes, float* scales, void* workspace,
+                          size_t workspace_bytes, gmm_stream_t stream) {
+  gmm_status_t s = check_operand(op);
+  if (s != GMM_OK) return s;
+  if (op->kind != GMM_OPERAND_BF16) return GMM_ERR_RECIPE;
+  if (R < 0 || R >= (int64_t(1) << 31) || C <= 0 || C % 8 || C > MAX_DIM * 8) return GMM_ERR_SHAPE;
+  if (R > 0 && (!x || !codes)) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)x, (const void*)codes, (const void*)scales, (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t ws_need = needs_dyn_ws(op) ? dyn_ws_bytes(R) : 0;
+  if (ws_need && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
+  if (scales_are_input(op) && R > 0 && !scales) return GMM_ERR_NULL;
+  if (overlaps(codes, (size_t)R * C, x, (size_t)R * C * 2)) return GMM_ERR_ALIAS;
+  if (R == 0) return GMM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  Scaling sc;
+  if ((s = resolve_scaling(op, x, R, C, scales, workspace, st, sc)) != GMM_OK) return s;
+  return launch_quantize_rows(op->format, x, R, C, sc.blk, sc.inv, codes, st) == hipSuccess
+             ? GMM_OK : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_dynamic_scales(int32_t format, int64_t R, int64_t C, const void* x,
+                                float* scales, void* workspace, size_t workspace_bytes,
+                                gmm_stream_t stream) {
+  if (format != GMM_FP8_E4M3 && format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (R < 0 || R >= (int64_t(1) << 31) || C <= 0 || C % 8 || C > MAX_DIM * 8) return GMM_ERR_SHAPE;
+  if (R > 0 && (!x || !scales)) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)x, (const void*)scales, (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t ws_need = dyn_ws_bytes(R);
+  if (R > 0 && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
+  if (overlaps(scales, (size_t)nblocks(R) * 4, x, (size_t)R * C * 2)) return GMM_ERR_ALIAS;
+  if (R == 0) return GMM_OK;
+  DynWs w = carve(workspace, R);
+  return launch_dynamic_scales(format, x, R, C, w.partial, scales, (hipStream_t)stream) == hipSuccess
+             ? GMM_OK : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_quantize_rhs(int32_t format, int32_t channel_axis, int32_t layout, int64_t G,
+                              int64_t K, int64_t N, const void* w, uint8_t* codes,
+                              float* scales, gmm_stream_t stream) {
+  if (format != GMM_FP8_E4M3 && format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (channel_axis != 0 && channel_axis != 1) return GMM_ERR_RECIPE;
+  if (layout != GMM_RHS_KN && layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  gmm_status_t s = check_shape(0, K, N, (int32_t)std::min<int64_t>(G, GMM_MAX_GROUPS + 1));
+  if (s != GMM_OK || G < 1 || G > 65535) return GMM_ERR_SHAPE;
+  if (!w || !codes || !scales) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)w, (const void*)codes, (const void*)scales})
+    if (!aligned16(ptr)) return GMM_ERR_ALIGN;
+  if (overlaps(codes, (size_t)G * K * N, w, (size_t)G * K * N * 2) ||
+      overlaps(scales, (size_t)G * (channel_axis ? K : N) * 4, w, (size_t)G * K * N * 2) ||
+      overlaps(scales, (size_t)G * (channel_axis ? K : N) * 4, codes, (size_t)G * K * N))
+    return GMM_ERR_ALIAS;
+  return launch_quantize_rhs(format, channel_axis, layout == GMM_RHS_NK, G, K, N, w, codes,
+                             scales, (hipStream_t)stream) == hipSuccess
+             ? GMM_OK : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_static_scale_from_bound(float lo, float hi, int32_t format, float* scale) {
+  if (!scale) return GMM_ERR_NULL;
+  if (format != GMM_FP8_E4M3 && format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (!std::isfinite(lo) || !std::isfinite(hi) || !(hi > 0.0f) || lo != -hi) return GMM_ERR_SCALE;
+  const float s = hi / (format == GMM_FP8_E4M3 ? 448.0f : 57344.0f);
+  if (!(s >= FLT_MIN)) return GMM_ERR_SCALE;
+  *scale = s;
+  return GMM_OK;
+}
+
+const char* gmm_status_string(gmm_status_t s) {
+  switch (s) {
+    case GMM_OK: return "ok";
+    case GMM_ERR_NULL: return "a required pointer is NULL";
+    case GMM_ERR_SHAPE: return "invalid shape (M, K, N or G)";
+    case GMM_ERR_SCALE: return "invalid static scale or calibration range";
+    case GMM_ERR_RECIPE: return "unsupported quantization recipe";
+    case GMM_ERR_WORKSPACE: return "workspace missing or too small";
+    case GMM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GMM_ERR_GROUP_SIZES: return "group sizes negative or not summing to M";
+    case GMM_ERR_HIP: return "HIP runtime error";
+    case GMM_ERR_ALIAS: return "an output overlaps an input";
+  }
+  return "unknown status";
+}
+
+const char* gmm_version(void) { return "gmm_fp8 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Shared device helpers of the gfx950 FP8 grouped matmul kernels.
+//
+// Nothing here is used by the CPU oracle; the oracle and these kernels share no code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmm {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef int32_t v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// fp8 format selectors: the value is also the MFMA operand-format code of gfx950's
+// V_MFMA_*_F8F6F4 instructions (0 = E4M3, 1 = E5M2).
+enum : int { FMT_E4M3 = 0, FMT_E5M2 = 1 };
+
+template <int FMT>
+__device__ __host__ constexpr float qmax() {
+  return FMT == FMT_E4M3 ? 448.0f : 57344.0f;
+}
+
+constexpr int BLOCK_ROWS = 128;  // rows per dynamic-scale block
+constexpr int TILE_K = 128;      // contraction bytes per LDS row (one fp8 k-step)
+
+// ---------------------------------------------------------------------------------
+// Buffer resources: range-checked loads.  A lane whose byte offset lies beyond
+// num_records reads zeros without touching memory, which is how rows past the end of
+// a group (or past the last output channel) become zero operands.
+// ---------------------------------------------------------------------------------
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline v4u buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------
+// LDS tile layout: a tile is [rows][128 bytes] of fp8 codes, the contraction axis
+// contiguous.  16-byte chunk c of row r is stored at chunk position
+// c ^ (r & 7) ^ ((r >> 3) & 7): the eight rows an MFMA fragment read touches together
+// land in eight different chunk positions, and so do the rows one transposing store
+// touches together.
+// ---------------------------------------------------------------------------------
+__device__ inline uint32_t tile_off(uint32_t row, uint32_t chunk) {
+  return row * TILE_K + ((chunk ^ (row & 7u) ^ ((row >> 3) & 7u)) << 4);
+}
+
+// ---------------------------------------------------------------------------------
+// In-register quantization: code = fp8(clamp(RNE_f32(x * inv), -qmax, qmax)), RNE.
+// The multiply is an explicit round-to-nearest fp32 multiply (never fused), the clamp
+// is a median of three, and the conversion is gfx950's V_CVT_PK_{FP8,BF8}_F32
+// (round to nearest even, OCP encodings).
+// ---------------------------------------------------------------------------------
+template <int FMT>
+__device__ inline float quant_prep(float x, float inv) {
+  float y = __fmul_rn(x, inv);
+  return __builtin_amdgcn_fmed3f(y, -qmax<FMT>(), qmax<FMT>());
+}
+
+// Packs two codes into bytes 0-1 (HI == false) or 2-3 (HI == true) of `old`.
+template <int FMT, bool HI>
+__device__ inline uint32_t cvt_pk(float a, float b, uint32_t old) {
+  if constexpr (FMT == FMT_E4M3)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
+}
+
+// Inverse of a dynamic scale: RNE_f32(1/s), or 0 when s == 0 or 1/s is not finite.
+__device__ inline float inv_from_scale(float s) {
+  const float r = __fdiv_rn(1.0f, s);
+  return (s == 0.0f || !__builtin_isfinite(r)) ? 0.0f : r;
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 4 packed bf16 pairs (8 values, one 16-byte load) -> 8 fp8 codes (2 dwords).
+template <int FMT>
+__device__ inline v2u quant8(v4u w, float inv) {
+  v2u r;
+  uint32_t d0 = cvt_pk<FMT, false>(quant_prep<FMT>(bf16_lo(w.x), inv), quant_prep<FMT>(bf16_hi(w.x), inv), 0u);
+  d0 = cvt_pk<FMT, true>(quant_prep<FMT>(bf16_lo(w.y), inv), quant_prep<FMT>(bf16_hi(w.y), inv), d0);
+  uint32_t d1 = cvt_pk<FMT, false>(quant_prep<FMT>(bf16_lo(w.z), inv), quant_prep<FMT>(bf16_hi(w.z), inv), 0u);
+  d1 = cvt_pk<FMT, true>(quant_prep<FMT>(bf16_lo(w.w), inv), quant_prep<FMT>(bf16_hi(w.w), inv), d1);
+  r.x = d0;
+  r.y = d1;
+  return r;
+}
+
+// float -> bf16 bits, round to nearest even (inputs are finite or +-inf).
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA: D[32x32] += A[32x64] * B[64x32], fp8/bf8 operands, fp32 accumulation.  Lane l
+// holds row (l % 32) of A and column (l % 32) of B, 32 contraction bytes each; the
+// two operands use the same contraction order, so any consistent assignment of the
+// 64 contraction bytes to (lane half, byte) gives the same sum.  The result lane l,
+// register r is D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+// ---------------------------------------------------------------------------------
+template <int FMT_A, int FMT_B>
+__device__ inline v16f mfma32x32x64(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT_A, FMT_B, 0, 0, 0, 0);
+}
+
+__device__ inline v8i lds_read_frag(const uint8_t* lds, uint32_t row, uint32_t chunk0) {
+  v4u lo = *reinterpret_cast<const v4u*>(lds + tile_off(row, chunk0));
+  v4u hi = *reinterpret_cast<const v4u*>(lds + tile_off(row, chunk0 + 1));
+  v8i f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+// ---------------------------------------------------------------------------------
+// Wave-level inclusive prefix sum (64 lanes).
+// ---------------------------------------------------------------------------------
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+}  // namespace gmm

@@ -1,0 +1,57 @@
+// Kernel launch interface shared by the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace gmm {
+
+constexpr int AMAX_SPLIT = 8;    // row slices per 128-row block in the abs-max prepass
+constexpr int MAX_GROUPS = 1024;
+
+// Grouped GEMM: out[M, Nout] = A[M, Kc] x B(g) for the rows of group g.
+// B is either "contraction-contiguous" codes [G, Nout, Kc] (b_trans == 0) or
+// "output-contiguous" codes [G, Kc, Nout] (b_trans == 1).
+struct GemmParams {
+  const void* a;             // bf16 values or fp8 codes, [M, Kc]
+  const uint8_t* b;          // fp8 codes
+  const float* b_scale;      // [G, Nout], per output channel
+  const int32_t* group_sizes;
+  void* out;                 // [M, Nout] bf16 or f32
+  const float* a_scale_blk;  // dynamic: per-block scale (inverse derived in-kernel); else null
+  float a_inv_static;
+  float a_scale_static;
+  int64_t M;
+  int32_t Kc, Nout, G;
+  int32_t out_f32;
+};
+
+// tgmm: out[g] = A_g^T [Kout, m] x B_g [m, Nout], contraction over the rows of group g.
+struct TgmmParams {
+  const uint16_t* a;         // bf16 [M, Kout]
+  const uint16_t* b;         // bf16 [M, Nout]
+  const int32_t* group_sizes;
+  void* out;                 // [G, Kout, Nout] bf16 or f32
+  const float* a_scale_blk;  // dynamic: per-block scales; null -> static
+  const float* b_scale_blk;
+  float a_inv_static, a_scale_static, b_inv_static, b_scale_static;
+  int64_t M;
+  int32_t Kout, Nout, G;
+  int32_t out_f32;
+};
+
+hipError_t launch_gemm(int a_fmt, int b_fmt, bool a_fp8, bool b_trans, const GemmParams& p,
+                       hipStream_t st);
+hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st);
+hipError_t launch_dynamic_scales(int fmt, const void* x, int64_t R, int64_t C,
+                                 uint32_t* partial, float* scales_out, hipStream_t st);
+hipError_t launch_quantize_rows(int fmt, const void* x, int64_t R, int64_t C,
+                                const float* scale_blk, float inv_static, uint8_t* codes,
+                                hipStream_t st);
+hipError_t launch_quantize_rhs(int fmt, int axis, int layout_nk, int64_t G, int64_t K,
+                               int64_t N, const void* w, uint8_t* codes, float* scales,
+                               hipStream_t st);
+
+}  // namespace gmm

@@ -1,0 +1,241 @@
+/*
+ * gmm_fp8.h - C ABI of the MI355X (gfx950) FP8 grouped (ragged) matmul library.
+ *
+ * The library implements the three products of an MoE expert layer with FP8 operands
+ * and fp32 accumulation, as described on the MaxText pull-request pages
+ *   "FP8 Megablox for batch split" (PR #3770),
+ *   "Support quantization for tokamax gmm v2" (PR #4451) and
+ *   "add static LHS scaling support for GMM v2 FWD" (PR #4735):
+ *
+ *   gmm_fwd    out[m, :]   = lhs[m, :] . rhs[g]          for every row m of group g
+ *   gmm_dlhs   dlhs[m, :]  = grad[m, :] . rhs[g]^T       (the gmm against rhs transposed)
+ *   tgmm_drhs  drhs[g]     = lhs_g^T . grad_g            (one [K, N] slab per group)
+ *
+ * Rows of lhs / grad are sorted by group: group g owns rows [off_g, off_g + m_g) with
+ * off_0 = 0 and off_{g+1} = off_g + m_g, m_g = group_sizes[g].
+ *
+ * Common conventions
+ * ------------------
+ * - Every pointer argument is DEVICE memory owned by the caller, unless marked "host".
+ *   The library never allocates, frees or synchronises; all work is enqueued on the
+ *   caller's HIP stream and the call returns as soon as it is enqueued.
+ * - Tensors are dense, row-major (last index contiguous), 16-byte aligned.
+ * - bf16 is IEEE bfloat16 (stored as uint16); fp8 codes are OCP E4M3FN or E5M2 bytes.
+ * - group_sizes is int32 [G] in device memory and is never read by the host: the
+ *   caller guarantees m_g >= 0 and sum(m_g) == M (checked only when the environment
+ *   variable GMM_CHECK=1 is set, which synchronises the stream).
+ * - Shapes: M >= 0, 1 <= G <= GMM_MAX_GROUPS, K and N positive multiples of 128.
+ * - Inputs are read-only; outputs must not overlap inputs.
+ * - Errors are returned as gmm_status_t; argument validation happens before any work
+ *   is enqueued, so an error return leaves every output untouched.
+ * - The functions keep no global state and may be called concurrently on different
+ *   streams with different buffers.
+ *
+ * Quantization recipes
+ * --------------------
+ * An operand given as bf16 is quantized inside the kernel, in registers, right after
+ * it is loaded:  code = fp8( clamp( RNE_f32(x * inv), -qmax, +qmax ) )  with
+ * round-to-nearest-even to fp8 (qmax = 448 for e4m3, 57344 for e5m2), and the fp32
+ * product is multiplied back by the scale ("add static LHS scaling support for GMM v2
+ * FWD", review thread on the lhs docstring: clip(lhs/scale), result multiplied back by
+ * the scale).  The scale s and inv are:
+ *   GMM_SCALE_STATIC   one per-tensor scale s (the [1,1] scale of that page, derived
+ *                      from a fixed symmetric calibration range, see
+ *                      gmm_static_scale_from_bound); inv = RNE_f32(1/s).
+ *   GMM_SCALE_DYNAMIC  one scale per block of 128 consecutive rows spanning the full
+ *                      row width, blocks aligned to row 0 of the tensor:
+ *                      s_b = RNE_f32(amax_b / qmax); inv_b = 0 when s_b == 0 or 1/s_b
+ *                      overflows, else RNE_f32(1/s_b) (same page, review thread on
+ *                      block_scale_inv: zero inverse for a zero scale).  The call
+ *                      computes the scales with an abs-max prepass over the operand.
+ *   GMM_SCALE_DYNAMIC_GIVEN  the same per-block recipe with the scales s_b supplied by
+ *                      the caller (from gmm_dynamic_scales, or returned by an earlier
+ *                      call on the same tensor); the prepass is skipped and inv_b is
+ *                      derived from s_b in the kernel by the rule above.
+ * An operand given as fp8 codes (GMM_OPERAND_FP8) was quantized beforehand with the
+ * same formulas (the pre-quantized activation case of the same page's follow-up
+ * commits); its scales are then an input.
+ * The rhs of gmm_fwd / gmm_dlhs is always fp8 codes with one scale per output channel
+ * ("FP8 Megablox for batch split", Description (1): manually quantized weight;
+ * "Support quantization for tokamax gmm v2", review thread on per-channel scales).
+ */
+#ifndef GMM_FP8_H
+#define GMM_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque HIP stream (hipStream_t); NULL is the default stream. */
+typedef struct ihipStream_t* gmm_stream_t;
+
+#define GMM_BLOCK_ROWS 128   /* rows per dynamic-scale block */
+#define GMM_MAX_GROUPS 1024  /* largest supported number of groups (experts) */
+
+typedef enum gmm_status {
+  GMM_OK = 0,
+  GMM_ERR_NULL = 1,        /* a required pointer is NULL */
+  GMM_ERR_SHAPE = 2,       /* bad M, K, N or G */
+  GMM_ERR_SCALE = 3,       /* static scale not finite, positive and normal; asymmetric range */
+  GMM_ERR_RECIPE = 4,      /* unknown or unsupported format / scaling / kind / layout / dtype */
+  GMM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than gmm_workspace_size() */
+  GMM_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+  GMM_ERR_GROUP_SIZES = 7, /* GMM_CHECK=1 only: a negative size or sum != M */
+  GMM_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed */
+  GMM_ERR_ALIAS = 9        /* an output buffer overlaps an input buffer */
+} gmm_status_t;
+
+typedef enum gmm_fp8_format { GMM_FP8_E4M3 = 0, GMM_FP8_E5M2 = 1 } gmm_fp8_format_t;
+/* GMM_SCALE_DYNAMIC_GIVEN: dynamic per-block scales that were computed beforehand (by
+ * gmm_dynamic_scales or by an earlier call on the same tensor) and are passed in, so
+ * that a tensor used by several products has its block scales computed once. */
+typedef enum gmm_scaling {
+  GMM_SCALE_STATIC = 0,
+  GMM_SCALE_DYNAMIC = 1,
+  GMM_SCALE_DYNAMIC_GIVEN = 2
+} gmm_scaling_t;
+typedef enum gmm_operand_kind { GMM_OPERAND_BF16 = 0, GMM_OPERAND_FP8 = 1 } gmm_operand_kind_t;
+typedef enum gmm_out_dtype { GMM_OUT_BF16 = 0, GMM_OUT_F32 = 1 } gmm_out_dtype_t;
+
+/* Physical layout of the rhs codes of gmm_fwd / gmm_dlhs (logical shape [G, K, N]).
+ * GMM_RHS_KN: [G, K, N], N contiguous (the layout of the weight itself).
+ * GMM_RHS_NK: [G, N, K], K contiguous (the weight stored transposed, the pages'
+ *             transpose_rhs).  Both layouts are supported by both calls; the kernel
+ *             is fastest when the contraction axis is contiguous: NK for gmm_fwd, KN
+ *             for gmm_dlhs. */
+typedef enum gmm_rhs_layout { GMM_RHS_KN = 0, GMM_RHS_NK = 1 } gmm_rhs_layout_t;
+
+/* How one operand reaches the kernel and how it is scaled. */
+typedef struct gmm_operand {
+  int32_t kind;         /* gmm_operand_kind_t */
+  int32_t format;       /* gmm_fp8_format_t */
+  int32_t scaling;      /* gmm_scaling_t */
+  float static_scale;   /* GMM_SCALE_STATIC: the per-tensor scale s (finite, > 0, normal) */
+} gmm_operand_t;
+
+/* Operation identifiers for gmm_workspace_size. */
+typedef enum gmm_op { GMM_OP_FWD = 0, GMM_OP_DLHS = 1, GMM_OP_TGMM = 2 } gmm_op_t;
+
+/*
+ * gmm_fwd - forward grouped matmul ("FP8 Megablox for batch split", Description (1);
+ * "Support quantization for tokamax gmm v2", What this does: fwd_gmm2).
+ *
+ *   out[m, n] = RNE_out( (sum_k q(lhs)[m, k] * rhs[g, k, n]) * s_lhs(m) * rhs_scales[g, n] )
+ *
+ * lhs          [M, K]: bf16 values (lhs_op->kind == GMM_OPERAND_BF16) or fp8 codes.
+ * lhs_scales   f32 [ceil(M/128)].  DYNAMIC + BF16: OUTPUT, the block scales the call
+ *              computed (may be NULL).  DYNAMIC_GIVEN, or DYNAMIC + FP8: INPUT, the block
+ *              scales of the operand.  STATIC: unused (may be NULL); s_lhs is
+ *              lhs_op->static_scale.
+ * rhs          fp8 codes, layout rhs_layout, format rhs_format.
+ * rhs_scales   f32 [G, N]: the dequantization scale of every output channel n.
+ * group_sizes  int32 [G].
+ * out          [M, N], bf16 or f32 per out_dtype.  Every row is written exactly once.
+ * workspace    device scratch of gmm_workspace_size(GMM_OP_FWD, ...) bytes (may be NULL
+ *              when that size is 0); its contents are undefined after the call.
+ * Merged gate|up: pass rhs = concat(W0, W1) along N with concatenated scales; one call
+ * produces [gate | up] ("FP8 Megablox for batch split", Description (2)).
+ */
+gmm_status_t gmm_fwd(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                     int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                     const void* lhs, float* lhs_scales, const uint8_t* rhs,
+                     const float* rhs_scales, const int32_t* group_sizes, void* out,
+                     void* workspace, size_t workspace_bytes, gmm_stream_t stream);
+
+/*
+ * gmm_dlhs - lhs gradient: a gmm of grad against rhs transposed ("Support quantization
+ * for tokamax gmm v2", review of the dlhs call in ops.py: transpose_rhs flipped).
+ *
+ *   dlhs[m, k] = RNE_out( (sum_n q(grad)[m, n] * rhs[g, k, n]) * s_grad(m) * rhs_scales[g, k] )
+ *
+ * grad         [M, N]: bf16 values or fp8 codes (grad_op).  grad_scales as lhs_scales
+ *              of gmm_fwd.
+ * rhs          the same logical [G, K, N] weight as gmm_fwd, quantized per dlhs output
+ *              channel k: rhs_scales f32 [G, K].
+ * dlhs         [M, K] bf16 or f32.
+ */
+gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
+                      int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                      const void* grad, float* grad_scales, const uint8_t* rhs,
+                      const float* rhs_scales, const int32_t* group_sizes, void* dlhs,
+                      void* workspace, size_t workspace_bytes, gmm_stream_t stream);
+
+/*
+ * tgmm_drhs - weight gradient, the transposed grouped matmul ("Support quantization for
+ * tokamax gmm v2", What this does: drhs_tgmm2).
+ *
+ *   drhs[g, k, n] = sum over 128-row blocks c meeting group g of
+ *                   RNE( (sum_{m in c, m in g} q(lhs)[m, k] q(grad)[m, n]) * RNE(s_lhs[c] s_grad[c]) )
+ *
+ * lhs [M, K] and grad [M, N] are bf16, each quantized in-kernel by its own recipe
+ * (lhs_op, grad_op; kind must be GMM_OPERAND_BF16; DYNAMIC_GIVEN reuses the block scales
+ * of the forward / dlhs calls on the same tensors).  Because a dynamic scale changes
+ * every 128 rows, the contraction over rows is split at block boundaries and each
+ * block's partial sum is scaled before it is added.  lhs_scales / grad_scales: as
+ * gmm_fwd's lhs_scales (outputs for DYNAMIC, may be NULL).
+ * drhs [G, K, N] bf16 or f32.  A group with m_g == 0 gets a slab of +0.0.
+ */
+gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
+                       int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                       const void* lhs, float* lhs_scales, const void* grad,
+                       float* grad_scales, const int32_t* group_sizes, void* drhs,
+                       void* workspace, size_t workspace_bytes, gmm_stream_t stream);
+
+/* Bytes of device workspace the call `op` needs for these operands and sizes (0 when
+ * no operand is quantized dynamically in-kernel).  For GMM_OP_FWD / GMM_OP_DLHS, `a`
+ * is the lhs / grad operand and `b` is ignored; for GMM_OP_TGMM, `a` is the lhs and
+ * `b` the grad.  `rows` is M, `cols_a` / `cols_b` the row widths (K, N).
+ * Returns 0 and sets *bytes. */
+gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_operand_t* b,
+                                int64_t rows, int64_t cols_a, int64_t cols_b, size_t* bytes);
+
+/*
+ * gmm_dynamic_scales - the abs-max prepass alone: per-block scales of a bf16 matrix
+ * [R, C] for the DYNAMIC recipe of `format`, scales f32 [ceil(R/128)] (output).
+ * workspace: gmm_workspace_size(GMM_OP_FWD, op{BF16, format, DYNAMIC}, NULL, R, C, 0).
+ */
+gmm_status_t gmm_dynamic_scales(int32_t format, int64_t R, int64_t C, const void* x,
+                                float* scales, void* workspace, size_t workspace_bytes,
+                                gmm_stream_t stream);
+
+/*
+ * gmm_quantize - stand-alone quantization of a bf16 matrix [R, C] into fp8 codes with the
+ * static or dynamic recipe above (codes [R, C]; scales f32 [ceil(R/128)]: output for
+ * DYNAMIC, input for DYNAMIC_GIVEN, unused for STATIC).  The codes are byte-identical to those the fused
+ * kernels form in registers.  Used for the pre-quantized-operand path (hybrid dlhs).
+ * workspace: gmm_workspace_size(GMM_OP_FWD, op, NULL, R, C, 0, &bytes).
+ */
+gmm_status_t gmm_quantize(const gmm_operand_t* op, int64_t R, int64_t C, const void* x,
+                          uint8_t* codes, float* scales, void* workspace,
+                          size_t workspace_bytes, gmm_stream_t stream);
+
+/*
+ * gmm_quantize_rhs - per-channel quantization of a bf16 weight w [G, K, N] ("FP8
+ * Megablox for batch split", Description (1): the weight is quantized manually).
+ *   channel_axis 0 -> one scale per (g, n), abs-max over k: scales [G, N]  (gmm_fwd)
+ *   channel_axis 1 -> one scale per (g, k), abs-max over n: scales [G, K]  (gmm_dlhs)
+ * s = RNE_f32(amax / qmax), inv = 0 if s == 0 or 1/s overflows else RNE_f32(1/s),
+ * code = fp8(clamp(RNE_f32(w * inv), +-qmax)).  Codes are written in `layout`.
+ */
+gmm_status_t gmm_quantize_rhs(int32_t format, int32_t channel_axis, int32_t layout, int64_t G,
+                              int64_t K, int64_t N, const void* w, uint8_t* codes,
+                              float* scales, gmm_stream_t stream);
+
+/* Host: per-tensor scale from a fixed calibration range [lo, hi]: requires lo == -hi > 0
+ * (asymmetric ranges are rejected, "add static LHS scaling support for GMM v2 FWD",
+ * review thread on the helper's docstring); *scale = RNE_f32(hi / qmax(format)). */
+gmm_status_t gmm_static_scale_from_bound(float lo, float hi, int32_t format, float* scale);
+
+/* Host: static text for a status code. */
+const char* gmm_status_string(gmm_status_t status);
+
+/* Host: library version string. */
+const char* gmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GMM_FP8_H */

@@ -30,3 +30,11 @@ def lib():
 
     g.load()  # raises if the shared library is missing: no fallback
     return g
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stdout (flushed) before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield

@@ -1,0 +1,144 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, its host-only
+functions work, and every validation error is reported before any work is enqueued."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp8_grouped_gemm_ragged_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gmm_fp8.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(g.library_path()),
+                                reason="libgmm_fp8.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = g.load()
+    names = declared_functions()
+    assert {"gmm_fwd", "gmm_dlhs", "tgmm_drhs", "gmm_quantize", "gmm_quantize_rhs"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(g.EXPORTED)
+
+
+def test_host_helpers():
+    assert "gfx950" in g.gmm_version()
+    assert g.gmm_status_string(0) == "ok"
+    s = g.gmm_static_scale_from_bound(-4.0, 4.0, "e4m3")
+    assert np.float32(s).view(np.uint32) == 0x3C124925  # RNE_f32(4/448), hand-derived
+    assert g.gmm_static_scale_from_bound(-57344.0, 57344.0, "e5m2") == 1.0
+    for lo, hi in [(-3.0, 4.0), (0.0, 0.0), (4.0, -4.0), (-np.inf, np.inf), (-1e-40, 1e-40)]:
+        with pytest.raises(g.GmmError) as e:
+            g.gmm_static_scale_from_bound(lo, hi, "e4m3")
+        assert e.value.status == 3  # GMM_ERR_SCALE
+
+
+def test_workspace_sizes():
+    assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "static", 1000) == 0
+    n = g.gmm_workspace_size(g.OP_FWD, "e4m3", "dynamic", 1000)
+    nb = 8
+    assert n >= nb * (8 + 2) * 4 and n % 256 == 0
+    t = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "dynamic", 1000, b_fmt="e5m2", b_scaling="dynamic")
+    assert t == 2 * n
+    assert g.gmm_workspace_size(g.OP_TGMM, "e4m3", "static", 1000, b_scaling="static",
+                                static_scale=0.5) == 0
+
+
+# ---- validation: fake but aligned device pointers; nothing is dereferenced -------------
+FAKE = 0x7F0000000000
+
+
+def ptr(i):
+    return ctypes.c_void_p(FAKE + i * (1 << 32))
+
+
+def op(kind=0, fmt=0, scaling=1, s=0.0):
+    return g.Operand(kind, fmt, scaling, s)
+
+
+def call_fwd(o=None, rhs_format=0, layout=1, out_dtype=0, M=256, K=256, N=256, G=4, lhs=1,
+             lhs_scales=2, rhs=3, rhs_scales=4, gs=5, out=6, ws=7, ws_bytes=1 << 20):
+    lib = g.load()
+    o = o or op()
+    P = lambda i: None if i is None else (ptr(i) if isinstance(i, int) else i)
+    return lib.gmm_fwd(ctypes.byref(o), rhs_format, layout, out_dtype, M, K, N, G, P(lhs),
+                       P(lhs_scales), P(rhs), P(rhs_scales), P(gs), P(out), P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), 2), (dict(N=64), 2), (dict(K=0), 2), (dict(M=-1), 2), (dict(G=0), 2),
+    (dict(G=1025), 2), (dict(K=1 << 23), 2),
+    (dict(rhs_format=1), 4), (dict(layout=7), 4), (dict(out_dtype=5), 4),
+    (dict(o=op(kind=3)), 4), (dict(o=op(fmt=2)), 4), (dict(o=op(scaling=9)), 4),
+    (dict(o=op(scaling=0, s=0.0)), 3), (dict(o=op(scaling=0, s=-1.0)), 3),
+    (dict(o=op(scaling=0, s=float("nan"))), 3), (dict(o=op(scaling=0, s=1e-40)), 3),
+    (dict(rhs=None), 1), (dict(gs=None), 1), (dict(lhs=None), 1), (dict(out=None), 1),
+    (dict(rhs_scales=None), 1), (dict(o=op(kind=1, scaling=1), lhs_scales=None), 1),
+    (dict(ws=None), 5), (dict(ws_bytes=16), 5),
+    (dict(lhs=ctypes.c_void_p(FAKE + 8)), 6),
+    (dict(out=1), 9), (dict(ws=6, out=6), 9),
+])
+def test_fwd_validation_errors(kw, status):
+    assert call_fwd(**kw) == status
+
+
+def test_fwd_empty_problem_is_ok_without_gpu():
+    # M == 0: validated, nothing to enqueue
+    assert call_fwd(M=0) == 0
+
+
+def test_dlhs_and_tgmm_validation():
+    lib = g.load()
+    o = op(fmt=1)
+    assert lib.gmm_dlhs(ctypes.byref(o), 0, 0, 0, 256, 200, 256, 2, ptr(1), ptr(2), ptr(3),
+                        ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20, None) == 2
+    a, b = op(fmt=0), op(fmt=1)
+    pre = op(kind=1)
+    assert lib.tgmm_drhs(ctypes.byref(pre), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
+                         ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20, None) == 4
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
+                         ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 64, None) == 5
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
+                         ptr(3), ptr(4), ptr(5), ptr(1), ptr(7), 1 << 20, None) == 9  # drhs aliases lhs
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
+                         ptr(3), ptr(4), None, ptr(6), ptr(7), 1 << 20, None) == 1
+
+
+def test_given_scales_validation():
+    lib = g.load()
+    given = op(scaling=2)
+    # DYNAMIC_GIVEN: scales are an input (NULL rejected) and no workspace is needed
+    assert call_fwd(o=given, lhs_scales=None) == 1
+    assert call_fwd(o=given, ws=None, ws_bytes=0, M=0) == 0
+    n = ctypes.c_size_t()
+    assert lib.gmm_workspace_size(0, ctypes.byref(given), ctypes.byref(given), 1000, 256, 0, ctypes.byref(n)) == 0
+    assert n.value == 0
+    a, b = op(fmt=0, scaling=2), op(fmt=1, scaling=2)
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), None,
+                         ptr(3), ptr(4), ptr(5), ptr(6), None, 0, None) == 1
+    assert lib.gmm_dynamic_scales(0, 100, 12, ptr(1), ptr(2), ptr(3), 1 << 20, None) == 2
+    assert lib.gmm_dynamic_scales(2, 100, 16, ptr(1), ptr(2), ptr(3), 1 << 20, None) == 4
+    assert lib.gmm_dynamic_scales(0, 100, 16, ptr(1), ptr(2), None, 0, None) == 5
+    assert lib.gmm_dynamic_scales(0, 0, 16, None, None, None, 0, None) == 0
+
+
+def test_quantize_validation():
+    lib = g.load()
+    o = op()
+    assert lib.gmm_quantize(ctypes.byref(o), 100, 12, ptr(1), ptr(2), ptr(3), ptr(4), 1 << 20, None) == 2
+    assert lib.gmm_quantize(ctypes.byref(op(kind=1)), 100, 16, ptr(1), ptr(2), ptr(3), ptr(4), 1 << 20, None) == 4
+    assert lib.gmm_quantize(ctypes.byref(o), 100, 16, ptr(1), ptr(2), ptr(3), None, 0, None) == 5
+    assert lib.gmm_quantize_rhs(0, 2, 0, 2, 128, 128, ptr(1), ptr(2), ptr(3), None) == 4
+    assert lib.gmm_quantize_rhs(0, 0, 0, 2, 100, 128, ptr(1), ptr(2), ptr(3), None) == 2
+    assert lib.gmm_quantize_rhs(0, 0, 0, 2, 128, 128, None, ptr(2), ptr(3), None) == 1

@@ -1,0 +1,218 @@
+"""GPU parity of gmm_fwd and gmm_dlhs against the oracle (same bf16 inputs, own quantization)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ops as ops
+from oracle.gmm import gmm_fwd_ref
+from oracle.quant import quantize_rhs_per_channel
+from synth.workloads import WORKLOADS
+from tests.gpu_util import DEV, channel_varied, gen, gs_tensor, sync
+from tests.parity import (
+    TOL,
+    assert_bf16_close,
+    group_rel_err,
+    group_row_ranges,
+    to_np,
+)
+
+pytestmark = pytest.mark.gpu
+
+S_4_448 = float(np.float32(4.0) / np.float32(448.0))
+
+
+def quantized_weight(lib, w, axis, layout):
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", axis, layout)
+    return codes, scales
+
+
+def run_fwd(lib, x, xbits, w, wbits, sizes, scaling, layout, out_dtype, s=S_4_448):
+    codes, scales = quantized_weight(lib, w, 0, layout)
+    c_ref, s_ref = quantize_rhs_per_channel(wbits, "e4m3", "n")
+    assert np.array_equal(to_np(scales).view(np.uint32), s_ref.view(np.uint32))
+    out, sc = lib.gmm_fwd(x, codes, scales, gs_tensor(sizes), lhs_format="e4m3",
+                          lhs_scaling=scaling, static_scale=s, rhs_layout=layout,
+                          out_dtype=out_dtype, return_scales=True)
+    R, _, s_blk = ops.fwd(xbits, c_ref, s_ref, np.asarray(sizes), "e4m3", scaling,
+                          np.float32(s), "e4m3", "f32")
+    if scaling == "dynamic":
+        assert np.array_equal(to_np(sc).view(np.uint32), s_blk.view(np.uint32))
+    return to_np(out), R
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fwd_tiny_workload(lib, out_dtype):
+    wl = WORKLOADS["tiny"]
+    sizes = wl.group_sizes()
+    assert sizes[1] == 0 and sizes.sum() == wl.M
+    x, xb = gen((wl.M, wl.K), 1.0, 101)
+    w, wb = gen((wl.G, wl.K, wl.N), 0.02, 102)
+    Y, R = run_fwd(lib, x, xb, w, wb, sizes, "static", "nk", out_dtype)
+    if out_dtype == torch.float32:
+        assert group_rel_err(Y, R, group_row_ranges(sizes)) <= TOL
+    else:
+        assert_bf16_close(Y, R, group_row_ranges(sizes))
+
+
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("scaling", ["static", "dynamic"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fwd_ragged_medium(lib, layout, scaling, out_dtype):
+    # several M-tiles per group, ragged group ends, empty groups first and in the middle,
+    # and an N tail (640 = 2.5 tiles of 256)
+    sizes = [0, 700, 1, 0, 299, 500]
+    M, K, N = sum(sizes), 512, 640
+    x, xb = gen((M, K), 1.0, 111)
+    w, wb = channel_varied((len(sizes), K, N), 0.02, 112, 2)
+    Y, R = run_fwd(lib, x, xb, w, wb, sizes, scaling, layout, out_dtype)
+    if out_dtype == torch.float32:
+        err = group_rel_err(Y, R, group_row_ranges(sizes))
+        print(f"max group relative error {err:.3e}")
+        assert err <= TOL, err
+    else:
+        assert_bf16_close(Y, R, group_row_ranges(sizes))
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dlhs_ragged_medium(lib, layout, out_dtype):
+    sizes = [257, 0, 511, 128, 104]
+    M, K, N = sum(sizes), 640, 384
+    gr, gb = gen((M, N), 1e-3, 121)
+    w, wb = channel_varied((len(sizes), K, N), 0.02, 122, 1)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 1, layout)
+    c_ref, s_ref = quantize_rhs_per_channel(wb, "e4m3", "k")
+    assert np.array_equal(to_np(scales).view(np.uint32), s_ref.view(np.uint32))
+    out, sc = lib.gmm_dlhs(gr, codes, scales, gs_tensor(sizes), grad_format="e5m2",
+                           grad_scaling="dynamic", rhs_layout=layout, out_dtype=out_dtype,
+                           return_scales=True)
+    R, _, s_blk = ops.dlhs(gb, c_ref, s_ref, np.asarray(sizes))
+    assert np.array_equal(to_np(sc).view(np.uint32), s_blk.view(np.uint32))
+    Y = to_np(out)
+    if out_dtype == torch.float32:
+        err = group_rel_err(Y, R, group_row_ranges(sizes))
+        print(f"max group relative error {err:.3e}")
+        assert err <= TOL, err
+    else:
+        assert_bf16_close(Y, R, group_row_ranges(sizes))
+
+
+def test_hybrid_dlhs_equals_fused(lib):
+    """Pre-quantized grad (stand-alone quantizer) through the fp8-A kernel gives the same
+    bits as the fused in-kernel quantization."""
+    sizes = [300, 212, 0, 500]
+    M, K, N = sum(sizes), 384, 512
+    gr, _ = gen((M, N), 1e-3, 131)
+    w, _ = channel_varied((len(sizes), K, N), 0.02, 132, 1)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 1, "kn")
+    gs = gs_tensor(sizes)
+    fused = lib.gmm_dlhs(gr, codes, scales, gs, out_dtype=torch.float32)
+    gq, gsc = lib.gmm_quantize(gr, "e5m2", "dynamic")
+    hybrid = lib.gmm_dlhs(gq, codes, scales, gs, grad_scales=gsc, out_dtype=torch.float32)
+    assert torch.equal(fused.view(torch.int32), hybrid.view(torch.int32))
+
+
+def test_prequantized_static_forward_equals_fused(lib):
+    sizes = [129, 383]
+    M, K, N = sum(sizes), 256, 256
+    x, _ = gen((M, K), 1.0, 141)
+    w, _ = gen((2, K, N), 0.02, 142)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    gs = gs_tensor(sizes)
+    fused = lib.gmm_fwd(x, codes, scales, gs, lhs_scaling="static", static_scale=S_4_448,
+                        out_dtype=torch.float32)
+    xq, _ = lib.gmm_quantize(x, "e4m3", "static", S_4_448)
+    pre = lib.gmm_fwd(xq, codes, scales, gs, lhs_scaling="static", static_scale=S_4_448,
+                      out_dtype=torch.float32)
+    assert torch.equal(fused.view(torch.int32), pre.view(torch.int32))
+
+
+def test_merged_gate_up_equals_two_calls(lib):
+    sizes = [200, 0, 350]
+    M, K, Nh = sum(sizes), 256, 384
+    x, _ = gen((M, K), 1.0, 151)
+    w0, _ = gen((3, K, Nh), 0.02, 152)
+    w1, _ = gen((3, K, Nh), 0.02, 153)
+    gs = gs_tensor(sizes)
+    c, s = lib.gmm_quantize_rhs(torch.cat([w0, w1], dim=2).contiguous(), "e4m3", 0, "nk")
+    c0, s0 = lib.gmm_quantize_rhs(w0, "e4m3", 0, "nk")
+    c1, s1 = lib.gmm_quantize_rhs(w1, "e4m3", 0, "nk")
+    merged = lib.gmm_fwd(x, c, s, gs, out_dtype=torch.float32)
+    a = lib.gmm_fwd(x, c0, s0, gs, out_dtype=torch.float32)
+    b = lib.gmm_fwd(x, c1, s1, gs, out_dtype=torch.float32)
+    assert torch.equal(merged.view(torch.int32), torch.cat([a, b], 1).view(torch.int32))
+
+
+def test_rows_written_exactly_once_with_canaries(lib):
+    sizes = [0, 300, 0, 45, 211]
+    M, K, N = sum(sizes), 256, 384
+    x, _ = gen((M, K), 1.0, 161)
+    w, _ = gen((5, K, N), 0.02, 162)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    pad = 64
+    buf = torch.full(((M + 2 * pad) * N,), float("nan"), dtype=torch.float32, device=DEV)
+    out = buf[pad * N:(pad + M) * N].view(M, N)
+    lib.gmm_fwd(x, codes, scales, gs_tensor(sizes), out_dtype=torch.float32, out=out)
+    sync()
+    assert not torch.isnan(out).any()
+    assert torch.isnan(buf[:pad * N]).all() and torch.isnan(buf[(pad + M) * N:]).all()
+
+
+def compositions(M, G):
+    import itertools
+
+    for cuts in itertools.combinations(range(M + G - 1), G - 1):
+        prev, sizes = -1, []
+        for c in cuts + (M + G - 1,):
+            sizes.append(c - prev - 1)
+            prev = c
+        yield sizes
+
+
+def test_every_composition_of_nine_rows(lib):
+    K, N = 128, 128
+    x, xb = gen((9, K), 1.0, 171)
+    w, wb = gen((3, K, N), 0.02, 172)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    c_ref, s_ref = quantize_rhs_per_channel(wb, "e4m3", "n")
+    n = 0
+    for sizes in compositions(9, 3):
+        out = lib.gmm_fwd(x, codes, scales, gs_tensor(sizes), lhs_scaling="dynamic",
+                          out_dtype=torch.float32)
+        R, _, _ = ops.fwd(xb, c_ref, s_ref, np.asarray(sizes), "e4m3", "dynamic")
+        assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL, sizes
+        n += 1
+    assert n == 55
+
+
+def test_empty_and_single_group_edge_cases(lib):
+    K, N = 128, 256
+    x, xb = gen((1, K), 1.0, 181)
+    w, wb = gen((2, K, N), 0.02, 182)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "kn")
+    c_ref, s_ref = quantize_rhs_per_channel(wb, "e4m3", "n")
+    for sizes in ([1, 0], [0, 1]):
+        out = lib.gmm_fwd(x, codes, scales, gs_tensor(sizes), rhs_layout="kn", out_dtype=torch.float32)
+        R, _, _ = ops.fwd(xb, c_ref, s_ref, np.asarray(sizes), "e4m3", "dynamic")
+        assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL
+    # M == 0: nothing to do, no error
+    empty = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    out = lib.gmm_fwd(empty, codes, scales, gs_tensor([0, 0]), rhs_layout="kn")
+    assert out.shape == (0, N)
+
+
+def test_given_scales_equal_in_call_scales(lib):
+    """Block scales computed once (gmm_dynamic_scales) and passed in give the same bits."""
+    sizes = [130, 0, 400, 90]
+    M, K, N = sum(sizes), 384, 256
+    x, xb = gen((M, K), 1.0, 191)
+    w, _ = gen((4, K, N), 0.02, 192)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    gs = gs_tensor(sizes)
+    s = lib.gmm_dynamic_scales(x, "e4m3")
+    a, sa = lib.gmm_fwd(x, codes, scales, gs, out_dtype=torch.float32, return_scales=True)
+    b = lib.gmm_fwd(x, codes, scales, gs, lhs_scaling="dynamic_given", lhs_scales=s,
+                    out_dtype=torch.float32)
+    assert torch.equal(s.view(torch.int32), sa.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

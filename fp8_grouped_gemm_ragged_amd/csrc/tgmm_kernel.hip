@@ -61,10 +61,15 @@ void tgmm_kernel(TgmmParams p) {
   const int total = tiles_per_group * p.G;
   const int wg = blockIdx.x;
   if (wg >= total) return;
+  // Workgroup i runs on XCD i % 8.  Remap so each XCD owns a contiguous range of the
+  // tile order, and order tiles group-fastest: every XCD then holds an equal share of
+  // every group (the work of a tile grows with its group's row count, so a group-major
+  // order would load one XCD with the largest group), while the concurrent tiles of
+  // one XCD still cover a few neighbouring slab tiles of each group.
   const int xcd = wg & 7, jx = wg >> 3, qx = total >> 3, rx = total & 7;
   const int L = xcd * qx + min(xcd, rx) + jx;
-  const int g = L / tiles_per_group;
-  const int t = L - g * tiles_per_group;
+  const int g = L % p.G;
+  const int t = L / p.G;
   const int kt = t / n_nt, nt = t - kt * n_nt;
   const int k0 = kt * TBM, n0 = nt * TBN;
 

@@ -85,9 +85,11 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0
 template <int FMT>
 __device__ inline v2u quant8(v4u w, float inv) {
   v2u r;
-  uint32_t d0 = cvt_pk<FMT, false>(quant_prep<FMT>(bf16_lo(w.x), inv), quant_prep<FMT>(bf16_hi(w.x), inv), 0u);
+  // the first conversion of each dword writes bytes 0-1 and keeps 2-3 of its `old`
+  // operand, which the second one overwrites: any register serves as `old`
+  uint32_t d0 = cvt_pk<FMT, false>(quant_prep<FMT>(bf16_lo(w.x), inv), quant_prep<FMT>(bf16_hi(w.x), inv), w.x);
   d0 = cvt_pk<FMT, true>(quant_prep<FMT>(bf16_lo(w.y), inv), quant_prep<FMT>(bf16_hi(w.y), inv), d0);
-  uint32_t d1 = cvt_pk<FMT, false>(quant_prep<FMT>(bf16_lo(w.z), inv), quant_prep<FMT>(bf16_hi(w.z), inv), 0u);
+  uint32_t d1 = cvt_pk<FMT, false>(quant_prep<FMT>(bf16_lo(w.z), inv), quant_prep<FMT>(bf16_hi(w.z), inv), w.z);
   d1 = cvt_pk<FMT, true>(quant_prep<FMT>(bf16_lo(w.w), inv), quant_prep<FMT>(bf16_hi(w.w), inv), d1);
   r.x = d0;
   r.y = d1;

@@ -8,21 +8,23 @@
 // "Support quantization for tokamax gmm v2", the dlhs call with transpose_rhs flipped)
 // uses A = grad and B = rhs[g]^T.  Both are this one kernel with different strides.
 //
-// Work decomposition (one workgroup = one 256 x 256 output tile):
+// Work decomposition (one workgroup = one 256 x 256 output tile, 4 waves):
 //   * expert-tile scheduler: every workgroup prefix-sums group_sizes into per-group
 //     M-tile counts ceil(m_g / 256) in LDS; a tile never spans two groups, empty groups
 //     own no tile, and workgroups past the real tile count exit at once;
 //   * XCD-aware order: the hardware places workgroup i on XCD i % 8, so workgroup ids
-//     are remapped to give each XCD a contiguous range of tiles, and tiles are ordered
-//     in bands of 8 M-tiles sweeping the N-tiles, so the 32 concurrent tiles of one XCD
-//     share A rows and B columns in that XCD's L2;
-//   * K-loop over 128-byte contraction steps, double-buffered in LDS (2 x 64 KB): the
-//     next step's bf16 A tile is loaded with 16-byte range-checked buffer loads (rows
-//     past the group end read as zero), quantized in registers to fp8 and stored to a
-//     swizzled LDS tile; the fp8 B tile is copied (or transposed 8x8 in registers
-//     when B is stored output-contiguous);
-//   * 4 waves, each a 128 x 128 sub-tile of 4 x 4 MFMA 32x32x64 fp8 instructions with
-//     fp32 accumulators;
+//     are remapped to give each XCD a contiguous range of tiles, ordered in bands of 8
+//     M-tiles sweeping the N-tiles: the 32 concurrent tiles of one XCD share A rows and
+//     B columns in that XCD's L2;
+//   * K-loop over 128-byte contraction steps with two LDS stages (2 x 64 KB).  fp8
+//     operands go from HBM straight into the swizzled LDS tile with buffer_load...lds
+//     (the swizzle is realised by the per-lane global address); the bf16 A operand is
+//     prefetched two steps ahead into registers with range-checked 16-byte buffer loads
+//     (rows past the group end read as zero), quantized in registers and stored to LDS;
+//   * each wave owns a 128 x 128 sub-tile: 4 x 4 MFMA 32x32x64 fp8 instructions per
+//     64-deep half step, fp32 accumulators in AGPRs.  The loop body is one basic block
+//     and the quantization of the next step (about 14 VALU instructions per MFMA) is
+//     interleaved between the MFMAs, so vector ALU and matrix core run concurrently;
 //   * epilogue: (acc * s_A(m)) * s_B(n), RNE to bf16 (or f32), stored only for rows
 //     inside the group and columns inside N.
 #include "kernels.hpp"
@@ -38,11 +40,16 @@ constexpr int B_TILE = BN * BK;
 constexpr int STAGE = A_TILE + B_TILE;         // 64 KB
 constexpr int BAND = 8;                        // M-tiles per band of the tile order
 
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100,
+              SG_DS_WR = 0x200;
+
 struct TileCoord {
   int g, row0, row_end, n0;
 };
 
-// Expert-tile scheduler.  Returns false for a workgroup without a tile.
+// Expert-tile scheduler.  Returns false for a workgroup without a tile.  The two LDS
+// arrays alias the stage buffers: they are dead once the tile is known.
 __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int64_t M,
                                      int n_ntiles, int* s_tile_cum, int* s_row_off,
                                      TileCoord& tc) {
@@ -72,28 +79,38 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
   const int total_mt = s_tile_cum[G];
   const int total = total_mt * n_ntiles;
   const int wg = blockIdx.x;
-  if (wg >= total) return false;
-  // XCD-aware remap: workgroups of XCD x = wg % 8 take a contiguous range of tiles.
-  const int xcd = wg & 7, j = wg >> 3, q = total >> 3, r = total & 7;
-  const int L = xcd * q + min(xcd, r) + j;
-  // bands of BAND M-tiles; inside a band the M-tile index runs fastest
-  const int band = L / (BAND * n_ntiles);
-  const int rem = L - band * BAND * n_ntiles;
-  const int mt0 = band * BAND;
-  const int gm = min(BAND, total_mt - mt0);
-  const int nt = rem / gm;
-  const int mt = mt0 + (rem - nt * gm);
-  // group owning global M-tile mt: s_tile_cum[g] <= mt < s_tile_cum[g + 1]
-  int lo = 0, hi = G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_tile_cum[mid] <= mt) lo = mid; else hi = mid;
+  bool ok = wg < total;
+  if (ok) {
+    // XCD-aware remap: workgroups of XCD x = wg % 8 take a contiguous range of tiles.
+    const int xcd = wg & 7, j = wg >> 3, q = total >> 3, r = total & 7;
+    const int L = xcd * q + min(xcd, r) + j;
+    // bands of BAND M-tiles; inside a band the M-tile index runs fastest
+    const int band = L / (BAND * n_ntiles);
+    const int rem = L - band * BAND * n_ntiles;
+    const int mt0 = band * BAND;
+    const int gm = min(BAND, total_mt - mt0);
+    const int nt = rem / gm;
+    const int mt = mt0 + (rem - nt * gm);
+    // group owning global M-tile mt: s_tile_cum[g] <= mt < s_tile_cum[g + 1]
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tile_cum[mid] <= mt) lo = mid; else hi = mid;
+    }
+    tc.g = lo;
+    tc.row0 = s_row_off[lo] + (mt - s_tile_cum[lo]) * BM;
+    tc.row_end = (int)min((int64_t)s_row_off[lo + 1], M);
+    tc.n0 = nt * BN;
+    ok = tc.row0 < tc.row_end;
   }
-  tc.g = lo;
-  tc.row0 = s_row_off[lo] + (mt - s_tile_cum[lo]) * BM;
-  tc.row_end = (int)min((int64_t)s_row_off[lo + 1], M);
-  tc.n0 = nt * BN;
-  return tc.row0 < tc.row_end;
+  __syncthreads();  // the scheduler arrays alias stage memory
+  // every lane computed the same tile: make that visible to the compiler, so the buffer
+  // resources built from it live in scalar registers
+  tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+  tc.n0 = __builtin_amdgcn_readfirstlane(tc.n0);
+  return __builtin_amdgcn_readfirstlane((int)ok) != 0;
 }
 
 // 8x8 byte transpose: in[r] holds bytes (r, 0..7) as two dwords; out[c] gets bytes
@@ -119,12 +136,27 @@ __device__ inline void transpose8x8(const v2u in[8], v2u out[8]) {
   }
 }
 
+// One wave fills 8 rows (1 KB) of a swizzled [rows][128 B] tile straight from global
+// memory: lane l lands at physical chunk l % 8 of row R0 + l / 8, so it fetches the
+// logical chunk tile_off() keeps there.
+__device__ inline void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_rows,
+                                        uint32_t goff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_rows, 16, goff, 0, 0, 0);
+}
+
 template <int A_FMT, int B_FMT, bool A_FP8, bool B_TRANS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void gmm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ int s_tile_cum[MAX_GROUPS + 1];
-  __shared__ int s_row_off[MAX_GROUPS + 1];
+  // one LDS object per stage and operand, so that accesses to one stage provably do not
+  // alias the asynchronous direct loads into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_TILE];
+  int* s_tile_cum = reinterpret_cast<int*>(sA0);
+  int* s_row_off = s_tile_cum + (MAX_GROUPS + 1);
+  static_assert(2 * (MAX_GROUPS + 1) * sizeof(int) <= A_TILE, "scheduler arrays fit a tile");
 
   const int n_ntiles = (p.Nout + BN - 1) / BN;
   TileCoord tc;
@@ -149,8 +181,7 @@ void gmm_kernel(GemmParams p) {
                    (uint32_t)((int64_t)Kc * p.Nout - tc.n0));
   }
 
-  // ---- per-thread load mapping ----
-  // A: item i -> row i*32 + tid/8, 16-element (bf16) or 16-byte (fp8) chunk tid%8
+  // ---- bf16 A register mapping: piece i -> row i*32 + tid/8, 32-byte pair tid%8 ----
   const int lrow = tid >> 3, lchunk = tid & 7;
   float inv_row[8];
   if constexpr (!A_FP8) {
@@ -162,79 +193,75 @@ void gmm_kernel(GemmParams p) {
     }
   }
 
-  v4u a_reg[A_FP8 ? 8 : 16];
+  v4u a_reg[A_FP8 ? 1 : 16];
   v2u b_reg[B_TRANS ? 16 : 1];
-  v4u bt_reg[B_TRANS ? 1 : 8];
 
-  auto load_a = [&](int kt) {
-    const uint32_t kb = (uint32_t)kt * BK * AES;
+  // Direct loads of the fp8 operands of step kt into one stage: wave w fills tile rows
+  // 64w .. 64w+63, eight rows per instruction.  Physical chunk (lane & 7) of row R holds
+  // logical chunk (lane & 7) ^ (R & 7) ^ ((R >> 3) & 7).
+  auto issue_direct = [&](int kt, uint8_t* at, uint8_t* bt) {
+    const uint32_t koff = (uint32_t)kt * BK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t off = (uint32_t)(i * 32 + lrow) * Kc * AES + kb;
-      if constexpr (A_FP8) {
-        a_reg[i] = buf_load16(ra, off + lchunk * 16);
-      } else {
-        a_reg[2 * i] = buf_load16(ra, off + lchunk * 32);
-        a_reg[2 * i + 1] = buf_load16(ra, off + lchunk * 32 + 16);
+    for (int q = 0; q < 8; ++q) {
+      const int r0 = wave * 64 + q * 8;
+      const int row = r0 + (lane >> 3);
+      const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
+      const uint32_t goff = (uint32_t)row * Kc + koff + c * 16;
+      if constexpr (A_FP8) load_rows_to_lds(ra, at + r0 * BK, goff);
+      if constexpr (!B_TRANS) load_rows_to_lds(rb, bt + r0 * BK, goff);
+    }
+  };
+  // register loads of step kt: bf16 A pieces and 8x8 blocks of an output-contiguous B
+  auto load_a_piece = [&](int kt, int i) {
+    if constexpr (!A_FP8) {
+      const uint32_t off = (uint32_t)(i * 32 + lrow) * Kc * 2 + (uint32_t)kt * BK * 2 + lchunk * 32;
+      a_reg[2 * i] = buf_load16(ra, off);
+      a_reg[2 * i + 1] = buf_load16(ra, off + 16);
+    }
+  };
+  auto load_b_block = [&](int kt, int it) {
+    if constexpr (B_TRANS) {
+      const int q = it * 256 + tid;
+      const int nb = (q & 7) | (((q >> 4) & 3) << 3);
+      const int kb = ((q >> 3) & 1) | ((q >> 6) << 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t off = (uint32_t)(kt * BK + kb * 8 + e) * p.Nout + nb * 8;
+        b_reg[it * 8 + e] = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
       }
     }
   };
-  // B (contraction-contiguous): item i -> out column i*32 + tid/8, chunk tid%8
-  // B (output-contiguous): 8x8 byte blocks; block q = it*256 + tid, see below
-  auto load_b = [&](int kt) {
-    if constexpr (!B_TRANS) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bt_reg[i] = buf_load16(rb, (uint32_t)(i * 32 + lrow) * Kc + kt * BK + lchunk * 16);
-    } else {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int q = it * 256 + tid;
-        const int nb = (q & 7) | (((q >> 4) & 3) << 3);
-        const int kb = ((q >> 3) & 1) | ((q >> 6) << 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t off = (uint32_t)(kt * BK + kb * 8 + e) * p.Nout + nb * 8;
-          b_reg[it * 8 + e] = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
-        }
-      }
-    }
-  };
-  auto store_stage = [&](int stage) {
-    uint8_t* at = smem + stage * STAGE;
-    uint8_t* bt = at + A_TILE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = i * 32 + lrow;
+  auto store_a_piece = [&](uint8_t* at, int i) {
+    if constexpr (!A_FP8) {
+      const v2u lo = quant8<A_FMT>(a_reg[2 * i], inv_row[i]);
+      const v2u hi = quant8<A_FMT>(a_reg[2 * i + 1], inv_row[i]);
       v4u q;
-      if constexpr (A_FP8) {
-        q = a_reg[i];
-      } else {
-        const v2u lo = quant8<A_FMT>(a_reg[2 * i], inv_row[i]);
-        const v2u hi = quant8<A_FMT>(a_reg[2 * i + 1], inv_row[i]);
-        q.x = lo.x; q.y = lo.y; q.z = hi.x; q.w = hi.y;
-      }
-      *reinterpret_cast<v4u*>(at + tile_off(row, lchunk)) = q;
+      q.x = lo.x; q.y = lo.y; q.z = hi.x; q.w = hi.y;
+      *reinterpret_cast<v4u*>(at + tile_off(i * 32 + lrow, lchunk)) = q;
     }
-    if constexpr (!B_TRANS) {
+  };
+  auto store_b_block = [&](uint8_t* bt, int it) {
+    if constexpr (B_TRANS) {
+      const int q = it * 256 + tid;
+      const int nb = (q & 7) | (((q >> 4) & 3) << 3);
+      const int kb = ((q >> 3) & 1) | ((q >> 6) << 1);
+      v2u t[8];
+      transpose8x8(&b_reg[it * 8], t);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<v4u*>(bt + tile_off(i * 32 + lrow, lchunk)) = bt_reg[i];
-    } else {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int q = it * 256 + tid;
-        const int nb = (q & 7) | (((q >> 4) & 3) << 3);
-        const int kb = ((q >> 3) & 1) | ((q >> 6) << 1);
-        v2u t[8];
-        transpose8x8(&b_reg[it * 8], t);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int n = nb * 8 + c;
-          *reinterpret_cast<v2u*>(bt + tile_off(n, kb >> 1) + (kb & 1) * 8) = t[c];
-        }
-      }
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<v2u*>(bt + tile_off(nb * 8 + c, kb >> 1) + (kb & 1) * 8) = t[c];
     }
+  };
+  // Wait until this wave's direct loads into the stage being filled have landed (the
+  // register prefetches issued after them may still be in flight) and its LDS stores
+  // are done, then synchronise the workgroup.
+  auto stage_barrier = [&]() {
+    if constexpr (A_FP8 && B_TRANS) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    else if constexpr (A_FP8) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    else if constexpr (B_TRANS) asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   v16f acc[4][4];
@@ -243,35 +270,115 @@ void gmm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
 
-  load_a(0);
-  load_b(0);
-  store_stage(0);
-  __syncthreads();
-
   const int frow = lane & 31, fhalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) {
-      load_a(kt + 1);
-      load_b(kt + 1);
-    }
-    const uint8_t* at = smem + stage * STAGE;
-    const uint8_t* bt = at + A_TILE;
+  // Fragment addressing.  A fragment row is R = base + 32 i + frow (base a multiple of
+  // 128), so its swizzle key (R & 7) ^ ((R >> 3) & 7) is f0 ^ 4 (i & 1) with
+  // f0 = (frow & 7) ^ (frow >> 3), and the physical chunk of logical chunk
+  // 4 ks + 2 fhalf + e is (2 fhalf + e) ^ f0 ^ 4 (ks ^ (i & 1)).  Two per-lane byte
+  // offsets per e (t = ks ^ (i & 1)) plus the immediate 4096 i cover every fragment.
+  uint32_t fo[2][2];
+  {
+    const uint32_t f0 = (uint32_t)((frow & 7) ^ (frow >> 3));
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8i af[4], bf[4];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = lds_read_frag(at, wr * 128 + i * 32 + frow, ks * 4 + fhalf * 2);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = lds_read_frag(bt, wc * 128 + j * 32 + frow, ks * 4 + fhalf * 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x64<B_FMT, A_FMT>(bf[j], af[i], acc[i][j]);
-    }
-    if (kt + 1 < nk) store_stage(stage ^ 1);
-    __syncthreads();
+      for (int e = 0; e < 2; ++e)
+        fo[t][e] = (uint32_t)frow * BK + ((((uint32_t)(2 * fhalf + e)) ^ f0 ^ (4u * t)) << 4);
   }
+  auto frag = [&](const uint8_t* tile, int base_row, int i, int ks) -> v8i {
+    const int t = ks ^ (i & 1);
+    const uint8_t* p0 = tile + base_row * BK + i * 32 * BK;
+    const v4u lo = *reinterpret_cast<const v4u*>(p0 + fo[t][0]);
+    const v4u hi = *reinterpret_cast<const v4u*>(p0 + fo[t][1]);
+    v8i f;
+    f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+    f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+    return f;
+  };
+  // Store address of quantized A piece p (row 32 p + lrow): swizzle key
+  // g0 ^ 4 (p & 1) with g0 = (lrow & 7) ^ (lrow >> 3).
+  uint32_t so[2];
+  {
+    const uint32_t g0 = (uint32_t)((lrow & 7) ^ (lrow >> 3));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) so[t] = (uint32_t)lrow * BK + ((((uint32_t)lchunk) ^ g0 ^ (4u * t)) << 4);
+  }
+
+  // One quarter of an A piece: the 4 values that make one output dword.
+  auto quant_dword = [&](int i, int d) -> uint32_t {
+    const v4u w = a_reg[2 * i + (d >> 1)];
+    const uint32_t w0 = (d & 1) ? w.z : w.x, w1 = (d & 1) ? w.w : w.y;
+    const float inv = inv_row[i];
+    uint32_t r = cvt_pk<A_FMT, false>(quant_prep<A_FMT>(bf16_lo(w0), inv),
+                                      quant_prep<A_FMT>(bf16_hi(w0), inv), w0);
+    return cvt_pk<A_FMT, true>(quant_prep<A_FMT>(bf16_lo(w1), inv),
+                               quant_prep<A_FMT>(bf16_hi(w1), inv), r);
+  };
+
+  // One contraction step: the 32 MFMAs on stage (at, bt) = step kt, while step kt+1 is
+  // completed in stage (an, bn) and step kt+2 is prefetched into registers.  The step
+  // is written as 32 units of one MFMA plus one slice of register work each, fenced so
+  // that the scheduler keeps the interleaving (the matrix core works through each MFMA
+  // while the vector ALU runs the next slice).
+  auto step = [&](int kt, const uint8_t* at, const uint8_t* bt, uint8_t* an, uint8_t* bn) {
+    issue_direct(kt + 1, an, bn);
+    v8i af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = frag(at, wr * 128, i, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = frag(bt, wc * 128, j, 0);
+    uint32_t qd[4];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int ks = u >> 4, i = (u >> 2) & 3, j = u & 3;
+      acc[i][j] = mfma32x32x64<B_FMT, A_FMT>(bf[j], af[i], acc[i][j]);
+      // fragments of the second half step, each right after its last use
+      if (ks == 0 && j == 3) af[i] = frag(at, wr * 128, i, 1);
+      if (ks == 0 && i == 3) bf[j] = frag(bt, wc * 128, j, 1);
+      if constexpr (!A_FP8) {
+        // piece u/4 of step kt+1: quarter u%4, then store it and refill its registers
+        const int piece = u >> 2, d = u & 3;
+        qd[d] = quant_dword(piece, d);
+        if (d == 3) {
+          v4u q;
+          q.x = qd[0]; q.y = qd[1]; q.z = qd[2]; q.w = qd[3];
+          *reinterpret_cast<v4u*>(an + piece * 32 * BK + so[piece & 1]) = q;
+          load_a_piece(kt + 2, piece);
+        }
+      }
+      if constexpr (B_TRANS) {
+        if (u == 7) { store_b_block(bn, 0); load_b_block(kt + 2, 0); }
+        if (u == 23) { store_b_block(bn, 1); load_b_block(kt + 2, 1); }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_barrier();
+  };
+
+  // ---- prologue: step 0 into stage 0, step 1 into registers ----
+  issue_direct(0, sA0, sB0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_a_piece(0, i);
+  load_b_block(0, 0);
+  load_b_block(0, 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) store_a_piece(sA0, i);
+  store_b_block(sB0, 0);
+  store_b_block(sB0, 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_a_piece(1, i);
+  load_b_block(1, 0);
+  load_b_block(1, 1);
+  stage_barrier();
+
+  // two steps per trip so that every LDS access names a fixed stage object; past the
+  // last step the loads read zeros or in-range bytes that are never used
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, sA0, sB0, sA1, sB1);
+    step(kt + 1, sA1, sB1, sA0, sB0);
+  }
+  if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
 
   // ---- epilogue ----
   // lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) + 4*(lane/32) + r%4]

@@ -92,7 +92,8 @@ void tgmm_kernel(TgmmParams p) {
     }
   }
   __syncthreads();
-  const int off0 = s_off[0], off1 = s_off[1];
+  const int off0 = __builtin_amdgcn_readfirstlane(s_off[0]);
+  const int off1 = __builtin_amdgcn_readfirstlane(s_off[1]);
 
   const int wr = wave >> 1, wc = wave & 1;   // wave sub-tile: 128 (k) x 64 (n)
   const int frow = lane & 31, fhalf = lane >> 5;

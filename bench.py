@@ -80,16 +80,22 @@ class Step:
         op = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC, 0.0)
         n = g._SZ()
         self._chk(lib.gmm_workspace_size(g.OP_FWD, ctypes.byref(op), ctypes.byref(op), M,
-                                         max(K, N), 0, ctypes.byref(n)))
+                                         max(K, N), 0, 1, ctypes.byref(n)))
         self.ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
         self.ws_n = n.value
+        opl = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
+        opg = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC_GIVEN, 0.0)
+        self._chk(lib.gmm_workspace_size(g.OP_TGMM, ctypes.byref(opl), ctypes.byref(opg), M, K, N,
+                                         G, ctypes.byref(n)))
+        self.ws_t = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+        self.ws_t_n = n.value
         self.op_lhs = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
         self.op_grad = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC_GIVEN, 0.0)
         self.r_lhs, self.r_grad = ctypes.byref(self.op_lhs), ctypes.byref(self.op_grad)
         P = lambda t: t.data_ptr()
         self.p = {k: P(getattr(self, k)) for k in
                   ("lhs", "grad", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs", "drhs",
-                   "s_lhs", "s_grad", "ws", "gs")}
+                   "s_lhs", "s_grad", "ws", "ws_t", "gs")}
         torch.cuda.synchronize()
 
     def run(self, stream, ev=None):
@@ -110,7 +116,7 @@ class Step:
                          p["grad"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, s))
         rec(4)
         chk(lib.tgmm_drhs(self.r_lhs, self.r_grad, self.g.OUT_BF16, M, K, N, G, p["lhs"], p["s_lhs"],
-                          p["grad"], p["s_grad"], p["gs"], p["drhs"], None, 0, s))
+                          p["grad"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
         rec(5)
 
     def _chk(self, status):

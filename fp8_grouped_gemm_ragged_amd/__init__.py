@@ -64,7 +64,7 @@ _SIGNATURES = {
     "gmm_fwd": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_dlhs": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "tgmm_drhs": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
-    "gmm_workspace_size": [_I32, _OPP, _OPP, _I64, _I64, _I64, ctypes.POINTER(_SZ)],
+    "gmm_workspace_size": [_I32, _OPP, _OPP, _I64, _I64, _I64, _I32, ctypes.POINTER(_SZ)],
     "gmm_dynamic_scales": [_I32, _I64, _I64, _P, _P, _P, _SZ, _P],
     "gmm_quantize": [_OPP, _I64, _I64, _P, _P, _P, _P, _SZ, _P],
     "gmm_quantize_rhs": [_I32, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _P],
@@ -150,12 +150,13 @@ def gmm_static_scale_from_bound(lo, hi, fmt="e4m3"):
 
 
 def gmm_workspace_size(op, a_fmt, a_scaling, rows, cols_a=0, cols_b=0, b_fmt="e5m2",
-                       b_scaling="dynamic", a_kind=KIND_BF16, static_scale=1.0):
+                       b_scaling="dynamic", a_kind=KIND_BF16, static_scale=1.0, groups=1):
     a = _operand(a_kind, a_fmt, a_scaling, static_scale)
     b = _operand(KIND_BF16, b_fmt, b_scaling, static_scale)
     n = _SZ()
     _check(load().gmm_workspace_size(int(op), ctypes.byref(a), ctypes.byref(b), int(rows),
-                                     int(cols_a), int(cols_b), ctypes.byref(n)), "gmm_workspace_size")
+                                     int(cols_a), int(cols_b), int(groups), ctypes.byref(n)),
+           "gmm_workspace_size")
     return n.value
 
 
@@ -204,7 +205,7 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
     if a_scales is not None:
         _need(a_scales, torch.float32, "scales", 1)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), M, K_or_N, 0,
+    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), M, K_or_N, 0, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, a.device)
     fn = getattr(lib, cname)
@@ -275,7 +276,7 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
     sa = scales_for(lhs_scaling, lhs_scales)
     sg = scales_for(grad_scaling, grad_scales)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_TGMM, ctypes.byref(aop), ctypes.byref(bop), M, K, N,
+    _check(lib.gmm_workspace_size(OP_TGMM, ctypes.byref(aop), ctypes.byref(bop), M, K, N, G,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, lhs.device)
     _check(lib.tgmm_drhs(ctypes.byref(aop), ctypes.byref(bop), OUT_F32 if odt == torch.float32 else OUT_BF16,
@@ -294,7 +295,7 @@ def gmm_dynamic_scales(x, fmt="e4m3"):
     scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
     op = _operand(KIND_BF16, fmt, "dynamic", None)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0,
+    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, x.device)
     _check(lib.gmm_dynamic_scales(_FMT[fmt], R, C, _ptr(x), _ptr(scales), _ptr(ws), ws_n.value,
@@ -319,7 +320,7 @@ def gmm_quantize(x, fmt="e4m3", scaling="dynamic", static_scale=None, scales=Non
     if mode == DYNAMIC and scales is None:
         scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0,
+    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, x.device)
     _check(lib.gmm_quantize(ctypes.byref(op), R, C, _ptr(x), _ptr(codes), _ptr(scales), _ptr(ws),

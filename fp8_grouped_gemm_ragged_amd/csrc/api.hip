@@ -57,6 +57,13 @@ DynWs carve(void* base, int64_t rows) {
 
 // The call runs the abs-max prepass itself (and needs workspace) only for a bf16
 // operand with GMM_SCALE_DYNAMIC.
+// tgmm: plan (3 G + 1 ints) and the two quantized, transposed segment buffers.
+size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int32_t G) {
+  const size_t seg_row = (size_t)tgmm_segment_row_bytes(M, G);
+  return align256((size_t)(3 * G + 1) * 4) + align256((size_t)nblocks(M) * 4) +
+         align256((size_t)K * seg_row) + align256((size_t)N * seg_row);
+}
+
 bool needs_dyn_ws(const gmm_operand_t* op) {
   return op && op->kind == GMM_OPERAND_BF16 && op->scaling == GMM_SCALE_DYNAMIC;
 }
@@ -243,12 +250,15 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
     if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
   const size_t wa = needs_dyn_ws(lhs_op) ? dyn_ws_bytes(M) : 0;
   const size_t wb = needs_dyn_ws(grad_op) ? dyn_ws_bytes(M) : 0;
-  if ((wa + wb) && (!workspace || workspace_bytes < wa + wb)) return GMM_ERR_WORKSPACE;
+  const size_t wt = tgmm_ws_bytes(M, K, N, G);
+  if (!workspace || workspace_bytes < wa + wb + wt) return GMM_ERR_WORKSPACE;
   const size_t out_bytes = (size_t)G * K * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
   if (overlaps(drhs, out_bytes, lhs, (size_t)M * K * 2) ||
       overlaps(drhs, out_bytes, grad, (size_t)M * N * 2) ||
       overlaps(drhs, out_bytes, group_sizes, (size_t)G * 4) ||
-      overlaps(workspace, wa + wb, drhs, out_bytes))
+      overlaps(workspace, wa + wb + wt, drhs, out_bytes) ||
+      overlaps(workspace, wa + wb + wt, lhs, (size_t)M * K * 2) ||
+      overlaps(workspace, wa + wb + wt, grad, (size_t)M * N * 2))
     return GMM_ERR_ALIAS;
   if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
   trace("tgmm_drhs", M, K, N, G);
@@ -264,6 +274,14 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
   p.Nout = (int32_t)N;
   p.G = G;
   p.out_f32 = out_dtype == GMM_OUT_F32;
+  {
+    uint8_t* base = (uint8_t*)workspace + wa + wb;
+    const size_t seg_row = (size_t)tgmm_segment_row_bytes(M, G);
+    p.plan = (int32_t*)base;
+    p.scprod = (float*)(base + align256((size_t)(3 * G + 1) * 4));
+    p.a_seg = (uint8_t*)p.scprod + align256((size_t)nblocks(M) * 4);
+    p.b_seg = p.a_seg + align256((size_t)K * seg_row);
+  }
   if (M > 0) {
     Scaling sa, sg;
     if ((s = resolve_scaling(lhs_op, lhs, M, K, lhs_scales, workspace, st, sa)) != GMM_OK) return s;
@@ -282,11 +300,10 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
 }
 
 gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_operand_t* b,
-                                int64_t rows, int64_t cols_a, int64_t cols_b, size_t* bytes) {
-  (void)cols_a;
-  (void)cols_b;
+                                int64_t rows, int64_t cols_a, int64_t cols_b, int32_t G,
+                                size_t* bytes) {
   if (!bytes || !a) return GMM_ERR_NULL;
-  if (rows < 0) return GMM_ERR_SHAPE;
+  if (rows < 0 || cols_a < 0 || cols_b < 0 || G < 1 || G > GMM_MAX_GROUPS) return GMM_ERR_SHAPE;
   gmm_status_t s = check_operand(a);
   if (s != GMM_OK) return s;
   size_t n = needs_dyn_ws(a) ? dyn_ws_bytes(rows) : 0;
@@ -294,6 +311,7 @@ gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_op
     if (!b) return GMM_ERR_NULL;
     if ((s = check_operand(b)) != GMM_OK) return s;
     n += needs_dyn_ws(b) ? dyn_ws_bytes(rows) : 0;
+    n += tgmm_ws_bytes(rows, cols_a, cols_b, G);
   } else if (op != GMM_OP_FWD && op != GMM_OP_DLHS) {
     return GMM_ERR_RECIPE;
   }

@@ -34,6 +34,10 @@ struct TgmmParams {
   const uint16_t* b;         // bf16 [M, Nout]
   const int32_t* group_sizes;
   void* out;                 // [G, Kout, Nout] bf16 or f32
+  int32_t* plan;             // workspace: 3 G + 1 ints
+  float* scprod;             // workspace: one scale product per 128-row block
+  uint8_t* a_seg;            // workspace: Kout x tgmm_segment_row_bytes(M, G)
+  uint8_t* b_seg;            // workspace: Nout x tgmm_segment_row_bytes(M, G)
   const float* a_scale_blk;  // dynamic: per-block scales; null -> static
   const float* b_scale_blk;
   float a_inv_static, a_scale_static, b_inv_static, b_scale_static;
@@ -41,6 +45,19 @@ struct TgmmParams {
   int32_t Kout, Nout, G;
   int32_t out_f32;
 };
+
+// the fp8 tgmm on quantized, transposed segments
+struct TgmmSegParams {
+  const uint8_t* a_seg;
+  const uint8_t* b_seg;
+  const int32_t* plan;
+  const float* scprod;
+  void* out;
+  int32_t Kout, Nout, G, out_f32;
+  int64_t seg_row;
+};
+
+int64_t tgmm_segment_row_bytes(int64_t M, int G);
 
 hipError_t launch_gemm(int a_fmt, int b_fmt, bool a_fp8, bool b_trans, const GemmParams& p,
                        hipStream_t st);

@@ -1,35 +1,77 @@
-// Transposed grouped matmul on gfx950: the kernel behind tgmm_drhs ("Support
+// Transposed grouped matmul on gfx950: the kernels behind tgmm_drhs ("Support
 // quantization for tokamax gmm v2", PR #4451, What this does: drhs_tgmm2).
 //
 //   drhs[g, k, n] = sum over 128-row blocks c meeting group g of
 //                   RNE( P_c[k, n] * RNE(s_lhs[c] * s_grad[c]) ),
 //   P_c[k, n]     = sum_{m in c, m in g} q(lhs)[m, k] * q(grad)[m, n]   (fp32 MFMA sums)
 //
-// One workgroup computes a 256 (k) x 128 (n) slab tile of one group.  The contraction
-// runs over the group's rows, one 128-row block per step; the steps are aligned to the
-// global 128-row grid of the dynamic scales, so the first and last blocks of a group
-// are partial and rows outside the group read as zero.  Both operands arrive as bf16
-// with the contraction (row) axis strided: each thread loads an 8-row x 8-column block
-// (eight 16-byte loads), and the paired fp8 conversion packs two rows of one column
-// into each half of a dword, so the quantized codes come out row-contiguous per column
-// (transposed) without any byte shuffles.  Each step's MFMA result goes to a fresh
-// fp32 partial that is scaled and added to the running slab (scale promotion), since a
-// dynamic scale changes from block to block.  A group without rows stores +0.0.
+// The contraction runs over the rows of a group, and both operands are stored with
+// that axis strided.  The path therefore has three kernels:
+//   1. tgmm_plan: per group the first row, the row count and the offset of its
+//      "segment": the 128-row blocks the group meets, laid end to end.
+//   2. quant_transpose (once per operand): every element quantized exactly once (with
+//      its block's scale) and written transposed, [columns][segment], so that each
+//      group's rows start on a 128-byte boundary and rows of other groups inside a
+//      shared block are zero codes.  The per-block dynamic scales stay aligned with
+//      128-byte steps of the contraction.
+//   3. tgmm_fp8: per (group, 256 k x 128 n) tile, one contraction step per block of
+//      the group's segment: fp8 tiles go straight from HBM into swizzled LDS, each
+//      step's MFMA sums land in a fresh fp32 partial (AGPRs), and the partial of the
+//      previous step is scaled and added to the VGPR accumulators (scale promotion,
+//      one fused multiply-add) in between the current step's MFMAs.  A group without
+//      rows stores +0.0.
 #include "kernels.hpp"
 
 namespace gmm {
 
 namespace {
 
-constexpr int TBM = 256;   // k rows of the slab tile
-constexpr int TBN = 128;   // n columns of the slab tile
+constexpr int TBM = 256;   // k rows of a slab tile
+constexpr int TBN = 128;   // n columns of a slab tile
 constexpr int NT = 256;
 constexpr int A_TILE = TBM * TILE_K;  // [256 k][128 m] fp8
 constexpr int B_TILE = TBN * TILE_K;  // [128 n][128 m] fp8
-constexpr int STAGE = A_TILE + B_TILE;  // 48 KB
+
+// plan layout in the workspace: off[G], cnt[G], seg[G + 1] (segment offsets in blocks),
+// then one float per 128-row block: RNE(s_lhs[c] * s_grad[c]).
+__global__ void tgmm_plan_kernel(const int32_t* __restrict__ gs, int G, int64_t M,
+                                 const float* __restrict__ a_scale_blk, float a_scale_static,
+                                 const float* __restrict__ b_scale_blk, float b_scale_static,
+                                 int32_t* __restrict__ plan, float* __restrict__ scprod) {
+  const int lane = threadIdx.x;  // one wave
+  const int64_t nb = (M + BLOCK_ROWS - 1) / BLOCK_ROWS;
+  for (int64_t c = lane; c < nb; c += 64) {
+    const float sa = a_scale_blk ? a_scale_blk[c] : a_scale_static;
+    const float sb = b_scale_blk ? b_scale_blk[c] : b_scale_static;
+    scprod[c] = __fmul_rn(sa, sb);
+  }
+  int32_t* off = plan;
+  int32_t* cnt = plan + G;
+  int32_t* seg = plan + 2 * G;
+  int carry_r = 0, carry_b = 0;
+  for (int base = 0; base < G; base += 64) {
+    const int g = base + lane;
+    // sizes outside the contract are clamped so no access leaves the tensors
+    const int m = g < G ? max(gs[g], 0) : 0;
+    const int incl = wave_incl_scan(m, lane);
+    const int64_t o = min((int64_t)carry_r + incl - m, M);
+    const int c = (int)min((int64_t)m, M - o);
+    const int nb = c > 0 ? (int)((o + c - 1) / BLOCK_ROWS - o / BLOCK_ROWS + 1) : 0;
+    const int bincl = wave_incl_scan(nb, lane);
+    if (g < G) {
+      off[g] = (int)o;
+      cnt[g] = c;
+      seg[g] = carry_b + bincl - nb;
+    }
+    carry_r += __shfl(incl, 63, 64);
+    carry_b += __shfl(bincl, 63, 64);
+  }
+  if (lane == 0) seg[G] = carry_b;
+}
 
 // Quantize an 8 (rows) x 8 (cols) bf16 block held as 8 row vectors into 8 column
-// vectors of 8 codes each (rows 0..3 in .x, rows 4..7 in .y).
+// vectors of 8 codes each (rows 0..3 in .x, rows 4..7 in .y): the paired conversion
+// packs two rows of one column per instruction, so the transposition is free.
 template <int FMT>
 __device__ inline void quant_transpose8(const v4u in[8], float inv, v2u out[8]) {
 #pragma unroll
@@ -40,223 +82,303 @@ __device__ inline void quant_transpose8(const v4u in[8], float inv, v2u out[8]) 
       const uint32_t d = c < 2 ? in[r].x : c < 4 ? in[r].y : c < 6 ? in[r].z : in[r].w;
       v[r] = quant_prep<FMT>((c & 1) ? bf16_hi(d) : bf16_lo(d), inv);
     }
-    uint32_t lo = cvt_pk<FMT, false>(v[0], v[1], 0u);
+    uint32_t lo = cvt_pk<FMT, false>(v[0], v[1], __float_as_uint(v[0]));
     lo = cvt_pk<FMT, true>(v[2], v[3], lo);
-    uint32_t hi = cvt_pk<FMT, false>(v[4], v[5], 0u);
+    uint32_t hi = cvt_pk<FMT, false>(v[4], v[5], __float_as_uint(v[4]));
     hi = cvt_pk<FMT, true>(v[6], v[7], hi);
     out[c].x = lo;
     out[c].y = hi;
   }
 }
 
+// grid (segment blocks upper bound, C / 128).  Workgroup (b, ct): segment block b (a
+// pair (group g, 128-row block c)) and columns [128 ct, 128 ct + 128).
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_transpose_kernel(
+    const uint16_t* __restrict__ x, int64_t C, const int32_t* __restrict__ plan, int G,
+    const float* __restrict__ scale_blk, float inv_static, uint8_t* __restrict__ seg,
+    int64_t seg_row) {
+  const int32_t* off = plan;
+  const int32_t* cnt = plan + G;
+  const int32_t* sg = plan + 2 * G;
+  const int b = blockIdx.x;
+  if (b >= sg[G]) return;
+  int lo = 0, hi = G;  // sg[lo] <= b < sg[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sg[mid] <= b) lo = mid; else hi = mid;
+  }
+  const int g = __builtin_amdgcn_readfirstlane(lo);
+  const int o = __builtin_amdgcn_readfirstlane(off[g]);
+  const int n = __builtin_amdgcn_readfirstlane(cnt[g]);
+  const int c = o / BLOCK_ROWS + (b - __builtin_amdgcn_readfirstlane(sg[g]));
+  const int r_lo = max(o, c * BLOCK_ROWS), r_hi = min(o + n, (c + 1) * BLOCK_ROWS);
+  const int rel = r_lo - c * BLOCK_ROWS;  // first row of the block that belongs to g
+  const int64_t col0 = (int64_t)blockIdx.y * 128;
+  // rows [r_lo, r_hi) from column col0 on: later rows read as zero
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(x + (int64_t)r_lo * C + col0, (uint32_t)((int64_t)(r_hi - r_lo) * C * 2 - col0 * 2));
+  const float inv = scale_blk ? inv_from_scale(scale_blk[c]) : inv_static;
+  const int t = threadIdx.x;
+  const int rb = t & 15, cb = t >> 4;  // 8-row block, 8-column block
+  v4u in[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = rb * 8 + e - rel;  // relative to the first row of g in the block
+    uint32_t voff = (uint32_t)row * (uint32_t)(C * 2) + cb * 16;
+    if (row < 0) voff = 0xfffffff0u;  // rows of the previous group: zero codes
+    in[e] = buf_load16(r, voff);
+  }
+  v2u q[8];
+  quant_transpose8<FMT>(in, inv, q);
+  uint8_t* dst = seg + (col0 + cb * 8) * seg_row + (int64_t)b * BLOCK_ROWS + rb * 8;
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<v2u*>(dst + cc * seg_row) = q[cc];
+}
+
+// One wave fills 8 rows (1 KB) of a swizzled [rows][128 B] tile from global memory.
+__device__ inline void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_rows,
+                                        uint32_t goff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_rows, 16, goff, 0, 0, 0);
+}
+
 template <int A_FMT, int B_FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
-void tgmm_kernel(TgmmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ int s_off[2];
+void tgmm_fp8_kernel(TgmmSegParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_TILE];
 
   const int n_kt = (p.Kout + TBM - 1) / TBM;
   const int n_nt = p.Nout / TBN;
-  const int tiles_per_group = n_kt * n_nt;
-  const int total = tiles_per_group * p.G;
+  const int total = n_kt * n_nt * p.G;
   const int wg = blockIdx.x;
   if (wg >= total) return;
-  // Workgroup i runs on XCD i % 8.  Remap so each XCD owns a contiguous range of the
-  // tile order, and order tiles group-fastest: every XCD then holds an equal share of
-  // every group (the work of a tile grows with its group's row count, so a group-major
-  // order would load one XCD with the largest group), while the concurrent tiles of
-  // one XCD still cover a few neighbouring slab tiles of each group.
+  // Workgroup i runs on XCD i % 8: each XCD owns a contiguous range of the tile order,
+  // and tiles are ordered group-fastest, so every XCD holds an equal share of every
+  // group (the work of a tile grows with its group's row count).
   const int xcd = wg & 7, jx = wg >> 3, qx = total >> 3, rx = total & 7;
   const int L = xcd * qx + min(xcd, rx) + jx;
   const int g = L % p.G;
   const int t = L / p.G;
   const int kt = t / n_nt, nt = t - kt * n_nt;
   const int k0 = kt * TBM, n0 = nt * TBN;
+  const int32_t* off = p.plan;
+  const int32_t* sg = p.plan + 2 * p.G;
+  const int seg0 = __builtin_amdgcn_readfirstlane(sg[g]);
+  const int nblk = __builtin_amdgcn_readfirstlane(sg[g + 1]) - seg0;
+  const int c0 = __builtin_amdgcn_readfirstlane(off[g]) / BLOCK_ROWS;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 64) {
-    // row offset of group g: prefix sum of group_sizes[0..g)
-    int acc = 0;
-    for (int base = 0; base < g; base += 64) {
-      const int gg = base + lane;
-      int v = gg < g ? max(p.group_sizes[gg], 0) : 0;
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-      acc += v;
-    }
-    if (lane == 0) {
-      // clamp to [0, M]: sizes outside the contract never move an access out of bounds
-      const int64_t lo = min((int64_t)acc, p.M);
-      s_off[0] = (int)lo;
-      s_off[1] = (int)min(lo + max(p.group_sizes[g], 0), p.M);
-    }
-  }
-  __syncthreads();
-  const int off0 = __builtin_amdgcn_readfirstlane(s_off[0]);
-  const int off1 = __builtin_amdgcn_readfirstlane(s_off[1]);
-
-  const int wr = wave >> 1, wc = wave & 1;   // wave sub-tile: 128 (k) x 64 (n)
+  const int wr = wave >> 1, wc = wave & 1;  // wave sub-tile: 128 (k) x 64 (n)
   const int frow = lane & 31, fhalf = lane >> 5;
 
-  v16f acc[4][2];
+  v16f acc[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{0};
+  for (int b = 0; b < 8; ++b) acc[b] = v16f{0};
 
-  // load mapping.  A: 512 blocks of 8 rows x 8 k-columns, 2 per thread;
-  // block q -> col block cb (k), row block rb (m); lanes 0-7 walk cb so that one load
-  // instruction reads 128 contiguous bytes of a row.
-  // B: 256 blocks of 8 rows x 8 n-columns, 1 per thread.
-  v4u a_reg[16], b_reg[8];
-
-  const int c_first = off0 / BLOCK_ROWS;
-  const int c_last = off1 > off0 ? (off1 - 1) / BLOCK_ROWS : c_first - 1;
-
-  auto load_step = [&](int c) {
-    const int lo = max(off0, c * BLOCK_ROWS), hi = min(off1, (c + 1) * BLOCK_ROWS);
-    const int rlo = lo - c * BLOCK_ROWS;  // first valid row within the block
+  if (nblk > 0) {
+    const uint32_t seg_row = (uint32_t)p.seg_row;
+    const int krows = min(p.Kout - k0, TBM);
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(p.a + (int64_t)lo * p.Kout, (uint32_t)(hi - lo) * p.Kout * 2);
+        make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * BLOCK_ROWS,
+                  (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * BLOCK_ROWS));
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(p.b + (int64_t)lo * p.Nout, (uint32_t)(hi - lo) * p.Nout * 2);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = it * 256 + tid;
-      const int cb = (q & 7) | (((q >> 4) & 3) << 3);
-      const int rb8 = ((q >> 3) & 1) | ((q >> 6) << 1);
-      const int col = k0 + cb * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = rb8 * 8 + e - rlo;  // row relative to the first valid row
-        uint32_t off = (uint32_t)r * p.Kout * 2 + col * 2;
-        if (r < 0 || col >= p.Kout) off = 0xfffffff0u;
-        a_reg[it * 8 + e] = buf_load16(ra, off);
-      }
-    }
-    {
-      const int q = tid;
-      const int cb = (q & 7) | (((q >> 4) & 1) << 3);
-      const int rb8 = ((q >> 3) & 1) | ((q >> 5) << 1);
-      const int col = n0 + cb * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = rb8 * 8 + e - rlo;
-        uint32_t off = (uint32_t)r * p.Nout * 2 + col * 2;
-        if (r < 0) off = 0xfffffff0u;
-        b_reg[e] = buf_load16(rb, off);
-      }
-    }
-  };
-  auto store_step = [&](int c, int stage) {
-    uint8_t* at = smem + stage * STAGE;
-    uint8_t* bt = at + A_TILE;
-    const float ia = p.a_scale_blk ? inv_from_scale(p.a_scale_blk[c]) : p.a_inv_static;
-    const float ib = p.b_scale_blk ? inv_from_scale(p.b_scale_blk[c]) : p.b_inv_static;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = it * 256 + tid;
-      const int cb = (q & 7) | (((q >> 4) & 3) << 3);
-      const int rb8 = ((q >> 3) & 1) | ((q >> 6) << 1);
-      v2u o[8];
-      quant_transpose8<A_FMT>(&a_reg[it * 8], ia, o);
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc)
-        *reinterpret_cast<v2u*>(at + tile_off(cb * 8 + cc, rb8 >> 1) + (rb8 & 1) * 8) = o[cc];
-    }
-    {
-      const int q = tid;
-      const int cb = (q & 7) | (((q >> 4) & 1) << 3);
-      const int rb8 = ((q >> 3) & 1) | ((q >> 5) << 1);
-      v2u o[8];
-      quant_transpose8<B_FMT>(b_reg, ib, o);
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc)
-        *reinterpret_cast<v2u*>(bt + tile_off(cb * 8 + cc, rb8 >> 1) + (rb8 & 1) * 8) = o[cc];
-    }
-  };
+        make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * BLOCK_ROWS,
+                  (uint32_t)((int64_t)TBN * p.seg_row - (int64_t)seg0 * BLOCK_ROWS));
 
-  if (c_first <= c_last) {
-    load_step(c_first);
-    store_step(c_first, 0);
-    __syncthreads();
-    for (int c = c_first; c <= c_last; ++c) {
-      const int stage = (c - c_first) & 1;
-      if (c < c_last) load_step(c + 1);
-      const uint8_t* at = smem + stage * STAGE;
-      const uint8_t* bt = at + A_TILE;
-      v16f part[4][2];
+    // direct loads of segment block s: A rows 64w..64w+63 (8 per wave-load),
+    // B rows 32w..32w+31
+    auto issue = [&](int s, uint8_t* at, uint8_t* bt) {
+      const uint32_t koff = (uint32_t)s * BLOCK_ROWS;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        v8i af[4], bf[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = lds_read_frag(at, wr * 128 + i * 32 + frow, ks * 4 + fhalf * 2);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = lds_read_frag(bt, wc * 64 + j * 32 + frow, ks * 4 + fhalf * 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            part[i][j] = mfma32x32x64<B_FMT, A_FMT>(bf[j], af[i], ks == 0 ? v16f{0} : part[i][j]);
+      for (int q = 0; q < 8; ++q) {
+        const int row = wave * 64 + q * 8 + (lane >> 3);
+        const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
+        load_rows_to_lds(ra, at + (wave * 64 + q * 8) * TILE_K, (uint32_t)row * seg_row + koff + c * 16);
       }
-      const float sa = p.a_scale_blk ? p.a_scale_blk[c] : p.a_scale_static;
-      const float sb = p.b_scale_blk ? p.b_scale_blk[c] : p.b_scale_static;
-      const float sc = __fmul_rn(sa, sb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < 4; ++q) {
+        const int row = wave * 32 + q * 8 + (lane >> 3);
+        const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
+        load_rows_to_lds(rb, bt + (wave * 32 + q * 8) * TILE_K, (uint32_t)row * seg_row + koff + c * 16);
+      }
+    };
+    // fragment addressing, as in the grouped GEMM: two per-lane offsets per half block
+    uint32_t fo[2][2];
+    {
+      const uint32_t f0 = (uint32_t)((frow & 7) ^ (frow >> 3));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] = __fadd_rn(acc[i][j][e], __fmul_rn(part[i][j][e], sc));
-      if (c < c_last) store_step(c + 1, stage ^ 1);
-      __syncthreads();
+        for (int e = 0; e < 2; ++e)
+          fo[tt][e] = (uint32_t)frow * TILE_K + ((((uint32_t)(2 * fhalf + e)) ^ f0 ^ (4u * tt)) << 4);
     }
+    auto frag = [&](const uint8_t* tile, int base_row, int i, int ks) -> v8i {
+      const int tt = ks ^ (i & 1);
+      const uint8_t* p0 = tile + base_row * TILE_K + i * 32 * TILE_K;
+      const v4u lo = *reinterpret_cast<const v4u*>(p0 + fo[tt][0]);
+      const v4u hi = *reinterpret_cast<const v4u*>(p0 + fo[tt][1]);
+      v8i f;
+      f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+      f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+      return f;
+    };
+    auto barrier = [&]() {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Partial sums of the current block, one 32x32 sub-block per entry, in block-major
+    // MFMA order: unit u = 2b + ks issues half step ks of sub-block b (the two halves are
+    // chained accumulations).  Sub-block b is complete after unit 2b + 1; its promotion
+    // acc += part * sc runs three units later, 8 values per unit, so every unit pairs
+    // one MFMA with 16 VALU instructions, and units 0..2 finish the previous block.
+    v16f part[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) part[b] = v16f{0};
+    float sc_prev = 0.0f;
+    // scale product of the block a step will multiply, loaded one step ahead so that
+    // waiting for it never waits for the direct loads issued after it
+    float sc_next = p.scprod[c0];
+
+    auto promote = [&](int b, int half, float sc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc[b][half * 8 + e] = __builtin_fmaf(part[b][half * 8 + e], sc, acc[b][half * 8 + e]);
+    };
+
+    auto step = [&](int s, const uint8_t* at, const uint8_t* bt, uint8_t* an, uint8_t* bn) {
+      const float sc_cur = sc_next;
+      sc_next = p.scprod[c0 + min(s + 1, nblk - 1)];
+      issue(s + 1, an, bn);
+      v8i bf[2][2], af[2][2];  // [j or i parity][ks]
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) bf[j][ks] = frag(bt, wc * 64, j, ks);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) af[0][ks] = frag(at, wr * 128, 0, ks);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int b = u >> 1, ks = u & 1, i = b >> 1, j = b & 1;
+        part[b] = mfma32x32x64<B_FMT, A_FMT>(bf[j][ks], af[i & 1][ks], ks == 0 ? v16f{0} : part[b]);
+        // next A fragments once the previous pair of sub-blocks has used its registers
+        if (u == 1 || u == 5 || u == 9) {
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) af[(i + 1) & 1][k2] = frag(at, wr * 128, i + 1, k2);
+        }
+        const int v = (u + 13) & 15;  // promotion slot: unit u handles value-half v
+        if (u < 3) promote(v >> 1, v & 1, sc_prev);
+        else promote(v >> 1, v & 1, sc_cur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sc_prev = sc_cur;
+      barrier();
+    };
+
+    issue(0, sA0, sB0);
+    barrier();
+    int s = 0;
+    for (; s + 1 < nblk; s += 2) {
+      step(s, sA0, sB0, sA1, sB1);
+      step(s + 1, sA1, sB1, sA0, sB0);
+    }
+    if (s < nblk) step(s, sA0, sB0, sA1, sB1);
+    // the last block's sub-blocks 6 (second half) and 7 are still unpromoted
+    promote(6, 1, sc_prev);
+    promote(7, 0, sc_prev);
+    promote(7, 1, sc_prev);
   }
 
-  // ---- store the slab tile: lane holds out[k = base + lane%32][n = base + 8*(r/4) + 4*(lane/32) + r%4]
+  // ---- store: lane holds out[k = base + lane%32][n = base + 8*(r/4) + 4*(lane/32) + r%4]
   const int64_t slab = (int64_t)g * p.Kout * p.Nout;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int blk = 0; blk < 8; ++blk) {
+    const int i = blk >> 1, j = blk & 1;
     const int k = k0 + wr * 128 + i * 32 + frow;
     if (k >= p.Kout) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int n = n0 + wc * 64 + j * 32 + 8 * r4 + 4 * fhalf;
+      const int64_t idx = slab + (int64_t)k * p.Nout + n;
+      float o[4];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + wc * 64 + j * 32 + 8 * r4 + 4 * fhalf;
-        const int64_t idx = slab + (int64_t)k * p.Nout + n;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * r4 + e];
-        if (p.out_f32) {
-          v4f v = {o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
-        } else {
-          v2u v;
-          v.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-          v.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-          *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
-        }
+      for (int e = 0; e < 4; ++e) o[e] = acc[blk][4 * r4 + e];
+      if (p.out_f32) {
+        v4f v = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
+      } else {
+        v2u v;
+        v.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+        v.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+        *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
       }
     }
   }
 }
 
+template <int FMT>
+hipError_t launch_qt(const uint16_t* x, int64_t M, int64_t C, const int32_t* plan, int G,
+                     const float* scale_blk, float inv_static, uint8_t* seg, int64_t seg_row,
+                     hipStream_t st) {
+  const int64_t max_blocks = (M + BLOCK_ROWS - 1) / BLOCK_ROWS + G;
+  dim3 grid((unsigned)max_blocks, (unsigned)(C / 128));
+  hipLaunchKernelGGL(quant_transpose_kernel<FMT>, grid, dim3(256), 0, st, x, C, plan, G,
+                     scale_blk, inv_static, seg, seg_row);
+  return hipGetLastError();
+}
+
 template <int A_FMT, int B_FMT>
-hipError_t launch_one(const TgmmParams& p, hipStream_t st) {
+hipError_t launch_tgmm_fp8(const TgmmSegParams& p, hipStream_t st) {
   const int64_t tiles = (int64_t)((p.Kout + TBM - 1) / TBM) * (p.Nout / TBN) * p.G;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((tgmm_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(NT), 0, st, p);
+  hipLaunchKernelGGL((tgmm_fp8_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t tgmm_segment_row_bytes(int64_t M, int G) {
+  // every group's rows start on a block boundary: at most ceil(M/128) + G blocks
+  return ((M + BLOCK_ROWS - 1) / BLOCK_ROWS + G) * BLOCK_ROWS;
+}
+
 hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st) {
-  if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_one<FMT_E4M3, FMT_E5M2>(p, st);
-  if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_one<FMT_E4M3, FMT_E4M3>(p, st);
-  if (a_fmt == FMT_E5M2 && b_fmt == FMT_E5M2) return launch_one<FMT_E5M2, FMT_E5M2>(p, st);
-  if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_one<FMT_E5M2, FMT_E4M3>(p, st);
+  const int64_t seg_row = tgmm_segment_row_bytes(p.M, p.G);
+  hipLaunchKernelGGL(tgmm_plan_kernel, dim3(1), dim3(64), 0, st, p.group_sizes, p.G, p.M,
+                     p.a_scale_blk, p.a_scale_static, p.b_scale_blk, p.b_scale_static, p.plan,
+                     p.scprod);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.M > 0) {
+    e = a_fmt == FMT_E4M3
+            ? launch_qt<FMT_E4M3>(p.a, p.M, p.Kout, p.plan, p.G, p.a_scale_blk, p.a_inv_static, p.a_seg, seg_row, st)
+            : launch_qt<FMT_E5M2>(p.a, p.M, p.Kout, p.plan, p.G, p.a_scale_blk, p.a_inv_static, p.a_seg, seg_row, st);
+    if (e != hipSuccess) return e;
+    e = b_fmt == FMT_E4M3
+            ? launch_qt<FMT_E4M3>(p.b, p.M, p.Nout, p.plan, p.G, p.b_scale_blk, p.b_inv_static, p.b_seg, seg_row, st)
+            : launch_qt<FMT_E5M2>(p.b, p.M, p.Nout, p.plan, p.G, p.b_scale_blk, p.b_inv_static, p.b_seg, seg_row, st);
+    if (e != hipSuccess) return e;
+  }
+  TgmmSegParams q{};
+  q.a_seg = p.a_seg;
+  q.b_seg = p.b_seg;
+  q.plan = p.plan;
+  q.out = p.out;
+  q.scprod = p.scprod;
+  q.Kout = p.Kout;
+  q.Nout = p.Nout;
+  q.G = p.G;
+  q.out_f32 = p.out_f32;
+  q.seg_row = seg_row;
+  if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_tgmm_fp8<FMT_E4M3, FMT_E5M2>(q, st);
+  if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_tgmm_fp8<FMT_E4M3, FMT_E4M3>(q, st);
+  if (a_fmt == FMT_E5M2 && b_fmt == FMT_E5M2) return launch_tgmm_fp8<FMT_E5M2, FMT_E5M2>(q, st);
+  if (a_fmt == FMT_E5M2 && b_fmt == FMT_E4M3) return launch_tgmm_fp8<FMT_E5M2, FMT_E4M3>(q, st);
   return hipErrorInvalidValue;
 }
 

@@ -177,6 +177,9 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
  * block's partial sum is scaled before it is added.  lhs_scales / grad_scales: as
  * gmm_fwd's lhs_scales (outputs for DYNAMIC, may be NULL).
  * drhs [G, K, N] bf16 or f32.  A group with m_g == 0 gets a slab of +0.0.
+ * workspace    required: gmm_workspace_size(GMM_OP_TGMM, lhs_op, grad_op, M, K, N, G)
+ *              bytes.  It holds each operand quantized once and transposed so that the
+ *              rows of every group start on a 128-row block boundary.
  */
 gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
                        int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
@@ -184,18 +187,20 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
                        float* grad_scales, const int32_t* group_sizes, void* drhs,
                        void* workspace, size_t workspace_bytes, gmm_stream_t stream);
 
-/* Bytes of device workspace the call `op` needs for these operands and sizes (0 when
- * no operand is quantized dynamically in-kernel).  For GMM_OP_FWD / GMM_OP_DLHS, `a`
- * is the lhs / grad operand and `b` is ignored; for GMM_OP_TGMM, `a` is the lhs and
- * `b` the grad.  `rows` is M, `cols_a` / `cols_b` the row widths (K, N).
- * Returns 0 and sets *bytes. */
+/* Bytes of device workspace the call `op` needs for these operands and sizes.  For
+ * GMM_OP_FWD / GMM_OP_DLHS, `a` is the lhs / grad operand and `b` is ignored: the size
+ * is 0 unless the call computes dynamic block scales.  For GMM_OP_TGMM, `a` is the lhs
+ * and `b` the grad; tgmm always needs workspace for its quantized, transposed copies of
+ * both operands (about (K + N) x (M + 128 G) bytes).  `rows` is M, `cols_a` / `cols_b`
+ * the row widths (K and N), G the number of groups.  Sets *bytes. */
 gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_operand_t* b,
-                                int64_t rows, int64_t cols_a, int64_t cols_b, size_t* bytes);
+                                int64_t rows, int64_t cols_a, int64_t cols_b, int32_t G,
+                                size_t* bytes);
 
 /*
  * gmm_dynamic_scales - the abs-max prepass alone: per-block scales of a bf16 matrix
  * [R, C] for the DYNAMIC recipe of `format`, scales f32 [ceil(R/128)] (output).
- * workspace: gmm_workspace_size(GMM_OP_FWD, op{BF16, format, DYNAMIC}, NULL, R, C, 0).
+ * workspace: gmm_workspace_size(GMM_OP_FWD, op{BF16, format, DYNAMIC}, NULL, R, C, 0, 1).
  */
 gmm_status_t gmm_dynamic_scales(int32_t format, int64_t R, int64_t C, const void* x,
                                 float* scales, void* workspace, size_t workspace_bytes,
@@ -206,7 +211,7 @@ gmm_status_t gmm_dynamic_scales(int32_t format, int64_t R, int64_t C, const void
  * static or dynamic recipe above (codes [R, C]; scales f32 [ceil(R/128)]: output for
  * DYNAMIC, input for DYNAMIC_GIVEN, unused for STATIC).  The codes are byte-identical to those the fused
  * kernels form in registers.  Used for the pre-quantized-operand path (hybrid dlhs).
- * workspace: gmm_workspace_size(GMM_OP_FWD, op, NULL, R, C, 0, &bytes).
+ * workspace: gmm_workspace_size(GMM_OP_FWD, op, NULL, R, C, 0, 1, &bytes).
  */
 gmm_status_t gmm_quantize(const gmm_operand_t* op, int64_t R, int64_t C, const void* x,
                           uint8_t* codes, float* scales, void* workspace,

@@ -49,10 +49,15 @@ def test_workspace_sizes():
     n = g.gmm_workspace_size(g.OP_FWD, "e4m3", "dynamic", 1000)
     nb = 8
     assert n >= nb * (8 + 2) * 4 and n % 256 == 0
-    t = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "dynamic", 1000, b_fmt="e5m2", b_scaling="dynamic")
-    assert t == 2 * n
-    assert g.gmm_workspace_size(g.OP_TGMM, "e4m3", "static", 1000, b_scaling="static",
-                                static_scale=0.5) == 0
+    t = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "dynamic", 1000, 256, 384, b_fmt="e5m2",
+                             b_scaling="dynamic", groups=5)
+    seg = (8 + 5) * 128  # bytes per transposed row: ceil(1000/128) + G blocks
+    plan = 256  # 3 G + 1 ints, aligned
+    sc = 256  # one float per 128-row block, aligned
+    assert t == 2 * n + plan + sc + 256 * seg + 384 * seg
+    s = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "static", 1000, 256, 384, b_scaling="static",
+                             static_scale=0.5, groups=5)
+    assert s == plan + sc + 256 * seg + 384 * seg
 
 
 # ---- validation: fake but aligned device pointers; nothing is dereferenced -------------
@@ -122,7 +127,7 @@ def test_given_scales_validation():
     assert call_fwd(o=given, lhs_scales=None) == 1
     assert call_fwd(o=given, ws=None, ws_bytes=0, M=0) == 0
     n = ctypes.c_size_t()
-    assert lib.gmm_workspace_size(0, ctypes.byref(given), ctypes.byref(given), 1000, 256, 0, ctypes.byref(n)) == 0
+    assert lib.gmm_workspace_size(0, ctypes.byref(given), ctypes.byref(given), 1000, 256, 0, 1, ctypes.byref(n)) == 0
     assert n.value == 0
     a, b = op(fmt=0, scaling=2), op(fmt=1, scaling=2)
     assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), None,

@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=2048, help="at most 4096")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="copy 1 GiB device-to-device once before the steps (a known-size "
+                        "transfer for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -178,6 +181,13 @@ def main():
 
     wl = WORKLOADS[args.workload]
     step = Step(g, wl, seed=wl.seed * 100)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
     for _ in range(args.warmup):

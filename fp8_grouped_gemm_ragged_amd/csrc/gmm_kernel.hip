@@ -136,20 +136,11 @@ __device__ inline void transpose8x8(const v2u in[8], v2u out[8]) {
   }
 }
 
-// One wave fills 8 rows (1 KB) of a swizzled [rows][128 B] tile straight from global
-// memory: lane l lands at physical chunk l % 8 of row R0 + l / 8, so it fetches the
-// logical chunk tile_off() keeps there.
-__device__ inline void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_rows,
-                                        uint32_t goff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_rows, 16, goff, 0, 0, 0);
-}
-
 template <int A_FMT, int B_FMT, bool A_FP8, bool B_TRANS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void gmm_kernel(GemmParams p) {
-  // one LDS object per stage and operand, so that accesses to one stage provably do not
-  // alias the asynchronous direct loads into the other
+  // one LDS object per stage and operand: the compiler then sees that stores into the
+  // next stage never alias fragment reads of the current one
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_TILE];
@@ -193,31 +184,26 @@ void gmm_kernel(GemmParams p) {
     }
   }
 
-  v4u a_reg[A_FP8 ? 1 : 16];
+  // register stage of step kt+2: bf16 A pieces (2 x 16 B), fp8 A pieces (16 B), fp8 B
+  // pieces (16 B) or 8x8 blocks of an output-contiguous B
+  v4u a_reg[A_FP8 ? 8 : 16];
+  v4u bk_reg[B_TRANS ? 1 : 8];
   v2u b_reg[B_TRANS ? 16 : 1];
 
-  // Direct loads of the fp8 operands of step kt into one stage: wave w fills tile rows
-  // 64w .. 64w+63, eight rows per instruction.  Physical chunk (lane & 7) of row R holds
-  // logical chunk (lane & 7) ^ (R & 7) ^ ((R >> 3) & 7).
-  auto issue_direct = [&](int kt, uint8_t* at, uint8_t* bt) {
-    const uint32_t koff = (uint32_t)kt * BK;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r0 = wave * 64 + q * 8;
-      const int row = r0 + (lane >> 3);
-      const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
-      const uint32_t goff = (uint32_t)row * Kc + koff + c * 16;
-      if constexpr (A_FP8) load_rows_to_lds(ra, at + r0 * BK, goff);
-      if constexpr (!B_TRANS) load_rows_to_lds(rb, bt + r0 * BK, goff);
-    }
-  };
-  // register loads of step kt: bf16 A pieces and 8x8 blocks of an output-contiguous B
+  // piece i of a tile = rows 32 i .. 32 i + 31, one row per 8 lanes (row 32 i + tid/8),
+  // 16 contraction bytes per lane (chunk tid%8)
   auto load_a_piece = [&](int kt, int i) {
     if constexpr (!A_FP8) {
       const uint32_t off = (uint32_t)(i * 32 + lrow) * Kc * 2 + (uint32_t)kt * BK * 2 + lchunk * 32;
       a_reg[2 * i] = buf_load16(ra, off);
       a_reg[2 * i + 1] = buf_load16(ra, off + 16);
+    } else {
+      a_reg[i] = buf_load16(ra, (uint32_t)(i * 32 + lrow) * Kc + (uint32_t)kt * BK + lchunk * 16);
     }
+  };
+  auto load_bk_piece = [&](int kt, int i) {
+    if constexpr (!B_TRANS)
+      bk_reg[i] = buf_load16(rb, (uint32_t)(i * 32 + lrow) * Kc + (uint32_t)kt * BK + lchunk * 16);
   };
   auto load_b_block = [&](int kt, int it) {
     if constexpr (B_TRANS) {
@@ -238,7 +224,12 @@ void gmm_kernel(GemmParams p) {
       v4u q;
       q.x = lo.x; q.y = lo.y; q.z = hi.x; q.w = hi.y;
       *reinterpret_cast<v4u*>(at + tile_off(i * 32 + lrow, lchunk)) = q;
+    } else {
+      *reinterpret_cast<v4u*>(at + tile_off(i * 32 + lrow, lchunk)) = a_reg[i];
     }
+  };
+  auto store_bk_piece = [&](uint8_t* bt, int i) {
+    if constexpr (!B_TRANS) *reinterpret_cast<v4u*>(bt + tile_off(i * 32 + lrow, lchunk)) = bk_reg[i];
   };
   auto store_b_block = [&](uint8_t* bt, int it) {
     if constexpr (B_TRANS) {
@@ -252,14 +243,10 @@ void gmm_kernel(GemmParams p) {
         *reinterpret_cast<v2u*>(bt + tile_off(nb * 8 + c, kb >> 1) + (kb & 1) * 8) = t[c];
     }
   };
-  // Wait until this wave's direct loads into the stage being filled have landed (the
-  // register prefetches issued after them may still be in flight) and its LDS stores
-  // are done, then synchronise the workgroup.
+  // This wave's LDS stores of the stage being filled are done; then the workgroup.
+  // (Global loads only feed registers, so nothing else needs to land.)
   auto stage_barrier = [&]() {
-    if constexpr (A_FP8 && B_TRANS) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
-    else if constexpr (A_FP8) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    else if constexpr (B_TRANS) asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -321,7 +308,6 @@ void gmm_kernel(GemmParams p) {
   // that the scheduler keeps the interleaving (the matrix core works through each MFMA
   // while the vector ALU runs the next slice).
   auto step = [&](int kt, const uint8_t* at, const uint8_t* bt, uint8_t* an, uint8_t* bn) {
-    issue_direct(kt + 1, an, bn);
     v8i af[4], bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[i] = frag(at, wr * 128, i, 0);
@@ -335,15 +321,27 @@ void gmm_kernel(GemmParams p) {
       // fragments of the second half step, each right after its last use
       if (ks == 0 && j == 3) af[i] = frag(at, wr * 128, i, 1);
       if (ks == 0 && i == 3) bf[j] = frag(bt, wc * 128, j, 1);
-      if constexpr (!A_FP8) {
-        // piece u/4 of step kt+1: quarter u%4, then store it and refill its registers
+      {
+        // piece u/4 of step kt+1: A (quantized a quarter per MFMA), then B; each piece is
+        // stored to the next stage and its registers refilled with step kt+2
         const int piece = u >> 2, d = u & 3;
-        qd[d] = quant_dword(piece, d);
-        if (d == 3) {
-          v4u q;
-          q.x = qd[0]; q.y = qd[1]; q.z = qd[2]; q.w = qd[3];
-          *reinterpret_cast<v4u*>(an + piece * 32 * BK + so[piece & 1]) = q;
+        if constexpr (!A_FP8) {
+          qd[d] = quant_dword(piece, d);
+          if (d == 3) {
+            v4u q;
+            q.x = qd[0]; q.y = qd[1]; q.z = qd[2]; q.w = qd[3];
+            *reinterpret_cast<v4u*>(an + piece * 32 * BK + so[piece & 1]) = q;
+            load_a_piece(kt + 2, piece);
+          }
+        } else if (d == 1) {
+          *reinterpret_cast<v4u*>(an + piece * 32 * BK + so[piece & 1]) = a_reg[piece];
           load_a_piece(kt + 2, piece);
+        }
+        if constexpr (!B_TRANS) {
+          if (d == 2) {
+            *reinterpret_cast<v4u*>(bn + piece * 32 * BK + so[piece & 1]) = bk_reg[piece];
+            load_bk_piece(kt + 2, piece);
+          }
         }
       }
       if constexpr (B_TRANS) {
@@ -356,17 +354,16 @@ void gmm_kernel(GemmParams p) {
   };
 
   // ---- prologue: step 0 into stage 0, step 1 into registers ----
-  issue_direct(0, sA0, sB0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) load_a_piece(0, i);
+  for (int i = 0; i < 8; ++i) { load_a_piece(0, i); load_bk_piece(0, i); }
   load_b_block(0, 0);
   load_b_block(0, 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) store_a_piece(sA0, i);
+  for (int i = 0; i < 8; ++i) { store_a_piece(sA0, i); store_bk_piece(sB0, i); }
   store_b_block(sB0, 0);
   store_b_block(sB0, 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) load_a_piece(1, i);
+  for (int i = 0; i < 8; ++i) { load_a_piece(1, i); load_bk_piece(1, i); }
   load_b_block(1, 0);
   load_b_block(1, 1);
   stage_barrier();

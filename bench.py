@@ -6,14 +6,15 @@ routing), inputs resident in HBM:
 
   1. block scales of lhs  (abs-max prepass, e4m3, 128 rows x K)
   2. gmm_fwd   out[M, N]      = q(lhs) . rhs[g]        (bf16 lhs quantized in-kernel)
-  3. block scales of grad (abs-max prepass, e5m2, 128 rows x N)
-  4. gmm_dlhs  dlhs[M, K]     = q(grad) . rhs[g]^T
+  3. quantize grad once       (e5m2 codes [M, N] + 128-row block scales)
+  4. gmm_dlhs  dlhs[M, K]     = q(grad) . rhs[g]^T     (hybrid: fp8 codes of step 3)
   5. tgmm_drhs drhs[G, K, N]  = q(lhs)_g^T . q(grad)_g  (scales of steps 1 and 3 reused)
 
-value = 3 * 2*M*K*N / step time (TFLOP/s).  Each product call is a single kernel launch,
-timed with HIP events on the stream it runs on; the slowest one is reported against the
-dense FP8 MFMA peak (5.0 PFLOP/s).  The CPU oracle is timed on a bounded sample of the same
-workload (rank 0, N=1) for reference.
+value = 3 * 2*M*K*N / step time (TFLOP/s).  Every call is timed with HIP events on the
+stream it runs on.  gmm_fwd and gmm_dlhs are one kernel launch each; tgmm_drhs is a plan
+kernel, two quantize-transpose kernels and the fp8 tgmm kernel, and its window holds all
+four.  The slowest product window is reported against the dense FP8 MFMA peak (5.0
+PFLOP/s).  The CPU oracle is timed on a bounded sample of the same workload (N=1).
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 """
@@ -80,6 +81,7 @@ class Step:
         nb = (M + 127) // 128
         self.s_lhs = torch.empty(nb, dtype=torch.float32, device=dev)
         self.s_grad = torch.empty(nb, dtype=torch.float32, device=dev)
+        self.grad_q = torch.empty((M, N), dtype=torch.uint8, device=dev)
         op = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC, 0.0)
         n = g._SZ()
         self._chk(lib.gmm_workspace_size(g.OP_FWD, ctypes.byref(op), ctypes.byref(op), M,
@@ -94,15 +96,18 @@ class Step:
         self.ws_t_n = n.value
         self.op_lhs = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
         self.op_grad = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC_GIVEN, 0.0)
+        self.op_gq = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC, 0.0)     # quantizer recipe
+        self.op_g8 = g.Operand(g.KIND_FP8, g.E5M2, g.DYNAMIC, 0.0)      # its codes as dlhs A
         self.r_lhs, self.r_grad = ctypes.byref(self.op_lhs), ctypes.byref(self.op_grad)
+        self.r_gq, self.r_g8 = ctypes.byref(self.op_gq), ctypes.byref(self.op_g8)
         P = lambda t: t.data_ptr()
         self.p = {k: P(getattr(self, k)) for k in
-                  ("lhs", "grad", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs", "drhs",
+                  ("lhs", "grad", "grad_q", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs", "drhs",
                    "s_lhs", "s_grad", "ws", "ws_t", "gs")}
         torch.cuda.synchronize()
 
     def run(self, stream, ev=None):
-        """Enqueue one step; ev (6 events) brackets: scales, fwd, scales, dlhs, tgmm."""
+        """Enqueue one step; ev (6 events) brackets: scales, fwd, quantize, dlhs, tgmm."""
         lib, p, s = self.lib, self.p, stream
         M, K, N, G = self.M, self.K, self.N, self.G
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
@@ -113,10 +118,10 @@ class Step:
         chk(lib.gmm_fwd(self.r_lhs, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
                         p["lhs"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"], None, 0, s))
         rec(2)
-        chk(lib.gmm_dynamic_scales(self.g.E5M2, M, N, p["grad"], p["s_grad"], p["ws"], self.ws_n, s))
+        chk(lib.gmm_quantize(self.r_gq, M, N, p["grad"], p["grad_q"], p["s_grad"], p["ws"], self.ws_n, s))
         rec(3)
-        chk(lib.gmm_dlhs(self.r_grad, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
-                         p["grad"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, s))
+        chk(lib.gmm_dlhs(self.r_g8, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
+                         p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, s))
         rec(4)
         chk(lib.tgmm_drhs(self.r_lhs, self.r_grad, self.g.OUT_BF16, M, K, N, G, p["lhs"], p["s_lhs"],
                           p["grad"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
@@ -200,7 +205,7 @@ def main():
         step.run(s, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["scales_lhs", "gmm_fwd", "scales_grad", "gmm_dlhs", "tgmm_drhs"]
+    names = ["scales_lhs", "gmm_fwd", "quantize_grad", "gmm_dlhs", "tgmm_drhs"]
     per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
            for j, n in enumerate(names)}
     ms_step = wall * 1000.0 / args.steps
@@ -211,9 +216,10 @@ def main():
            for n in ("gmm_fwd", "gmm_dlhs", "tgmm_drhs")}
     dom = max(ops, key=lambda n: per[n])
     ach = flop_op / (per[dom] / 1000.0) / 1e12
-    kern = {"gmm_fwd": "gmm_kernel<e4m3,e4m3,bf16-A,K-contiguous B>",
-            "gmm_dlhs": "gmm_kernel<e5m2,e4m3,bf16-A,N-contiguous B>",
-            "tgmm_drhs": "tgmm_kernel<e4m3,e5m2>"}[dom]
+    kern = {"gmm_fwd": "gmm_kernel<e4m3,e4m3,bf16 A,contraction-contiguous B>",
+            "gmm_dlhs": "gmm_kernel<e5m2,e4m3,fp8 A,contraction-contiguous B>",
+            "tgmm_drhs": "tgmm_plan + quant_transpose<e4m3> + quant_transpose<e5m2> + "
+                         "tgmm_fp8_kernel<e4m3,e5m2>"}[dom]
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -222,8 +228,10 @@ def main():
         "config": {"workload": wl.name, "G": wl.G, "M": wl.M, "K": wl.K, "N": wl.N,
                    "routing": f"zipf{wl.zipf_s}", "group_sizes": [int(x) for x in wl.group_sizes()],
                    "lhs": "bf16 -> e4m3 dynamic 128-row blocks", "grad": "bf16 -> e5m2 dynamic 128-row blocks",
-                   "rhs": "e4m3 per-channel", "out": "bf16", "step": "scales+fwd+scales+dlhs+tgmm"},
-        "ops": ops, "scales_ms": {"lhs": round(per["scales_lhs"], 4), "grad": round(per["scales_grad"], 4)},
+                   "rhs": "e4m3 per-channel", "out": "bf16",
+                   "step": "lhs scales + fused fwd + grad quantize + hybrid dlhs + tgmm"},
+        "ops": ops, "prep_ms": {"lhs_scales": round(per["scales_lhs"], 4),
+                                "grad_quantize": round(per["quantize_grad"], 4)},
         "roofline": {"kernel": kern, "op": dom, "bound": "mfma", "achieved": round(ach, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
                      "traffic": None},

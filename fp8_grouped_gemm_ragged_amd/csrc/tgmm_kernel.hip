@@ -28,6 +28,7 @@ namespace {
 
 constexpr int TBM = 256;   // k rows of a slab tile
 constexpr int TBN = 128;   // n columns of a slab tile
+constexpr int ST_K = 4;    // k-tiles per band of the tile order
 constexpr int NT = 256;
 constexpr int A_TILE = TBM * TILE_K;  // [256 k][128 m] fp8
 constexpr int B_TILE = TBN * TILE_K;  // [128 n][128 m] fp8
@@ -156,14 +157,31 @@ void tgmm_fp8_kernel(TgmmSegParams p) {
   const int total = n_kt * n_nt * p.G;
   const int wg = blockIdx.x;
   if (wg >= total) return;
-  // Workgroup i runs on XCD i % 8: each XCD owns a contiguous range of the tile order,
-  // and tiles are ordered group-fastest, so every XCD holds an equal share of every
-  // group (the work of a tile grows with its group's row count).
+  // Workgroup i runs on XCD i % 8 and each XCD owns a contiguous range of the tile
+  // order.  That order is made of 32-tile super-tiles (the workgroups one XCD runs at a
+  // time), cycling over the groups so that every XCD holds an equal share of every
+  // group's work (a tile's work grows with its group's row count).  Inside a group,
+  // tiles run in bands of ST_K k-tiles, k-tile fastest, so one super-tile is ST_K k-tiles
+  // x 32/ST_K n-tiles: each A block it reads is shared by 32/ST_K workgroups and each
+  // B block by ST_K of them while they sit together in the XCD's L2.  Tiles past the
+  // last whole super-tile of each group follow, group-fastest.
   const int xcd = wg & 7, jx = wg >> 3, qx = total >> 3, rx = total & 7;
   const int L = xcd * qx + min(xcd, rx) + jx;
-  const int g = L % p.G;
-  const int t = L / p.G;
-  const int kt = t / n_nt, nt = t - kt * n_nt;
+  const int T = n_kt * n_nt, T32 = T & ~31;
+  int g, t;
+  if (L < p.G * T32) {
+    const int S = L >> 5;
+    g = S % p.G;
+    t = (S / p.G) * 32 + (L & 31);
+  } else {
+    const int r = L - p.G * T32;
+    g = r % p.G;
+    t = T32 + r / p.G;
+  }
+  const int kt_base = t / (ST_K * n_nt) * ST_K;
+  const int band_rows = min(ST_K, n_kt - kt_base);
+  const int rt = t - kt_base * n_nt;
+  const int kt = kt_base + rt % band_rows, nt = rt / band_rows;
   const int k0 = kt * TBM, n0 = nt * TBN;
   const int32_t* off = p.plan;
   const int32_t* sg = p.plan + 2 * p.G;

@@ -12,8 +12,8 @@ routing), inputs resident in HBM:
 
 value = 3 * 2*M*K*N / step time (TFLOP/s).  Every call is timed with HIP events on the
 stream it runs on.  gmm_fwd and gmm_dlhs are one kernel launch each; tgmm_drhs is a plan
-kernel, two quantize-transpose kernels and the fp8 tgmm kernel, and its window holds all
-four.  The slowest product window is reported against the dense FP8 MFMA peak (5.0
+kernel, two quantize-transpose kernels, the fp8 tgmm kernel and its wide-range fallback
+(which exits at once here), and its window holds all five.  The slowest product window is reported against the dense FP8 MFMA peak (5.0
 PFLOP/s).  The CPU oracle is timed on a bounded sample of the same workload (N=1).
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
@@ -219,7 +219,7 @@ def main():
     kern = {"gmm_fwd": "gmm_kernel<e4m3,e4m3,bf16 A,contraction-contiguous B>",
             "gmm_dlhs": "gmm_kernel<e5m2,e4m3,fp8 A,contraction-contiguous B>",
             "tgmm_drhs": "tgmm_plan + quant_transpose<e4m3> + quant_transpose<e5m2> + "
-                         "tgmm_fp8_kernel<e4m3,e5m2>"}[dom]
+                         "tgmm_ratio_kernel<e4m3,e5m2> + tgmm_promote_kernel (exits: no wide group)"}[dom]
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -57,11 +57,13 @@ DynWs carve(void* base, int64_t rows) {
 
 // The call runs the abs-max prepass itself (and needs workspace) only for a bf16
 // operand with GMM_SCALE_DYNAMIC.
-// tgmm: plan (3 G + 1 ints) and the two quantized, transposed segment buffers.
+// tgmm: plan words, per-block scale products, per-segment-block ratios and the two
+// quantized, transposed segment buffers.
 size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int32_t G) {
   const size_t seg_row = (size_t)tgmm_segment_row_bytes(M, G);
-  return align256((size_t)(3 * G + 1) * 4) + align256((size_t)nblocks(M) * 4) +
-         align256((size_t)K * seg_row) + align256((size_t)N * seg_row);
+  return align256((size_t)tgmm_plan_words(G) * 4) + align256((size_t)nblocks(M) * 4) +
+         align256((size_t)(nblocks(M) + 2 * G) * 4) + align256((size_t)K * seg_row) +
+         align256((size_t)N * seg_row);
 }
 
 bool needs_dyn_ws(const gmm_operand_t* op) {
@@ -278,8 +280,9 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
     uint8_t* base = (uint8_t*)workspace + wa + wb;
     const size_t seg_row = (size_t)tgmm_segment_row_bytes(M, G);
     p.plan = (int32_t*)base;
-    p.scprod = (float*)(base + align256((size_t)(3 * G + 1) * 4));
-    p.a_seg = (uint8_t*)p.scprod + align256((size_t)nblocks(M) * 4);
+    p.scprod = (float*)(base + align256((size_t)tgmm_plan_words(G) * 4));
+    p.ratio = (float*)((uint8_t*)p.scprod + align256((size_t)nblocks(M) * 4));
+    p.a_seg = (uint8_t*)p.ratio + align256((size_t)(nblocks(M) + 2 * G) * 4);
     p.b_seg = p.a_seg + align256((size_t)K * seg_row);
   }
   if (M > 0) {

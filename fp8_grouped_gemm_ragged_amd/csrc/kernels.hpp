@@ -34,8 +34,9 @@ struct TgmmParams {
   const uint16_t* b;         // bf16 [M, Nout]
   const int32_t* group_sizes;
   void* out;                 // [G, Kout, Nout] bf16 or f32
-  int32_t* plan;             // workspace: 3 G + 1 ints
+  int32_t* plan;             // workspace: tgmm_plan_words(G) words
   float* scprod;             // workspace: one scale product per 128-row block
+  float* ratio;              // workspace: ceil(M / 128) + 2 G floats
   uint8_t* a_seg;            // workspace: Kout x tgmm_segment_row_bytes(M, G)
   uint8_t* b_seg;            // workspace: Nout x tgmm_segment_row_bytes(M, G)
   const float* a_scale_blk;  // dynamic: per-block scales; null -> static
@@ -52,12 +53,15 @@ struct TgmmSegParams {
   const uint8_t* b_seg;
   const int32_t* plan;
   const float* scprod;
+  const float* ratio;
   void* out;
   int32_t Kout, Nout, G, out_f32;
   int64_t seg_row;
 };
 
 int64_t tgmm_segment_row_bytes(int64_t M, int G);
+// plan words: off, cnt, seg (G + 1), wide, final scale per group, one any-wide flag
+inline int64_t tgmm_plan_words(int G) { return 5 * (int64_t)G + 2; }
 
 hipError_t launch_gemm(int a_fmt, int b_fmt, bool a_fp8, bool b_trans, const GemmParams& p,
                        hipStream_t st);

@@ -52,12 +52,13 @@ def test_workspace_sizes():
     t = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "dynamic", 1000, 256, 384, b_fmt="e5m2",
                              b_scaling="dynamic", groups=5)
     seg = (8 + 5) * 128  # bytes per transposed row: ceil(1000/128) + G blocks
-    plan = 256  # 3 G + 1 ints, aligned
+    plan = 256  # 5 G + 2 words, aligned
     sc = 256  # one float per 128-row block, aligned
-    assert t == 2 * n + plan + sc + 256 * seg + 384 * seg
+    ratio = 256  # ceil(1000/128) + 2 G floats, aligned
+    assert t == 2 * n + plan + sc + ratio + 256 * seg + 384 * seg
     s = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "static", 1000, 256, 384, b_scaling="static",
                              static_scale=0.5, groups=5)
-    assert s == plan + sc + 256 * seg + 384 * seg
+    assert s == plan + sc + ratio + 256 * seg + 384 * seg
 
 
 # ---- validation: fake but aligned device pointers; nothing is dereferenced -------------

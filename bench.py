@@ -32,6 +32,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "FP8 GMM TFLOP/s (fwd/dlhs/drhs) and % of MI355X FP8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash():
+    """sha256 (first 16 hex) over the HIP sources, as recorded with the HBM counters."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_grouped_gemm_ragged_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(op, workload):
+    """HBM bytes per launch of `op` from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when there is none for this workload or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_hash") != kernel_source_hash():
+        return None
+    entry = t.get("ops", {}).get(op)
+    return int(entry["traffic_bytes"]) if entry else None
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 
 
@@ -234,7 +263,9 @@ def main():
                                 "grad_quantize": round(per["quantize_grad"], 4)},
         "roofline": {"kernel": kern, "op": dom, "bound": "mfma", "achieved": round(ach, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dom, wl.name),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
+                                     "1 GiB copy; null once the kernel sources changed)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)

@@ -1,0 +1,202 @@
+"""Full-size GPU parity at the benchmark workloads' shapes, on sampled outputs.
+
+Each product runs through the library as bench.py launches it: device-resident bf16
+inputs from the seeded generators, block scales from the abs-max prepass handed in as
+given scales, bf16 outputs (and once more with f32 outputs for the 1e-3 metric).  The
+oracle then recomputes a sample of the outputs from the same bf16 inputs: the dynamic
+block scales from whole 128-row blocks, the codes only for the sampled rows (and, for
+the weights, only the sampled channels), the grouped products over the sample.  Scales
+and sampled codes are compared byte for byte.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.fp8 import bf16_bits_to_f32
+from oracle.gmm import gmm_dlhs_ref, gmm_fwd_ref, tgmm_ref
+from oracle.quant import (block_amax, dynamic_scale_from_amax, quantize_rhs_per_channel,
+                          quantize_with_inv, static_inv)
+from synth.workloads import WORKLOADS, bf16_to_bits, normal_bf16
+from tests.gpu_util import DEV, gs_tensor, sync
+from tests.parity import TOL, assert_bf16_close, group_rel_err, group_row_ranges, to_np
+
+pytestmark = pytest.mark.gpu
+
+S_4_448 = float(np.float32(4.0) / np.float32(448.0))
+
+
+def sample_rows(sizes, rng, per_group=3):
+    """First and last row of every group, rows on both sides of a 128-row block boundary
+    inside it, and a few random rows."""
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    rows = set()
+    for g in range(len(sizes)):
+        a, b = int(off[g]), int(off[g + 1])
+        if b == a:
+            continue
+        rows.update({a, b - 1})
+        rows.update(int(r) for r in rng.integers(a, b, size=per_group))
+        edge = (a // 128 + 1) * 128
+        if edge < b:
+            rows.update({edge - 1, edge})
+    return np.array(sorted(rows), np.int64)
+
+
+def sample_cols(n, rng, count=64):
+    """Both ends, both sides of the gate|up seam at n/2, and random columns."""
+    cols = {0, n - 1, n // 2 - 1, n // 2}
+    cols.update(int(c) for c in rng.integers(0, n, size=count))
+    return np.array(sorted(cols), np.int64)
+
+
+def sampled_sizes(rows, sizes):
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    return np.array([int(((rows >= off[g]) & (rows < off[g + 1])).sum())
+                     for g in range(len(sizes))], np.int32)
+
+
+def dynamic_block_scales(x_bits, fmt):
+    return dynamic_scale_from_amax(block_amax(x_bits, 128), fmt)
+
+
+def check_sampled(Ybf, Y32, R, sub_sizes):
+    ranges = group_row_ranges(sub_sizes)
+    err = group_rel_err(Y32, R, ranges)
+    print(f"sampled max group relative error {err:.3e} over {R.size} outputs", flush=True)
+    assert err <= TOL, err
+    assert_bf16_close(Ybf, R, ranges)
+
+
+def test_mixtral_gate_up_forward(lib):
+    wl = WORKLOADS["mixtral_gate_up"]
+    G, M, K, N = wl.G, wl.M, wl.K, wl.N
+    sizes = wl.group_sizes()
+    seed = wl.seed * 100
+    x = normal_bf16((M, K), 1.0, seed, DEV)
+    w = normal_bf16((G, K, N), 0.02, seed + 1, DEV)
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    s = lib.gmm_dynamic_scales(x, "e4m3")
+    out = lib.gmm_fwd(x, wq, ws, gs, lhs_scaling="dynamic_given", lhs_scales=s)
+    out32 = lib.gmm_fwd(x, wq, ws, gs, lhs_scaling="dynamic_given", lhs_scales=s,
+                        out_dtype=torch.float32)
+    sync()
+    rng = np.random.default_rng(2)
+    rows, cols = sample_rows(sizes, rng), sample_cols(N, rng)
+    xb = bf16_to_bits(x)
+    s_ref, inv_ref = dynamic_block_scales(xb, "e4m3")
+    assert np.array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    a_codes = quantize_with_inv(bf16_bits_to_f32(xb[rows]), inv_ref[rows // 128], "e4m3")
+    b_codes, b_s = quantize_rhs_per_channel(bf16_to_bits(w[:, :, cols]), "e4m3", "n")
+    ci = torch.as_tensor(cols, device=DEV)
+    assert np.array_equal(to_np(ws[:, ci]).view(np.uint32), b_s.view(np.uint32))
+    assert np.array_equal(np.transpose(to_np(wq[:, ci, :]), (0, 2, 1)), b_codes)
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_fwd_ref(a_codes, "e4m3", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    ri = torch.as_tensor(rows, device=DEV)
+    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub)
+
+
+@pytest.fixture(scope="module")
+def deepseek():
+    """The DeepSeek-style local-expert tensors, generated once for the module."""
+    wl = WORKLOADS["deepseek_local"]
+    G, M, K, N = wl.G, wl.M, wl.K, wl.N
+    seed = wl.seed * 100
+    sizes = wl.group_sizes()
+    assert sizes[0] == 0 and sizes[17] == 0
+    x = normal_bf16((M, K), 1.0, seed, DEV)
+    w = normal_bf16((G, K, N), 0.02, seed + 1, DEV)
+    grad = normal_bf16((M, N), 1e-3, seed + 2, DEV)
+    return wl, sizes, x, w, grad
+
+
+def test_deepseek_local_forward_static(lib, deepseek):
+    wl, sizes, x, w, _ = deepseek
+    N = wl.N
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    out = lib.gmm_fwd(x, wq, ws, gs, lhs_scaling="static", static_scale=S_4_448)
+    out32 = lib.gmm_fwd(x, wq, ws, gs, lhs_scaling="static", static_scale=S_4_448,
+                        out_dtype=torch.float32)
+    sync()
+    rng = np.random.default_rng(3)
+    rows, cols = sample_rows(sizes, rng), sample_cols(N, rng)
+    inv = static_inv(np.float32(S_4_448))
+    a_codes = quantize_with_inv(bf16_bits_to_f32(bf16_to_bits(x[torch.as_tensor(rows, device=DEV)])),
+                                np.full(len(rows), inv, np.float32), "e4m3")
+    b_codes, b_s = quantize_rhs_per_channel(bf16_to_bits(w[:, :, cols]), "e4m3", "n")
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_fwd_ref(a_codes, "e4m3", np.full(len(rows), S_4_448, np.float32), b_codes, "e4m3",
+                    b_s, sub)
+    ri, ci = torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)
+    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub)
+
+
+@pytest.mark.parametrize("route", ["hybrid", "fused"])
+def test_deepseek_local_dlhs(lib, deepseek, route):
+    wl, sizes, _, w, grad = deepseek
+    K = wl.K
+    gs = gs_tensor(sizes)
+    wk, sk = lib.gmm_quantize_rhs(w, "e4m3", 1, "kn")
+    if route == "hybrid":  # as the benchmark step: quantize once, then the fp8-A product
+        gq, sg = lib.gmm_quantize(grad, "e5m2", "dynamic")
+        a, kw = gq, dict(grad_format="e5m2", grad_scaling="dynamic", grad_scales=sg)
+    else:
+        sg = lib.gmm_dynamic_scales(grad, "e5m2")
+        a, kw = grad, dict(grad_format="e5m2", grad_scaling="dynamic_given", grad_scales=sg)
+    out = lib.gmm_dlhs(a, wk, sk, gs, **kw)
+    out32 = lib.gmm_dlhs(a, wk, sk, gs, out_dtype=torch.float32, **kw)
+    sync()
+    rng = np.random.default_rng(4)
+    rows, kcols = sample_rows(sizes, rng), sample_cols(K, rng)
+    gb = bf16_to_bits(grad)
+    s_ref, inv_ref = dynamic_block_scales(gb, "e5m2")
+    assert np.array_equal(to_np(sg).view(np.uint32), s_ref.view(np.uint32))
+    g_codes = quantize_with_inv(bf16_bits_to_f32(gb[rows]), inv_ref[rows // 128], "e5m2")
+    if route == "hybrid":
+        assert np.array_equal(to_np(gq[torch.as_tensor(rows, device=DEV)]), g_codes)
+    b_codes, b_s = quantize_rhs_per_channel(bf16_to_bits(w[:, kcols, :]), "e4m3", "k")
+    ki = torch.as_tensor(kcols, device=DEV)
+    assert np.array_equal(to_np(sk[:, ki]).view(np.uint32), b_s.view(np.uint32))
+    assert np.array_equal(to_np(wk[:, ki, :]), b_codes)
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_dlhs_ref(g_codes, "e5m2", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    ri = torch.as_tensor(rows, device=DEV)
+    check_sampled(to_np(out[ri][:, ki]), to_np(out32[ri][:, ki]), R, sub)
+
+
+def test_deepseek_local_tgmm(lib, deepseek):
+    wl, sizes, x, _, grad = deepseek
+    G, K, N = wl.G, wl.K, wl.N
+    gs = gs_tensor(sizes)
+    sa = lib.gmm_dynamic_scales(x, "e4m3")
+    sg = lib.gmm_dynamic_scales(grad, "e5m2")
+    kw = dict(lhs_scaling="dynamic_given", lhs_scales=sa, grad_scaling="dynamic_given",
+              grad_scales=sg)
+    out = lib.tgmm_drhs(x, grad, gs, **kw)
+    out32 = lib.tgmm_drhs(x, grad, gs, out_dtype=torch.float32, **kw)
+    sync()
+    rng = np.random.default_rng(5)
+    ks, ns = sample_cols(K, rng, 32), sample_cols(N, rng, 32)
+    xb, gb = bf16_to_bits(x), bf16_to_bits(grad)
+    sa_ref, ia = dynamic_block_scales(xb, "e4m3")
+    sg_ref, ig = dynamic_block_scales(gb, "e5m2")
+    assert np.array_equal(to_np(sa).view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(to_np(sg).view(np.uint32), sg_ref.view(np.uint32))
+    rb = np.arange(wl.M) // 128
+    a_codes = quantize_with_inv(bf16_bits_to_f32(xb[:, ks]), ia[rb], "e4m3")
+    g_codes = quantize_with_inv(bf16_bits_to_f32(gb[:, ns]), ig[rb], "e5m2")
+    R = tgmm_ref(a_codes, "e4m3", sa_ref, g_codes, "e5m2", sg_ref, np.asarray(sizes))
+    ki, ni = torch.as_tensor(ks, device=DEV), torch.as_tensor(ns, device=DEV)
+    Ybf = to_np(out[:, ki][:, :, ni])
+    Y32 = to_np(out32[:, ki][:, :, ni])
+    for g in (0, 17):  # the empty experts: whole slabs of +0.0
+        assert (to_np(out32[g]).view(np.uint32) == 0).all()
+        assert (to_np(out[g]) == 0).all()
+    ranges = [(g, g + 1) for g in range(G)]
+    err = group_rel_err(Y32, R, ranges)
+    print(f"sampled max slab relative error {err:.3e}", flush=True)
+    assert err <= TOL, err
+    assert_bf16_close(Ybf, R, ranges)

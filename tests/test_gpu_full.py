@@ -200,3 +200,148 @@ def test_deepseek_local_tgmm(lib, deepseek):
     print(f"sampled max slab relative error {err:.3e}", flush=True)
     assert err <= TOL, err
     assert_bf16_close(Ybf, R, ranges)
+
+
+# ---- the MoE SwiGLU feed-forward chain, forward and backward -------------------------
+
+def _check_fwd(lib, lhs, scaling, s_gpu, w_bits_cols, wq, ws, cols, sizes, out, out32, rng,
+               w_layout="nk"):
+    """One forward product against the oracle on sampled rows x the sampled columns."""
+    rows = sample_rows(sizes, rng)
+    lb = bf16_to_bits(lhs)
+    if scaling == "static":
+        inv = static_inv(np.float32(S_4_448))
+        s_row = np.full(len(rows), S_4_448, np.float32)
+        a_codes = quantize_with_inv(bf16_bits_to_f32(lb[rows]), np.full(len(rows), inv, np.float32), "e4m3")
+    else:
+        s_ref, inv_ref = dynamic_block_scales(lb, "e4m3")
+        assert np.array_equal(to_np(s_gpu).view(np.uint32), s_ref.view(np.uint32))
+        s_row = s_ref[rows // 128]
+        a_codes = quantize_with_inv(bf16_bits_to_f32(lb[rows]), inv_ref[rows // 128], "e4m3")
+    b_codes, b_s = quantize_rhs_per_channel(w_bits_cols, "e4m3", "n")
+    ci = torch.as_tensor(cols, device=DEV)
+    assert np.array_equal(to_np(ws[:, ci]).view(np.uint32), b_s.view(np.uint32))
+    assert np.array_equal(np.transpose(to_np(wq[:, ci, :]), (0, 2, 1)), b_codes)
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_fwd_ref(a_codes, "e4m3", s_row, b_codes, "e4m3", b_s, sub)
+    ri = torch.as_tensor(rows, device=DEV)
+    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub)
+
+
+def _check_dlhs(grad, s_gpu, w_bits_krows, wk, sk, kcols, sizes, out, out32, rng):
+    rows = sample_rows(sizes, rng)
+    gb = bf16_to_bits(grad)
+    s_ref, inv_ref = dynamic_block_scales(gb, "e5m2")
+    assert np.array_equal(to_np(s_gpu).view(np.uint32), s_ref.view(np.uint32))
+    g_codes = quantize_with_inv(bf16_bits_to_f32(gb[rows]), inv_ref[rows // 128], "e5m2")
+    b_codes, b_s = quantize_rhs_per_channel(w_bits_krows, "e4m3", "k")
+    ki = torch.as_tensor(kcols, device=DEV)
+    assert np.array_equal(to_np(sk[:, ki]).view(np.uint32), b_s.view(np.uint32))
+    assert np.array_equal(to_np(wk[:, ki, :]), b_codes)
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_dlhs_ref(g_codes, "e5m2", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    ri = torch.as_tensor(rows, device=DEV)
+    check_sampled(to_np(out[ri][:, ki]), to_np(out32[ri][:, ki]), R, sub)
+
+
+def _check_tgmm(lhs, grad, sa, sg, sizes, out, out32, rng):
+    M, K = lhs.shape
+    N = grad.shape[1]
+    ks, ns = sample_cols(K, rng, 24), sample_cols(N, rng, 24)
+    lb, gb = bf16_to_bits(lhs), bf16_to_bits(grad)
+    sa_ref, ia = dynamic_block_scales(lb, "e4m3")
+    sg_ref, ig = dynamic_block_scales(gb, "e5m2")
+    assert np.array_equal(to_np(sa).view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(to_np(sg).view(np.uint32), sg_ref.view(np.uint32))
+    rb = np.arange(M) // 128
+    a_codes = quantize_with_inv(bf16_bits_to_f32(lb[:, ks]), ia[rb], "e4m3")
+    g_codes = quantize_with_inv(bf16_bits_to_f32(gb[:, ns]), ig[rb], "e5m2")
+    R = tgmm_ref(a_codes, "e4m3", sa_ref, g_codes, "e5m2", sg_ref, np.asarray(sizes))
+    ki, ni = torch.as_tensor(ks, device=DEV), torch.as_tensor(ns, device=DEV)
+    ranges = [(g, g + 1) for g in range(len(sizes))]
+    err = group_rel_err(to_np(out32[:, ki][:, :, ni]), R, ranges)
+    print(f"sampled max slab relative error {err:.3e}", flush=True)
+    assert err <= TOL, err
+    assert_bf16_close(to_np(out[:, ki][:, :, ni]), R, ranges)
+
+
+@pytest.fixture(scope="module")
+def swiglu():
+    wl = WORKLOADS["moe_swiglu"]
+    G, M, H = wl.G, wl.M, wl.K
+    inter = wl.extra["intermediate"]
+    seed = wl.seed * 100
+    sizes = wl.group_sizes()
+    x = normal_bf16((M, H), 1.0, seed, DEV)
+    w_gu = normal_bf16((G, H, 2 * inter), 0.02, seed + 1, DEV)
+    w_down = normal_bf16((G, inter, H), 0.02, seed + 2, DEV)
+    grad_y = normal_bf16((M, H), 1e-3, seed + 3, DEV)
+    return wl, sizes, x, w_gu, w_down, grad_y
+
+
+@pytest.mark.parametrize("scaling", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", ["pure", "hybrid"])
+def test_moe_swiglu_chain(lib, swiglu, mode, scaling):
+    """gate|up gmm, SwiGLU, down gmm; dlhs of both; tgmm of both.  Every product is
+    checked against the oracle on the GPU-produced inputs it was given (the SwiGLU
+    itself is test glue, computed with torch in fp32)."""
+    wl, sizes, x, w_gu, w_down, grad_y = swiglu
+    inter = wl.extra["intermediate"]
+    gs = gs_tensor(sizes)
+    rng = np.random.default_rng(6)
+    fwd_kw = (dict(lhs_scaling="static", static_scale=S_4_448) if scaling == "static"
+              else dict(lhs_scaling="dynamic"))
+
+    def fwd(lhs, wq, ws):
+        out, s = lib.gmm_fwd(lhs, wq, ws, gs, return_scales=True, **fwd_kw)
+        out32 = lib.gmm_fwd(lhs, wq, ws, gs, out_dtype=torch.float32, **fwd_kw)
+        return out, out32, s
+
+    def dlhs(grad, wk, sk):
+        if mode == "hybrid":
+            gq, sg = lib.gmm_quantize(grad, "e5m2", "dynamic")
+            a, kw = gq, dict(grad_scaling="dynamic", grad_scales=sg)
+        else:
+            a, kw = grad, dict(grad_scaling="dynamic")
+        out, sg = lib.gmm_dlhs(a, wk, sk, gs, return_scales=True, **kw)
+        out32 = lib.gmm_dlhs(a, wk, sk, gs, out_dtype=torch.float32, **kw)
+        return out, out32, sg
+
+    # forward
+    wgu_q, wgu_s = lib.gmm_quantize_rhs(w_gu, "e4m3", 0, "nk")
+    wdn_q, wdn_s = lib.gmm_quantize_rhs(w_down, "e4m3", 0, "nk")
+    gu, gu32, s_x = fwd(x, wgu_q, wgu_s)
+    g, u = gu[:, :inter].float(), gu[:, inter:].float()
+    h = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+    y, y32, s_h = fwd(h, wdn_q, wdn_s)
+    # backward
+    wgu_k, wgu_sk = lib.gmm_quantize_rhs(w_gu, "e4m3", 1, "kn")
+    wdn_k, wdn_sk = lib.gmm_quantize_rhs(w_down, "e4m3", 1, "kn")
+    dh, dh32, s_gy = dlhs(grad_y, wdn_k, wdn_sk)
+    sig = torch.sigmoid(g)
+    dhf = dh.float()
+    d_gu = torch.cat([dhf * u * sig * (1 + g * (1 - sig)), dhf * g * sig], dim=1).to(torch.bfloat16)
+    dx, dx32, s_dgu = dlhs(d_gu, wgu_k, wgu_sk)
+    tk = dict(lhs_scaling="dynamic", grad_scaling="dynamic", return_scales=True)
+    dwd, sa_h, sg_y = lib.tgmm_drhs(h, grad_y, gs, **tk)
+    dwd32 = lib.tgmm_drhs(h, grad_y, gs, out_dtype=torch.float32, lhs_scaling="dynamic",
+                          grad_scaling="dynamic")
+    dwg, sa_x, sg_dgu = lib.tgmm_drhs(x, d_gu, gs, **tk)
+    dwg32 = lib.tgmm_drhs(x, d_gu, gs, out_dtype=torch.float32, lhs_scaling="dynamic",
+                          grad_scaling="dynamic")
+    sync()
+    assert torch.isfinite(h.float()).all() and torch.isfinite(d_gu.float()).all()
+
+    H = wl.K
+    cols = sample_cols(2 * inter, rng)
+    _check_fwd(lib, x, scaling, s_x, bf16_to_bits(w_gu[:, :, cols]), wgu_q, wgu_s, cols, sizes,
+               gu, gu32, rng)
+    cols = sample_cols(H, rng)
+    _check_fwd(lib, h, scaling, s_h, bf16_to_bits(w_down[:, :, cols]), wdn_q, wdn_s, cols, sizes,
+               y, y32, rng)
+    kc = sample_cols(inter, rng)
+    _check_dlhs(grad_y, s_gy, bf16_to_bits(w_down[:, kc, :]), wdn_k, wdn_sk, kc, sizes, dh, dh32, rng)
+    kc = sample_cols(H, rng)
+    _check_dlhs(d_gu, s_dgu, bf16_to_bits(w_gu[:, kc, :]), wgu_k, wgu_sk, kc, sizes, dx, dx32, rng)
+    _check_tgmm(h, grad_y, sa_h, sg_y, sizes, dwd, dwd32, rng)
+    _check_tgmm(x, d_gu, sa_x, sg_dgu, sizes, dwg, dwg32, rng)

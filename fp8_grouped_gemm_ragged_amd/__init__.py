@@ -34,7 +34,7 @@ STATIC, DYNAMIC, DYNAMIC_GIVEN = 0, 1, 2
 KIND_BF16, KIND_FP8 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 RHS_KN, RHS_NK = 0, 1
-OP_FWD, OP_DLHS, OP_TGMM = 0, 1, 2
+OP_FWD, OP_DLHS, OP_TGMM, OP_FWD_FUSED, OP_DLHS_FUSED, OP_QUANTIZE = 0, 1, 2, 3, 4, 5
 BLOCK_ROWS = 128
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
@@ -171,7 +171,7 @@ def _nblocks(rows):
 
 
 def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_scales,
-          rhs_layout, out_dtype, out, contraction_dim, out_cols):
+          rhs_layout, out_dtype, out, contraction_dim, out_cols, fused):
     import torch
 
     lib = load()
@@ -205,7 +205,11 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
     if a_scales is not None:
         _need(a_scales, torch.float32, "scales", 1)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), M, K_or_N, 0, 1,
+    if cname == "gmm_fwd":
+        wop = OP_FWD_FUSED if fused else OP_FWD
+    else:
+        wop = OP_DLHS_FUSED if fused else OP_DLHS
+    _check(lib.gmm_workspace_size(wop, ctypes.byref(op), ctypes.byref(op), M, K_or_N, n_out, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, a.device)
     fn = getattr(lib, cname)
@@ -217,7 +221,7 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
 
 def gmm_fwd(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic",
             static_scale=None, lhs_scales=None, rhs_layout="nk", out_dtype=None, out=None,
-            return_scales=False):
+            return_scales=False, fused=False):
     """Forward grouped matmul: out[M, N] = q(lhs)[rows of g] . rhs[g] (scales applied).
 
     lhs: bf16 [M, K] (quantized in-kernel) or uint8 fp8 codes [M, K] (pre-quantized,
@@ -225,18 +229,21 @@ def gmm_fwd(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3", lhs_scaling
     "dynamic" (block scales computed by the call; returned with return_scales) or
     "dynamic_given" (block scales from an earlier call in ``lhs_scales``).  rhs: uint8 codes,
     [G, N, K] for rhs_layout "nk" or [G, K, N] for "kn"; rhs_scales f32 [G, N].
+    fused=True hands the call only the workspace of the in-kernel quantization route
+    (a bf16 lhs is then quantized inside the product kernel even for wide outputs).
     """
     o, s = _gemm("gmm_fwd", lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
-                 static_scale, lhs_scales, rhs_layout, out_dtype, out, "K", "N")
+                 static_scale, lhs_scales, rhs_layout, out_dtype, out, "K", "N", fused)
     return (o, s) if return_scales else o
 
 
 def gmm_dlhs(grad, rhs, rhs_scales, group_sizes, *, grad_format="e5m2", grad_scaling="dynamic",
              static_scale=None, grad_scales=None, rhs_layout="kn", out_dtype=None, out=None,
-             return_scales=False):
-    """lhs gradient: dlhs[M, K] = q(grad)[rows of g] . rhs[g]^T; rhs_scales f32 [G, K]."""
+             return_scales=False, fused=False):
+    """lhs gradient: dlhs[M, K] = q(grad)[rows of g] . rhs[g]^T; rhs_scales f32 [G, K].
+    fused: as for gmm_fwd."""
     o, s = _gemm("gmm_dlhs", grad, rhs, rhs_scales, group_sizes, grad_format, grad_scaling,
-                 static_scale, grad_scales, rhs_layout, out_dtype, out, "N", "K")
+                 static_scale, grad_scales, rhs_layout, out_dtype, out, "N", "K", fused)
     return (o, s) if return_scales else o
 
 
@@ -295,7 +302,7 @@ def gmm_dynamic_scales(x, fmt="e4m3"):
     scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
     op = _operand(KIND_BF16, fmt, "dynamic", None)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
+    _check(lib.gmm_workspace_size(OP_QUANTIZE, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, x.device)
     _check(lib.gmm_dynamic_scales(_FMT[fmt], R, C, _ptr(x), _ptr(scales), _ptr(ws), ws_n.value,
@@ -320,7 +327,7 @@ def gmm_quantize(x, fmt="e4m3", scaling="dynamic", static_scale=None, scales=Non
     if mode == DYNAMIC and scales is None:
         scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
     ws_n = _SZ()
-    _check(lib.gmm_workspace_size(OP_FWD, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
+    _check(lib.gmm_workspace_size(OP_QUANTIZE, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, x.device)
     _check(lib.gmm_quantize(ctypes.byref(op), R, C, _ptr(x), _ptr(codes), _ptr(scales), _ptr(ws),

@@ -146,6 +146,16 @@ void trace(const char* what, int64_t M, int64_t K, int64_t N, int32_t G) {
                  (long long)K, (long long)N, G);
 }
 
+// A bf16 operand is quantized once into the workspace, and the product then reads fp8
+// codes, when the call has at least this many 256-column output tiles and the workspace
+// holds the codes: the in-kernel quantization repeats per output tile, and on gfx950 its
+// vector work (about 20 instructions per MFMA) cannot hide under the matrix core.
+constexpr int64_t QUANT_ONCE_MIN_TILES = 4;
+
+size_t quant_once_bytes(int64_t M, int64_t Kc) { return align256((size_t)M * Kc); }
+
+bool quant_once_applies(int64_t Nout) { return Nout <= 0 || (Nout + 255) / 256 >= QUANT_ONCE_MIN_TILES; }
+
 // Shared body of gmm_fwd / gmm_dlhs: out[M, Nout] = A[M, Kc] x B.
 gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rhs_format,
                           bool b_trans, int32_t out_dtype, int64_t M, int64_t Kc,
@@ -169,6 +179,9 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
     if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
   const size_t ws_need = needs_dyn_ws(aop) ? dyn_ws_bytes(M) : 0;
   if (ws_need && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
+  const bool quant_once = !a_fp8 && quant_once_applies(Nout) && workspace &&
+                          workspace_bytes >= ws_need + quant_once_bytes(M, Kc);
+  const size_t ws_used = ws_need + (quant_once ? quant_once_bytes(M, Kc) : 0);
   const size_t a_bytes = (size_t)M * Kc * (a_fp8 ? 1 : 2);
   const size_t out_bytes = (size_t)M * Nout * (out_dtype == GMM_OUT_F32 ? 4 : 2);
   const size_t b_bytes = (size_t)G * Kc * Nout;
@@ -177,7 +190,8 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
       overlaps(out, out_bytes, rhs_scales, (size_t)G * Nout * 4) ||
       overlaps(out, out_bytes, group_sizes, (size_t)G * 4) ||
       (needs_dyn_ws(aop) && overlaps(a_scales, as_bytes, a, a_bytes)) ||
-      overlaps(workspace, ws_need, a, a_bytes) || overlaps(workspace, ws_need, out, out_bytes))
+      overlaps(workspace, ws_used, a, a_bytes) || overlaps(workspace, ws_used, out, out_bytes) ||
+      overlaps(workspace, ws_used, a_scales, as_bytes))
     return GMM_ERR_ALIAS;
   if ((s = check_group_sizes(group_sizes, G, M, st)) != GMM_OK) return s;
   trace(name, M, Kc, Nout, G);
@@ -199,7 +213,16 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.a_scale_blk = sc.blk;
   p.a_scale_static = sc.s;
   p.a_inv_static = sc.inv;
-  if (launch_gemm(aop->format, FMT_E4M3, a_fp8, b_trans, p, st) != hipSuccess) return GMM_ERR_HIP;
+  bool a_codes = a_fp8;
+  if (quant_once) {
+    uint8_t* codes = (uint8_t*)workspace + ws_need;
+    if (launch_quantize_rows(aop->format, (const uint16_t*)a, M, Kc, sc.blk, sc.inv, codes, st) !=
+        hipSuccess)
+      return GMM_ERR_HIP;
+    p.a = codes;
+    a_codes = true;
+  }
+  if (launch_gemm(aop->format, FMT_E4M3, a_codes, b_trans, p, st) != hipSuccess) return GMM_ERR_HIP;
   return GMM_OK;
 }
 
@@ -310,12 +333,16 @@ gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_op
   gmm_status_t s = check_operand(a);
   if (s != GMM_OK) return s;
   size_t n = needs_dyn_ws(a) ? dyn_ws_bytes(rows) : 0;
+  if ((op == GMM_OP_FWD || op == GMM_OP_DLHS) && a->kind == GMM_OPERAND_BF16 &&
+      quant_once_applies(cols_b))
+    n += quant_once_bytes(rows, cols_a);
   if (op == GMM_OP_TGMM) {
     if (!b) return GMM_ERR_NULL;
     if ((s = check_operand(b)) != GMM_OK) return s;
     n += needs_dyn_ws(b) ? dyn_ws_bytes(rows) : 0;
     n += tgmm_ws_bytes(rows, cols_a, cols_b, G);
-  } else if (op != GMM_OP_FWD && op != GMM_OP_DLHS) {
+  } else if (op != GMM_OP_FWD && op != GMM_OP_DLHS && op != GMM_OP_FWD_FUSED &&
+             op != GMM_OP_DLHS_FUSED && op != GMM_OP_QUANTIZE) {
     return GMM_ERR_RECIPE;
   }
   *bytes = n;

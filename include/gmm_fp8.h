@@ -116,8 +116,17 @@ typedef struct gmm_operand {
   float static_scale;   /* GMM_SCALE_STATIC: the per-tensor scale s (finite, > 0, normal) */
 } gmm_operand_t;
 
-/* Operation identifiers for gmm_workspace_size. */
-typedef enum gmm_op { GMM_OP_FWD = 0, GMM_OP_DLHS = 1, GMM_OP_TGMM = 2 } gmm_op_t;
+/* Operation identifiers for gmm_workspace_size.  The _FUSED variants size the workspace
+ * of gmm_fwd / gmm_dlhs calls that quantize a bf16 operand inside the product kernel;
+ * GMM_OP_QUANTIZE sizes that of gmm_quantize and gmm_dynamic_scales. */
+typedef enum gmm_op {
+  GMM_OP_FWD = 0,
+  GMM_OP_DLHS = 1,
+  GMM_OP_TGMM = 2,
+  GMM_OP_FWD_FUSED = 3,
+  GMM_OP_DLHS_FUSED = 4,
+  GMM_OP_QUANTIZE = 5
+} gmm_op_t;
 
 /*
  * gmm_fwd - forward grouped matmul ("FP8 Megablox for batch split", Description (1);
@@ -134,8 +143,13 @@ typedef enum gmm_op { GMM_OP_FWD = 0, GMM_OP_DLHS = 1, GMM_OP_TGMM = 2 } gmm_op_
  * rhs_scales   f32 [G, N]: the dequantization scale of every output channel n.
  * group_sizes  int32 [G].
  * out          [M, N], bf16 or f32 per out_dtype.  Every row is written exactly once.
- * workspace    device scratch of gmm_workspace_size(GMM_OP_FWD, ...) bytes (may be NULL
- *              when that size is 0); its contents are undefined after the call.
+ * workspace    device scratch; its contents are undefined after the call.  With at least
+ *              gmm_workspace_size(GMM_OP_FWD, ...) bytes, a bf16 lhs feeding 4 or more
+ *              256-column output tiles is quantized once into the workspace and the
+ *              product reads the codes; with at least gmm_workspace_size(
+ *              GMM_OP_FWD_FUSED, ...) bytes (0 unless the call computes dynamic block
+ *              scales; then NULL is allowed) every workgroup quantizes its lhs tile in
+ *              registers.  Both routes produce the same codes and the same outputs.
  * Merged gate|up: pass rhs = concat(W0, W1) along N with concatenated scales; one call
  * produces [gate | up] ("FP8 Megablox for batch split", Description (2)).
  */
@@ -156,6 +170,7 @@ gmm_status_t gmm_fwd(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rh
  * rhs          the same logical [G, K, N] weight as gmm_fwd, quantized per dlhs output
  *              channel k: rhs_scales f32 [G, K].
  * dlhs         [M, K] bf16 or f32.
+ * workspace    as gmm_fwd's (GMM_OP_DLHS / GMM_OP_DLHS_FUSED; output tiles of 256 k).
  */
 gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
                       int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
@@ -187,12 +202,19 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
                        float* grad_scales, const int32_t* group_sizes, void* drhs,
                        void* workspace, size_t workspace_bytes, gmm_stream_t stream);
 
-/* Bytes of device workspace the call `op` needs for these operands and sizes.  For
- * GMM_OP_FWD / GMM_OP_DLHS, `a` is the lhs / grad operand and `b` is ignored: the size
- * is 0 unless the call computes dynamic block scales.  For GMM_OP_TGMM, `a` is the lhs
- * and `b` the grad; tgmm always needs workspace for its quantized, transposed copies of
- * both operands (about (K + N) x (M + 128 G) bytes).  `rows` is M, `cols_a` / `cols_b`
- * the row widths (K and N), G the number of groups.  Sets *bytes. */
+/* Bytes of device workspace the call `op` needs for these operands and sizes.
+ * GMM_OP_FWD / GMM_OP_DLHS: `a` is the lhs / grad operand and `b` is ignored; `rows` is
+ *   M, `cols_a` the operand's width (the contraction: K for fwd, N for dlhs) and `cols_b`
+ *   the output width (N for fwd, K for dlhs; 0 = unknown, counted as wide).  The size
+ *   covers the dynamic block scales the call computes, plus, for a bf16 operand of a
+ *   wide output, its fp8 codes (rows x cols_a bytes).
+ * GMM_OP_FWD_FUSED / GMM_OP_DLHS_FUSED: the same without the codes (0 unless the call
+ *   computes dynamic block scales).
+ * GMM_OP_QUANTIZE: gmm_quantize / gmm_dynamic_scales on `a` [rows, cols_a].
+ * GMM_OP_TGMM: `a` is the lhs and `b` the grad; tgmm always needs workspace for its
+ *   quantized, transposed copies of both operands (about (K + N) x (M + 128 G) bytes).
+ *   `rows` is M, `cols_a` / `cols_b` the row widths (K and N), G the number of groups.
+ * Sets *bytes. */
 gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_operand_t* b,
                                 int64_t rows, int64_t cols_a, int64_t cols_b, int32_t G,
                                 size_t* bytes);
@@ -200,7 +222,7 @@ gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_op
 /*
  * gmm_dynamic_scales - the abs-max prepass alone: per-block scales of a bf16 matrix
  * [R, C] for the DYNAMIC recipe of `format`, scales f32 [ceil(R/128)] (output).
- * workspace: gmm_workspace_size(GMM_OP_FWD, op{BF16, format, DYNAMIC}, NULL, R, C, 0, 1).
+ * workspace: gmm_workspace_size(GMM_OP_QUANTIZE, op{BF16, format, DYNAMIC}, NULL, R, C, 0, 1).
  */
 gmm_status_t gmm_dynamic_scales(int32_t format, int64_t R, int64_t C, const void* x,
                                 float* scales, void* workspace, size_t workspace_bytes,
@@ -211,7 +233,7 @@ gmm_status_t gmm_dynamic_scales(int32_t format, int64_t R, int64_t C, const void
  * static or dynamic recipe above (codes [R, C]; scales f32 [ceil(R/128)]: output for
  * DYNAMIC, input for DYNAMIC_GIVEN, unused for STATIC).  The codes are byte-identical to those the fused
  * kernels form in registers.  Used for the pre-quantized-operand path (hybrid dlhs).
- * workspace: gmm_workspace_size(GMM_OP_FWD, op, NULL, R, C, 0, 1, &bytes).
+ * workspace: gmm_workspace_size(GMM_OP_QUANTIZE, op, NULL, R, C, 0, 1, &bytes).
  */
 gmm_status_t gmm_quantize(const gmm_operand_t* op, int64_t R, int64_t C, const void* x,
                           uint8_t* codes, float* scales, void* workspace,

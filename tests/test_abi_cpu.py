@@ -46,6 +46,18 @@ def test_host_helpers():
 
 def test_workspace_sizes():
     assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "static", 1000) == 0
+    # a bf16 operand of a wide output (>= 4 tiles of 256, or unknown) gets room for its codes
+    assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "static", 1000, 512) == 512000
+    assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "static", 1000, 512, 1024) == 512000
+    assert g.gmm_workspace_size(g.OP_DLHS, "e5m2", "static", 1000, 640, 769) == 640000
+    assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "static", 1000, 512, 768) == 0  # 3 tiles
+    assert g.gmm_workspace_size(g.OP_FWD_FUSED, "e4m3", "static", 1000, 512) == 0
+    assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "static", 1000, 512, a_kind=g.KIND_FP8) == 0
+    d = g.gmm_workspace_size(g.OP_QUANTIZE, "e4m3", "dynamic", 1000, 512)
+    assert g.gmm_workspace_size(g.OP_DLHS_FUSED, "e4m3", "dynamic", 1000, 512) == d
+    assert g.gmm_workspace_size(g.OP_FWD, "e4m3", "dynamic", 1000, 512) == d + 512000
+    with pytest.raises(g.GmmError):
+        g.gmm_workspace_size(9, "e4m3", "static", 1000)
     n = g.gmm_workspace_size(g.OP_FWD, "e4m3", "dynamic", 1000)
     nb = 8
     assert n >= nb * (8 + 2) * 4 and n % 256 == 0
@@ -124,12 +136,15 @@ def test_dlhs_and_tgmm_validation():
 def test_given_scales_validation():
     lib = g.load()
     given = op(scaling=2)
-    # DYNAMIC_GIVEN: scales are an input (NULL rejected) and no workspace is needed
+    # DYNAMIC_GIVEN: scales are an input (NULL rejected) and the in-kernel route needs no
+    # workspace; the quantize-once route needs room for the codes only
     assert call_fwd(o=given, lhs_scales=None) == 1
     assert call_fwd(o=given, ws=None, ws_bytes=0, M=0) == 0
     n = ctypes.c_size_t()
-    assert lib.gmm_workspace_size(0, ctypes.byref(given), ctypes.byref(given), 1000, 256, 0, 1, ctypes.byref(n)) == 0
+    assert lib.gmm_workspace_size(3, ctypes.byref(given), ctypes.byref(given), 1000, 256, 0, 1, ctypes.byref(n)) == 0
     assert n.value == 0
+    assert lib.gmm_workspace_size(0, ctypes.byref(given), ctypes.byref(given), 1000, 256, 0, 1, ctypes.byref(n)) == 0
+    assert n.value == 256000
     a, b = op(fmt=0, scaling=2), op(fmt=1, scaling=2)
     assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), None,
                          ptr(3), ptr(4), ptr(5), ptr(6), None, 0, None) == 1

@@ -216,3 +216,78 @@ def test_given_scales_equal_in_call_scales(lib):
                     out_dtype=torch.float32)
     assert torch.equal(s.view(torch.int32), sa.view(torch.int32))
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+QO_SIZES = [300, 0, 1, 511, 212]  # 1024 rows; 1152 output columns = 4.5 tiles of 256
+
+
+@pytest.mark.parametrize("scaling", ["static", "dynamic", "dynamic_given"])
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+def test_fwd_quantize_once_route(lib, scaling, layout):
+    """A wide output makes the call quantize the bf16 lhs once into its workspace and run
+    the fp8-A kernel: the same bits as the in-kernel quantization, and oracle parity."""
+    sizes = QO_SIZES
+    M, K, N = sum(sizes), 384, 1152
+    x, xb = gen((M, K), 1.0, 251)
+    w, wb = channel_varied((len(sizes), K, N), 0.02, 252, 2)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, layout)
+    gs = gs_tensor(sizes)
+    kw = dict(lhs_scaling=scaling, static_scale=S_4_448, rhs_layout=layout, out_dtype=torch.float32)
+    if scaling == "dynamic_given":
+        kw["lhs_scales"] = lib.gmm_dynamic_scales(x, "e4m3")
+    once = lib.gmm_fwd(x, codes, scales, gs, **kw)
+    fused = lib.gmm_fwd(x, codes, scales, gs, fused=True, **kw)
+    assert torch.equal(once.view(torch.int32), fused.view(torch.int32))
+    c_ref, s_ref = quantize_rhs_per_channel(wb, "e4m3", "n")
+    rec = "static" if scaling == "static" else "dynamic"
+    R, _, _ = ops.fwd(xb, c_ref, s_ref, sizes, "e4m3", rec, np.float32(S_4_448))
+    err = group_rel_err(to_np(once), R, group_row_ranges(sizes))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_dlhs_quantize_once_route(lib, layout):
+    sizes = QO_SIZES
+    M, K, N = sum(sizes), 1152, 640
+    gr, gb = gen((M, N), 1e-3, 261)
+    w, wb = channel_varied((len(sizes), K, N), 0.02, 262, 1)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 1, layout)
+    gs = gs_tensor(sizes)
+    once, s1 = lib.gmm_dlhs(gr, codes, scales, gs, rhs_layout=layout, out_dtype=torch.float32,
+                            return_scales=True)
+    fused = lib.gmm_dlhs(gr, codes, scales, gs, rhs_layout=layout, out_dtype=torch.float32,
+                         fused=True)
+    assert torch.equal(once.view(torch.int32), fused.view(torch.int32))
+    c_ref, s_ref = quantize_rhs_per_channel(wb, "e4m3", "k")
+    R, _, sg = ops.dlhs(gb, c_ref, s_ref, sizes)
+    assert np.array_equal(to_np(s1).view(np.uint32), sg.view(np.uint32))
+    err = group_rel_err(to_np(once), R, group_row_ranges(sizes))
+    assert err <= TOL, err
+
+
+def test_quantize_once_route_writes_the_codes_into_the_workspace(lib):
+    """The route really taken: after the call the workspace holds the lhs codes, equal to
+    the stand-alone quantizer's."""
+    import ctypes
+
+    sizes = QO_SIZES
+    M, K, N = sum(sizes), 256, 1024
+    x, _ = gen((M, K), 1.0, 271)
+    w, _ = gen((len(sizes), K, N), 0.02, 272)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    gs = gs_tensor(sizes)
+    n = lib.gmm_workspace_size(lib.OP_FWD, "e4m3", "static", M, K, N, static_scale=S_4_448)
+    assert n == M * K
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    op = lib.Operand(lib.KIND_BF16, lib.E4M3, lib.STATIC, S_4_448)
+    c = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.load().gmm_fwd(ctypes.byref(op), lib.E4M3, lib.RHS_NK, lib.OUT_BF16, M, K, N,
+                            len(sizes), c(x), None, c(codes), c(scales), c(gs), c(out), c(ws), n,
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    xq, _ = lib.gmm_quantize(x, "e4m3", "static", S_4_448)
+    sync()
+    assert torch.equal(ws.view(M, K), xq)
+    ref = lib.gmm_fwd(x, codes, scales, gs, lhs_scaling="static", static_scale=S_4_448, fused=True)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

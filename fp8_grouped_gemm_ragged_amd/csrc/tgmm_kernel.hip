@@ -11,9 +11,11 @@
 //      "segment" (the 128-row blocks the group meets, laid end to end); per block the
 //      scale product sc_c; per segment block the ratio of scale products used below.
 //   2. quant_transpose (once per operand): every element quantized exactly once (with
-//      its block's scale) and written transposed, [columns][segment], so that each
-//      group's rows start on a 128-byte boundary and rows of other groups inside a
-//      shared block are zero codes.
+//      its block's scale) and written transposed into the segment, so that each group's
+//      rows start on a block boundary and rows of other groups inside a shared block are
+//      zero codes.  Columns are stored in pairs: block b of columns 2p, 2p + 1 is 256
+//      bytes, [2p: m 0..63][2p + 1: m 0..63][2p: m 64..127][2p + 1: m 64..127], so a
+//      half block of two columns is one 128-byte line.
 //   3. tgmm_ratio: per (group, 256 k x 256 n) tile, one contraction step per block of
 //      the group's segment.  Instead of scaling each block's partial sum and adding it
 //      (two vector ops per value per block), the fp32 accumulators are kept in units of
@@ -47,6 +49,7 @@ constexpr int RA_TILE = RBM * TILE_K;
 constexpr int RB_TILE = RBN * TILE_K;
 constexpr int ST_K = 4;    // k-tiles per band of the tile order
 constexpr int PLAN_NT = 1024;
+constexpr int PAIR_BLOCK = 2 * BLOCK_ROWS;  // bytes of one block of a column pair
 static_assert(MAX_GROUPS <= PLAN_NT, "one plan thread per group");
 // widest spread of nonzero scale products in a group that the rescaled accumulators
 // take: with |P_c| <= 128 * 57344^2 and at most 2^15 blocks the values stay below 2^114
@@ -299,9 +302,13 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(
   }
   v2u q[8];
   quant_transpose8<FMT>(in, inv, q);
-  uint8_t* dst = seg + (col0 + cb * 8) * seg_row + (int64_t)b * BLOCK_ROWS + rb * 8;
+  // segment layout by column pairs: pair p, block b holds 256 bytes, [col 2p, m 0..63]
+  // [col 2p + 1, m 0..63] [col 2p, m 64..127] [col 2p + 1, m 64..127]
+  uint8_t* dst = seg + (col0 + cb * 8) * seg_row + (int64_t)b * PAIR_BLOCK + (rb >> 3) * 128 +
+                 (rb & 7) * 8;
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<v2u*>(dst + cc * seg_row) = q[cc];
+  for (int cc = 0; cc < 8; ++cc)
+    *reinterpret_cast<v2u*>(dst + (cc >> 1) * 2 * seg_row + (cc & 1) * 64) = q[cc];
 }
 
 // One wave fills 8 rows (1 KB) of a swizzled [rows][128 B] tile from global memory.
@@ -311,17 +318,34 @@ __device__ inline void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_r
       r, (__attribute__((address_space(3))) void*)lds_rows, 16, goff, 0, 0, 0);
 }
 
+// Half-block stage of the rescaling kernel: [256 rows][64 contraction bytes] per operand.
+// 16-byte chunk c of row r sits at chunk position c ^ (((r >> 1) ^ (r >> 3)) & 3): the
+// rows one phase of a fragment read touches (8 rows over 32 banks, or 16 over 64) then
+// fall on distinct 16-byte bank groups.
+constexpr int HROW = 64;
+constexpr int RH_TILE = RBM * HROW;  // 16 KB
+
 // One (group, 256 k x 256 n) tile per workgroup of 8 waves, each wave 128 k x 64 n
 // (2 x 4 waves; two waves per SIMD, so one wave's vector work overlaps the other's
-// MFMAs).  Per segment block s: the fp8 tiles of block s + 1 go straight from memory
-// into the other LDS stage while block s is contracted.
+// MFMAs).  The contraction runs in half-blocks of 64 rows through a ring of 4 LDS
+// stages: half-step h's fp8 tiles are loaded straight from memory into stage h % 4
+// three half-steps ahead, and half-step h + 1's fragments are read into registers
+// while half-step h's MFMAs run, so no step waits on LDS reads when it starts.
 template <int A_FMT, int B_FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(RNT, RNT), amdgpu_waves_per_eu(2, 2)))
-void tgmm_ratio_kernel(TgmmSegParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[RA_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[RB_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[RA_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[RB_TILE];
+void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
+  // one array for the 4 stages (A tile, then B tile, per stage): every LDS address is
+  // then a per-lane register plus a constant that fits the instruction's offset field
+  // (two base registers in all), instead of one register per stage and operand
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[8 * RH_TILE];
+  uint8_t* const sA0 = s_lds;
+  uint8_t* const sB0 = s_lds + RH_TILE;
+  uint8_t* const sA1 = s_lds + 2 * RH_TILE;
+  uint8_t* const sB1 = s_lds + 3 * RH_TILE;
+  uint8_t* const sA2 = s_lds + 4 * RH_TILE;
+  uint8_t* const sB2 = s_lds + 5 * RH_TILE;
+  uint8_t* const sA3 = s_lds + 6 * RH_TILE;
+  uint8_t* const sB3 = s_lds + 7 * RH_TILE;
 
   const int n_kt = (p.Kout + RBM - 1) / RBM;
   const int n_nt = (p.Nout + RBN - 1) / RBN;
@@ -371,118 +395,193 @@ void tgmm_ratio_kernel(TgmmSegParams p) {
 
   if (nblk > 0) {
     fin = pl.fin[g];
+    const int H = 2 * nblk;  // half-steps
     const uint32_t seg_row = (uint32_t)p.seg_row;
     const int krows = min(p.Kout - k0, RBM), nrows = min(p.Nout - n0, RBN);
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * BLOCK_ROWS,
-                  (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * BLOCK_ROWS));
+        make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
+                  (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * BLOCK_ROWS,
-                  (uint32_t)((int64_t)nrows * p.seg_row - (int64_t)seg0 * BLOCK_ROWS));
+        make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
+                  (uint32_t)((int64_t)nrows * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
+    // The ratio half-step h applies: block (h + 1) / 2's (the tail of the move into
+    // block h / 2 for even h, the head of the move into block h / 2 + 1 for odd h).  The
+    // group's ratios are followed by a 1 (for the move past its last block); the index
+    // stops there.  A uniform read through a restrict pointer: a scalar load, outside
+    // the vector-load count the pipeline waits on.
+    const float* gratio = ratio + seg0 + g;
+    auto ratio_of = [&](int h) -> float { return gratio[min((h + 1) >> 1, nblk)]; };
 
-    // Direct loads of segment block s: rows 32 w .. 32 w + 31 of both tiles.  Past the
-    // group's last block the offset leaves both ranges, so nothing is fetched (the
-    // unused stage receives zeros) and the step stays free of branches.
-    auto issue = [&](int s, uint8_t* at, uint8_t* bt) {
-      const uint32_t koff = s < nblk ? (uint32_t)s * BLOCK_ROWS : 0x80000000u;
+    // Half-step X of both tiles goes through registers: thread t holds 16-byte chunks t
+    // and t + 512 of each tile (row idx / 4, logical chunk idx % 4); in the column-pair
+    // layout 8 consecutive threads cover one 128-byte line (rows 2p, 2p + 1).  Past the
+    // last half-step the offsets leave the ranges and the loads return zeros.
+    auto gload = [&](int X, v4u (&sa)[2], v4u (&sb)[2]) {
+      const uint32_t hoff =
+          X < H ? (uint32_t)(X >> 1) * PAIR_BLOCK + (uint32_t)(X & 1) * 128 : 0x80000000u;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wave * 32 + q * 8 + (lane >> 3);
-        const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
-        const uint32_t go = (uint32_t)row * seg_row + koff + c * 16;
-        load_rows_to_lds(ra, at + (wave * 32 + q * 8) * TILE_K, go);
-        load_rows_to_lds(rb, bt + (wave * 32 + q * 8) * TILE_K, go);
+      for (int q = 0; q < 2; ++q) {
+        const int idx = q * RNT + tid, row = idx >> 2;
+        const uint32_t go = (uint32_t)(row >> 1) * 2 * seg_row + (uint32_t)(row & 1) * 64 + hoff +
+                            (uint32_t)(idx & 3) * 16;
+        sa[q] = buf_load16(ra, go);
+        sb[q] = buf_load16(rb, go);
       }
     };
-    uint32_t fo[2][2];
-    {
-      const uint32_t f0 = (uint32_t)((frow & 7) ^ (frow >> 3));
+    uint32_t wo[2];  // the chunks' places in a stage tile
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          fo[tt][e] = (uint32_t)frow * TILE_K + ((((uint32_t)(2 * fhalf + e)) ^ f0 ^ (4u * tt)) << 4);
+    for (int q = 0; q < 2; ++q) {
+      const int idx = q * RNT + tid, row = idx >> 2;
+      wo[q] = (uint32_t)row * HROW + ((uint32_t)((idx & 3) ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
     }
-    auto frag = [&](const uint8_t* tile, int base_row, int i, int ks) -> v8i {
-      const int tt = ks ^ (i & 1);
-      const uint8_t* p0 = tile + base_row * TILE_K + i * 32 * TILE_K;
-      const v4u lo = *reinterpret_cast<const v4u*>(p0 + fo[tt][0]);
-      const v4u hi = *reinterpret_cast<const v4u*>(p0 + fo[tt][1]);
+    auto lwrite = [&](uint8_t* t, const v4u (&sv)[2]) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(t + wo[q]) = sv[q];
+    };
+    uint32_t fo[2];
+    {
+      const uint32_t f0 = (uint32_t)(((frow >> 1) ^ (frow >> 3)) & 3);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) fo[e] = (uint32_t)frow * HROW + ((((uint32_t)(2 * fhalf + e)) ^ f0) << 4);
+    }
+    auto frag = [&](const uint8_t* tile, int base_row, int i) -> v8i {
+      const uint8_t* p0 = tile + (base_row + i * 32) * HROW;
+      const v4u lo = *reinterpret_cast<const v4u*>(p0 + fo[0]);
+      const v4u hi = *reinterpret_cast<const v4u*>(p0 + fo[1]);
       v8i f;
       f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
       f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
       return f;
-    };
-    auto barrier = [&]() {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
     };
     auto rescale = [&](int b, int half, float r) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[b][half * 8 + e] *= r;
     };
 
-    // Block s in 16 units u = 8 ks + b: MFMA of half step ks on sub-block b = 2 i + j,
-    // chained into acc[b].  The accumulators hold units of the scale product of the
-    // last live block; the move to block s + 1 multiplies sub-block b by ratio[s + 1]
-    // (in two halves) after its last MFMA of block s (unit 8 + b) has finished and
-    // before its first MFMA of block s + 1 (unit b there): halves at units b + 10 and
-    // b + 13, counted on into the next block.  ratio of a block that adds nothing is 1.
-    // Ratios come through a vector load issued before the step's direct loads, so that
-    // waiting for one never waits for those.  The group's ratios are followed by a 1
-    // (for the move past its last block); the read one further is out of range and
-    // never used.
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.ratio + seg0 + g, (uint32_t)(nblk + 1) * 4);
-    auto ratio_of = [&](int s) {
-      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)s * 4, 0, 0));
-    };
-    float rc = ratio_of(0);  // into block s
-    float rn = ratio_of(1);  // into block s + 1
-    v8i af[4], bf[2][2];
-    auto step = [&](int s, const uint8_t* at, const uint8_t* bt, uint8_t* an, uint8_t* bn) {
-      const float rnn = ratio_of(s + 2);
-      issue(s + 1, an, bn);
-      af[0] = frag(at, wr * 128, 0, 0);
-      bf[0][0] = frag(bt, wc * 64, 0, 0);
-      bf[1][0] = frag(bt, wc * 64, 1, 0);
+    // Half-step h on stage (at, bt).  Unit u: MFMA on sub-block u = 2 i + j (acc[u] holds
+    // A rows 32 i.., B rows 32 j..).  B fragments stay in bf for the whole half-step; A
+    // fragment i is read into slot i % 2 two units before its first use.  After the
+    // first MFMA: this wave's LDS writes of stage h + 1 (made during h - 1) and its reads
+    // are done; then the workgroup barrier, after which all of stage h + 1 may be read.
+    // Then: the loads of half-step h + 3 into staging set (la, lb); at units 4 and 5
+    // staging set (wa, wb), loaded during h - 1, written to stage h + 2 (the four loads
+    // of h + 3 may stay in flight); at units 6 and 7 half-step h + 1's first fragments
+    // from stage h + 1 (bf[0] and A fragment 0 after the last uses here, bf[1] last).
+    // Rescales: the accumulators hold units of the last live block's scale product; the
+    // move into block c + 1 multiplies acc[u] by ratio[c + 1] in two halves, at units
+    // u + 10 and u + 13 counted from block c's first half-step (after its last MFMA of
+    // block c, before its first of block c + 1).  The ratio register r serves
+    // half-steps h, h + 4, ...: it is reloaded after its last use here.
+    v8i af[2], bf[2];
+    auto half = [&](int h, const uint8_t* at, const uint8_t* an, const uint8_t* bn, uint8_t* aw,
+                    uint8_t* bw, v4u (&la)[2], v4u (&lb)[2], const v4u (&wa)[2],
+                    const v4u (&wb)[2], float& r) {
+      const bool second = h & 1;
+      float rn = 1.0f;
 #pragma unroll
-      for (int i = 1; i < 4; ++i) af[i] = frag(at, wr * 128, i, 0);
-      bf[0][1] = frag(bt, wc * 64, 0, 1);
-      bf[1][1] = frag(bt, wc * 64, 1, 1);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int ks = u >> 3, b = u & 7, i = b >> 1, j = b & 1;
-        acc[b] = mfma32x32x64<B_FMT, A_FMT>(bf[j][ks], af[i], acc[b]);
-        // the second half step's A fragment once both sub-blocks of row i used the first
-        if (u < 8 && (u & 1)) af[u >> 1] = frag(at, wr * 128, u >> 1, 1);
-        if (u == 0) { rescale(6, 0, rc); rescale(3, 1, rc); }
-        if (u == 1) { rescale(7, 0, rc); rescale(4, 1, rc); }
-        if (u == 2) rescale(5, 1, rc);
-        if (u == 3) rescale(6, 1, rc);
-        if (u == 4) rescale(7, 1, rc);
-        if (u >= 10) rescale(u - 10, 0, rn);
-        if (u >= 13) rescale(u - 13, 1, rn);
+      for (int u = 0; u < 8; ++u) {
+        const int i = u >> 1, j = u & 1;
+        acc[u] = mfma32x32x64<B_FMT, A_FMT>(bf[j], af[i & 1], acc[u]);
+        if (u == 0) {
+          __builtin_amdgcn_sched_barrier(0);  // the first MFMA goes out before the wait
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          // this half-step's ratio, loaded long ago: taken into a fresh register here,
+          // where nothing else is pending, so its uses below wait for nothing
+          asm volatile("s_mov_b32 %0, %1" : "=s"(rn) : "s"(r));
+          gload(h + 3, la, lb);
+        }
+        if (!(u & 1) && u < 6) af[(i + 1) & 1] = frag(at, wr * 128, i + 1);
+        if (u == 4) {
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          lwrite(aw, wa);
+        }
+        if (u == 5) lwrite(bw, wb);
+        if (u == 6) {
+          bf[0] = frag(bn, wc * 64, 0);
+          af[0] = frag(an, wr * 128, 0);
+        }
+        if (u == 7) bf[1] = frag(bn, wc * 64, 1);
+        if (!second) {
+          if (u == 0) { rescale(6, 0, rn); rescale(3, 1, rn); }
+          if (u == 1) { rescale(7, 0, rn); rescale(4, 1, rn); }
+          if (u == 2) rescale(5, 1, rn);
+          if (u == 3) rescale(6, 1, rn);
+          if (u == 4) rescale(7, 1, rn);
+        } else {
+          if (u >= 2) rescale(u - 2, 0, rn);
+          if (u >= 5) rescale(u - 5, 1, rn);
+        }
+        if (u == 7) r = ratio_of(h + 4);
         __builtin_amdgcn_sched_barrier(0);
       }
-      rc = rn;
-      rn = rnn;
-      barrier();
     };
 
-    issue(0, sA0, sB0);
-    barrier();
-    int s = 0;
-    for (; s + 1 < nblk; s += 2) {
-      step(s, sA0, sB0, sA1, sB1);
-      step(s + 1, sA1, sB1, sA0, sB0);
+    // prologue: half-steps 0 and 1 into stages 0 and 1, half-step 2 loaded; stage 0's
+    // first fragments
+    v4u s0a[2], s0b[2], s1a[2], s1b[2];
+    gload(0, s0a, s0b);
+    gload(1, s1a, s1b);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lwrite(sA0, s0a);
+    lwrite(sB0, s0b);
+    gload(2, s0a, s0b);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lwrite(sA1, s1a);
+    lwrite(sB1, s1b);
+    float r0 = ratio_of(0), r1 = ratio_of(1), r2 = ratio_of(2), r3 = ratio_of(3);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    af[0] = frag(sA0, wr * 128, 0);
+    bf[0] = frag(sB0, wc * 64, 0);
+    bf[1] = frag(sB0, wc * 64, 1);
+    int h = 0;
+    for (; h + 4 <= H; h += 4) {
+      half(h, sA0, sA1, sB1, sA2, sB2, s1a, s1b, s0a, s0b, r0);
+      half(h + 1, sA1, sA2, sB2, sA3, sB3, s0a, s0b, s1a, s1b, r1);
+      half(h + 2, sA2, sA3, sB3, sA0, sB0, s1a, s1b, s0a, s0b, r2);
+      half(h + 3, sA3, sA0, sB0, sA1, sB1, s0a, s0b, s1a, s1b, r3);
     }
-    if (s < nblk) step(s, sA0, sB0, sA1, sB1);
+    if (h < H) {  // H is even: two half-steps remain
+      half(h, sA0, sA1, sB1, sA2, sB2, s1a, s1b, s0a, s0b, r0);
+      half(h + 1, sA1, sA2, sB2, sA3, sB3, s0a, s0b, s1a, s1b, r1);
+    }
     // the halves still owed to a next block would multiply by 1
   }
 
   // ---- store: lane holds out[k = base + lane%32][n = base + 8*(r/4) + 4*(lane/32) + r%4]
   const int64_t slab = (int64_t)g * p.Kout * p.Nout;
+  if (!p.out_f32) {
+    // bf16: each wave puts its 128 x 64 sub-tile into its own 16 KB of LDS ([row][128 B],
+    // 16-byte chunk c of row r at c ^ (r & 7)), then stores whole 128-byte rows, 16 bytes
+    // per lane: full lines instead of 16-byte pieces of 32 rows per store.
+    __syncthreads();  // every wave is done with the stage tiles
+    uint8_t* const wl = s_lds + wave * (128 * 128);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const int i = blk >> 1, j = blk & 1;
+      const int row = i * 32 + frow;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int col = j * 64 + r4 * 16 + fhalf * 8;  // byte column
+        v2u v;
+        v.x = f32_to_bf16_rne(acc[blk][4 * r4] * fin) | (f32_to_bf16_rne(acc[blk][4 * r4 + 1] * fin) << 16);
+        v.y = f32_to_bf16_rne(acc[blk][4 * r4 + 2] * fin) | (f32_to_bf16_rne(acc[blk][4 * r4 + 3] * fin) << 16);
+        *reinterpret_cast<v2u*>(wl + row * 128 + ((((col >> 4) ^ (row & 7)) << 4) | (col & 15))) = v;
+      }
+    }
+    const bool cols_ok = n0 + wc * 64 < p.Nout;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = q * 8 + (lane >> 3), c = lane & 7;
+      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 128 + ((c ^ (row & 7)) << 4));
+      const int k = k0 + wr * 128 + row;
+      if (cols_ok && k < p.Kout)
+        *reinterpret_cast<v4u*>((uint16_t*)p.out + slab + (int64_t)k * p.Nout + n0 + wc * 64 + c * 8) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
     const int i = blk >> 1, j = blk & 1;
@@ -493,18 +592,10 @@ void tgmm_ratio_kernel(TgmmSegParams p) {
       const int n = n0 + wc * 64 + j * 32 + 8 * r4 + 4 * fhalf;
       if (n >= p.Nout) continue;
       const int64_t idx = slab + (int64_t)k * p.Nout + n;
-      float o[4];
+      v4f v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = acc[blk][4 * r4 + e] * fin;
-      if (p.out_f32) {
-        v4f v = {o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
-      } else {
-        v2u v;
-        v.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-        v.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-        *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = acc[blk][4 * r4 + e] * fin;
+      *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
     }
   }
 }
@@ -549,27 +640,33 @@ void tgmm_promote_kernel(TgmmSegParams p) {
       const uint32_t seg_row = (uint32_t)p.seg_row;
       const int krows = min(p.Kout - k0, TBM);
       const __amdgpu_buffer_rsrc_t ra =
-          make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * BLOCK_ROWS,
-                    (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * BLOCK_ROWS));
+          make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
+                    (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
       const __amdgpu_buffer_rsrc_t rb =
-          make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * BLOCK_ROWS,
-                    (uint32_t)((int64_t)TBN * p.seg_row - (int64_t)seg0 * BLOCK_ROWS));
+          make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
+                    (uint32_t)((int64_t)TBN * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
 
       // direct loads of segment block s: A rows 64w..64w+63 (8 per wave-load),
       // B rows 32w..32w+31
+      // byte of (row, logical 16-byte chunk c of the block) from the block's start in the
+      // column-pair layout
+      auto pair_off = [&](int row, uint32_t c) -> uint32_t {
+        return (uint32_t)(row >> 1) * 2 * seg_row + (c >> 2) * 128 + (uint32_t)(row & 1) * 64 +
+               (c & 3) * 16;
+      };
       auto issue = [&](int s, uint8_t* at, uint8_t* bt) {
-        const uint32_t koff = (uint32_t)s * BLOCK_ROWS;
+        const uint32_t koff = (uint32_t)s * PAIR_BLOCK;
   #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int row = wave * 64 + q * 8 + (lane >> 3);
           const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
-          load_rows_to_lds(ra, at + (wave * 64 + q * 8) * TILE_K, (uint32_t)row * seg_row + koff + c * 16);
+          load_rows_to_lds(ra, at + (wave * 64 + q * 8) * TILE_K, pair_off(row, c) + koff);
         }
   #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = wave * 32 + q * 8 + (lane >> 3);
           const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
-          load_rows_to_lds(rb, bt + (wave * 32 + q * 8) * TILE_K, (uint32_t)row * seg_row + koff + c * 16);
+          load_rows_to_lds(rb, bt + (wave * 32 + q * 8) * TILE_K, pair_off(row, c) + koff);
         }
       };
       // fragment addressing, as in the grouped GEMM: two per-lane offsets per half block
@@ -703,7 +800,8 @@ template <int A_FMT, int B_FMT>
 hipError_t launch_tgmm_fp8(const TgmmSegParams& p, hipStream_t st) {
   const int64_t tiles = (int64_t)((p.Kout + RBM - 1) / RBM) * ((p.Nout + RBN - 1) / RBN) * p.G;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((tgmm_ratio_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(RNT), 0, st, p);
+  hipLaunchKernelGGL((tgmm_ratio_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(RNT), 0, st, p,
+                     p.ratio);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ptiles = (int64_t)((p.Kout + TBM - 1) / TBM) * (p.Nout / TBN) * p.G;

@@ -114,55 +114,55 @@ class Step:
         self.s_lhs = torch.empty(nb, dtype=torch.float32, device=dev)
         self.s_grad = torch.empty(nb, dtype=torch.float32, device=dev)
         self.grad_q = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        self.lhs_q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        # quantizer workspace (the abs-max prepass), sized for the wider operand
         op = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC, 0.0)
         n = g._SZ()
-        self._chk(lib.gmm_workspace_size(g.OP_FWD, ctypes.byref(op), ctypes.byref(op), M,
+        self._chk(lib.gmm_workspace_size(g.OP_QUANTIZE, ctypes.byref(op), ctypes.byref(op), M,
                                          max(K, N), 0, 1, ctypes.byref(n)))
         self.ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
         self.ws_n = n.value
-        opg = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
-        self._chk(lib.gmm_workspace_size(g.OP_FWD, ctypes.byref(opg), ctypes.byref(opg), M, K, N,
-                                         1, ctypes.byref(n)))
-        self.ws_f = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
-        self.ws_f_n = n.value
-        opl = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
-        opg = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC_GIVEN, 0.0)
-        self._chk(lib.gmm_workspace_size(g.OP_TGMM, ctypes.byref(opl), ctypes.byref(opg), M, K, N,
-                                         G, ctypes.byref(n)))
+        # each tensor is quantized once (dynamic 128-row blocks) and its codes feed every
+        # product that uses it: lhs codes -> fwd and tgmm, grad codes -> dlhs and tgmm
+        self.op_lq = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC, 0.0)     # lhs quantizer recipe
+        self.op_l8 = g.Operand(g.KIND_FP8, g.E4M3, g.DYNAMIC, 0.0)      # its codes
+        self.op_gq = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC, 0.0)     # grad quantizer recipe
+        self.op_g8 = g.Operand(g.KIND_FP8, g.E5M2, g.DYNAMIC, 0.0)      # its codes
+        self._chk(lib.gmm_workspace_size(g.OP_TGMM, ctypes.byref(self.op_l8), ctypes.byref(self.op_g8),
+                                         M, K, N, G, ctypes.byref(n)))
         self.ws_t = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
         self.ws_t_n = n.value
+        # the forward with in-kernel quantization of the bf16 lhs (timed outside the step)
         self.op_lhs = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
-        self.op_grad = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC_GIVEN, 0.0)
-        self.op_gq = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC, 0.0)     # quantizer recipe
-        self.op_g8 = g.Operand(g.KIND_FP8, g.E5M2, g.DYNAMIC, 0.0)      # its codes as dlhs A
-        self.r_lhs, self.r_grad = ctypes.byref(self.op_lhs), ctypes.byref(self.op_grad)
+        self.r_lhs = ctypes.byref(self.op_lhs)
+        self.r_lq, self.r_l8 = ctypes.byref(self.op_lq), ctypes.byref(self.op_l8)
         self.r_gq, self.r_g8 = ctypes.byref(self.op_gq), ctypes.byref(self.op_g8)
         P = lambda t: t.data_ptr()
         self.p = {k: P(getattr(self, k)) for k in
-                  ("lhs", "grad", "grad_q", "ws_f", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs", "drhs",
-                   "s_lhs", "s_grad", "ws", "ws_t", "gs")}
+                  ("lhs", "grad", "lhs_q", "grad_q", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs",
+                   "drhs", "s_lhs", "s_grad", "ws", "ws_t", "gs")}
         torch.cuda.synchronize()
 
     def run(self, stream, ev=None):
-        """Enqueue one step; ev (6 events) brackets: scales, fwd, quantize, dlhs, tgmm."""
+        """Enqueue one step; ev (6 events) brackets: lhs quantize, fwd, grad quantize, dlhs,
+        tgmm."""
         lib, p, s = self.lib, self.p, stream
         M, K, N, G = self.M, self.K, self.N, self.G
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         chk = self._chk
         rec(0)
-        chk(lib.gmm_dynamic_scales(self.g.E4M3, M, K, p["lhs"], p["s_lhs"], p["ws"], self.ws_n, s))
+        chk(lib.gmm_quantize(self.r_lq, M, K, p["lhs"], p["lhs_q"], p["s_lhs"], p["ws"], self.ws_n, s))
         rec(1)
-        chk(lib.gmm_fwd(self.r_lhs, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
-                        p["lhs"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"],
-                        p["ws_f"], self.ws_f_n, s))
+        chk(lib.gmm_fwd(self.r_l8, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
+                        p["lhs_q"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"], None, 0, s))
         rec(2)
         chk(lib.gmm_quantize(self.r_gq, M, N, p["grad"], p["grad_q"], p["s_grad"], p["ws"], self.ws_n, s))
         rec(3)
         chk(lib.gmm_dlhs(self.r_g8, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
                          p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, s))
         rec(4)
-        chk(lib.tgmm_drhs(self.r_lhs, self.r_grad, self.g.OUT_BF16, M, K, N, G, p["lhs"], p["s_lhs"],
-                          p["grad"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
+        chk(lib.tgmm_drhs(self.r_l8, self.r_g8, self.g.OUT_BF16, M, K, N, G, p["lhs_q"], p["s_lhs"],
+                          p["grad_q"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
         rec(5)
 
     def fused_fwd(self, stream):
@@ -250,7 +250,7 @@ def main():
         step.run(s, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["scales_lhs", "gmm_fwd", "quantize_grad", "gmm_dlhs", "tgmm_drhs"]
+    names = ["quantize_lhs", "gmm_fwd", "quantize_grad", "gmm_dlhs", "tgmm_drhs"]
     per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
            for j, n in enumerate(names)}
     ms_step = wall * 1000.0 / args.steps
@@ -270,9 +270,9 @@ def main():
            for n in ("gmm_fwd", "gmm_dlhs", "tgmm_drhs")}
     dom = max(ops, key=lambda n: per[n])
     ach = flop_op / (per[dom] / 1000.0) / 1e12
-    kern = {"gmm_fwd": "quantize_rows<e4m3> + gmm_kernel<e4m3,e4m3,fp8 A,contraction-contiguous B>",
+    kern = {"gmm_fwd": "gmm_kernel<e4m3,e4m3,fp8 A,contraction-contiguous B>",
             "gmm_dlhs": "gmm_kernel<e5m2,e4m3,fp8 A,contraction-contiguous B>",
-            "tgmm_drhs": "tgmm_plan + quant_transpose<e4m3> + quant_transpose<e5m2> + "
+            "tgmm_drhs": "tgmm_plan + quant_transpose<e4m3 codes> + quant_transpose<e5m2 codes> + "
                          "tgmm_ratio_kernel<e4m3,e5m2> + tgmm_promote_kernel (exits: no wide group)"}[dom]
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -283,15 +283,15 @@ def main():
                    "routing": f"zipf{wl.zipf_s}", "group_sizes": [int(x) for x in wl.group_sizes()],
                    "lhs": "bf16 -> e4m3 dynamic 128-row blocks", "grad": "bf16 -> e5m2 dynamic 128-row blocks",
                    "rhs": "e4m3 per-channel", "out": "bf16",
-                   "step": "lhs scales + fwd (lhs quantized once in the call) + grad quantize + "
-                           "hybrid dlhs + tgmm"},
+                   "step": "lhs quantize + fwd + grad quantize + hybrid dlhs + tgmm; each tensor "
+                           "quantized once, its codes used by every product"},
         "ops": ops,
         "fwd_in_kernel_quantization": {"ms": round(fused_ms, 4),
                                        "TFLOP/s": round(flop_op / (fused_ms / 1000) / 1e12, 1),
                                        "note": "gmm_fwd without workspace (lhs quantized inside "
                                                "the product kernel); not part of the step"},
-        "prep_ms": {"lhs_scales": round(per["scales_lhs"], 4),
-                                "grad_quantize": round(per["quantize_grad"], 4)},
+        "prep_ms": {"lhs_quantize": round(per["quantize_lhs"], 4),
+                    "grad_quantize": round(per["quantize_grad"], 4)},
         "roofline": {"kernel": kern, "op": dom, "bound": "mfma", "achieved": round(ach, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(dom, wl.name),

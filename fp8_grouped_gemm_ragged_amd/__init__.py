@@ -251,12 +251,17 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
               lhs_static_scale=None, lhs_scales=None, grad_format="e5m2",
               grad_scaling="dynamic", grad_static_scale=None, grad_scales=None,
               out_dtype=None, out=None, return_scales=False):
-    """Weight gradient: drhs[g] = q(lhs)_g^T . q(grad)_g, [G, K, N]; empty groups give zeros."""
+    """Weight gradient: drhs[g] = q(lhs)_g^T . q(grad)_g, [G, K, N]; empty groups give zeros.
+
+    lhs / grad are bf16 values, or uint8 fp8 codes quantized beforehand (then their
+    block scales, or the static scale, are an input)."""
     import torch
 
     lib = load()
-    _need(lhs, torch.bfloat16, "lhs", 2)
-    _need(grad, torch.bfloat16, "grad", 2)
+    a_codes = isinstance(lhs, torch.Tensor) and lhs.dtype == torch.uint8
+    g_codes = isinstance(grad, torch.Tensor) and grad.dtype == torch.uint8
+    _need(lhs, torch.uint8 if a_codes else torch.bfloat16, "lhs", 2)
+    _need(grad, torch.uint8 if g_codes else torch.bfloat16, "grad", 2)
     _need(group_sizes, torch.int32, "group_sizes", 1)
     M, K = lhs.shape
     if grad.shape[0] != M:
@@ -268,20 +273,20 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
         out = torch.empty((G, K, N), dtype=odt, device=lhs.device)
     else:
         _need(out, odt, "out", 3)
-    aop = _operand(KIND_BF16, lhs_format, lhs_scaling, lhs_static_scale)
-    bop = _operand(KIND_BF16, grad_format, grad_scaling, grad_static_scale)
-    def scales_for(mode, given):
-        if _SCALING[mode] == DYNAMIC_GIVEN:
+    aop = _operand(KIND_FP8 if a_codes else KIND_BF16, lhs_format, lhs_scaling, lhs_static_scale)
+    bop = _operand(KIND_FP8 if g_codes else KIND_BF16, grad_format, grad_scaling, grad_static_scale)
+    def scales_for(mode, given, codes):
+        if _SCALING[mode] == DYNAMIC_GIVEN or (codes and _SCALING[mode] == DYNAMIC):
             if given is None:
-                raise ValueError("dynamic_given needs the block scales")
+                raise ValueError("this recipe needs the operand's block scales as an input")
             _need(given, torch.float32, "scales", 1)
             return given
         if _SCALING[mode] == DYNAMIC:
             return given if given is not None else torch.empty(_nblocks(M), dtype=torch.float32, device=lhs.device)
         return None
 
-    sa = scales_for(lhs_scaling, lhs_scales)
-    sg = scales_for(grad_scaling, grad_scales)
+    sa = scales_for(lhs_scaling, lhs_scales, a_codes)
+    sg = scales_for(grad_scaling, grad_scales, g_codes)
     ws_n = _SZ()
     _check(lib.gmm_workspace_size(OP_TGMM, ctypes.byref(aop), ctypes.byref(bop), M, K, N, G,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")

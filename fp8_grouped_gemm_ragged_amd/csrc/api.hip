@@ -262,7 +262,6 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
   gmm_status_t s;
   if ((s = check_operand(lhs_op)) != GMM_OK) return s;
   if ((s = check_operand(grad_op)) != GMM_OK) return s;
-  if (lhs_op->kind != GMM_OPERAND_BF16 || grad_op->kind != GMM_OPERAND_BF16) return GMM_ERR_RECIPE;
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, K, N, G)) != GMM_OK) return s;
   if (!group_sizes || !drhs) return GMM_ERR_NULL;
@@ -278,20 +277,29 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
   const size_t wt = tgmm_ws_bytes(M, K, N, G);
   if (!workspace || workspace_bytes < wa + wb + wt) return GMM_ERR_WORKSPACE;
   const size_t out_bytes = (size_t)G * K * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
-  if (overlaps(drhs, out_bytes, lhs, (size_t)M * K * 2) ||
-      overlaps(drhs, out_bytes, grad, (size_t)M * N * 2) ||
+  const bool a_codes = lhs_op->kind == GMM_OPERAND_FP8, g_codes = grad_op->kind == GMM_OPERAND_FP8;
+  const size_t lhs_bytes = (size_t)M * K * (a_codes ? 1 : 2);
+  const size_t grad_bytes = (size_t)M * N * (g_codes ? 1 : 2);
+  const size_t sc_bytes = (size_t)nblocks(M) * 4;
+  if (overlaps(drhs, out_bytes, lhs, lhs_bytes) || overlaps(drhs, out_bytes, grad, grad_bytes) ||
       overlaps(drhs, out_bytes, group_sizes, (size_t)G * 4) ||
+      overlaps(drhs, out_bytes, lhs_scales, sc_bytes) ||
+      overlaps(drhs, out_bytes, grad_scales, sc_bytes) ||
       overlaps(workspace, wa + wb + wt, drhs, out_bytes) ||
-      overlaps(workspace, wa + wb + wt, lhs, (size_t)M * K * 2) ||
-      overlaps(workspace, wa + wb + wt, grad, (size_t)M * N * 2))
+      overlaps(workspace, wa + wb + wt, lhs, lhs_bytes) ||
+      overlaps(workspace, wa + wb + wt, grad, grad_bytes) ||
+      overlaps(workspace, wa + wb + wt, lhs_scales, sc_bytes) ||
+      overlaps(workspace, wa + wb + wt, grad_scales, sc_bytes))
     return GMM_ERR_ALIAS;
   if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
   trace("tgmm_drhs", M, K, N, G);
   hipStream_t st = (hipStream_t)stream;
 
   TgmmParams p{};
-  p.a = (const uint16_t*)lhs;
-  p.b = (const uint16_t*)grad;
+  p.a = lhs;
+  p.b = grad;
+  p.a_codes = a_codes;
+  p.b_codes = g_codes;
   p.group_sizes = group_sizes;
   p.out = drhs;
   p.M = M;

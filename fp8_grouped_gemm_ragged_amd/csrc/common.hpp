@@ -125,6 +125,30 @@ __device__ inline v8i lds_read_frag(const uint8_t* lds, uint32_t row, uint32_t c
 }
 
 // ---------------------------------------------------------------------------------
+// 8x8 byte transpose: in[r] holds bytes (r, 0..7) as two dwords; out[c] gets bytes
+// (0..7, c).  Two rounds of v_perm byte shuffles.
+__device__ inline void transpose8x8(const v2u in[8], v2u out[8]) {
+  uint32_t x[4][2][2];  // [row pair][dword lo/hi][even/odd column pair]
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t r0 = d ? in[2 * p].y : in[2 * p].x;
+      const uint32_t r1 = d ? in[2 * p + 1].y : in[2 * p + 1].x;
+      x[p][d][0] = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
+      x[p][d][1] = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int d = c >> 2, h = (c >> 1) & 1;
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    out[c].x = __builtin_amdgcn_perm(x[1][d][h], x[0][d][h], sel);
+    out[c].y = __builtin_amdgcn_perm(x[3][d][h], x[2][d][h], sel);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Wave-level inclusive prefix sum (64 lanes).
 // ---------------------------------------------------------------------------------
 __device__ inline int wave_incl_scan(int v, int lane) {

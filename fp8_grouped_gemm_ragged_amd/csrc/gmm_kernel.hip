@@ -16,11 +16,10 @@
 //     are remapped to give each XCD a contiguous range of tiles, ordered in bands of 8
 //     M-tiles sweeping the N-tiles: the 32 concurrent tiles of one XCD share A rows and
 //     B columns in that XCD's L2;
-//   * K-loop over 128-byte contraction steps with two LDS stages (2 x 64 KB).  fp8
-//     operands go from HBM straight into the swizzled LDS tile with buffer_load...lds
-//     (the swizzle is realised by the per-lane global address); the bf16 A operand is
-//     prefetched two steps ahead into registers with range-checked 16-byte buffer loads
-//     (rows past the group end read as zero), quantized in registers and stored to LDS;
+//   * K-loop over 128-byte contraction steps with two LDS stages (2 x 64 KB).  Every
+//     operand is prefetched two steps ahead into registers with range-checked 16-byte
+//     buffer loads (rows past the group end read as zero) and stored into the swizzled
+//     LDS tile one step later; a bf16 A operand is quantized in registers on the way;
 //   * each wave owns a 128 x 128 sub-tile: 4 x 4 MFMA 32x32x64 fp8 instructions per
 //     64-deep half step, fp32 accumulators in AGPRs.  The loop body is one basic block
 //     and the quantization of the next step (about 14 VALU instructions per MFMA) is
@@ -111,29 +110,6 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
   tc.n0 = __builtin_amdgcn_readfirstlane(tc.n0);
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
-}
-
-// 8x8 byte transpose: in[r] holds bytes (r, 0..7) as two dwords; out[c] gets bytes
-// (0..7, c).  Two rounds of v_perm byte shuffles.
-__device__ inline void transpose8x8(const v2u in[8], v2u out[8]) {
-  uint32_t x[4][2][2];  // [row pair][dword lo/hi][even/odd column pair]
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const uint32_t r0 = d ? in[2 * p].y : in[2 * p].x;
-      const uint32_t r1 = d ? in[2 * p + 1].y : in[2 * p + 1].x;
-      x[p][d][0] = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
-      x[p][d][1] = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int d = c >> 2, h = (c >> 1) & 1;
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    out[c].x = __builtin_amdgcn_perm(x[1][d][h], x[0][d][h], sel);
-    out[c].y = __builtin_amdgcn_perm(x[3][d][h], x[2][d][h], sel);
-  }
 }
 
 template <int A_FMT, int B_FMT, bool A_FP8, bool B_TRANS>

@@ -30,8 +30,8 @@ struct GemmParams {
 
 // tgmm: out[g] = A_g^T [Kout, m] x B_g [m, Nout], contraction over the rows of group g.
 struct TgmmParams {
-  const uint16_t* a;         // bf16 [M, Kout]
-  const uint16_t* b;         // bf16 [M, Nout]
+  const void* a;             // [M, Kout]: bf16 values, or fp8 codes when a_codes
+  const void* b;             // [M, Nout]: bf16 values, or fp8 codes when b_codes
   const int32_t* group_sizes;
   void* out;                 // [G, Kout, Nout] bf16 or f32
   int32_t* plan;             // workspace: tgmm_plan_words(G) words
@@ -45,6 +45,7 @@ struct TgmmParams {
   int64_t M;
   int32_t Kout, Nout, G;
   int32_t out_f32;
+  int32_t a_codes, b_codes;  // the operand is fp8 codes quantized beforehand
 };
 
 // the fp8 tgmm on quantized, transposed segments

@@ -11,9 +11,9 @@
 //      "segment" (the 128-row blocks the group meets, laid end to end); per block the
 //      scale product sc_c; per segment block the ratio of scale products used below.
 //   2. quant_transpose (once per operand): every element quantized exactly once (with
-//      its block's scale) and written transposed into the segment, so that each group's
-//      rows start on a block boundary and rows of other groups inside a shared block are
-//      zero codes.  Columns are stored in pairs: block b of columns 2p, 2p + 1 is 256
+//      its block's scale), or taken as it is when the operand arrives as fp8 codes, and
+//      written transposed into the segment, so that each group's rows start on a block
+//      boundary and rows of other groups inside a shared block are zero codes.  Columns are stored in pairs: block b of columns 2p, 2p + 1 is 256
 //      bytes, [2p: m 0..63][2p + 1: m 0..63][2p: m 64..127][2p + 1: m 64..127], so a
 //      half block of two columns is one 128-byte line.
 //   3. tgmm_ratio: per (group, 256 k x 256 n) tile, one contraction step per block of
@@ -28,7 +28,8 @@
 //
 // A block whose scale product is zero (an all-zero block, a scale whose inverse is not
 // finite, or a product that underflows) adds nothing in the method; its codes are
-// written as zeros and it keeps the accumulator units unchanged.
+// written as zeros and it keeps the accumulator units unchanged.  For an operand given
+// as codes only a zero product counts: its codes are used as they are.
 #include "kernels.hpp"
 
 namespace gmm {
@@ -68,12 +69,22 @@ __device__ inline Plan plan_view(const int32_t* w, int G) {
               w + 5 * G + 1};
 }
 
-__device__ inline float scale_product(int64_t c, const float* a_blk, float a_s, float a_inv,
-                                      const float* b_blk, float b_s, float b_inv, bool& dead) {
-  const float sa = a_blk ? a_blk[c] : a_s;
-  const float sb = b_blk ? b_blk[c] : b_s;
-  const float ia = a_blk ? inv_from_scale(sa) : a_inv;
-  const float ib = b_blk ? inv_from_scale(sb) : b_inv;
+// Operand scaling as the plan sees it: per-block scales (blk) or a static scale and
+// inverse; `codes` when the operand arrives as fp8 codes.
+struct OpScale {
+  const float* blk;
+  float s, inv;
+  int codes;
+};
+
+// Block c's scale product RNE(s_a * s_b), and whether the block adds nothing: a zero
+// product, or a bf16 operand whose block quantizes to zero codes (inverse 0).  Codes
+// given as input are used as they are, so for them only a zero product drops the block.
+__device__ inline float scale_product(int64_t c, const OpScale& a, const OpScale& b, bool& dead) {
+  const float sa = a.blk ? a.blk[c] : a.s;
+  const float sb = b.blk ? b.blk[c] : b.s;
+  const float ia = a.codes ? 1.0f : a.blk ? inv_from_scale(sa) : a.inv;
+  const float ib = b.codes ? 1.0f : b.blk ? inv_from_scale(sb) : b.inv;
   const float sc = __fmul_rn(sa, sb);
   dead = sc == 0.0f || ia == 0.0f || ib == 0.0f;
   return sc;
@@ -101,8 +112,7 @@ __device__ inline int block_incl_scan(int v, int* tmp, Op op) {
 // segment block b of group g, and 1 at ratio[seg[g + 1] + g], just past the group's
 // blocks.
 __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
-    const int32_t* __restrict__ gs, int G, int64_t M, const float* __restrict__ a_blk,
-    float a_s, float a_inv, const float* __restrict__ b_blk, float b_s, float b_inv,
+    const int32_t* __restrict__ gs, int G, int64_t M, OpScale a_sc, OpScale b_sc,
     int32_t* __restrict__ plan, float* __restrict__ scprod, float* __restrict__ ratio) {
   __shared__ int s_tmp[PLAN_NT / 64];
   __shared__ int s_incl[PLAN_NT];
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
   const int64_t nblk = (M + BLOCK_ROWS - 1) / BLOCK_ROWS;
   for (int64_t cb = t; cb < nblk; cb += PLAN_NT) {
     bool dead;
-    const float sc = scale_product(cb, a_blk, a_s, a_inv, b_blk, b_s, b_inv, dead);
+    const float sc = scale_product(cb, a_sc, b_sc, dead);
     scprod[cb] = dead ? 0.0f : sc;
   }
   __syncthreads();
@@ -172,7 +182,7 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
     for (int b = b0; b < b1; ++b) {
       while (b >= s_seg[g + 1]) ++g;
       bool dead;
-      scale_product(block_of(g, b), a_blk, a_s, a_inv, b_blk, b_s, b_inv, dead);
+      scale_product(block_of(g, b), a_sc, b_sc, dead);
       if (!dead) last = b;
     }
   }
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
     float sc_prev = 0.0f;
     if (prev >= s_seg[g]) {
       bool dead;
-      sc_prev = scale_product(block_of(g, prev), a_blk, a_s, a_inv, b_blk, b_s, b_inv, dead);
+      sc_prev = scale_product(block_of(g, prev), a_sc, b_sc, dead);
     } else {
       prev = -1;
     }
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
         prev = -1;
       }
       bool dead;
-      const float sc = scale_product(block_of(g, b), a_blk, a_s, a_inv, b_blk, b_s, b_inv, dead);
+      const float sc = scale_product(block_of(g, b), a_sc, b_sc, dead);
       float r = 1.0f;
       if (!dead) {
         if (prev >= 0) r = __fdiv_rn(sc_prev, sc);
@@ -262,12 +272,14 @@ __device__ inline void quant_transpose8(const v4u in[8], float inv, v2u out[8]) 
 
 // grid (segment blocks upper bound, C / 128).  Workgroup (b, ct): segment block b (a
 // pair (group g, 128-row block c)) and columns [128 ct, 128 ct + 128).  A block whose
-// scale product is zero gets zero codes.
-template <int FMT>
+// scale product is zero gets zero codes.  x holds bf16 values, quantized here with the
+// block's scale, or (CODES) fp8 codes quantized beforehand, which are only transposed.
+template <int FMT, bool CODES>
 __global__ __launch_bounds__(256) void quant_transpose_kernel(
-    const uint16_t* __restrict__ x, int64_t C, const int32_t* __restrict__ plan, int G,
+    const void* __restrict__ x, int64_t C, const int32_t* __restrict__ plan, int G,
     const float* __restrict__ scale_blk, float inv_static, const float* __restrict__ scprod,
     uint8_t* __restrict__ seg, int64_t seg_row) {
+  constexpr int ES = CODES ? 1 : 2;  // bytes per element of x
   const int32_t* off = plan;
   const int32_t* cnt = plan + G;
   const int32_t* sg = plan + 2 * G;
@@ -287,21 +299,34 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(
   const int64_t col0 = (int64_t)blockIdx.y * 128;
   // rows [r_lo, r_hi) from column col0 on: later rows read as zero
   const __amdgpu_buffer_rsrc_t r =
-      make_rsrc(x + (int64_t)r_lo * C + col0, (uint32_t)((int64_t)(r_hi - r_lo) * C * 2 - col0 * 2));
-  const float inv = scprod[c] == 0.0f ? 0.0f
-                    : scale_blk ? inv_from_scale(scale_blk[c]) : inv_static;
+      make_rsrc((const uint8_t*)x + ((int64_t)r_lo * C + col0) * ES,
+                (uint32_t)(((int64_t)(r_hi - r_lo) * C - col0) * ES));
+  const bool dead = scprod[c] == 0.0f;
   const int t = threadIdx.x;
   const int rb = t & 15, cb = t >> 4;  // 8-row block, 8-column block
-  v4u in[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = rb * 8 + e - rel;  // relative to the first row of g in the block
-    uint32_t voff = (uint32_t)row * (uint32_t)(C * 2) + cb * 16;
-    if (row < 0) voff = 0xfffffff0u;  // rows of the previous group: zero codes
-    in[e] = buf_load16(r, voff);
-  }
   v2u q[8];
-  quant_transpose8<FMT>(in, inv, q);
+  if constexpr (CODES) {
+    v2u in[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = rb * 8 + e - rel;  // relative to the first row of g in the block
+      uint32_t voff = (uint32_t)row * (uint32_t)C + cb * 8;
+      if (row < 0 || dead) voff = 0xfffffff8u;  // previous group's rows, or a dead block: zeros
+      in[e] = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    }
+    transpose8x8(in, q);
+  } else {
+    const float inv = dead ? 0.0f : scale_blk ? inv_from_scale(scale_blk[c]) : inv_static;
+    v4u in[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = rb * 8 + e - rel;
+      uint32_t voff = (uint32_t)row * (uint32_t)(C * 2) + cb * 16;
+      if (row < 0) voff = 0xfffffff0u;  // rows of the previous group: zero codes
+      in[e] = buf_load16(r, voff);
+    }
+    quant_transpose8<FMT>(in, inv, q);
+  }
   // segment layout by column pairs: pair p, block b holds 256 bytes, [col 2p, m 0..63]
   // [col 2p + 1, m 0..63] [col 2p, m 64..127] [col 2p + 1, m 64..127]
   uint8_t* dst = seg + (col0 + cb * 8) * seg_row + (int64_t)b * PAIR_BLOCK + (rb >> 3) * 128 +
@@ -328,9 +353,10 @@ constexpr int RH_TILE = RBM * HROW;  // 16 KB
 // One (group, 256 k x 256 n) tile per workgroup of 8 waves, each wave 128 k x 64 n
 // (2 x 4 waves; two waves per SIMD, so one wave's vector work overlaps the other's
 // MFMAs).  The contraction runs in half-blocks of 64 rows through a ring of 4 LDS
-// stages: half-step h's fp8 tiles are loaded straight from memory into stage h % 4
-// three half-steps ahead, and half-step h + 1's fragments are read into registers
-// while half-step h's MFMAs run, so no step waits on LDS reads when it starts.
+// stages: half-step h's fp8 tiles are loaded into one of two register staging sets
+// three half-steps ahead and written into stage h % 4 two half-steps ahead, and
+// half-step h + 1's fragments are read into registers while half-step h's MFMAs run,
+// so no step waits on LDS reads when it starts.
 template <int A_FMT, int B_FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(RNT, RNT), amdgpu_waves_per_eu(2, 2)))
 void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
@@ -785,15 +811,24 @@ void tgmm_promote_kernel(TgmmSegParams p) {
   }
 }
 
-template <int FMT>
-hipError_t launch_qt(const uint16_t* x, int64_t M, int64_t C, const int32_t* plan, int G,
-                     const float* scale_blk, float inv_static, const float* scprod, uint8_t* seg,
-                     int64_t seg_row, hipStream_t st) {
+// The transposing quantizer for one operand (bf16 values, or fp8 codes when `codes`).
+hipError_t launch_qt(int fmt, bool codes, const void* x, int64_t M, int64_t C,
+                     const int32_t* plan, int G, const float* scale_blk, float inv_static,
+                     const float* scprod, uint8_t* seg, int64_t seg_row, hipStream_t st) {
   const int64_t max_blocks = (M + BLOCK_ROWS - 1) / BLOCK_ROWS + G;
   dim3 grid((unsigned)max_blocks, (unsigned)(C / 128));
-  hipLaunchKernelGGL(quant_transpose_kernel<FMT>, grid, dim3(256), 0, st, x, C, plan, G,
-                     scale_blk, inv_static, scprod, seg, seg_row);
-  return hipGetLastError();
+#define GMM_QT(F, CD)                                                                     \
+  if (fmt == F && codes == CD) {                                                          \
+    hipLaunchKernelGGL((quant_transpose_kernel<F, CD>), grid, dim3(256), 0, st, x, C, plan, \
+                       G, scale_blk, inv_static, scprod, seg, seg_row);                   \
+    return hipGetLastError();                                                             \
+  }
+  GMM_QT(FMT_E4M3, false)
+  GMM_QT(FMT_E5M2, false)
+  GMM_QT(FMT_E4M3, true)
+  GMM_QT(FMT_E5M2, true)
+#undef GMM_QT
+  return hipErrorInvalidValue;
 }
 
 template <int A_FMT, int B_FMT>
@@ -819,19 +854,18 @@ int64_t tgmm_segment_row_bytes(int64_t M, int G) {
 
 hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st) {
   const int64_t seg_row = tgmm_segment_row_bytes(p.M, p.G);
+  const OpScale a_sc{p.a_scale_blk, p.a_scale_static, p.a_inv_static, p.a_codes};
+  const OpScale b_sc{p.b_scale_blk, p.b_scale_static, p.b_inv_static, p.b_codes};
   hipLaunchKernelGGL(tgmm_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p.group_sizes, p.G, p.M,
-                     p.a_scale_blk, p.a_scale_static, p.a_inv_static, p.b_scale_blk,
-                     p.b_scale_static, p.b_inv_static, p.plan, p.scprod, p.ratio);
+                     a_sc, b_sc, p.plan, p.scprod, p.ratio);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.M > 0) {
-    e = a_fmt == FMT_E4M3
-            ? launch_qt<FMT_E4M3>(p.a, p.M, p.Kout, p.plan, p.G, p.a_scale_blk, p.a_inv_static, p.scprod, p.a_seg, seg_row, st)
-            : launch_qt<FMT_E5M2>(p.a, p.M, p.Kout, p.plan, p.G, p.a_scale_blk, p.a_inv_static, p.scprod, p.a_seg, seg_row, st);
+    e = launch_qt(a_fmt, p.a_codes != 0, p.a, p.M, p.Kout, p.plan, p.G, p.a_scale_blk,
+                  p.a_inv_static, p.scprod, p.a_seg, seg_row, st);
     if (e != hipSuccess) return e;
-    e = b_fmt == FMT_E4M3
-            ? launch_qt<FMT_E4M3>(p.b, p.M, p.Nout, p.plan, p.G, p.b_scale_blk, p.b_inv_static, p.scprod, p.b_seg, seg_row, st)
-            : launch_qt<FMT_E5M2>(p.b, p.M, p.Nout, p.plan, p.G, p.b_scale_blk, p.b_inv_static, p.scprod, p.b_seg, seg_row, st);
+    e = launch_qt(b_fmt, p.b_codes != 0, p.b, p.M, p.Nout, p.plan, p.G, p.b_scale_blk,
+                  p.b_inv_static, p.scprod, p.b_seg, seg_row, st);
     if (e != hipSuccess) return e;
   }
   TgmmSegParams q{};

@@ -185,12 +185,15 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
  *   drhs[g, k, n] = sum over 128-row blocks c meeting group g of
  *                   RNE( (sum_{m in c, m in g} q(lhs)[m, k] q(grad)[m, n]) * RNE(s_lhs[c] s_grad[c]) )
  *
- * lhs [M, K] and grad [M, N] are bf16, each quantized in-kernel by its own recipe
- * (lhs_op, grad_op; kind must be GMM_OPERAND_BF16; DYNAMIC_GIVEN reuses the block scales
- * of the forward / dlhs calls on the same tensors).  Because a dynamic scale changes
- * every 128 rows, the contraction over rows is split at block boundaries and each
- * block's partial sum is scaled before it is added.  lhs_scales / grad_scales: as
- * gmm_fwd's lhs_scales (outputs for DYNAMIC, may be NULL).
+ * lhs [M, K] and grad [M, N] are each either bf16 values, quantized in-kernel by the
+ * operand's recipe (DYNAMIC_GIVEN reuses the block scales of the forward / dlhs calls
+ * on the same tensors), or fp8 codes quantized beforehand with that recipe
+ * (kind GMM_OPERAND_FP8: for instance the codes gmm_quantize made for gmm_fwd or
+ * gmm_dlhs; the codes are used as they are, and must not be NaN or Inf encodings).
+ * Because a dynamic scale changes every 128 rows, the contraction over rows is split at
+ * block boundaries and each block's partial sum is scaled before it is added.
+ * lhs_scales / grad_scales: as gmm_fwd's lhs_scales (outputs for DYNAMIC + BF16, may be
+ * NULL; inputs for DYNAMIC_GIVEN and for DYNAMIC + FP8).
  * drhs [G, K, N] bf16 or f32.  A group with m_g == 0 gets a slab of +0.0.
  * workspace    required: gmm_workspace_size(GMM_OP_TGMM, lhs_op, grad_op, M, K, N, G)
  *              bytes.  It holds each operand quantized once and transposed so that the

@@ -108,3 +108,28 @@ def bf16_to_bits(t):
     import torch
 
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def random_fp8_codes(shape, fmt, seed):
+    """numpy uint8 fp8 codes drawn uniformly from the finite encodings of ``fmt``, seeded.
+
+    e4m3 (fn): every byte but 0x7f and 0xff (the NaN encodings), which become 0x7e / 0xfe.
+    e5m2: every byte whose exponent field (bits 2..6) is not all ones; those get bit 2
+    cleared.  Stands in for an operand that was quantized before the call."""
+    rng = np.random.default_rng(int(seed))
+    c = rng.integers(0, 256, size=tuple(shape), dtype=np.uint16).astype(np.uint8)
+    if fmt == "e4m3":
+        bad = (c & 0x7F) == 0x7F
+        c[bad] ^= np.uint8(0x01)
+    elif fmt == "e5m2":
+        bad = (c & 0x7C) == 0x7C
+        c[bad] &= np.uint8(0xFB)
+    else:
+        raise ValueError(fmt)
+    return c
+
+
+def log_uniform_scales(n, lo, hi, seed):
+    """numpy float32 [n] with log10 uniform in [lo, hi), seeded (per-block scales)."""
+    rng = np.random.default_rng(int(seed))
+    return (10.0 ** rng.uniform(lo, hi, size=n)).astype(np.float32)

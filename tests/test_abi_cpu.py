@@ -122,9 +122,22 @@ def test_dlhs_and_tgmm_validation():
     assert lib.gmm_dlhs(ctypes.byref(o), 0, 0, 0, 256, 200, 256, 2, ptr(1), ptr(2), ptr(3),
                         ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20, None) == 2
     a, b = op(fmt=0), op(fmt=1)
+    # fp8 codes are accepted; their dynamic block scales are then an input
     pre = op(kind=1)
+    assert lib.tgmm_drhs(ctypes.byref(pre), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), None,
+                         ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20, None) == 1
     assert lib.tgmm_drhs(ctypes.byref(pre), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
-                         ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20, None) == 4
+                         ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 64, None) == 5
+    # aliasing is judged with the operand's element size: 1 byte for codes, 2 for bf16
+    lhs = ptr(1).value
+    near = lambda d: ctypes.c_void_p(lhs + d)
+    assert lib.tgmm_drhs(ctypes.byref(pre), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
+                         ptr(3), ptr(4), ptr(5), near(256 * 256 - 16), ptr(7), 1 << 26, None) == 9
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
+                         ptr(3), ptr(4), ptr(5), near(256 * 256), ptr(7), 1 << 26, None) == 9
+    # scales inside the workspace are rejected (the call overwrites its workspace)
+    assert lib.tgmm_drhs(ctypes.byref(pre), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(7),
+                         ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 1 << 26, None) == 9
     assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),
                          ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 64, None) == 5
     assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 2, ptr(1), ptr(2),

@@ -265,6 +265,49 @@ def _check_tgmm(lhs, grad, sa, sg, sizes, out, out32, rng):
     assert_bf16_close(to_np(out[:, ki][:, :, ni]), R, ranges)
 
 
+def test_mixtral_gate_up_step(lib):
+    """The benchmark step at full size, launched as bench.py launches it: lhs and grad each
+    quantized once (dynamic 128-row blocks), fwd and dlhs on those codes, tgmm on both
+    codes.  Sampled codes byte for byte, sampled outputs of all three products against
+    the oracle recomputed from the bf16 inputs."""
+    wl = WORKLOADS["mixtral_gate_up"]
+    G, M, K, N = wl.G, wl.M, wl.K, wl.N
+    sizes = wl.group_sizes()
+    seed = wl.seed * 100
+    x = normal_bf16((M, K), 1.0, seed, DEV)
+    w = normal_bf16((G, K, N), 0.02, seed + 1, DEV)
+    grad = normal_bf16((M, N), 1e-3, seed + 2, DEV)
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    wk, sk = lib.gmm_quantize_rhs(w, "e4m3", 1, "kn")
+    xq, sx = lib.gmm_quantize(x, "e4m3", "dynamic")
+    gq, sg = lib.gmm_quantize(grad, "e5m2", "dynamic")
+    fk = dict(lhs_scaling="dynamic", lhs_scales=sx)
+    out = lib.gmm_fwd(xq, wq, ws, gs, **fk)
+    out32 = lib.gmm_fwd(xq, wq, ws, gs, out_dtype=torch.float32, **fk)
+    dk = dict(grad_scaling="dynamic", grad_scales=sg)
+    dl = lib.gmm_dlhs(gq, wk, sk, gs, **dk)
+    dl32 = lib.gmm_dlhs(gq, wk, sk, gs, out_dtype=torch.float32, **dk)
+    tk = dict(lhs_scales=sx, grad_scales=sg)
+    dw = lib.tgmm_drhs(xq, gq, gs, **tk)
+    dw32 = lib.tgmm_drhs(xq, gq, gs, out_dtype=torch.float32, **tk)
+    sync()
+    rng = np.random.default_rng(7)
+    rows = sample_rows(sizes, rng)
+    ri = torch.as_tensor(rows, device=DEV)
+    for t, codes, fmt in ((x, xq, "e4m3"), (grad, gq, "e5m2")):
+        b = bf16_to_bits(t)
+        _, inv = dynamic_block_scales(b, fmt)
+        ref = quantize_with_inv(bf16_bits_to_f32(b[rows]), inv[rows // 128], fmt)
+        assert np.array_equal(to_np(codes[ri]), ref)
+    cols = sample_cols(N, rng)
+    _check_fwd(lib, x, "dynamic", sx, bf16_to_bits(w[:, :, cols]), wq, ws, cols, sizes, out,
+               out32, rng)
+    kc = sample_cols(K, rng)
+    _check_dlhs(grad, sg, bf16_to_bits(w[:, kc, :]), wk, sk, kc, sizes, dl, dl32, rng)
+    _check_tgmm(x, grad, sx, sg, sizes, dw, dw32, rng)
+
+
 @pytest.fixture(scope="module")
 def swiglu():
     wl = WORKLOADS["moe_swiglu"]

@@ -132,3 +132,100 @@ def test_tgmm_wide_scale_range_groups(lib, sizes):
             assert err <= TOL, err
         else:
             assert_bf16_close(Y, R, [(g, g + 1) for g in range(len(sizes))])
+
+
+def _codes_operand(which, name, M, C, fmt, seed, lo, hi, scaling="dynamic"):
+    """(tensor for the call, call kwargs, oracle codes, oracle per-block scales).
+
+    Codes operands are seeded random finite fp8 codes with seeded per-block scales (or one
+    static scale); bf16 operands are seeded normals that both sides quantize themselves."""
+    from synth.workloads import log_uniform_scales, random_fp8_codes
+
+    nb = -(-M // 128)
+    if which:
+        codes = random_fp8_codes((M, C), fmt, seed)
+        t = torch.from_numpy(codes).to(DEV)
+        if scaling == "static":
+            s = float(log_uniform_scales(1, lo, hi, seed + 1)[0])
+            return t, {f"{name}_scaling": "static", f"{name}_static_scale": s}, codes, \
+                np.full(nb, np.float32(s), np.float32)
+        s = log_uniform_scales(nb, lo, hi, seed + 1)
+        return t, {f"{name}_scaling": "dynamic", f"{name}_scales": torch.from_numpy(s).to(DEV)}, codes, s
+    x, xb = gen((M, C), 1.0 if name == "lhs" else 1e-3, seed)
+    codes, s = ops.quantize_operand(xb, fmt, "dynamic")
+    return x, {}, codes, s
+
+
+@pytest.mark.parametrize("which", ["lhs", "grad", "both", "both_static"])
+def test_tgmm_codes_operands(lib, which):
+    # operands handed over as fp8 codes quantized beforehand (with their scales): the call
+    # only transposes them; ragged groups with empty ones and a K tail, as above
+    from oracle.gmm import tgmm_ref
+
+    sizes = [0, 300, 5, 0, 457, 130]
+    M, K, N = sum(sizes), 640, 384
+    st = "static" if which == "both_static" else "dynamic"
+    lhs, lkw, ac, sa = _codes_operand(which != "grad", "lhs", M, K, "e4m3", 301, -3, -1, st)
+    grad, gkw, gc, sg = _codes_operand(which != "lhs", "grad", M, N, "e5m2", 303, -8, -6, st)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = lib.tgmm_drhs(lhs, grad, gs_tensor(sizes), out_dtype=out_dtype, **lkw, **gkw)
+        R = tgmm_ref(ac, "e4m3", sa, gc, "e5m2", sg, np.asarray(sizes), 128, "f32")
+        Y = to_np(out)
+        for g in np.flatnonzero(np.asarray(sizes) == 0):
+            assert (Y[g].view(np.uint32 if out_dtype == torch.float32 else np.uint16) == 0).all()
+        if out_dtype == torch.float32:
+            err = slab_rel_err(Y, R)
+            print(f"{which}: max slab relative error {err:.3e}")
+            assert err <= TOL, err
+        else:
+            assert_bf16_close(Y, R, [(g, g + 1) for g in range(len(sizes))])
+
+
+def test_tgmm_codes_route_equals_bf16_route(lib):
+    # the codes gmm_quantize makes for a tensor, handed to tgmm with their scales, give
+    # the same bits as tgmm quantizing the bf16 tensor itself (GPU against GPU)
+    sizes = [200, 0, 313, 129, 6]
+    M, K, N = sum(sizes), 512, 384
+    x, _ = gen((M, K), 1.0, 311)
+    gr, _ = gen((M, N), 1e-3, 312)
+    gs = gs_tensor(sizes)
+    xq, sx = lib.gmm_quantize(x, "e4m3", "dynamic")
+    gq, sgr = lib.gmm_quantize(gr, "e5m2", "dynamic")
+    for out_dtype, view in ((torch.float32, torch.int32), (torch.bfloat16, torch.int16)):
+        a = lib.tgmm_drhs(x, gr, gs, out_dtype=out_dtype)
+        b = lib.tgmm_drhs(xq, gq, gs, lhs_scales=sx, grad_scales=sgr, out_dtype=out_dtype)
+        c = lib.tgmm_drhs(x, gq, gs, grad_scales=sgr, out_dtype=out_dtype)
+        assert torch.equal(a.view(view), b.view(view))
+        assert torch.equal(a.view(view), c.view(view))
+
+
+@pytest.mark.parametrize("sizes", [[200, 0, 250, 190], [640]])
+def test_tgmm_codes_zero_and_subnormal_scale_blocks(lib, sizes):
+    # codes are used as given: a block adds nothing only when its scale product is 0
+    # (block 1: grad scale 0; block 3: the product underflows).  Block 2 has a subnormal
+    # grad scale and nonzero codes: it adds its (tiny) product, and its group's scale
+    # products then span more than 2^60, so that group takes the exact promotion.
+    from oracle.gmm import tgmm_ref
+    from synth.workloads import log_uniform_scales, random_fp8_codes
+
+    M, K, N = 640, 256, 256
+    ac = random_fp8_codes((M, K), "e4m3", 321)
+    gc = random_fp8_codes((M, N), "e5m2", 322)
+    sa = log_uniform_scales(5, -3, -1, 323)
+    sg = log_uniform_scales(5, -8, -6, 324)
+    sa[3] = np.float32(1e-30)
+    sg[1] = np.float32(0.0)
+    sg[2] = np.float32(1e-40)
+    sg[3] = np.float32(1e-20)
+    prod = sa * sg
+    assert prod[1] == 0 and prod[3] == 0 and 0 < prod[2] < np.finfo(np.float32).tiny
+    out = torch.full((len(sizes), K, N), float("nan"), dtype=torch.float32, device=DEV)
+    lib.tgmm_drhs(torch.from_numpy(ac).to(DEV), torch.from_numpy(gc).to(DEV), gs_tensor(sizes),
+                  lhs_scales=torch.from_numpy(sa).to(DEV), grad_scales=torch.from_numpy(sg).to(DEV),
+                  out_dtype=torch.float32, out=out)
+    R = tgmm_ref(ac, "e4m3", sa, gc, "e5m2", sg, np.asarray(sizes), 128, "f32")
+    Y = to_np(out)
+    assert np.isfinite(Y).all()
+    err = slab_rel_err(Y, R)
+    print(f"max slab relative error {err:.3e}")
+    assert err <= TOL, err

@@ -47,18 +47,17 @@ struct TileCoord {
   int g, row0, row_end, n0;
 };
 
-// Expert-tile scheduler.  Returns false for a workgroup without a tile.  The two LDS
-// arrays alias the stage buffers: they are dead once the tile is known.
-__device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int64_t M,
-                                     int n_ntiles, int* s_tile_cum, int* s_row_off,
-                                     TileCoord& tc) {
+// Per-group prefix sums into LDS (first wave): s_tile_cum[g] = M-tiles of groups < g,
+// s_row_off[g] = rows of groups < g.  The caller synchronizes before reading them.
+__device__ inline void group_prefix(const int32_t* __restrict__ gs, int G, int* s_tile_cum,
+                                    int* s_row_off) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid < 64) {
     int carry_t = 0, carry_r = 0;
     for (int base = 0; base < G; base += 64) {
       const int g = base + lane;
       // sizes outside the contract (negative) are read as 0, and rows past M are
-      // dropped below, so no access ever leaves the tensors
+      // dropped by the tile coordinates, so no access ever leaves the tensors
       const int m = g < G ? max(gs[g], 0) : 0;
       const int it = wave_incl_scan((m + BM - 1) / BM, lane);
       const int ir = wave_incl_scan(m, lane);
@@ -74,6 +73,40 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
       s_row_off[0] = 0;
     }
   }
+}
+
+// Tile L of the tile order: bands of BAND M-tiles, the M-tile index fastest inside a band,
+// so the tiles one XCD runs together share A rows and B columns in its L2.  Returns false
+// when the tile holds no row (group sizes that overrun M).  Every lane gets the same
+// tile; the fields come back wave-uniform (scalar registers).
+__device__ inline bool tile_coord(int L, int total_mt, int n_ntiles, int G, int64_t M,
+                                  const int* s_tile_cum, const int* s_row_off, TileCoord& tc) {
+  const int band = L / (BAND * n_ntiles);
+  const int rem = L - band * BAND * n_ntiles;
+  const int mt0 = band * BAND;
+  const int gm = min(BAND, total_mt - mt0);
+  const int nt = rem / gm;
+  const int mt = mt0 + (rem - nt * gm);
+  // group owning global M-tile mt: s_tile_cum[g] <= mt < s_tile_cum[g + 1]
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_tile_cum[mid] <= mt) lo = mid; else hi = mid;
+  }
+  tc.g = __builtin_amdgcn_readfirstlane(lo);
+  tc.row0 = __builtin_amdgcn_readfirstlane(s_row_off[lo] + (mt - s_tile_cum[lo]) * BM);
+  tc.row_end = __builtin_amdgcn_readfirstlane((int)min((int64_t)s_row_off[lo + 1], M));
+  tc.n0 = __builtin_amdgcn_readfirstlane(nt * BN);
+  return tc.row0 < tc.row_end;
+}
+
+// Expert-tile scheduler of the one-tile-per-workgroup kernel.  Returns false for a
+// workgroup without a tile.  The two LDS arrays alias the stage buffers: they are dead
+// once the tile is known.
+__device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int64_t M,
+                                     int n_ntiles, int* s_tile_cum, int* s_row_off,
+                                     TileCoord& tc) {
+  group_prefix(gs, G, s_tile_cum, s_row_off);
   __syncthreads();
   const int total_mt = s_tile_cum[G];
   const int total = total_mt * n_ntiles;
@@ -82,25 +115,7 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
   if (ok) {
     // XCD-aware remap: workgroups of XCD x = wg % 8 take a contiguous range of tiles.
     const int xcd = wg & 7, j = wg >> 3, q = total >> 3, r = total & 7;
-    const int L = xcd * q + min(xcd, r) + j;
-    // bands of BAND M-tiles; inside a band the M-tile index runs fastest
-    const int band = L / (BAND * n_ntiles);
-    const int rem = L - band * BAND * n_ntiles;
-    const int mt0 = band * BAND;
-    const int gm = min(BAND, total_mt - mt0);
-    const int nt = rem / gm;
-    const int mt = mt0 + (rem - nt * gm);
-    // group owning global M-tile mt: s_tile_cum[g] <= mt < s_tile_cum[g + 1]
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_tile_cum[mid] <= mt) lo = mid; else hi = mid;
-    }
-    tc.g = lo;
-    tc.row0 = s_row_off[lo] + (mt - s_tile_cum[lo]) * BM;
-    tc.row_end = (int)min((int64_t)s_row_off[lo + 1], M);
-    tc.n0 = nt * BN;
-    ok = tc.row0 < tc.row_end;
+    ok = tile_coord(xcd * q + min(xcd, r) + j, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
   }
   __syncthreads();  // the scheduler arrays alias stage memory
   // every lane computed the same tile: make that visible to the compiler, so the buffer
@@ -354,22 +369,39 @@ void gmm_kernel(GemmParams p) {
   if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
 
   // ---- epilogue ----
-  // lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) + 4*(lane/32) + r%4]
+  // lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) + 4*(lane/32) + r%4].
+  // Every scale is loaded before the first store: a load issued after a store waits for
+  // that store too (the vector-memory counter retires in order), and the compiler cannot
+  // keep scales across stores to a buffer it must assume they alias.
+  float sa[4];
+  v4f sb[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = max(min(tc.row0 + wr * 128 + i * 32 + frow, tc.row_end - 1), 0);
+    sa[i] = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
+  }
+  {
+    const int n_ok = min(tc.n0 + wc * 128, p.Nout - 128);  // a column block inside N
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + n_ok +
+                                                  j * 32 + 8 * r4 + 4 * fhalf);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = tc.row0 + wr * 128 + i * 32 + frow;
     if (m >= tc.row_end) continue;
-    const float sa = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int n = tc.n0 + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf;
         if (n >= p.Nout) continue;
-        const v4f sb = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + n);
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa), sb[e]);
+        for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
         const int64_t idx = (int64_t)m * p.Nout + n;
         if (p.out_f32) {
           v4f v = {o[0], o[1], o[2], o[3]};

@@ -96,11 +96,13 @@ __device__ inline v2u quant8(v4u w, float inv) {
   return r;
 }
 
-// float -> bf16 bits, round to nearest even (inputs are finite or +-inf).
-__device__ inline uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> a packed bf16 pair (a in bits 0-15), each rounded to nearest even:
+// gfx950's V_CVT_PK_BF16_F32, one instruction for both.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------------

@@ -408,8 +408,8 @@ void gmm_kernel(GemmParams p) {
           *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
         } else {
           v2u v;
-          v.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-          v.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
           *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
         }
       }

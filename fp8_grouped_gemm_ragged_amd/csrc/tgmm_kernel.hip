@@ -592,8 +592,8 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
       for (int r4 = 0; r4 < 4; ++r4) {
         const int col = j * 64 + r4 * 16 + fhalf * 8;  // byte column
         v2u v;
-        v.x = f32_to_bf16_rne(acc[blk][4 * r4] * fin) | (f32_to_bf16_rne(acc[blk][4 * r4 + 1] * fin) << 16);
-        v.y = f32_to_bf16_rne(acc[blk][4 * r4 + 2] * fin) | (f32_to_bf16_rne(acc[blk][4 * r4 + 3] * fin) << 16);
+        v.x = pack_bf16x2(acc[blk][4 * r4] * fin, acc[blk][4 * r4 + 1] * fin);
+        v.y = pack_bf16x2(acc[blk][4 * r4 + 2] * fin, acc[blk][4 * r4 + 3] * fin);
         *reinterpret_cast<v2u*>(wl + row * 128 + ((((col >> 4) ^ (row & 7)) << 4) | (col & 15))) = v;
       }
     }
@@ -802,8 +802,8 @@ void tgmm_promote_kernel(TgmmSegParams p) {
           *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
         } else {
           v2u v;
-          v.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-          v.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
           *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
         }
       }

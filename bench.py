@@ -177,6 +177,53 @@ class Step:
             raise RuntimeError(f"library call failed: {self.g.gmm_status_string(status)}")
 
 
+def gfx_clock_during(run, seconds=1.0):
+    """Run `run` back to back for `seconds` while amdsmi samples the GFX clock of every XCD;
+    return the mean in MHz over the samples taken once the clock had left idle (the first
+    readings of the metrics table can be stale), or None when amdsmi is unavailable."""
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                clks = m.get("current_gfxclks")
+                vals = [c for c in clks if isinstance(c, (int, float))] if isinstance(clks, list) else []
+                if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+                    vals = [m["current_gfxclk"]]
+                if vals:
+                    samples.append(sum(vals) / len(vals))
+            except Exception:
+                pass
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    busy = [x for x in samples if x >= 500.0]  # below the lowest DPM level: idle or stale
+    return round(sum(busy) / len(busy), 1) if busy else None
+
+
 def cpu_baseline(step, rows, cols):
     """Time the CPU oracle on a bounded sample: the first `rows` rows (with their group
     split), all K, the first `cols` columns of the merged weight; fwd + dlhs + tgmm."""
@@ -263,6 +310,9 @@ def main():
     fe[1].record()
     torch.cuda.synchronize()
     fused_ms = fe[0].elapsed_time(fe[1]) / 3
+    # the GFX clock the chip holds under this load (FP8 MFMA work draws enough power to
+    # keep it well below the 2.4 GHz the published peak assumes)
+    clock_mhz = gfx_clock_during(lambda: [step.run(s) for _ in range(8)])
     flop_op = 2.0 * wl.M * wl.K * wl.N
     value = 3 * flop_op / (ms_step / 1000.0) / 1e12
     ops = {n: {"ms": round(per[n], 4), "TFLOP/s": round(flop_op / (per[n] / 1000) / 1e12, 1),
@@ -294,6 +344,12 @@ def main():
                     "grad_quantize": round(per["quantize_grad"], 4)},
         "roofline": {"kernel": kern, "op": dom, "bound": "mfma", "achieved": round(ach, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
+                     "clock_mhz": clock_mhz,
+                     "peak_at_clock": round(256 * 8192 * clock_mhz / 1e6, 1) if clock_mhz else None,
+                     "frac_at_clock": round(ach / (256 * 8192 * clock_mhz / 1e6), 4) if clock_mhz else None,
+                     "clock_note": "mean GFX clock over the XCDs (amdsmi current_gfxclks) during 1 s "
+                                   "of back-to-back steps after the timed region; peak_at_clock = "
+                                   "256 CUs x 8192 FP8 FLOP/clk x clock",
                      "traffic": measured_traffic(dom, wl.name),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
                                      "1 GiB copy; null once the kernel sources changed)"},

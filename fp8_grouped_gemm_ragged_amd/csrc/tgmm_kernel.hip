@@ -270,16 +270,19 @@ __device__ inline void quant_transpose8(const v4u in[8], float inv, v2u out[8]) 
   }
 }
 
-// grid (segment blocks upper bound, C / 128).  Workgroup (b, ct): segment block b (a
-// pair (group g, 128-row block c)) and columns [128 ct, 128 ct + 128).  A block whose
+// grid (segment blocks upper bound, ceil(C / CW)).  Workgroup (b, ct): segment block b
+// (a pair (group g, 128-row block c)) and columns [CW ct, CW ct + CW).  A block whose
 // scale product is zero gets zero codes.  x holds bf16 values, quantized here with the
-// block's scale, or (CODES) fp8 codes quantized beforehand, which are only transposed.
+// block's scale (CW = 128: 8 rows x 8 columns per thread), or (CODES) fp8 codes quantized
+// beforehand, which are only transposed (CW = 256: 8 rows x 16 columns per thread, so a
+// load reads 16 bytes of a row).
 template <int FMT, bool CODES>
 __global__ __launch_bounds__(256) void quant_transpose_kernel(
     const void* __restrict__ x, int64_t C, const int32_t* __restrict__ plan, int G,
     const float* __restrict__ scale_blk, float inv_static, const float* __restrict__ scprod,
     uint8_t* __restrict__ seg, int64_t seg_row) {
-  constexpr int ES = CODES ? 1 : 2;  // bytes per element of x
+  constexpr int ES = CODES ? 1 : 2;     // bytes per element of x
+  constexpr int CW = CODES ? 256 : 128;  // columns per workgroup
   const int32_t* off = plan;
   const int32_t* cnt = plan + G;
   const int32_t* sg = plan + 2 * G;
@@ -296,25 +299,42 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(
   const int c = o / BLOCK_ROWS + (b - __builtin_amdgcn_readfirstlane(sg[g]));
   const int r_lo = max(o, c * BLOCK_ROWS), r_hi = min(o + n, (c + 1) * BLOCK_ROWS);
   const int rel = r_lo - c * BLOCK_ROWS;  // first row of the block that belongs to g
-  const int64_t col0 = (int64_t)blockIdx.y * 128;
+  const int64_t col0 = (int64_t)blockIdx.y * CW;
   // rows [r_lo, r_hi) from column col0 on: later rows read as zero
   const __amdgpu_buffer_rsrc_t r =
       make_rsrc((const uint8_t*)x + ((int64_t)r_lo * C + col0) * ES,
                 (uint32_t)(((int64_t)(r_hi - r_lo) * C - col0) * ES));
   const bool dead = scprod[c] == 0.0f;
   const int t = threadIdx.x;
-  const int rb = t & 15, cb = t >> 4;  // 8-row block, 8-column block
-  v2u q[8];
+  const int rb = t & 15, cb = t >> 4;  // 8-row block; 8- (bf16) or 16-column (codes) block
+  // segment layout by column pairs: pair p, block b holds 256 bytes, [col 2p, m 0..63]
+  // [col 2p + 1, m 0..63] [col 2p, m 64..127] [col 2p + 1, m 64..127]
+  auto store8 = [&](int64_t col, const v2u (&q)[8]) {
+    uint8_t* dst = seg + col * seg_row + (int64_t)b * PAIR_BLOCK + (rb >> 3) * 128 + (rb & 7) * 8;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      *reinterpret_cast<v2u*>(dst + (cc >> 1) * 2 * seg_row + (cc & 1) * 64) = q[cc];
+  };
   if constexpr (CODES) {
-    v2u in[8];
+    if (col0 + cb * 16 >= C) return;  // C is a multiple of 128: whole 16-column blocks
+    v4u in[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = rb * 8 + e - rel;  // relative to the first row of g in the block
-      uint32_t voff = (uint32_t)row * (uint32_t)C + cb * 8;
-      if (row < 0 || dead) voff = 0xfffffff8u;  // previous group's rows, or a dead block: zeros
-      in[e] = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+      uint32_t voff = (uint32_t)row * (uint32_t)C + cb * 16;
+      if (row < 0 || dead) voff = 0xfffffff0u;  // previous group's rows, or a dead block: zeros
+      in[e] = buf_load16(r, voff);
     }
-    transpose8x8(in, q);
+    v2u lo8[8], hi8[8], q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo8[e].x = in[e].x; lo8[e].y = in[e].y;
+      hi8[e].x = in[e].z; hi8[e].y = in[e].w;
+    }
+    transpose8x8(lo8, q);
+    store8(col0 + cb * 16, q);
+    transpose8x8(hi8, q);
+    store8(col0 + cb * 16 + 8, q);
   } else {
     const float inv = dead ? 0.0f : scale_blk ? inv_from_scale(scale_blk[c]) : inv_static;
     v4u in[8];
@@ -325,15 +345,10 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(
       if (row < 0) voff = 0xfffffff0u;  // rows of the previous group: zero codes
       in[e] = buf_load16(r, voff);
     }
+    v2u q[8];
     quant_transpose8<FMT>(in, inv, q);
+    store8(col0 + cb * 8, q);
   }
-  // segment layout by column pairs: pair p, block b holds 256 bytes, [col 2p, m 0..63]
-  // [col 2p + 1, m 0..63] [col 2p, m 64..127] [col 2p + 1, m 64..127]
-  uint8_t* dst = seg + (col0 + cb * 8) * seg_row + (int64_t)b * PAIR_BLOCK + (rb >> 3) * 128 +
-                 (rb & 7) * 8;
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc)
-    *reinterpret_cast<v2u*>(dst + (cc >> 1) * 2 * seg_row + (cc & 1) * 64) = q[cc];
 }
 
 // One wave fills 8 rows (1 KB) of a swizzled [rows][128 B] tile from global memory.
@@ -816,7 +831,8 @@ hipError_t launch_qt(int fmt, bool codes, const void* x, int64_t M, int64_t C,
                      const int32_t* plan, int G, const float* scale_blk, float inv_static,
                      const float* scprod, uint8_t* seg, int64_t seg_row, hipStream_t st) {
   const int64_t max_blocks = (M + BLOCK_ROWS - 1) / BLOCK_ROWS + G;
-  dim3 grid((unsigned)max_blocks, (unsigned)(C / 128));
+  const int64_t cw = codes ? 256 : 128;
+  dim3 grid((unsigned)max_blocks, (unsigned)((C + cw - 1) / cw));
 #define GMM_QT(F, CD)                                                                     \
   if (fmt == F && codes == CD) {                                                          \
     hipLaunchKernelGGL((quant_transpose_kernel<F, CD>), grid, dim3(256), 0, st, x, C, plan, \

@@ -168,6 +168,8 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   if (rhs_format != GMM_FP8_E4M3) return GMM_ERR_RECIPE;  // weights are e4m3 codes
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, Kc, Nout, G)) != GMM_OK) return s;
+  // the kernels number output tiles with 32-bit integers
+  if ((M / 256 + 1 + G) * ((Nout + 255) / 256) >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
   if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
   if (M > 0 && (!a || !out)) return GMM_ERR_NULL;
   const bool a_fp8 = aop->kind == GMM_OPERAND_FP8;
@@ -264,6 +266,9 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
   if ((s = check_operand(grad_op)) != GMM_OK) return s;
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, K, N, G)) != GMM_OK) return s;
+  // 32-bit tile numbers, and byte offsets inside a 256-row slice of a transposed segment
+  if (((K + 255) / 256) * ((N + 255) / 256) * G >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  if (256 * tgmm_segment_row_bytes(M, G) >= (int64_t(1) << 32)) return GMM_ERR_SHAPE;
   if (!group_sizes || !drhs) return GMM_ERR_NULL;
   if (M > 0 && (!lhs || !grad)) return GMM_ERR_NULL;
   if (M > 0 && ((scales_are_input(lhs_op) && !lhs_scales) || (scales_are_input(grad_op) && !grad_scales)))

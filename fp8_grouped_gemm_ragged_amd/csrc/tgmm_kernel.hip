@@ -121,7 +121,7 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
   __shared__ unsigned s_min[PLAN_NT], s_max[PLAN_NT], s_bad[PLAN_NT];
   __shared__ int s_last[PLAN_NT];
   const int t = threadIdx.x;
-  const int Mi = (int)M;  // M < 2^23
+  const int Mi = (int)M;  // M < 2^31 (and below 2^24 - 128 G, see tgmm_drhs)
   int32_t* off = plan;
   int32_t* cnt = plan + G;
   int32_t* seg = plan + 2 * G;

@@ -24,7 +24,10 @@
  * - group_sizes is int32 [G] in device memory and is never read by the host: the
  *   caller guarantees m_g >= 0 and sum(m_g) == M (checked only when the environment
  *   variable GMM_CHECK=1 is set, which synchronises the stream).
- * - Shapes: M >= 0, 1 <= G <= GMM_MAX_GROUPS, K and N positive multiples of 128.
+ * - Shapes: 0 <= M < 2^31, 1 <= G <= GMM_MAX_GROUPS, K and N positive multiples of 128
+ *   up to 2^22 with K * N < 2^32, and fewer than 2^31 output tiles of 256 x 256
+ *   ((M / 256 + 1 + G) * ceil(N_out / 256) for gmm_fwd / gmm_dlhs); tgmm_drhs adds its
+ *   own limits.  Anything else is GMM_ERR_SHAPE.
  * - Inputs are read-only; outputs must not overlap inputs.
  * - Errors are returned as gmm_status_t; argument validation happens before any work
  *   is enqueued, so an error return leaves every output untouched.
@@ -195,6 +198,9 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
  * lhs_scales / grad_scales: as gmm_fwd's lhs_scales (outputs for DYNAMIC + BF16, may be
  * NULL; inputs for DYNAMIC_GIVEN and for DYNAMIC + FP8).
  * drhs [G, K, N] bf16 or f32.  A group with m_g == 0 gets a slab of +0.0.
+ * Limits beyond the common ones: ceil(M / 128) + G <= 131071 (its transposed copies are
+ * addressed with 32-bit offsets inside 256-row slices; about 16.7 million rows), and
+ * ceil(K / 256) * ceil(N / 256) * G < 2^31; otherwise GMM_ERR_SHAPE.
  * workspace    required: gmm_workspace_size(GMM_OP_TGMM, lhs_op, grad_op, M, K, N, G)
  *              bytes.  It holds each operand quantized once and transposed so that the
  *              rows of every group start on a 128-row block boundary.

@@ -146,6 +146,17 @@ def test_dlhs_and_tgmm_validation():
                          ptr(3), ptr(4), None, ptr(6), ptr(7), 1 << 20, None) == 1
 
 
+def test_size_limits():
+    lib = g.load()
+    a, b = op(fmt=0, scaling=0, s=1.0), op(fmt=1, scaling=0, s=1.0)
+    # tgmm: ceil(M/128) + G <= 131071 (32-bit offsets inside 256-row segment slices)
+    M = (131071 - 2) * 128
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, M + 1, 256, 256, 2, ptr(1), None,
+                         ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 40, None) == 2
+    # gmm: fewer than 2^31 output tiles
+    assert call_fwd(M=(1 << 31) - 1, K=128, N=(1 << 22), G=1, o=op(scaling=0, s=1.0)) == 2
+
+
 def test_given_scales_validation():
     lib = g.load()
     given = op(scaling=2)

@@ -34,7 +34,7 @@ STATIC, DYNAMIC, DYNAMIC_GIVEN = 0, 1, 2
 KIND_BF16, KIND_FP8 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 RHS_KN, RHS_NK = 0, 1
-OP_FWD, OP_DLHS, OP_TGMM, OP_FWD_FUSED, OP_DLHS_FUSED, OP_QUANTIZE = 0, 1, 2, 3, 4, 5
+OP_FWD, OP_DLHS, OP_TGMM, OP_FWD_FUSED, OP_DLHS_FUSED, OP_QUANTIZE, OP_FWD_SWIGLU = 0, 1, 2, 3, 4, 5, 6
 BLOCK_ROWS = 128
 
 _FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
@@ -64,6 +64,8 @@ _SIGNATURES = {
     "gmm_fwd": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_dlhs": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "tgmm_drhs": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_fwd_swiglu": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
     "gmm_workspace_size": [_I32, _OPP, _OPP, _I64, _I64, _I64, _I32, ctypes.POINTER(_SZ)],
     "gmm_dynamic_scales": [_I32, _I64, _I64, _P, _P, _P, _SZ, _P],
     "gmm_quantize": [_OPP, _I64, _I64, _P, _P, _P, _P, _SZ, _P],
@@ -295,6 +297,75 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
                          M, K, N, G, _ptr(lhs), _ptr(sa), _ptr(grad), _ptr(sg), _ptr(group_sizes),
                          _ptr(out), _ptr(ws), ws_n.value, _stream()), "tgmm_drhs")
     return (out, sa, sg) if return_scales else out
+
+
+def gmm_fwd_swiglu(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3",
+                   lhs_scaling="dynamic", static_scale=None, lhs_scales=None, out_dtype=None,
+                   out=None, gu=False, return_scales=False):
+    """Merged gate|up forward with SwiGLU: h[M, I] = silu(x[:, :I]) * x[:, I:] where x is the
+    gmm_fwd product over rhs [G, 2I, K] (layout "nk") with rhs_scales [G, 2I].
+
+    lhs: bf16 [M, K] (quantized once in the call) or uint8 codes (then lhs_scales holds its
+    block scales when dynamic).  gu=True also returns x itself ([M, 2I], the backward's
+    input); returns h, or (h, x) with gu=True, with the lhs scales appended when
+    return_scales."""
+    import torch
+
+    lib = load()
+    prequant = lhs.dtype == torch.uint8
+    _need(lhs, torch.uint8 if prequant else torch.bfloat16, "lhs", 2)
+    _need(rhs, torch.uint8, "rhs", 3)
+    _need(rhs_scales, torch.float32, "rhs_scales", 2)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = lhs.shape
+    G, N2 = rhs.shape[0], rhs.shape[1]
+    if rhs.shape[2] != K or N2 % 2:
+        raise ValueError("rhs must be [G, 2I, K] codes matching the lhs width")
+    I = N2 // 2
+    odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, I), dtype=odt, device=lhs.device)
+    else:
+        _need(out, odt, "out", 2)
+    x = torch.empty((M, N2), dtype=odt, device=lhs.device) if gu else None
+    op = _operand(KIND_FP8 if prequant else KIND_BF16, lhs_format, lhs_scaling, static_scale)
+    mode = _SCALING[lhs_scaling]
+    if mode != STATIC and lhs_scales is None:
+        if prequant or mode == DYNAMIC_GIVEN:
+            raise ValueError("this recipe needs the operand's block scales as an input")
+        lhs_scales = torch.empty(_nblocks(M), dtype=torch.float32, device=lhs.device)
+    if lhs_scales is not None:
+        _need(lhs_scales, torch.float32, "scales", 1)
+    ws_n = _SZ()
+    _check(lib.gmm_workspace_size(OP_FWD_SWIGLU, ctypes.byref(op), ctypes.byref(op), M, K, N2, 1,
+                                  ctypes.byref(ws_n)), "gmm_workspace_size")
+    ws = _workspace(ws_n.value, lhs.device)
+    _check(lib.gmm_fwd_swiglu(ctypes.byref(op), E4M3, RHS_NK, OUT_F32 if odt == torch.float32 else OUT_BF16,
+                              M, K, I, G, _ptr(lhs), _ptr(lhs_scales), _ptr(rhs), _ptr(rhs_scales),
+                              _ptr(group_sizes), _ptr(x), _ptr(out), _ptr(ws), ws_n.value, _stream()),
+           "gmm_fwd_swiglu")
+    res = (out, x) if gu else (out,)
+    if return_scales:
+        res = res + (lhs_scales,)
+    return res if len(res) > 1 else res[0]
+
+
+def gmm_swiglu_bwd(dh, gu, out=None):
+    """d_gu [M, 2I] bf16 = [dL/dg | dL/du] of h = silu(g) * u, from dh [M, I] and gu = [g | u]."""
+    import torch
+
+    lib = load()
+    _need(dh, torch.bfloat16, "dh", 2)
+    _need(gu, torch.bfloat16, "gu", 2)
+    M, I = dh.shape
+    if tuple(gu.shape) != (M, 2 * I):
+        raise ValueError("gu must be [M, 2I] for dh [M, I]")
+    if out is None:
+        out = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dh.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+    _check(lib.gmm_swiglu_bwd(M, I, _ptr(dh), _ptr(gu), _ptr(out), _stream()), "gmm_swiglu_bwd")
+    return out
 
 
 def gmm_dynamic_scales(x, fmt="e4m3"):

@@ -162,12 +162,15 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                           int64_t Nout, int32_t G, const void* a, float* a_scales,
                           const uint8_t* rhs, const float* rhs_scales,
                           const int32_t* group_sizes, void* out, void* workspace,
-                          size_t workspace_bytes, hipStream_t st) {
+                          size_t workspace_bytes, hipStream_t st, bool swiglu = false,
+                          void* gu = nullptr) {
   gmm_status_t s = check_operand(aop);
   if (s != GMM_OK) return s;
   if (rhs_format != GMM_FP8_E4M3) return GMM_ERR_RECIPE;  // weights are e4m3 codes
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, Kc, Nout, G)) != GMM_OK) return s;
+  // SwiGLU: Nout = 2 I channels, I a multiple of 128, contraction-contiguous weights
+  if (swiglu && (Nout % 256 || b_trans)) return swiglu && b_trans ? GMM_ERR_RECIPE : GMM_ERR_SHAPE;
   // the kernels number output tiles with 32-bit integers
   if ((M / 256 + 1 + G) * ((Nout + 255) / 256) >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
   if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
@@ -181,11 +184,15 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
     if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
   const size_t ws_need = needs_dyn_ws(aop) ? dyn_ws_bytes(M) : 0;
   if (ws_need && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
-  const bool quant_once = !a_fp8 && quant_once_applies(Nout) && workspace &&
+  const bool quant_once = !a_fp8 && (swiglu || quant_once_applies(Nout)) && workspace &&
                           workspace_bytes >= ws_need + quant_once_bytes(M, Kc);
+  // the SwiGLU epilogue exists on the fp8-A route only: a bf16 lhs is quantized once
+  if (swiglu && !a_fp8 && !quant_once) return GMM_ERR_WORKSPACE;
   const size_t ws_used = ws_need + (quant_once ? quant_once_bytes(M, Kc) : 0);
   const size_t a_bytes = (size_t)M * Kc * (a_fp8 ? 1 : 2);
-  const size_t out_bytes = (size_t)M * Nout * (out_dtype == GMM_OUT_F32 ? 4 : 2);
+  const size_t esize = out_dtype == GMM_OUT_F32 ? 4 : 2;
+  const size_t out_bytes = (size_t)M * (swiglu ? Nout / 2 : Nout) * esize;
+  const size_t gu_bytes = swiglu && gu ? (size_t)M * Nout * esize : 0;
   const size_t b_bytes = (size_t)G * Kc * Nout;
   const size_t as_bytes = (size_t)nblocks(M) * 4;
   if (overlaps(out, out_bytes, a, a_bytes) || overlaps(out, out_bytes, rhs, b_bytes) ||
@@ -195,6 +202,14 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
       overlaps(workspace, ws_used, a, a_bytes) || overlaps(workspace, ws_used, out, out_bytes) ||
       overlaps(workspace, ws_used, a_scales, as_bytes))
     return GMM_ERR_ALIAS;
+  if (gu_bytes && (overlaps(gu, gu_bytes, a, a_bytes) || overlaps(gu, gu_bytes, rhs, b_bytes) ||
+                   overlaps(gu, gu_bytes, rhs_scales, (size_t)G * Nout * 4) ||
+                   overlaps(gu, gu_bytes, group_sizes, (size_t)G * 4) ||
+                   overlaps(gu, gu_bytes, out, out_bytes) ||
+                   overlaps(gu, gu_bytes, workspace, ws_used) ||
+                   overlaps(gu, gu_bytes, a_scales, as_bytes)))
+    return GMM_ERR_ALIAS;
+  if (gu && !aligned16(gu)) return GMM_ERR_ALIGN;
   if ((s = check_group_sizes(group_sizes, G, M, st)) != GMM_OK) return s;
   trace(name, M, Kc, Nout, G);
   if (M == 0) return GMM_OK;
@@ -210,6 +225,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.Nout = (int32_t)Nout;
   p.G = G;
   p.out_f32 = out_dtype == GMM_OUT_F32;
+  p.gu = gu;
   Scaling sc;
   if ((s = resolve_scaling(aop, a, M, Kc, a_scales, workspace, st, sc)) != GMM_OK) return s;
   p.a_scale_blk = sc.blk;
@@ -224,8 +240,9 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
     p.a = codes;
     a_codes = true;
   }
-  if (launch_gemm(aop->format, FMT_E4M3, a_codes, b_trans, p, st) != hipSuccess) return GMM_ERR_HIP;
-  return GMM_OK;
+  const hipError_t e = swiglu ? launch_gemm_swiglu(aop->format, p, st)
+                              : launch_gemm(aop->format, FMT_E4M3, a_codes, b_trans, p, st);
+  return e == hipSuccess ? GMM_OK : GMM_ERR_HIP;
 }
 
 }  // namespace
@@ -254,6 +271,33 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
   return grouped_gemm("gmm_dlhs", grad_op, rhs_format, rhs_layout == GMM_RHS_NK, out_dtype, M,
                       N, K, G, grad, grad_scales, rhs, rhs_scales, group_sizes, dlhs, workspace,
                       workspace_bytes, (hipStream_t)stream);
+}
+
+gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                            int32_t out_dtype, int64_t M, int64_t K, int64_t I, int32_t G,
+                            const void* lhs, float* lhs_scales, const uint8_t* rhs,
+                            const float* rhs_scales, const int32_t* group_sizes, void* gu,
+                            void* h, void* workspace, size_t workspace_bytes,
+                            gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
+  return grouped_gemm("gmm_fwd_swiglu", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN,
+                      out_dtype, M, K, 2 * I, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes,
+                      h, workspace, workspace_bytes, (hipStream_t)stream, true, gu);
+}
+
+gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu, void* d_gu,
+                            gmm_stream_t stream) {
+  if (M < 0 || M >= (int64_t(1) << 31) || I <= 0 || I % 128 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
+  if (M == 0) return GMM_OK;
+  if (!dh || !gu || !d_gu) return GMM_ERR_NULL;
+  for (const void* ptr : {dh, gu, (const void*)d_gu})
+    if (!aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t hb = (size_t)M * I * 2, gb = 2 * hb;
+  if (overlaps(d_gu, gb, dh, hb) || overlaps(d_gu, gb, gu, gb)) return GMM_ERR_ALIAS;
+  trace("gmm_swiglu_bwd", M, I, 2 * I, 1);
+  return launch_swiglu_bwd((const uint16_t*)dh, (const uint16_t*)gu, (uint16_t*)d_gu, M, I,
+                           (hipStream_t)stream) == hipSuccess ? GMM_OK : GMM_ERR_HIP;
 }
 
 gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
@@ -349,13 +393,14 @@ gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_op
   if ((op == GMM_OP_FWD || op == GMM_OP_DLHS) && a->kind == GMM_OPERAND_BF16 &&
       quant_once_applies(cols_b))
     n += quant_once_bytes(rows, cols_a);
+  if (op == GMM_OP_FWD_SWIGLU && a->kind == GMM_OPERAND_BF16) n += quant_once_bytes(rows, cols_a);
   if (op == GMM_OP_TGMM) {
     if (!b) return GMM_ERR_NULL;
     if ((s = check_operand(b)) != GMM_OK) return s;
     n += needs_dyn_ws(b) ? dyn_ws_bytes(rows) : 0;
     n += tgmm_ws_bytes(rows, cols_a, cols_b, G);
   } else if (op != GMM_OP_FWD && op != GMM_OP_DLHS && op != GMM_OP_FWD_FUSED &&
-             op != GMM_OP_DLHS_FUSED && op != GMM_OP_QUANTIZE) {
+             op != GMM_OP_DLHS_FUSED && op != GMM_OP_QUANTIZE && op != GMM_OP_FWD_SWIGLU) {
     return GMM_ERR_RECIPE;
   }
   *bytes = n;

@@ -127,9 +127,101 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
 }
 
-template <int A_FMT, int B_FMT, bool A_FP8, bool B_TRANS>
+// SwiGLU epilogue of a gate|up tile.  The product values x = (acc * s_A(m)) * s_B(n) are
+// the ones gmm_fwd stores (written to gu when given).  The up waves pass theirs through
+// LDS, in the lane order every wave's accumulators share, and each gate wave then stores
+// h = silu(g) * u = (g / (1 + exp(-g))) * u for its 128 x 128 block, all in fp32.
+__device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc, int c0, int wr,
+                                       int wc, int lane, v16f (&acc)[4][4], uint8_t* sA0,
+                                       uint8_t* sB0, uint8_t* sA1, uint8_t* sB1) {
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int I = p.Nout >> 1;
+  const int cb = wc == 0 ? c0 : I + c0;  // this wave's first channel
+  float sa[4];
+  v4f sb[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = max(min(tc.row0 + wr * 128 + i * 32 + frow, tc.row_end - 1), 0);
+    sa[i] = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + cb + j * 32 +
+                                                8 * r4 + 4 * fhalf);
+  auto value = [&](int i, int j, int r4) {
+    v4f o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
+    return o;
+  };
+  // chunk r = 16 i + 4 j + r4 of the up wave of row half wr, lane-interleaved
+  uint8_t* const xa = wr == 0 ? sA0 : sA1;
+  uint8_t* const xb = wr == 0 ? sB0 : sB1;
+  auto chunk = [&](int r) { return reinterpret_cast<v4f*>((r < 32 ? xa : xb) + ((r & 31) * 64 + lane) * 16); };
+  __syncthreads();  // every wave is done with the stages
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = tc.row0 + wr * 128 + i * 32 + frow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const v4f o = value(i, j, r4);
+        const int64_t idx = (int64_t)m * p.Nout + cb + j * 32 + 8 * r4 + 4 * fhalf;
+        if (p.gu && m < tc.row_end) {
+          if (p.out_f32) {
+            *reinterpret_cast<v4f*>((float*)p.gu + idx) = o;
+          } else {
+            v2u v;
+            v.x = pack_bf16x2(o[0], o[1]);
+            v.y = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<v2u*>((uint16_t*)p.gu + idx) = v;
+          }
+        }
+        if (wc == 1) *chunk(i * 16 + j * 4 + r4) = o;
+      }
+    }
+  }
+  __syncthreads();  // the up values are in LDS
+  if (wc != 0) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = tc.row0 + wr * 128 + i * 32 + frow;
+    if (m >= tc.row_end) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const v4f g = value(i, j, r4);
+        const v4f u = *chunk(i * 16 + j * 4 + r4);
+        v4f h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          h[e] = __fmul_rn(__fdiv_rn(g[e], __fadd_rn(1.0f, expf(-g[e]))), u[e]);
+        const int64_t idx = (int64_t)m * I + c0 + j * 32 + 8 * r4 + 4 * fhalf;
+        if (p.out_f32) {
+          *reinterpret_cast<v4f*>((float*)p.out + idx) = h;
+        } else {
+          v2u v;
+          v.x = pack_bf16x2(h[0], h[1]);
+          v.y = pack_bf16x2(h[2], h[3]);
+          *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
+        }
+      }
+    }
+  }
+}
+
+// SW: the merged gate|up forward with the SwiGLU epilogue (fp8 A, contraction-contiguous
+// B only).  Its tiles are 256 rows x 128 channel pairs: B rows 0..127 are gate channels
+// c0..c0+127 and rows 128..255 the up channels I + c0.., so the waves with wc = 0 hold
+// gate values and those with wc = 1 the matching up values of the same outputs.
+template <int A_FMT, int B_FMT, bool A_FP8, bool B_TRANS, bool SW = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 void gmm_kernel(GemmParams p) {
+  static_assert(!SW || (A_FP8 && !B_TRANS), "the SwiGLU epilogue runs on the fp8-A route");
   // one LDS object per stage and operand: the compiler then sees that stores into the
   // next stage never alias fragment reads of the current one
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_TILE];
@@ -140,9 +232,10 @@ void gmm_kernel(GemmParams p) {
   int* s_row_off = s_tile_cum + (MAX_GROUPS + 1);
   static_assert(2 * (MAX_GROUPS + 1) * sizeof(int) <= A_TILE, "scheduler arrays fit a tile");
 
-  const int n_ntiles = (p.Nout + BN - 1) / BN;
+  const int n_ntiles = SW ? (p.Nout >> 1) / 128 : (p.Nout + BN - 1) / BN;
   TileCoord tc;
   if (!schedule_tile(p.group_sizes, p.G, p.M, n_ntiles, s_tile_cum, s_row_off, tc)) return;
+  const int c0 = SW ? (tc.n0 >> 1) : 0;  // SW: first channel pair of the tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -155,7 +248,9 @@ void gmm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(
       (const uint8_t*)p.a + (int64_t)tc.row0 * Kc * AES, (uint32_t)rows_here * Kc * AES);
   __amdgpu_buffer_rsrc_t rb;
-  if constexpr (!B_TRANS) {
+  if constexpr (SW) {
+    rb = make_rsrc(p.b + (int64_t)tc.g * p.Nout * Kc, (uint32_t)p.Nout * Kc);
+  } else if constexpr (!B_TRANS) {
     const int cols_here = min(p.Nout - tc.n0, BN);
     rb = make_rsrc(p.b + ((int64_t)tc.g * p.Nout + tc.n0) * Kc, (uint32_t)cols_here * Kc);
   } else {
@@ -193,8 +288,12 @@ void gmm_kernel(GemmParams p) {
     }
   };
   auto load_bk_piece = [&](int kt, int i) {
-    if constexpr (!B_TRANS)
-      bk_reg[i] = buf_load16(rb, (uint32_t)(i * 32 + lrow) * Kc + (uint32_t)kt * BK + lchunk * 16);
+    if constexpr (!B_TRANS) {
+      // SW: pieces 0..3 are gate channels c0.., pieces 4..7 the up channels I + c0..
+      const uint32_t row = SW ? (uint32_t)((i < 4 ? c0 + i * 32 : (p.Nout >> 1) + c0 + (i - 4) * 32) + lrow)
+                              : (uint32_t)(i * 32 + lrow);
+      bk_reg[i] = buf_load16(rb, row * Kc + (uint32_t)kt * BK + lchunk * 16);
+    }
   };
   auto load_b_block = [&](int kt, int it) {
     if constexpr (B_TRANS) {
@@ -368,6 +467,11 @@ void gmm_kernel(GemmParams p) {
   }
   if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
 
+  if constexpr (SW) {
+    swiglu_epilogue(p, tc, c0, wr, wc, lane, acc, sA0, sB0, sA1, sB1);
+    return;
+  }
+
   // ---- epilogue ----
   // lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) + 4*(lane/32) + r%4].
   // Every scale is loaded before the first store: a load issued after a store waits for
@@ -430,6 +534,21 @@ hipError_t launch_one(const GemmParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_swiglu(int a_fmt, const GemmParams& p, hipStream_t st) {
+  const int64_t max_mt = (p.M + BM - 1) / BM + p.G;
+  const int64_t grid = max_mt * ((p.Nout / 2) / 128);
+  if (grid == 0 || p.M == 0) return hipSuccess;
+  if (a_fmt == FMT_E4M3)
+    hipLaunchKernelGGL((gmm_kernel<FMT_E4M3, FMT_E4M3, true, false, true>), dim3((unsigned)grid),
+                       dim3(NT), 0, st, p);
+  else if (a_fmt == FMT_E5M2)
+    hipLaunchKernelGGL((gmm_kernel<FMT_E5M2, FMT_E4M3, true, false, true>), dim3((unsigned)grid),
+                       dim3(NT), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(int a_fmt, int b_fmt, bool a_fp8, bool b_trans, const GemmParams& p,
                        hipStream_t st) {

@@ -26,6 +26,9 @@ struct GemmParams {
   int64_t M;
   int32_t Kc, Nout, G;
   int32_t out_f32;
+  // SwiGLU epilogue (gmm_fwd_swiglu): B holds the merged [W0 | W1] channels (Nout = 2 I),
+  // out is h [M, I], gu (optional) the product itself [M, 2 I]
+  void* gu;
 };
 
 // tgmm: out[g] = A_g^T [Kout, m] x B_g [m, Nout], contraction over the rows of group g.
@@ -66,6 +69,11 @@ inline int64_t tgmm_plan_words(int G) { return 5 * (int64_t)G + 2; }
 
 hipError_t launch_gemm(int a_fmt, int b_fmt, bool a_fp8, bool b_trans, const GemmParams& p,
                        hipStream_t st);
+// fp8-A product over merged gate|up channels with the SwiGLU epilogue
+hipError_t launch_gemm_swiglu(int a_fmt, const GemmParams& p, hipStream_t st);
+// d_gu [M, 2 I] from dh [M, I] and gu [M, 2 I], all bf16
+hipError_t launch_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, uint16_t* d_gu, int64_t M,
+                             int64_t I, hipStream_t st);
 hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st);
 hipError_t launch_dynamic_scales(int fmt, const void* x, int64_t R, int64_t C,
                                  uint32_t* partial, float* scales_out, hipStream_t st);

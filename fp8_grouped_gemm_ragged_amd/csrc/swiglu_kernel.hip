@@ -1,0 +1,66 @@
+// SwiGLU backward on gfx950: the elementwise step between the down projection's dlhs and
+// the merged gate|up dlhs of an MoE feed-forward block ("FP8 Megablox for batch split",
+// Description (2): the gate and up projections W0 | W1 merged along N).
+//
+// With gu = [g | u] (the merged forward product, [M, 2 I]) and dh = dL/dh ([M, I]),
+// h = silu(g) * u and s = sigmoid(g) = 1 / (1 + exp(-g)):
+//   dL/dg = dh * u * s * (1 + g * (1 - s))      dL/du = dh * silu(g) = dh * g * s
+// computed in fp32 from the bf16 inputs, each operation rounded to nearest, and stored as
+// d_gu = [dL/dg | dL/du] in bf16 (round to nearest even).  HBM-bound: it reads 6 and
+// writes 4 bytes per channel and row.
+#include <algorithm>
+
+#include "kernels.hpp"
+
+namespace gmm {
+
+namespace {
+
+// 8 channels per thread (16-byte accesses), grid-stride over the M * I / 8 pieces.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restrict__ dh,
+                                                         const uint16_t* __restrict__ gu,
+                                                         uint16_t* __restrict__ d_gu,
+                                                         int64_t M, int64_t I) {
+  const int64_t per_row = I / 8;
+  const int64_t total = M * per_row;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * 256) {
+    const int64_t m = t / per_row, c = (t - m * per_row) * 8;
+    const v4u dv = *reinterpret_cast<const v4u*>(dh + m * I + c);
+    const v4u gv = *reinterpret_cast<const v4u*>(gu + m * 2 * I + c);
+    const v4u uv = *reinterpret_cast<const v4u*>(gu + m * 2 * I + I + c);
+    v4u og, ou;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float dg[2], du[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float g = h ? bf16_hi(gv[k]) : bf16_lo(gv[k]);
+        const float u = h ? bf16_hi(uv[k]) : bf16_lo(uv[k]);
+        const float d = h ? bf16_hi(dv[k]) : bf16_lo(dv[k]);
+        const float s = __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-g)));
+        const float grow = __fadd_rn(1.0f, __fmul_rn(g, __fsub_rn(1.0f, s)));
+        dg[h] = __fmul_rn(__fmul_rn(__fmul_rn(d, u), s), grow);
+        du[h] = __fmul_rn(d, __fmul_rn(g, s));
+      }
+      og[k] = pack_bf16x2(dg[0], dg[1]);
+      ou[k] = pack_bf16x2(du[0], du[1]);
+    }
+    *reinterpret_cast<v4u*>(d_gu + m * 2 * I + c) = og;
+    *reinterpret_cast<v4u*>(d_gu + m * 2 * I + I + c) = ou;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, uint16_t* d_gu, int64_t M,
+                             int64_t I, hipStream_t st) {
+  const int64_t pieces = M * (I / 8);
+  if (pieces == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 256 * 16);
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dh, gu, d_gu,
+                     M, I);
+  return hipGetLastError();
+}
+
+}  // namespace gmm

@@ -121,14 +121,16 @@ typedef struct gmm_operand {
 
 /* Operation identifiers for gmm_workspace_size.  The _FUSED variants size the workspace
  * of gmm_fwd / gmm_dlhs calls that quantize a bf16 operand inside the product kernel;
- * GMM_OP_QUANTIZE sizes that of gmm_quantize and gmm_dynamic_scales. */
+ * GMM_OP_QUANTIZE sizes that of gmm_quantize and gmm_dynamic_scales; GMM_OP_FWD_SWIGLU
+ * that of gmm_fwd_swiglu. */
 typedef enum gmm_op {
   GMM_OP_FWD = 0,
   GMM_OP_DLHS = 1,
   GMM_OP_TGMM = 2,
   GMM_OP_FWD_FUSED = 3,
   GMM_OP_DLHS_FUSED = 4,
-  GMM_OP_QUANTIZE = 5
+  GMM_OP_QUANTIZE = 5,
+  GMM_OP_FWD_SWIGLU = 6
 } gmm_op_t;
 
 /*
@@ -182,6 +184,45 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
                       void* workspace, size_t workspace_bytes, gmm_stream_t stream);
 
 /*
+ * gmm_fwd_swiglu - the merged gate|up forward with SwiGLU in its epilogue ("FP8 Megablox
+ * for batch split", Description (2): W0 | W1 merged along N, one call for both).
+ *
+ *   x[m, n] = (sum_k q(lhs)[m, k] * rhs[g, k, n]) * s_lhs(m) * rhs_scales[g, n]   (fp32,
+ *             exactly as gmm_fwd computes it before rounding), n < 2 I;
+ *   h[m, c] = silu(x[m, c]) * x[m, I + c],  silu(v) = v / (1 + exp(-v)),  c < I,
+ *
+ * in fp32 with each operation rounded to nearest, then stored in out_dtype.  rhs holds the
+ * merged codes: channels 0..I-1 are the gate (W0), I..2I-1 the up projection (W1); only
+ * rhs_layout GMM_RHS_NK ([G, 2I, K]) is accepted (else GMM_ERR_RECIPE), with rhs_scales f32
+ * [G, 2I].  I is a positive multiple of 128.  lhs: as gmm_fwd; a bf16 lhs is quantized once
+ * into the workspace, which must then hold gmm_workspace_size(GMM_OP_FWD_SWIGLU, ...)
+ * bytes (else GMM_ERR_WORKSPACE).
+ * gu           optional [M, 2I] in out_dtype: x itself (the values gmm_fwd would store),
+ *              which the backward needs; NULL skips it.
+ * h            [M, I] in out_dtype.  Rows outside every group are not written.
+ */
+gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                            int32_t out_dtype, int64_t M, int64_t K, int64_t I, int32_t G,
+                            const void* lhs, float* lhs_scales, const uint8_t* rhs,
+                            const float* rhs_scales, const int32_t* group_sizes, void* gu,
+                            void* h, void* workspace, size_t workspace_bytes,
+                            gmm_stream_t stream);
+
+/*
+ * gmm_swiglu_bwd - the SwiGLU backward between the down projection's dlhs and the merged
+ * gate|up dlhs.  From gu = [g | u] (bf16 [M, 2I], as gmm_fwd_swiglu returns it) and
+ * dh = dL/dh (bf16 [M, I]), with s = 1 / (1 + exp(-g)):
+ *
+ *   d_gu[m, c]     = dh * u * s * (1 + g * (1 - s))      (dL/dg)
+ *   d_gu[m, I + c] = dh * g * s                          (dL/du = dh * silu(g))
+ *
+ * in fp32 with each operation rounded to nearest, stored as bf16 [M, 2I].  I is a
+ * positive multiple of 128; d_gu must not overlap the inputs.
+ */
+gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu, void* d_gu,
+                            gmm_stream_t stream);
+
+/*
  * tgmm_drhs - weight gradient, the transposed grouped matmul ("Support quantization for
  * tokamax gmm v2", What this does: drhs_tgmm2).
  *
@@ -220,6 +261,8 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
  * GMM_OP_FWD_FUSED / GMM_OP_DLHS_FUSED: the same without the codes (0 unless the call
  *   computes dynamic block scales).
  * GMM_OP_QUANTIZE: gmm_quantize / gmm_dynamic_scales on `a` [rows, cols_a].
+ * GMM_OP_FWD_SWIGLU: gmm_fwd_swiglu, `a` the lhs, `rows` M, `cols_a` K; a bf16 lhs always
+ *   gets room for its codes (the SwiGLU epilogue reads fp8 codes).
  * GMM_OP_TGMM: `a` is the lhs and `b` the grad; tgmm always needs workspace for its
  *   quantized, transposed copies of both operands (about (K + N) x (M + 128 G) bytes).
  *   `rows` is M, `cols_a` / `cols_b` the row widths (K and N), G the number of groups.

@@ -12,6 +12,7 @@ fp8    OCP E4M3FN / E5M2 and bfloat16 codecs, written from the format definition
 quant  in-kernel lhs quantization (static per-tensor, dynamic per-128-row block) and
        the per-channel weight quantization used to prepare the pre-quantized rhs.
 gmm    the three grouped products: gmm forward, gmm dlhs and the transposed tgmm.
+swiglu SwiGLU of the merged gate|up product, forward and backward.
 
 Sources (the MaxText pull-request pages this method is taken from):
   * "FP8 Megablox for batch split" (PR #3770), Description (1) and (2): fp8 recipes
@@ -48,3 +49,4 @@ from .gmm import (  # noqa: F401
     gmm_fwd_ref,
     tgmm_ref,
 )
+from .swiglu import silu, swiglu_bwd_ref, swiglu_ref  # noqa: F401

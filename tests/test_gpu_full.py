@@ -308,6 +308,37 @@ def test_mixtral_gate_up_step(lib):
     _check_tgmm(x, grad, sx, sg, sizes, dw, dw32, rng)
 
 
+def test_moe_swiglu_fused_forward(lib, swiglu):
+    """gmm_fwd_swiglu at the full SwiGLU block shape: sampled rows x sampled channel pairs
+    of h against the oracle's product and SwiGLU, and the product half against gmm_fwd."""
+    wl, sizes, x, w_gu, _, _ = swiglu
+    I = wl.extra["intermediate"]
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w_gu, "e4m3", 0, "nk")
+    xq, sx = lib.gmm_quantize(x, "e4m3", "dynamic")
+    h, gu = lib.gmm_fwd_swiglu(xq, wq, ws, gs, lhs_scales=sx, out_dtype=torch.float32, gu=True)
+    plain = lib.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out_dtype=torch.float32)
+    sync()
+    assert torch.equal(gu.view(torch.int32), plain.view(torch.int32))
+    rng = np.random.default_rng(8)
+    rows = sample_rows(sizes, rng)
+    cols = sample_cols(I, rng, 24)
+    both = np.concatenate([cols, I + cols])
+    xb = bf16_to_bits(x)
+    s_ref, inv_ref = dynamic_block_scales(xb, "e4m3")
+    a_codes = quantize_with_inv(bf16_bits_to_f32(xb[rows]), inv_ref[rows // 128], "e4m3")
+    bi = torch.as_tensor(both, device=DEV)
+    b_codes, b_s = quantize_rhs_per_channel(bf16_to_bits(w_gu[:, :, bi]), "e4m3", "n")
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_fwd_ref(a_codes, "e4m3", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    from oracle.swiglu import swiglu_ref
+    Rh = swiglu_ref(R, len(cols))
+    ri, ci = torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)
+    err = group_rel_err(to_np(h[ri][:, ci]), Rh, group_row_ranges(sub))
+    print(f"sampled max group relative error of h {err:.3e}", flush=True)
+    assert err <= TOL, err
+
+
 @pytest.fixture(scope="module")
 def swiglu():
     wl = WORKLOADS["moe_swiglu"]

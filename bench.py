@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="mixtral_gate_up")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-swiglu", action="store_true",
+                   help="skip the SwiGLU block measurement (moe_swiglu shape)")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=2048, help="at most 4096")
     p.add_argument("--copy-calibration", action="store_true",
@@ -224,6 +226,61 @@ def gfx_clock_during(run, seconds=1.0):
     return round(sum(busy) / len(busy), 1) if busy else None
 
 
+def swiglu_block(g, reps=10):
+    """The SwiGLU steps of an MoE feed-forward block at the moe_swiglu shape (G=64,
+    M=65536, hidden 2048, intermediate 1408): gmm_fwd_swiglu (merged gate|up product with
+    SwiGLU in its epilogue) against gmm_fwd alone, and gmm_swiglu_bwd, each timed with
+    HIP events on the current stream; synthetic inputs as the workload's."""
+    import torch
+
+    from synth.workloads import WORKLOADS, normal_bf16
+
+    wl = WORKLOADS["moe_swiglu"]
+    G, M, K, I = wl.G, wl.M, wl.K, wl.extra["intermediate"]
+    gs = torch.tensor(wl.group_sizes(), dtype=torch.int32, device="cuda")
+    x = normal_bf16((M, K), 1.0, wl.seed * 100, "cuda")
+    w = normal_bf16((G, K, 2 * I), 0.02, wl.seed * 100 + 1, "cuda")
+    wq, ws = g.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    del w
+    xq, sx = g.gmm_quantize(x, "e4m3", "dynamic")
+    dh = normal_bf16((M, I), 1e-3, wl.seed * 100 + 3, "cuda")
+    h = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
+    d_gu = torch.empty_like(gu)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_plain = timed(lambda: g.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out=gu))
+    t_fused = timed(lambda: g.gmm_fwd_swiglu(xq, wq, ws, gs, lhs_scales=sx, out=h))
+    g.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out=gu)
+    t_bwd = timed(lambda: g.gmm_swiglu_bwd(dh, gu, out=d_gu))
+    flop = 2.0 * M * K * 2 * I
+    bwd_bytes = 10.0 * M * I  # reads dh (2 B) and gu (4 B), writes d_gu (4 B) per channel
+    res = {
+        "workload": wl.name, "G": G, "M": M, "K": K, "I": I,
+        "fwd_swiglu": {"ms": round(t_fused, 4), "TFLOP/s": round(flop / t_fused / 1e9, 1),
+                       "frac_peak": round(flop / t_fused / 1e9 / FP8_PEAK_TFLOPS, 4)},
+        "fwd_product_only_ms": round(t_plain, 4),
+        "swiglu_bwd": {"ms": round(t_bwd, 4), "GB/s": round(bwd_bytes / t_bwd / 1e6, 1),
+                       "frac_hbm": round(bwd_bytes / t_bwd / 1e6 / 8000.0, 4)},
+        "note": "fwd_swiglu writes h [M, I] only; the unfused path would add a bf16 [M, 2I] "
+                "write and read around an elementwise SwiGLU",
+    }
+    del x, xq, wq, ws, dh, h, gu, d_gu
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(step, rows, cols):
     """Time the CPU oracle on a bounded sample: the first `rows` rows (with their group
     split), all K, the first `cols` columns of the merged weight; fwd + dlhs + tgmm."""
@@ -354,6 +411,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
                                      "1 GiB copy; null once the kernel sources changed)"},
     }
+    if not args.no_swiglu:
+        line["swiglu_block"] = swiglu_block(g)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)
     print(json.dumps(line), flush=True)

@@ -49,4 +49,4 @@ from .gmm import (  # noqa: F401
     gmm_fwd_ref,
     tgmm_ref,
 )
-from .swiglu import silu, swiglu_bwd_ref, swiglu_ref  # noqa: F401
+from .swiglu import silu, swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref  # noqa: F401

@@ -11,12 +11,20 @@ definitions, written out in float64 and rounded once to float32:
   dL/dg    = dL/dh * u * sigmoid(g) * (1 + g * (1 - sigmoid(g)))     (d silu / dv)
   dL/du    = dL/dh * silu(g)
 
+With h emitted as fp8 codes for the down projection (its lhs, quantized with a fixed
+per-tensor scale as in "add static LHS scaling support for GMM v2 FWD", Description), the
+codes are those of the static quantization O2/O3 applied to the float32 h:
+code = encode(clip(RNE_f32(h * RNE_f32(1/s)), -qmax, qmax)).
+
 Parity: pinned by closed forms (sigmoid(ln 3) = 3/4), the identity silu(v) - silu(-v) = v,
-the large-|v| limits, and central finite differences of the forward for the backward
-(``tests/test_oracle_swiglu.py``).
+the large-|v| limits, and central finite differences of the forward for the backward;
+the fp8 codes of h by a brute-force nearest search over all 256 codes, saturation and
+signed zeros (``tests/test_oracle_swiglu.py``).
 """
 
 import numpy as np
+
+from .quant import quantize_with_inv, static_inv
 
 
 def silu(v):
@@ -48,3 +56,11 @@ def swiglu_bwd_ref(dh, gu, I):
     dg = dh * u * s * (1.0 + g * (1.0 - s))
     du = dh * g * s
     return np.concatenate([dg, du], axis=1).astype(np.float32)
+
+
+def swiglu_fp8_ref(x, I, s, fmt):
+    """x [M, 2I] (the merged product) -> (codes uint8 [M, I], h float32 [M, I]): h as in
+    swiglu_ref, then its static fp8 quantization under the per-tensor scale s."""
+    h = swiglu_ref(x, I)
+    inv = static_inv(s)
+    return quantize_with_inv(h, np.full(h.shape[0], inv, np.float32), fmt), h

@@ -77,3 +77,55 @@ def assert_bf16_close(Ybits, R, ranges=None, tol=TOL, min_exact=0.95):
 def group_row_ranges(group_sizes):
     off = np.concatenate([[0], np.cumsum(np.asarray(group_sizes, np.int64))])
     return [(int(off[g]), int(off[g + 1])) for g in range(len(off) - 1)]
+
+
+def fp8_order(codes):
+    """fp8 codes -> integers in value order (sign-magnitude; +0 and -0 both map to 0)."""
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def swiglu_h_bound(R, absR, K, I):
+    """(h, dh): the float64 SwiGLU of the oracle's fp32 products R [M, 2I] and a bound on
+    how far a correct fp32 evaluation of it can lie from h.  absR holds sum |a||b| s_A s_B
+    of every product (the oracle's product of the codes' magnitudes).  Each product may
+    differ from R by the rounding of two fp32 sums of K terms (the oracle's in its order,
+    the library's in MFMA blocks of 64: at most K + 7 K / 64 roundings) and the two scale
+    multiplies; silu is 1.1-Lipschitz; the fp32 evaluation of silu(g) * u adds a few
+    ulp."""
+    from oracle.swiglu import silu
+
+    R = np.asarray(R, np.float64)
+    absR = np.asarray(absR, np.float64)
+    gamma = (K + 7 * K / 64 + 4) * 2.0 ** -24
+    g, u = R[:, :I], R[:, I:2 * I]
+    dg, du = gamma * absR[:, :I], gamma * absR[:, I:2 * I]
+    h = silu(g) * u
+    dh = 1.1 * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + 8 * 2.0 ** -24 * np.abs(h)
+    return h, dh
+
+
+def assert_fp8_codes_in_band(codes, h, dh, s, fmt, ref_codes, min_exact=0.95):
+    """Every code lies between the codes of (h - dh) / s and (h + dh) / s (quantized as the
+    oracle does, widened by an fp32 rounding), and most equal the oracle's codes.  Returns
+    (fraction not equal to ref_codes, fraction of elements whose band spans two codes)."""
+    from oracle.fp8 import encode_fp8
+    from oracle.quant import qmax_of
+
+    inv = np.float64(np.float32(1.0) / np.float32(s))
+    q = qmax_of(fmt)
+
+    def code_of(y):
+        y = np.clip(y, -q, q).astype(np.float32)
+        return fp8_order(encode_fp8(y, fmt))
+
+    lo = (h - dh) * inv
+    hi = (h + dh) * inv
+    lo_c = code_of(lo - 2.0 ** -22 * np.abs(lo))
+    hi_c = code_of(hi + 2.0 ** -22 * np.abs(hi))
+    c = fp8_order(codes)
+    bad = (c < lo_c) | (c > hi_c)
+    assert not bad.any(), f"{int(bad.sum())} fp8 codes outside their rounding band"
+    exact = float(np.mean(c == fp8_order(ref_codes)))
+    assert exact >= min_exact, f"only {exact:.4f} of the codes equal the oracle's"
+    return 1.0 - exact, float(np.mean(lo_c != hi_c))

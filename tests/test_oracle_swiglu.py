@@ -3,8 +3,9 @@
 import math
 
 import numpy as np
+import pytest
 
-from oracle.swiglu import silu, swiglu_bwd_ref, swiglu_ref
+from oracle.swiglu import silu, swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref
 
 
 def test_silu_closed_forms_and_limits():
@@ -55,3 +56,83 @@ def test_backward_at_a_closed_form_point():
     d = swiglu_bwd_ref(np.array([[2.0]]), np.array([[l3, 5.0]]), 1)
     assert abs(d[0, 0] - np.float32(2.0 * 5.0 * 0.75 * (1 + l3 / 4))) <= 1e-6 * abs(d[0, 0])
     assert abs(d[0, 1] - np.float32(2.0 * 0.75 * l3)) <= 1e-6 * abs(d[0, 1])
+
+
+def _nearest_code(y, fmt):
+    """Brute force: the finite code nearest to y, ties to the even code (mantissa LSB 0)."""
+    from oracle.fp8 import decode_fp8
+
+    codes = np.arange(256, dtype=np.uint8)
+    vals = decode_fp8(codes, fmt).astype(np.float64)
+    ok = np.isfinite(vals)
+    codes, vals = codes[ok], vals[ok]
+    out = np.empty(y.shape, np.uint8)
+    for i, v in np.ndenumerate(y):
+        d = np.abs(vals - v)
+        best = codes[d == d.min()]
+        if len(best) > 1:  # a tie (or +0 / -0): the even code, keeping the sign of v
+            best = best[(best & 1) == 0]
+            if len(best) > 1:
+                best = best[(best >= 0x80) == bool(np.signbit(v))]
+        out[i] = best[0]
+    return out
+
+
+@pytest.mark.parametrize("fmt,qmax", [("e4m3", 448.0), ("e5m2", 57344.0)])
+def test_swiglu_fp8_codes_are_the_nearest_fp8_of_h_over_s(fmt, qmax):
+    rng = np.random.default_rng(7)
+    M, I = 24, 16
+    x = rng.normal(0.0, 2.0, (M, 2 * I)).astype(np.float32)
+    x[0, :4] = [0.0, -0.0, -30.0, 80.0]  # h = 0, -0 * u, a tiny negative, a large value
+    s = np.float32(0.01)
+    codes, h = swiglu_fp8_ref(x, I, s, fmt)
+    assert np.array_equal(h, swiglu_ref(x, I))
+    inv = np.float64(np.float32(1.0) / s)
+    # RNE_f32 of the exact product of two float32 values, then the clip to +-qmax
+    y = np.clip((h.astype(np.float64) * inv).astype(np.float32).astype(np.float64), -qmax, qmax)
+    assert np.array_equal(codes, _nearest_code(y, fmt))
+    # saturation: a scale that puts every |h| above qmax gives only the two extreme codes
+    big, _ = swiglu_fp8_ref(np.full((2, 2 * I), 5.0, np.float32), I, 1e-6, fmt)
+    assert np.all(big == (0x7E if fmt == "e4m3" else 0x7B))
+    neg = np.concatenate([np.full((2, I), 5.0), np.full((2, I), -5.0)], axis=1)
+    small, _ = swiglu_fp8_ref(neg.astype(np.float32), I, 1e-6, fmt)
+    assert np.all(small == (0xFE if fmt == "e4m3" else 0xFB))
+    # signed zero: silu(-200) * 1 underflows to -0.0 and stays -0
+    z, hz = swiglu_fp8_ref(np.array([[-200.0, 1.0]], np.float32), 1, 1.0, fmt)
+    assert hz[0, 0] == 0 and np.signbit(hz[0, 0]) and z[0, 0] == 0x80
+
+
+def test_fp8_band_check_accepts_the_oracle_and_catches_a_one_step_error():
+    """The GPU test's band for h's codes: the oracle's own codes pass, the band (a worst-case
+    bound on the fp32 sums) spans two codes for a minority of elements, and a code moved
+    by one step where the band holds one code fails."""
+    from oracle.gmm import gmm_fwd_ref
+    from oracle.quant import quantize_rhs_per_channel, quantize_rowblock
+    from tests.parity import assert_fp8_codes_in_band, fp8_order, swiglu_h_bound
+
+    rng = np.random.default_rng(11)
+    sizes = [70, 0, 186]
+    M, K, I = sum(sizes), 256, 64
+    xb = (rng.normal(0, 1, (M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wb = (rng.normal(0, 0.02, (3, K, 2 * I)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    a, sa, _ = quantize_rowblock(xb, "e4m3")
+    b, sb = quantize_rhs_per_channel(wb, "e4m3", "n")
+    rs = np.repeat(sa, 128)[:M]
+    R = gmm_fwd_ref(a, "e4m3", rs, b, "e4m3", sb, sizes)
+    absR = gmm_fwd_ref(a & 0x7F, "e4m3", rs, b & 0x7F, "e4m3", sb, sizes)
+    s = np.float32(np.abs(swiglu_ref(R, I)).max() / 448.0)
+    codes, _ = swiglu_fp8_ref(R, I, s, "e4m3")
+    h, dh = swiglu_h_bound(R, absR, K, I)
+    diff, amb = assert_fp8_codes_in_band(codes, h, dh, s, "e4m3", codes, min_exact=1.0)
+    assert diff == 0 and amb < 0.1
+    # one code moved one step further from zero, at 50 elements in turn: most are caught
+    cand = np.flatnonzero((np.abs(fp8_order(codes)) > 8) & (np.abs(fp8_order(codes)) < 100))
+    caught = 0
+    for i in cand[:50]:
+        bad = codes.copy()
+        bad.flat[i] = codes.flat[i] + 1
+        try:
+            assert_fp8_codes_in_band(bad, h, dh, s, "e4m3", codes, min_exact=0.0)
+        except AssertionError:
+            caught += 1
+    assert caught >= 40, caught

@@ -229,8 +229,10 @@ def gfx_clock_during(run, seconds=1.0):
 def swiglu_block(g, reps=10):
     """The SwiGLU steps of an MoE feed-forward block at the moe_swiglu shape (G=64,
     M=65536, hidden 2048, intermediate 1408): gmm_fwd_swiglu (merged gate|up product with
-    SwiGLU in its epilogue) against gmm_fwd alone, and gmm_swiglu_bwd, each timed with
-    HIP events on the current stream; synthetic inputs as the workload's."""
+    SwiGLU in its epilogue) against gmm_fwd alone, the same with h written as static-scale
+    e4m3 codes, the down projection on those codes against the same on the bf16 h, and
+    gmm_swiglu_bwd, each timed with HIP events on the current stream; synthetic inputs as
+    the workload's."""
     import torch
 
     from synth.workloads import WORKLOADS, normal_bf16
@@ -243,8 +245,13 @@ def swiglu_block(g, reps=10):
     wq, ws = g.gmm_quantize_rhs(w, "e4m3", 0, "nk")
     del w
     xq, sx = g.gmm_quantize(x, "e4m3", "dynamic")
+    wd = normal_bf16((G, I, K), 0.02, wl.seed * 100 + 2, "cuda")
+    wdq, wds = g.gmm_quantize_rhs(wd, "e4m3", 0, "nk")
+    del wd
     dh = normal_bf16((M, I), 1e-3, wl.seed * 100 + 3, "cuda")
     h = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    hq = torch.empty((M, I), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
     d_gu = torch.empty_like(gu)
 
@@ -262,6 +269,11 @@ def swiglu_block(g, reps=10):
 
     t_plain = timed(lambda: g.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out=gu))
     t_fused = timed(lambda: g.gmm_fwd_swiglu(xq, wq, ws, gs, lhs_scales=sx, out=h))
+    s_h = 4.0 / 448.0  # a static scale for h (its value does not change the work)
+    t_fp8 = timed(lambda: g.gmm_fwd_swiglu_fp8(xq, wq, ws, gs, s_h, lhs_scales=sx, out=hq))
+    down = dict(lhs_scaling="static", static_scale=s_h, out=y)
+    t_down_codes = timed(lambda: g.gmm_fwd(hq, wdq, wds, gs, **down))
+    t_down_bf16 = timed(lambda: g.gmm_fwd(h, wdq, wds, gs, **down))
     g.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out=gu)
     t_bwd = timed(lambda: g.gmm_swiglu_bwd(dh, gu, out=d_gu))
     flop = 2.0 * M * K * 2 * I
@@ -271,12 +283,15 @@ def swiglu_block(g, reps=10):
         "fwd_swiglu": {"ms": round(t_fused, 4), "TFLOP/s": round(flop / t_fused / 1e9, 1),
                        "frac_peak": round(flop / t_fused / 1e9 / FP8_PEAK_TFLOPS, 4)},
         "fwd_product_only_ms": round(t_plain, 4),
+        "fwd_swiglu_fp8_h_ms": round(t_fp8, 4),
+        "down_on_h_codes_ms": round(t_down_codes, 4),
+        "down_on_bf16_h_ms": round(t_down_bf16, 4),
         "swiglu_bwd": {"ms": round(t_bwd, 4), "GB/s": round(bwd_bytes / t_bwd / 1e6, 1),
                        "frac_hbm": round(bwd_bytes / t_bwd / 1e6 / 8000.0, 4)},
         "note": "fwd_swiglu writes h [M, I] only; the unfused path would add a bf16 [M, 2I] "
                 "write and read around an elementwise SwiGLU",
     }
-    del x, xq, wq, ws, dh, h, gu, d_gu
+    del x, xq, wq, ws, wdq, wds, dh, h, hq, y, gu, d_gu
     torch.cuda.empty_cache()
     return res
 

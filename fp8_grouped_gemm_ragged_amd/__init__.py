@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "load", "library_path", "GmmError", "gmm_fwd", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
-    "gmm_dynamic_scales",
+    "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8", "gmm_swiglu_bwd",
     "gmm_quantize_rhs", "gmm_static_scale_from_bound", "gmm_workspace_size",
     "gmm_status_string", "gmm_version", "E4M3", "E5M2", "STATIC", "DYNAMIC", "BLOCK_ROWS",
 ]
@@ -65,6 +65,7 @@ _SIGNATURES = {
     "gmm_dlhs": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "tgmm_drhs": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_fwd_swiglu": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_fwd_swiglu_fp8": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _OPP, _P, _P, _SZ, _P],
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
     "gmm_workspace_size": [_I32, _OPP, _OPP, _I64, _I64, _I64, _I32, ctypes.POINTER(_SZ)],
     "gmm_dynamic_scales": [_I32, _I64, _I64, _P, _P, _P, _SZ, _P],
@@ -309,6 +310,25 @@ def gmm_fwd_swiglu(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3",
     block scales when dynamic).  gu=True also returns x itself ([M, 2I], the backward's
     input); returns h, or (h, x) with gu=True, with the lhs scales appended when
     return_scales."""
+    return _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
+                       static_scale, lhs_scales, out_dtype, out, gu, return_scales, None)
+
+
+def gmm_fwd_swiglu_fp8(lhs, rhs, rhs_scales, group_sizes, h_scale, *, h_format="e4m3",
+                       lhs_format="e4m3", lhs_scaling="dynamic", static_scale=None,
+                       lhs_scales=None, gu_dtype=None, out=None, gu=False,
+                       return_scales=False):
+    """gmm_fwd_swiglu with h returned as uint8 fp8 codes [M, I] (format h_format) under the
+    static per-tensor scale h_scale: code = fp8(clamp(RNE_f32(h * RNE_f32(1/h_scale)))).
+    The codes feed gmm_fwd(h_codes, ..., lhs_scaling="static", static_scale=h_scale).
+    gu=True also returns the product x in gu_dtype (bf16 unless torch.float32)."""
+    return _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
+                       static_scale, lhs_scales, gu_dtype, out, gu, return_scales,
+                       (h_format, h_scale))
+
+
+def _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling, static_scale,
+                lhs_scales, out_dtype, out, gu, return_scales, h_fp8):
     import torch
 
     lib = load()
@@ -323,10 +343,11 @@ def gmm_fwd_swiglu(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3",
         raise ValueError("rhs must be [G, 2I, K] codes matching the lhs width")
     I = N2 // 2
     odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    hdt = torch.uint8 if h_fp8 else odt
     if out is None:
-        out = torch.empty((M, I), dtype=odt, device=lhs.device)
+        out = torch.empty((M, I), dtype=hdt, device=lhs.device)
     else:
-        _need(out, odt, "out", 2)
+        _need(out, hdt, "out", 2)
     x = torch.empty((M, N2), dtype=odt, device=lhs.device) if gu else None
     op = _operand(KIND_FP8 if prequant else KIND_BF16, lhs_format, lhs_scaling, static_scale)
     mode = _SCALING[lhs_scaling]
@@ -340,10 +361,16 @@ def gmm_fwd_swiglu(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3",
     _check(lib.gmm_workspace_size(OP_FWD_SWIGLU, ctypes.byref(op), ctypes.byref(op), M, K, N2, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, lhs.device)
-    _check(lib.gmm_fwd_swiglu(ctypes.byref(op), E4M3, RHS_NK, OUT_F32 if odt == torch.float32 else OUT_BF16,
-                              M, K, I, G, _ptr(lhs), _ptr(lhs_scales), _ptr(rhs), _ptr(rhs_scales),
-                              _ptr(group_sizes), _ptr(x), _ptr(out), _ptr(ws), ws_n.value, _stream()),
-           "gmm_fwd_swiglu")
+    odt_code = OUT_F32 if odt == torch.float32 else OUT_BF16
+    head = (ctypes.byref(op), E4M3, RHS_NK, odt_code, M, K, I, G, _ptr(lhs), _ptr(lhs_scales),
+            _ptr(rhs), _ptr(rhs_scales), _ptr(group_sizes), _ptr(x))
+    if h_fp8:
+        hop = _operand(KIND_FP8, h_fp8[0], "static", h_fp8[1])
+        _check(lib.gmm_fwd_swiglu_fp8(*head, ctypes.byref(hop), _ptr(out), _ptr(ws), ws_n.value,
+                                      _stream()), "gmm_fwd_swiglu_fp8")
+    else:
+        _check(lib.gmm_fwd_swiglu(*head, _ptr(out), _ptr(ws), ws_n.value, _stream()),
+               "gmm_fwd_swiglu")
     res = (out, x) if gu else (out,)
     if return_scales:
         res = res + (lhs_scales,)

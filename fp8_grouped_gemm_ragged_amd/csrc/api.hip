@@ -163,9 +163,14 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                           const uint8_t* rhs, const float* rhs_scales,
                           const int32_t* group_sizes, void* out, void* workspace,
                           size_t workspace_bytes, hipStream_t st, bool swiglu = false,
-                          void* gu = nullptr) {
+                          void* gu = nullptr, const gmm_operand_t* h_op = nullptr) {
   gmm_status_t s = check_operand(aop);
   if (s != GMM_OK) return s;
+  // SwiGLU with fp8 h: codes under a validated static per-tensor scale
+  if (h_op) {
+    if ((s = check_operand(h_op)) != GMM_OK) return s;
+    if (h_op->kind != GMM_OPERAND_FP8 || h_op->scaling != GMM_SCALE_STATIC) return GMM_ERR_RECIPE;
+  }
   if (rhs_format != GMM_FP8_E4M3) return GMM_ERR_RECIPE;  // weights are e4m3 codes
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, Kc, Nout, G)) != GMM_OK) return s;
@@ -191,7 +196,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   const size_t ws_used = ws_need + (quant_once ? quant_once_bytes(M, Kc) : 0);
   const size_t a_bytes = (size_t)M * Kc * (a_fp8 ? 1 : 2);
   const size_t esize = out_dtype == GMM_OUT_F32 ? 4 : 2;
-  const size_t out_bytes = (size_t)M * (swiglu ? Nout / 2 : Nout) * esize;
+  const size_t out_bytes = (size_t)M * (swiglu ? Nout / 2 : Nout) * (h_op ? 1 : esize);
   const size_t gu_bytes = swiglu && gu ? (size_t)M * Nout * esize : 0;
   const size_t b_bytes = (size_t)G * Kc * Nout;
   const size_t as_bytes = (size_t)nblocks(M) * 4;
@@ -226,6 +231,10 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.G = G;
   p.out_f32 = out_dtype == GMM_OUT_F32;
   p.gu = gu;
+  if (h_op) {
+    p.h_codes = 1 + h_op->format;
+    p.h_inv = 1.0f / h_op->static_scale;  // IEEE division on the host: RNE(1/s)
+  }
   Scaling sc;
   if ((s = resolve_scaling(aop, a, M, Kc, a_scales, workspace, st, sc)) != GMM_OK) return s;
   p.a_scale_blk = sc.blk;
@@ -284,6 +293,21 @@ gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int
   return grouped_gemm("gmm_fwd_swiglu", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN,
                       out_dtype, M, K, 2 * I, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes,
                       h, workspace, workspace_bytes, (hipStream_t)stream, true, gu);
+}
+
+gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
+                                int32_t rhs_layout, int32_t gu_dtype, int64_t M, int64_t K,
+                                int64_t I, int32_t G, const void* lhs, float* lhs_scales,
+                                const uint8_t* rhs, const float* rhs_scales,
+                                const int32_t* group_sizes, void* gu, const gmm_operand_t* h_op,
+                                uint8_t* h_codes, void* workspace, size_t workspace_bytes,
+                                gmm_stream_t stream) {
+  if (!h_op) return GMM_ERR_NULL;
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
+  return grouped_gemm("gmm_fwd_swiglu_fp8", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN,
+                      gu_dtype, M, K, 2 * I, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes,
+                      h_codes, workspace, workspace_bytes, (hipStream_t)stream, true, gu, h_op);
 }
 
 gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu, void* d_gu,

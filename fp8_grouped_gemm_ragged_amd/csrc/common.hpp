@@ -81,6 +81,13 @@ __device__ inline float inv_from_scale(float s) {
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// 4 fp32 values -> 4 fp8 codes (one dword, value e in byte e).
+template <int FMT>
+__device__ inline uint32_t quant4(v4f v, float inv) {
+  const uint32_t d = cvt_pk<FMT, false>(quant_prep<FMT>(v[0], inv), quant_prep<FMT>(v[1], inv), 0u);
+  return cvt_pk<FMT, true>(quant_prep<FMT>(v[2], inv), quant_prep<FMT>(v[3], inv), d);
+}
+
 // 4 packed bf16 pairs (8 values, one 16-byte load) -> 8 fp8 codes (2 dwords).
 template <int FMT>
 __device__ inline v2u quant8(v4u w, float inv) {

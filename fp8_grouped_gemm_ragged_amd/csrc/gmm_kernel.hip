@@ -130,7 +130,8 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
 // SwiGLU epilogue of a gate|up tile.  The product values x = (acc * s_A(m)) * s_B(n) are
 // the ones gmm_fwd stores (written to gu when given).  The up waves pass theirs through
 // LDS, in the lane order every wave's accumulators share, and each gate wave then stores
-// h = silu(g) * u = (g / (1 + exp(-g))) * u for its 128 x 128 block, all in fp32.
+// h = silu(g) * u = (g / (1 + exp(-g))) * u for its 128 x 128 block, all in fp32: in the
+// output dtype, or as fp8 codes fp8(clamp(RNE_f32(h * inv), +-qmax)) of a static scale.
 __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc, int c0, int wr,
                                        int wc, int lane, v16f (&acc)[4][4], uint8_t* sA0,
                                        uint8_t* sB0, uint8_t* sA1, uint8_t* sB1) {
@@ -201,7 +202,11 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
         for (int e = 0; e < 4; ++e)
           h[e] = __fmul_rn(__fdiv_rn(g[e], __fadd_rn(1.0f, expf(-g[e]))), u[e]);
         const int64_t idx = (int64_t)m * I + c0 + j * 32 + 8 * r4 + 4 * fhalf;
-        if (p.out_f32) {
+        if (p.h_codes) {
+          // fp8 codes of h under a static scale, the lhs of the down projection
+          *reinterpret_cast<uint32_t*>((uint8_t*)p.out + idx) =
+              p.h_codes == 1 + FMT_E4M3 ? quant4<FMT_E4M3>(h, p.h_inv) : quant4<FMT_E5M2>(h, p.h_inv);
+        } else if (p.out_f32) {
           *reinterpret_cast<v4f*>((float*)p.out + idx) = h;
         } else {
           v2u v;

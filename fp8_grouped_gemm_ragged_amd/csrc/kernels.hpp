@@ -29,6 +29,9 @@ struct GemmParams {
   // SwiGLU epilogue (gmm_fwd_swiglu): B holds the merged [W0 | W1] channels (Nout = 2 I),
   // out is h [M, I], gu (optional) the product itself [M, 2 I]
   void* gu;
+  // h as fp8 codes (1 + format; 0: h in the output dtype) under a static scale's inverse
+  int32_t h_codes;
+  float h_inv;
 };
 
 // tgmm: out[g] = A_g^T [Kout, m] x B_g [m, Nout], contraction over the rows of group g.

@@ -209,6 +209,33 @@ gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int
                             gmm_stream_t stream);
 
 /*
+ * gmm_fwd_swiglu_fp8 - gmm_fwd_swiglu with h written as fp8 codes, ready to be the lhs of
+ * the down projection without a bf16 round trip ("FP8 Megablox for batch split",
+ * Description (1) and (2): fp8 operands in the MoE gmms, gate|up merged; "add static LHS
+ * scaling support for GMM v2 FWD", Description: a fixed calibration scale per tensor).
+ *
+ *   h_codes[m, c] = fp8(clamp(RNE_f32(h[m, c] * inv), -qmax, qmax)),  inv = RNE_f32(1/s),
+ *
+ * with h the fp32 value gmm_fwd_swiglu computes and s = h_op->static_scale.
+ * h_op         kind GMM_OPERAND_FP8, scaling GMM_SCALE_STATIC, format e4m3 or e5m2 (else
+ *              GMM_ERR_RECIPE), static_scale finite, normal and positive (else
+ *              GMM_ERR_SCALE).  The same descriptor, passed as lhs_op of gmm_fwd with
+ *              h_codes as lhs, runs the down projection on these codes.
+ * h_codes      uint8 [M, I]; rows outside every group are not written.
+ * gu, gu_dtype the optional product [M, 2I] as in gmm_fwd_swiglu (gu_dtype bf16 or f32).
+ * Everything else, the workspace (GMM_OP_FWD_SWIGLU) included, is as gmm_fwd_swiglu's.
+ * A dynamic per-block scale for h would need the abs-max over all I channels of 128
+ * rows, which spans many output tiles: that route stores h in bf16 and runs gmm_quantize.
+ */
+gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
+                                int32_t rhs_layout, int32_t gu_dtype, int64_t M, int64_t K,
+                                int64_t I, int32_t G, const void* lhs, float* lhs_scales,
+                                const uint8_t* rhs, const float* rhs_scales,
+                                const int32_t* group_sizes, void* gu, const gmm_operand_t* h_op,
+                                uint8_t* h_codes, void* workspace, size_t workspace_bytes,
+                                gmm_stream_t stream);
+
+/*
  * gmm_swiglu_bwd - the SwiGLU backward between the down projection's dlhs and the merged
  * gate|up dlhs.  From gu = [g | u] (bf16 [M, 2I], as gmm_fwd_swiglu returns it) and
  * dh = dL/dh (bf16 [M, I]), with s = 1 / (1 + exp(-g)):

@@ -187,3 +187,37 @@ def test_quantize_validation():
     assert lib.gmm_quantize_rhs(0, 2, 0, 2, 128, 128, ptr(1), ptr(2), ptr(3), None) == 4
     assert lib.gmm_quantize_rhs(0, 0, 0, 2, 100, 128, ptr(1), ptr(2), ptr(3), None) == 2
     assert lib.gmm_quantize_rhs(0, 0, 0, 2, 128, 128, None, ptr(2), ptr(3), None) == 1
+
+
+def test_swiglu_validation():
+    lib = g.load()
+    o = op(kind=1)  # dynamic fp8 codes: block scales are an input
+    hop = op(kind=1, fmt=0, scaling=0, s=0.25)
+
+    def fwd_fp8(h=hop, layout=1, M=256, K=256, I=256, gu=None, h_codes=8, gu_dtype=0):
+        return lib.gmm_fwd_swiglu_fp8(ctypes.byref(o), 0, layout, gu_dtype, M, K, I, 4, ptr(1),
+                                      ptr(2), ptr(3), ptr(4), ptr(5),
+                                      None if gu is None else ptr(gu),
+                                      None if h is None else ctypes.byref(h),
+                                      None if h_codes is None else ptr(h_codes), ptr(7), 1 << 20,
+                                      None)
+
+    assert fwd_fp8(M=0) == 0  # validated, nothing to enqueue
+    assert fwd_fp8(h=None) == 1
+    assert fwd_fp8(h_codes=None) == 1
+    assert fwd_fp8(h=op(kind=0, scaling=0, s=0.25)) == 4  # h must be fp8 codes
+    assert fwd_fp8(h=op(kind=1, scaling=1)) == 4  # only a static scale fits one pass
+    assert fwd_fp8(h=op(kind=1, fmt=2, scaling=0, s=0.25)) == 4
+    for bad in (0.0, -1.0, float("inf"), 1e-40):
+        assert fwd_fp8(h=op(kind=1, scaling=0, s=bad)) == 3
+    assert fwd_fp8(layout=0) == 4  # [G, K, 2I] weights: not on the SwiGLU route
+    assert fwd_fp8(I=192) == 2  # 2I must be a multiple of 256
+    assert fwd_fp8(gu_dtype=3) == 4
+    assert fwd_fp8(h_codes=1) == 9  # h codes over the lhs
+    assert fwd_fp8(gu=8) == 9  # the product over h
+    assert lib.gmm_fwd_swiglu(ctypes.byref(o), 0, 1, 0, 256, 256, 256, 4, ptr(1), ptr(2), ptr(3),
+                              ptr(4), ptr(5), None, None, ptr(7), 1 << 20, None) == 1
+    assert lib.gmm_swiglu_bwd(256, 192, ptr(1), ptr(2), ptr(3), None) == 2
+    assert lib.gmm_swiglu_bwd(256, 256, ptr(1), None, ptr(3), None) == 1
+    assert lib.gmm_swiglu_bwd(256, 256, ptr(1), ptr(2), ptr(2), None) == 9
+    assert lib.gmm_swiglu_bwd(0, 256, None, None, None, None) == 0

@@ -310,7 +310,8 @@ def test_mixtral_gate_up_step(lib):
 
 def test_moe_swiglu_fused_forward(lib, swiglu):
     """gmm_fwd_swiglu at the full SwiGLU block shape: sampled rows x sampled channel pairs
-    of h against the oracle's product and SwiGLU, and the product half against gmm_fwd."""
+    of h against the oracle's product and SwiGLU, and the product half against gmm_fwd;
+    gmm_fwd_swiglu_fp8's codes of h on the same samples."""
     wl, sizes, x, w_gu, _, _ = swiglu
     I = wl.extra["intermediate"]
     gs = gs_tensor(sizes)
@@ -337,6 +338,21 @@ def test_moe_swiglu_fused_forward(lib, swiglu):
     err = group_rel_err(to_np(h[ri][:, ci]), Rh, group_row_ranges(sub))
     print(f"sampled max group relative error of h {err:.3e}", flush=True)
     assert err <= TOL, err
+    # h as e4m3 codes of a static scale (the largest sampled |h| at qmax): the sampled codes
+    # lie in the rounding band of the oracle's h
+    from oracle.swiglu import swiglu_fp8_ref
+    from tests.parity import assert_fp8_codes_in_band, swiglu_h_bound
+
+    s_h = np.float32(np.abs(Rh).max() / 448.0)
+    hq = lib.gmm_fwd_swiglu_fp8(xq, wq, ws, gs, float(s_h), lhs_scales=sx)
+    sync()
+    ref_codes, _ = swiglu_fp8_ref(R, len(cols), s_h, "e4m3")
+    absR = gmm_fwd_ref(a_codes & 0x7F, "e4m3", s_ref[rows // 128], b_codes & 0x7F, "e4m3", b_s, sub)
+    hb, dh = swiglu_h_bound(R, absR, x.shape[1], len(cols))
+    diff, amb = assert_fp8_codes_in_band(to_np(hq[ri][:, ci]), hb, dh, s_h, "e4m3", ref_codes,
+                                         min_exact=0.99)
+    print(f"sampled fp8 h codes differing from the oracle's {diff:.2e} (bands spanning two "
+          f"codes {amb:.2e})", flush=True)
 
 
 @pytest.fixture(scope="module")

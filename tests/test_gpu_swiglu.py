@@ -6,12 +6,13 @@ import pytest
 import torch
 
 import oracle.ops as ops
-from oracle.fp8 import bf16_bits_to_f32, f32_to_bf16_bits
+from oracle.fp8 import bf16_bits_to_f32, decode_fp8, f32_to_bf16_bits
 from oracle.gmm import gmm_fwd_ref, row_scales
-from oracle.quant import quantize_rhs_per_channel
-from oracle.swiglu import swiglu_bwd_ref, swiglu_ref
+from oracle.quant import qmax_of, quantize_rhs_per_channel
+from oracle.swiglu import swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref
 from tests.gpu_util import gen, gs_tensor
-from tests.parity import TOL, assert_bf16_close, group_rel_err, group_row_ranges, to_np
+from tests.parity import (TOL, assert_bf16_close, assert_fp8_codes_in_band, group_rel_err,
+                          group_row_ranges, swiglu_h_bound, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +67,55 @@ def test_swiglu_backward(lib):
     exact = np.mean(to_np(d) == f32_to_bf16_bits(R))
     print(f"bf16 outputs equal to RNE of the exact value: {exact:.5f}")
     assert exact >= 0.99
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fused_swiglu_forward_fp8_h(lib, fmt):
+    """gmm_fwd_swiglu_fp8: h as fp8 codes of a static scale, then the down projection on
+    those codes.  Codes lie within the rounding band of the oracle's h (the products'
+    fp32 sums may round differently) and nearly all equal the oracle's; the down output
+    matches the oracle's, allowing one code step where the band spans two codes."""
+    sizes = [0, 300, 5, 0, 457, 130]
+    G, M, K, I = len(sizes), sum(sizes), 256, 384
+    x, xb = gen((M, K), 1.0, 521)
+    w, wb = gen((G, K, 2 * I), 0.02, 522)
+    wd, wdb = gen((G, I, K), 0.02, 523)  # down projection [G, I, hidden]
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    wdq, wds = lib.gmm_quantize_rhs(wd, "e4m3", 0, "nk")
+    xq, sx = lib.gmm_quantize(x, "e4m3", "dynamic")
+    a_codes, s_blk = ops.quantize_operand(xb, "e4m3", "dynamic")
+    b_codes, b_s = quantize_rhs_per_channel(wb, "e4m3", "n")
+    sa = row_scales(s_blk, M)
+    R = gmm_fwd_ref(a_codes, "e4m3", sa, b_codes, "e4m3", b_s, sizes)
+    absR = gmm_fwd_ref(a_codes & 0x7F, "e4m3", sa, b_codes & 0x7F, "e4m3", b_s, sizes)
+    # a scale that puts the largest |h| at twice qmax: the top values saturate
+    s = np.float32(np.abs(swiglu_ref(R, I)).max() / (2 * qmax_of(fmt)))
+    ref_codes, _ = swiglu_fp8_ref(R, I, s, fmt)
+    h_codes, gu = lib.gmm_fwd_swiglu_fp8(xq, wq, ws, gs, float(s), h_format=fmt, lhs_scales=sx,
+                                         gu=True)
+    assert h_codes.dtype == torch.uint8 and tuple(h_codes.shape) == (M, I)
+    plain = lib.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx)
+    assert torch.equal(gu.view(torch.int16), plain.view(torch.int16))
+    h_only = lib.gmm_fwd_swiglu_fp8(xq, wq, ws, gs, float(s), h_format=fmt, lhs_scales=sx)
+    assert torch.equal(h_only, h_codes)
+    codes = to_np(h_codes)
+    h, dh = swiglu_h_bound(R, absR, K, I)
+    diff, amb = assert_fp8_codes_in_band(codes, h, dh, s, fmt, ref_codes, min_exact=0.99)
+    print(f"{fmt}: codes differing from the oracle's {diff:.2e}, bands spanning two codes {amb:.2e}")
+    assert np.mean(np.abs(swiglu_ref(R, I)) / s >= qmax_of(fmt)) > 0  # saturation exercised
+    # the down projection on the codes, against the oracle's on its own codes
+    y = lib.gmm_fwd(h_codes, wdq, wds, gs, lhs_format=fmt, lhs_scaling="static",
+                    static_scale=float(s), out_dtype=torch.float32)
+    bd, bds = quantize_rhs_per_channel(wdb, "e4m3", "n")
+    Ry = gmm_fwd_ref(ref_codes, fmt, np.full(M, s, np.float32), bd, "e4m3", bds, sizes)
+    # one code step of slack wherever the GPU code differs from the oracle's
+    step = np.abs(decode_fp8(codes, fmt).astype(np.float64) -
+                  decode_fp8(ref_codes, fmt).astype(np.float64)) * s
+    wabs = np.abs(decode_fp8(bd, "e4m3").astype(np.float64)) * bds[:, None, :]
+    Y = to_np(y).astype(np.float64)
+    for g, (lo, hi) in enumerate(group_row_ranges(sizes)):
+        if hi == lo:
+            continue
+        allow = TOL * np.abs(Ry[lo:hi]).max() + step[lo:hi] @ wabs[g] * (1 + 1e-6)
+        assert np.all(np.abs(Y[lo:hi] - Ry[lo:hi]) <= allow), g

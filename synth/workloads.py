@@ -2,6 +2,9 @@
 
 Recipe (all seeded; seed = workload index unless a test passes its own):
 
+* routing (``topk_expert_ids``): every token draws k distinct experts without
+  replacement, with Zipf(s) popularity over a seeded permutation of the expert ids.
+
 * ``group_sizes`` (int32 [G], rows sorted by expert, sum = M):
   - tiny: multinomial(M, uniform) over 3 experts, placed in experts {0, 2, 3} so the
     empty expert 1 sits between two non-empty ones;
@@ -133,3 +136,20 @@ def log_uniform_scales(n, lo, hi, seed):
     """numpy float32 [n] with log10 uniform in [lo, hi), seeded (per-block scales)."""
     rng = np.random.default_rng(int(seed))
     return (10.0 ** rng.uniform(lo, hi, size=n)).astype(np.float32)
+
+
+def topk_expert_ids(T, k, G, s, seed, drop=0.0):
+    """int32 [T, k]: each token's k distinct experts, drawn without replacement with
+    Zipf(s) popularity (rank i weighted i^-s, ranks assigned to expert ids by a seeded
+    permutation), in drawn order.  A fraction ``drop`` of the slots, chosen at random,
+    is set to -1 (a dropped choice)."""
+    rng = np.random.default_rng(int(seed))
+    w = 1.0 / np.arange(1, G + 1, dtype=np.float64) ** s
+    p = np.zeros(G)
+    p[rng.permutation(G)] = w / w.sum()
+    # Gumbel top-k: the k largest of log p + Gumbel noise, a draw without replacement
+    keys = np.log(p)[None, :] + rng.gumbel(size=(T, G))
+    ids = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    if drop > 0:
+        ids[rng.random((T, k)) < drop] = -1
+    return ids

@@ -11,8 +11,11 @@ Modules
 fp8    OCP E4M3FN / E5M2 and bfloat16 codecs, written from the format definitions.
 quant  in-kernel lhs quantization (static per-tensor, dynamic per-128-row block) and
        the per-channel weight quantization used to prepare the pre-quantized rhs.
-gmm    the three grouped products: gmm forward, gmm dlhs and the transposed tgmm.
+gmm    the three grouped products: gmm forward, gmm dlhs and the transposed tgmm, and
+       their local-expert windows.
 swiglu SwiGLU of the merged gate|up product, forward and backward.
+route  token routing around the products: the stable sort by expert, the row gather and
+       the weighted combine.
 
 Sources (the MaxText pull-request pages this method is taken from):
   * "FP8 Megablox for batch split" (PR #3770), Description (1) and (2): fp8 recipes
@@ -45,8 +48,12 @@ from .quant import (  # noqa: F401
 )
 from .gmm import (  # noqa: F401
     group_offsets,
+    gmm_dlhs_local_ref,
     gmm_dlhs_ref,
+    gmm_fwd_local_ref,
     gmm_fwd_ref,
+    tgmm_local_ref,
     tgmm_ref,
 )
+from .route import gather_rows_ref, permute_ref, unpermute_ref  # noqa: F401
 from .swiglu import silu, swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref  # noqa: F401

@@ -20,9 +20,16 @@ in the order (acc * s_row) * s_col; in tgmm the scales vary along the contractio
 before it is added.  Empty groups contribute no rows (gmm, dlhs) or an all-zero slab
 (tgmm).
 
+Local-expert window ("FP8 Megablox for batch split", the referencing commit's
+Description item 3: the group_offset of the ragged products): with G_local experts from
+group_offset on, group_sizes still lists every expert and the rows stay sorted by
+expert; only the rows of the local experts are multiplied (by the local rhs), the other
+output rows are zero, and tgmm yields the local experts' slabs.
+
 Parity: pinned by brute force with exact rationals on tiny inputs, by float64 dense
 loops over experts, by sums of per-row outer products and by the invariants listed in
-``tests/test_oracle_gmm.py``.
+``tests/test_oracle_gmm.py``; the windows by the full window (the plain products) and
+by disjoint windows that tile the experts adding up to the plain products.
 """
 
 import numpy as np
@@ -134,3 +141,39 @@ def tgmm_ref(a_codes, a_fmt, a_scale_blk, g_codes, g_fmt, g_scale_blk, group_siz
 def row_scales(scales_blk, M, block_rows=128):
     """Expand one scale per row block to one scale per row."""
     return np.repeat(np.asarray(scales_blk, np.float32), block_rows)[:M]
+
+
+def _window_rows(group_sizes, group_offset, G_local):
+    off = group_offsets(group_sizes)
+    sizes = np.asarray(group_sizes, np.int64)[group_offset:group_offset + G_local]
+    return int(off[group_offset]), int(off[group_offset + G_local]), sizes
+
+
+def gmm_fwd_local_ref(a_codes, a_fmt, a_scale_row, b_codes_local, b_fmt, b_scale_local,
+                      group_sizes, group_offset, out_dtype="f32"):
+    """gmm_fwd_ref over the window of len(b_codes_local) experts from group_offset on;
+    rows of the other experts are zero."""
+    lo, hi, sizes = _window_rows(group_sizes, group_offset, b_codes_local.shape[0])
+    out = np.zeros((a_codes.shape[0], b_codes_local.shape[2]), np.float32)
+    out[lo:hi] = gmm_fwd_ref(a_codes[lo:hi], a_fmt, np.asarray(a_scale_row)[lo:hi],
+                             b_codes_local, b_fmt, b_scale_local, sizes)
+    return _finish(out, out_dtype)
+
+
+def gmm_dlhs_local_ref(g_codes, g_fmt, g_scale_row, b_codes_local, b_fmt, b_scale_k_local,
+                       group_sizes, group_offset, out_dtype="f32"):
+    """gmm_dlhs_ref over the window (as gmm_fwd_local_ref); out [M, K]."""
+    lo, hi, sizes = _window_rows(group_sizes, group_offset, b_codes_local.shape[0])
+    out = np.zeros((g_codes.shape[0], b_codes_local.shape[1]), np.float32)
+    out[lo:hi] = gmm_dlhs_ref(g_codes[lo:hi], g_fmt, np.asarray(g_scale_row)[lo:hi],
+                              b_codes_local, b_fmt, b_scale_k_local, sizes)
+    return _finish(out, out_dtype)
+
+
+def tgmm_local_ref(a_codes, a_fmt, a_scale_blk, g_codes, g_fmt, g_scale_blk, group_sizes,
+                   group_offset, G_local, block_rows=128, out_dtype="f32"):
+    """The slabs group_offset .. group_offset + G_local - 1 of tgmm_ref (the 128-row scale
+    blocks stay aligned to the global row index)."""
+    full = tgmm_ref(a_codes, a_fmt, a_scale_blk, g_codes, g_fmt, g_scale_blk, group_sizes,
+                    block_rows, "f32")
+    return _finish(full[group_offset:group_offset + G_local], out_dtype)

@@ -249,3 +249,38 @@ def test_group_sizes_validation():
     with pytest.raises(ValueError):
         group_offsets([3, 1, 2], M=7)
     assert group_offsets([0, 0, 5], 5).tolist() == [0, 0, 0, 5]
+
+
+def test_local_windows_tile_the_plain_products(medium):
+    """Local-expert windows: the full window is the plain product; windows that tile the
+    experts (each zero outside its rows) add up to it exactly; tgmm windows are its slabs."""
+    from oracle.gmm import gmm_dlhs_local_ref, gmm_fwd_local_ref, tgmm_local_ref
+    from oracle.quant import quantize_rowblock
+
+    d = medium
+    M, G = d["M"], d["G"]
+    wq, ws = quantize_rhs_per_channel(d["w"], "e4m3", "n")
+    wk, sk = quantize_rhs_per_channel(d["w"], "e4m3", "k")
+    aq, sa, _ = quantize_rowblock(d["lhs"], "e4m3")
+    gq, sg, _ = quantize_rowblock(d["grad"], "e5m2")
+    ra, rg = row_scales(sa, M), row_scales(sg, M)
+    plain_f = gmm_fwd_ref(aq, "e4m3", ra, wq, "e4m3", ws, d["gs"])
+    plain_d = gmm_dlhs_ref(gq, "e5m2", rg, wk, "e4m3", sk, d["gs"])
+    plain_t = tgmm_ref(aq, "e4m3", sa, gq, "e5m2", sg, d["gs"])
+    assert np.array_equal(gmm_fwd_local_ref(aq, "e4m3", ra, wq, "e4m3", ws, d["gs"], 0), plain_f)
+    for cuts in ([0, 2, 5], [0, 1, 2, 3, 4, 5], [0, 3, 5]):
+        sum_f = np.zeros_like(plain_f)
+        sum_d = np.zeros_like(plain_d)
+        slabs = []
+        off = group_offsets(d["gs"], M)
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            f = gmm_fwd_local_ref(aq, "e4m3", ra, wq[a:b], "e4m3", ws[a:b], d["gs"], a)
+            dl = gmm_dlhs_local_ref(gq, "e5m2", rg, wk[a:b], "e4m3", sk[a:b], d["gs"], a)
+            outside = np.ones(M, bool)
+            outside[off[a]:off[b]] = False
+            assert not f[outside].any() and not dl[outside].any()
+            sum_f += f
+            sum_d += dl
+            slabs.append(tgmm_local_ref(aq, "e4m3", sa, gq, "e5m2", sg, d["gs"], a, b - a))
+        assert np.array_equal(sum_f, plain_f) and np.array_equal(sum_d, plain_d)
+        assert np.array_equal(np.concatenate(slabs), plain_t)

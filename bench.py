@@ -296,6 +296,60 @@ def swiglu_block(g, reps=10):
     return res
 
 
+def route_block(g, reps=10):
+    """Token routing at the moe_swiglu shape (8192 tokens x top-8 of 64 experts, Zipf(1.3)
+    popularity, hidden 2048): gmm_permute of bf16 rows and of e4m3 codes, and the weighted
+    gmm_unpermute, each against HBM peak on its algorithmic bytes (x read once, every
+    permuted row written once, the index arrays)."""
+    import torch
+
+    from synth.workloads import WORKLOADS, normal_bf16, topk_expert_ids
+
+    wl = WORKLOADS["moe_swiglu"]
+    G, H, k = wl.G, wl.K, 8
+    T = wl.M // k
+    ids = torch.as_tensor(topk_expert_ids(T, k, G, wl.zipf_s, wl.seed), device="cuda")
+    x = normal_bf16((T, H), 1.0, wl.seed * 100 + 7, "cuda")
+    codes, _ = g.gmm_quantize(x, "e4m3", "static", static_scale=4.0 / 448.0)
+    xp, gs, ros, sor = g.gmm_permute(ids, G, x)
+    cp = torch.empty((T * k, H), dtype=torch.uint8, device="cuda")
+    w = torch.rand((T, k), device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_perm = timed(lambda: g.gmm_permute(ids, G, x, xp))
+    t_perm8 = timed(lambda: g.gmm_permute(ids, G, codes, cp))
+    t_idx = timed(lambda: g.gmm_permute(ids, G))
+    t_comb = timed(lambda: g.gmm_unpermute(xp, ros, w, out))
+    n = T * k
+    idx_bytes = 12.0 * n
+    perm_b = T * H * 2.0 + n * H * 2.0 + idx_bytes
+    perm8_b = T * H * 1.0 + n * H * 1.0 + idx_bytes
+    comb_b = n * H * 2.0 + T * H * 2.0 + 8.0 * n
+
+    def rate(b, t):
+        return {"ms": round(t, 4), "GB/s": round(b / t / 1e6, 1),
+                "frac_hbm": round(b / t / 1e6 / 8000.0, 4)}
+
+    res = {"workload": wl.name, "tokens": T, "top_k": k, "G": G, "hidden": H,
+           "permute_bf16": rate(perm_b, t_perm), "permute_e4m3": rate(perm8_b, t_perm8),
+           "permute_index_only_ms": round(t_idx, 4), "unpermute": rate(comb_b, t_comb)}
+    del ids, x, codes, xp, gs, ros, sor, cp, w, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(step, rows, cols):
     """Time the CPU oracle on a bounded sample: the first `rows` rows (with their group
     split), all K, the first `cols` columns of the merged weight; fwd + dlhs + tgmm."""
@@ -428,6 +482,7 @@ def main():
     }
     if not args.no_swiglu:
         line["swiglu_block"] = swiglu_block(g)
+        line["route_block"] = route_block(g)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)
     print(json.dumps(line), flush=True)

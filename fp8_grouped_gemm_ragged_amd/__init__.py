@@ -19,6 +19,7 @@ import os
 __all__ = [
     "load", "library_path", "GmmError", "gmm_fwd", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
     "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8", "gmm_swiglu_bwd",
+    "gmm_permute", "gmm_unpermute", "gmm_fwd_local", "gmm_dlhs_local", "tgmm_drhs_local",
     "gmm_quantize_rhs", "gmm_static_scale_from_bound", "gmm_workspace_size",
     "gmm_status_string", "gmm_version", "E4M3", "E5M2", "STATIC", "DYNAMIC", "BLOCK_ROWS",
 ]
@@ -67,6 +68,12 @@ _SIGNATURES = {
     "gmm_fwd_swiglu": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_fwd_swiglu_fp8": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _OPP, _P, _P, _SZ, _P],
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
+    "gmm_permute_workspace_size": [_I64, _I32, _I32],
+    "gmm_fwd_local": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_dlhs_local": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "tgmm_drhs_local": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_permute": [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_unpermute": [_I64, _I32, _I64, _P, _P, _P, _P, _P],
     "gmm_workspace_size": [_I32, _OPP, _OPP, _I64, _I64, _I64, _I32, ctypes.POINTER(_SZ)],
     "gmm_dynamic_scales": [_I32, _I64, _I64, _P, _P, _P, _SZ, _P],
     "gmm_quantize": [_OPP, _I64, _I64, _P, _P, _P, _P, _SZ, _P],
@@ -96,7 +103,8 @@ def load(path=None):
     for name, args in _SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name in ("gmm_status_string", "gmm_version") else ctypes.c_int32
+        fn.restype = (ctypes.c_char_p if name in ("gmm_status_string", "gmm_version") else
+                      ctypes.c_size_t if name == "gmm_permute_workspace_size" else ctypes.c_int32)
     _lib = lib
     return lib
 
@@ -174,7 +182,7 @@ def _nblocks(rows):
 
 
 def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_scales,
-          rhs_layout, out_dtype, out, contraction_dim, out_cols, fused):
+          rhs_layout, out_dtype, out, contraction_dim, out_cols, fused, group_offset=None):
     import torch
 
     lib = load()
@@ -215,10 +223,18 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
     _check(lib.gmm_workspace_size(wop, ctypes.byref(op), ctypes.byref(op), M, K_or_N, n_out, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, a.device)
-    fn = getattr(lib, cname)
-    _check(fn(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], OUT_F32 if odt == torch.float32 else OUT_BF16,
-              M, K, N, G, _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales), _ptr(group_sizes),
-              _ptr(out), _ptr(ws), ws_n.value, _stream()), cname)
+    odt_code = OUT_F32 if odt == torch.float32 else OUT_BF16
+    if group_offset is None:
+        _check(getattr(lib, cname)(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], odt_code, M, K, N,
+                                   G, _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales),
+                                   _ptr(group_sizes), _ptr(out), _ptr(ws), ws_n.value, _stream()),
+               cname)
+    else:
+        # local-expert window: rhs holds the G experts from group_offset on
+        _check(getattr(lib, cname + "_local")(
+            ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], odt_code, M, K, N, group_sizes.shape[0],
+            int(group_offset), G, _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales),
+            _ptr(group_sizes), _ptr(out), _ptr(ws), ws_n.value, _stream()), cname + "_local")
     return out, a_scales
 
 
@@ -240,6 +256,27 @@ def gmm_fwd(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3", lhs_scaling
     return (o, s) if return_scales else o
 
 
+def gmm_fwd_local(lhs, rhs, rhs_scales, group_sizes, group_offset, *, lhs_format="e4m3",
+                  lhs_scaling="dynamic", static_scale=None, lhs_scales=None, rhs_layout="nk",
+                  out_dtype=None, out=None, return_scales=False, fused=False):
+    """gmm_fwd over a local-expert window: group_sizes has every expert, rhs / rhs_scales the
+    rhs.shape[0] local ones from group_offset on; rows of other experts come out zero."""
+    o, s = _gemm("gmm_fwd", lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
+                 static_scale, lhs_scales, rhs_layout, out_dtype, out, "K", "N", fused,
+                 group_offset)
+    return (o, s) if return_scales else o
+
+
+def gmm_dlhs_local(grad, rhs, rhs_scales, group_sizes, group_offset, *, grad_format="e5m2",
+                   grad_scaling="dynamic", static_scale=None, grad_scales=None,
+                   rhs_layout="kn", out_dtype=None, out=None, return_scales=False, fused=False):
+    """gmm_dlhs over a local-expert window (as gmm_fwd_local)."""
+    o, s = _gemm("gmm_dlhs", grad, rhs, rhs_scales, group_sizes, grad_format, grad_scaling,
+                 static_scale, grad_scales, rhs_layout, out_dtype, out, "N", "K", fused,
+                 group_offset)
+    return (o, s) if return_scales else o
+
+
 def gmm_dlhs(grad, rhs, rhs_scales, group_sizes, *, grad_format="e5m2", grad_scaling="dynamic",
              static_scale=None, grad_scales=None, rhs_layout="kn", out_dtype=None, out=None,
              return_scales=False, fused=False):
@@ -250,10 +287,16 @@ def gmm_dlhs(grad, rhs, rhs_scales, group_sizes, *, grad_format="e5m2", grad_sca
     return (o, s) if return_scales else o
 
 
+def tgmm_drhs_local(lhs, grad, group_sizes, group_offset, num_local, **kw):
+    """tgmm_drhs over a local-expert window: drhs [num_local, K, N] for the experts
+    group_offset .. group_offset + num_local - 1 of group_sizes."""
+    return tgmm_drhs(lhs, grad, group_sizes, _window=(int(group_offset), int(num_local)), **kw)
+
+
 def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic",
               lhs_static_scale=None, lhs_scales=None, grad_format="e5m2",
               grad_scaling="dynamic", grad_static_scale=None, grad_scales=None,
-              out_dtype=None, out=None, return_scales=False):
+              out_dtype=None, out=None, return_scales=False, _window=None):
     """Weight gradient: drhs[g] = q(lhs)_g^T . q(grad)_g, [G, K, N]; empty groups give zeros.
 
     lhs / grad are bf16 values, or uint8 fp8 codes quantized beforehand (then their
@@ -270,7 +313,8 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
     if grad.shape[0] != M:
         raise ValueError("lhs and grad must have the same number of rows")
     N = grad.shape[1]
-    G = group_sizes.shape[0]
+    G_total = group_sizes.shape[0]
+    offset, G = _window if _window else (0, G_total)
     odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((G, K, N), dtype=odt, device=lhs.device)
@@ -294,9 +338,16 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
     _check(lib.gmm_workspace_size(OP_TGMM, ctypes.byref(aop), ctypes.byref(bop), M, K, N, G,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, lhs.device)
-    _check(lib.tgmm_drhs(ctypes.byref(aop), ctypes.byref(bop), OUT_F32 if odt == torch.float32 else OUT_BF16,
-                         M, K, N, G, _ptr(lhs), _ptr(sa), _ptr(grad), _ptr(sg), _ptr(group_sizes),
-                         _ptr(out), _ptr(ws), ws_n.value, _stream()), "tgmm_drhs")
+    odt_code = OUT_F32 if odt == torch.float32 else OUT_BF16
+    if _window:
+        _check(lib.tgmm_drhs_local(ctypes.byref(aop), ctypes.byref(bop), odt_code, M, K, N, G_total,
+                                   offset, G, _ptr(lhs), _ptr(sa), _ptr(grad), _ptr(sg),
+                                   _ptr(group_sizes), _ptr(out), _ptr(ws), ws_n.value, _stream()),
+               "tgmm_drhs_local")
+    else:
+        _check(lib.tgmm_drhs(ctypes.byref(aop), ctypes.byref(bop), odt_code, M, K, N, G, _ptr(lhs),
+                             _ptr(sa), _ptr(grad), _ptr(sg), _ptr(group_sizes), _ptr(out),
+                             _ptr(ws), ws_n.value, _stream()), "tgmm_drhs")
     return (out, sa, sg) if return_scales else out
 
 
@@ -455,3 +506,62 @@ def gmm_quantize_rhs(w, fmt="e4m3", channel_axis=0, layout="kn"):
     _check(lib.gmm_quantize_rhs(_FMT[fmt], int(channel_axis), _LAYOUT[layout], G, K, N, _ptr(w),
                                 _ptr(codes), _ptr(scales), _stream()), "gmm_quantize_rhs")
     return codes, scales
+
+
+def gmm_permute(expert_ids, num_groups, x=None, x_perm=None):
+    """Sort token slots by expert: expert_ids int32 [T, k] (ids outside [0, num_groups) are
+    dropped).  Returns (group_sizes [G], row_of_slot [T, k], slot_of_row [T * k]) and, when
+    x ([T, ...], any dtype, 16-byte rows) is given, x_perm [T * k, ...] first: row r holds
+    x[slot_of_row[r] // k]; rows past sum(group_sizes) are left as allocated."""
+    import torch
+
+    lib = load()
+    _need(expert_ids, torch.int32, "expert_ids", 2)
+    T, k = expert_ids.shape
+    G = int(num_groups)
+    dev = expert_ids.device
+    gs = torch.empty(G, dtype=torch.int32, device=dev)
+    ros = torch.empty((T, k), dtype=torch.int32, device=dev)
+    sor = torch.empty(T * k, dtype=torch.int32, device=dev)
+    row_bytes = 0
+    if x is not None:
+        if x.device != dev or not x.is_contiguous() or x.shape[0] != T:
+            raise ValueError("x must be a contiguous [T, ...] tensor on the ids' device")
+        row_bytes = x.element_size()
+        for d in x.shape[1:]:
+            row_bytes *= int(d)
+        if x_perm is None:
+            x_perm = torch.empty((T * k,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+        elif (x_perm.dtype != x.dtype or tuple(x_perm.shape) != (T * k,) + tuple(x.shape[1:])
+              or not x_perm.is_contiguous() or x_perm.device != dev):
+            raise ValueError("x_perm must be a contiguous [T * k, ...] tensor of x's dtype")
+    ws_n = lib.gmm_permute_workspace_size(T, k, G)
+    ws = _workspace(ws_n, dev)
+    _check(lib.gmm_permute(T, k, G, _ptr(expert_ids), row_bytes, _ptr(x), _ptr(x_perm), _ptr(gs),
+                           _ptr(ros), _ptr(sor), _ptr(ws), ws_n, _stream()), "gmm_permute")
+    return (x_perm, gs, ros, sor) if x is not None else (gs, ros, sor)
+
+
+def gmm_unpermute(y, row_of_slot, weights=None, out=None):
+    """out [T, H] bf16 = sum over j of weights[t, j] * y[row_of_slot[t, j]] (fp32 in j order;
+    dropped slots skipped); y bf16 [T * k, H]; weights f32 [T, k] or None (all 1)."""
+    import torch
+
+    lib = load()
+    _need(y, torch.bfloat16, "y", 2)
+    _need(row_of_slot, torch.int32, "row_of_slot", 2)
+    T, k = row_of_slot.shape
+    H = y.shape[1]
+    if y.shape[0] != T * k:
+        raise ValueError("y must have T * k rows")
+    if weights is not None:
+        _need(weights, torch.float32, "weights", 2)
+        if tuple(weights.shape) != (T, k):
+            raise ValueError("weights must be [T, k]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+    _check(lib.gmm_unpermute(T, k, H, _ptr(y), _ptr(row_of_slot), _ptr(weights), _ptr(out),
+                             _stream()), "gmm_unpermute")
+    return out

@@ -157,9 +157,12 @@ size_t quant_once_bytes(int64_t M, int64_t Kc) { return align256((size_t)M * Kc)
 bool quant_once_applies(int64_t Nout) { return Nout <= 0 || (Nout + 255) / 256 >= QUANT_ONCE_MIN_TILES; }
 
 // Shared body of gmm_fwd / gmm_dlhs: out[M, Nout] = A[M, Kc] x B.
+// The products run over the window of G groups that follows the first g_before of the
+// G_total in group_sizes; output rows outside the window are zero-filled.
 gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rhs_format,
                           bool b_trans, int32_t out_dtype, int64_t M, int64_t Kc,
-                          int64_t Nout, int32_t G, const void* a, float* a_scales,
+                          int64_t Nout, int32_t G_total, int32_t g_before, int32_t G,
+                          const void* a, float* a_scales,
                           const uint8_t* rhs, const float* rhs_scales,
                           const int32_t* group_sizes, void* out, void* workspace,
                           size_t workspace_bytes, hipStream_t st, bool swiglu = false,
@@ -173,7 +176,9 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   }
   if (rhs_format != GMM_FP8_E4M3) return GMM_ERR_RECIPE;  // weights are e4m3 codes
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
-  if ((s = check_shape(M, Kc, Nout, G)) != GMM_OK) return s;
+  if ((s = check_shape(M, Kc, Nout, G_total)) != GMM_OK) return s;
+  if (g_before < 0 || G < 1 || g_before > G_total - G) return GMM_ERR_SHAPE;
+  const bool window = G != G_total;
   // SwiGLU: Nout = 2 I channels, I a multiple of 128, contraction-contiguous weights
   if (swiglu && (Nout % 256 || b_trans)) return swiglu && b_trans ? GMM_ERR_RECIPE : GMM_ERR_SHAPE;
   // the kernels number output tiles with 32-bit integers
@@ -202,22 +207,31 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   const size_t as_bytes = (size_t)nblocks(M) * 4;
   if (overlaps(out, out_bytes, a, a_bytes) || overlaps(out, out_bytes, rhs, b_bytes) ||
       overlaps(out, out_bytes, rhs_scales, (size_t)G * Nout * 4) ||
-      overlaps(out, out_bytes, group_sizes, (size_t)G * 4) ||
+      overlaps(out, out_bytes, group_sizes, (size_t)G_total * 4) ||
       (needs_dyn_ws(aop) && overlaps(a_scales, as_bytes, a, a_bytes)) ||
       overlaps(workspace, ws_used, a, a_bytes) || overlaps(workspace, ws_used, out, out_bytes) ||
       overlaps(workspace, ws_used, a_scales, as_bytes))
     return GMM_ERR_ALIAS;
   if (gu_bytes && (overlaps(gu, gu_bytes, a, a_bytes) || overlaps(gu, gu_bytes, rhs, b_bytes) ||
                    overlaps(gu, gu_bytes, rhs_scales, (size_t)G * Nout * 4) ||
-                   overlaps(gu, gu_bytes, group_sizes, (size_t)G * 4) ||
+                   overlaps(gu, gu_bytes, group_sizes, (size_t)G_total * 4) ||
                    overlaps(gu, gu_bytes, out, out_bytes) ||
                    overlaps(gu, gu_bytes, workspace, ws_used) ||
                    overlaps(gu, gu_bytes, a_scales, as_bytes)))
     return GMM_ERR_ALIAS;
   if (gu && !aligned16(gu)) return GMM_ERR_ALIGN;
-  if ((s = check_group_sizes(group_sizes, G, M, st)) != GMM_OK) return s;
+  if ((s = check_group_sizes(group_sizes, G_total, M, st)) != GMM_OK) return s;
   trace(name, M, Kc, Nout, G);
   if (M == 0) return GMM_OK;
+  if (window) {
+    // rows of the groups outside the window hold zeros (h and gu of the SwiGLU forward too)
+    const int64_t esz = h_op ? 1 : (int64_t)esize;
+    if (launch_zero_rows_outside(out, M, (swiglu ? Nout / 2 : Nout) * esz, group_sizes, g_before,
+                                 G, st) != hipSuccess ||
+        (gu_bytes && launch_zero_rows_outside(gu, M, Nout * (int64_t)esize, group_sizes, g_before,
+                                              G, st) != hipSuccess))
+      return GMM_ERR_HIP;
+  }
 
   GemmParams p{};
   p.a = a;
@@ -229,6 +243,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.Kc = (int32_t)Kc;
   p.Nout = (int32_t)Nout;
   p.G = G;
+  p.g_before = g_before;
   p.out_f32 = out_dtype == GMM_OUT_F32;
   p.gu = gu;
   if (h_op) {
@@ -266,8 +281,20 @@ gmm_status_t gmm_fwd(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rh
   if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
   // forward contracts over K: contiguous when the codes are stored [G, N, K]
   return grouped_gemm("gmm_fwd", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN, out_dtype, M, K,
-                      N, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes, out, workspace,
+                      N, G, 0, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes, out, workspace,
                       workspace_bytes, (hipStream_t)stream);
+}
+
+gmm_status_t gmm_fwd_local(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                           int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G_total,
+                           int32_t group_offset, int32_t G_local, const void* lhs,
+                           float* lhs_scales, const uint8_t* rhs, const float* rhs_scales,
+                           const int32_t* group_sizes, void* out, void* workspace,
+                           size_t workspace_bytes, gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  return grouped_gemm("gmm_fwd_local", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN, out_dtype,
+                      M, K, N, G_total, group_offset, G_local, lhs, lhs_scales, rhs, rhs_scales,
+                      group_sizes, out, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
@@ -278,8 +305,21 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
   if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
   // dlhs contracts over N: contiguous when the codes are stored [G, K, N]
   return grouped_gemm("gmm_dlhs", grad_op, rhs_format, rhs_layout == GMM_RHS_NK, out_dtype, M,
-                      N, K, G, grad, grad_scales, rhs, rhs_scales, group_sizes, dlhs, workspace,
-                      workspace_bytes, (hipStream_t)stream);
+                      N, K, G, 0, G, grad, grad_scales, rhs, rhs_scales, group_sizes, dlhs,
+                      workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+gmm_status_t gmm_dlhs_local(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
+                            int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G_total,
+                            int32_t group_offset, int32_t G_local, const void* grad,
+                            float* grad_scales, const uint8_t* rhs, const float* rhs_scales,
+                            const int32_t* group_sizes, void* dlhs, void* workspace,
+                            size_t workspace_bytes, gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  return grouped_gemm("gmm_dlhs_local", grad_op, rhs_format, rhs_layout == GMM_RHS_NK,
+                      out_dtype, M, N, K, G_total, group_offset, G_local, grad, grad_scales, rhs,
+                      rhs_scales, group_sizes, dlhs, workspace, workspace_bytes,
+                      (hipStream_t)stream);
 }
 
 gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
@@ -291,8 +331,8 @@ gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int
   if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
   if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
   return grouped_gemm("gmm_fwd_swiglu", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN,
-                      out_dtype, M, K, 2 * I, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes,
-                      h, workspace, workspace_bytes, (hipStream_t)stream, true, gu);
+                      out_dtype, M, K, 2 * I, G, 0, G, lhs, lhs_scales, rhs, rhs_scales,
+                      group_sizes, h, workspace, workspace_bytes, (hipStream_t)stream, true, gu);
 }
 
 gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
@@ -306,8 +346,69 @@ gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
   if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
   if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
   return grouped_gemm("gmm_fwd_swiglu_fp8", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN,
-                      gu_dtype, M, K, 2 * I, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes,
-                      h_codes, workspace, workspace_bytes, (hipStream_t)stream, true, gu, h_op);
+                      gu_dtype, M, K, 2 * I, G, 0, G, lhs, lhs_scales, rhs, rhs_scales,
+                      group_sizes, h_codes, workspace, workspace_bytes, (hipStream_t)stream, true,
+                      gu, h_op);
+}
+
+size_t gmm_permute_workspace_size(int64_t T, int32_t k, int32_t G) {
+  if (T < 0 || k < 1 || G < 1) return 0;
+  return align256((size_t)route_chunks(T * k) * (G + 1) * 4);
+}
+
+gmm_status_t gmm_permute(int64_t T, int32_t k, int32_t G, const int32_t* expert_ids,
+                         int64_t row_bytes, const void* x, void* x_perm, int32_t* group_sizes,
+                         int32_t* row_of_slot, int32_t* slot_of_row, void* workspace,
+                         size_t workspace_bytes, gmm_stream_t stream) {
+  if (T < 0 || k < 1 || k > 64 || G < 1 || G > GMM_MAX_GROUPS) return GMM_ERR_SHAPE;
+  const int64_t n = T * k;
+  if (n >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  if (!group_sizes || (n > 0 && (!expert_ids || !row_of_slot || !slot_of_row)))
+    return GMM_ERR_NULL;
+  if ((x == nullptr) != (x_perm == nullptr)) return GMM_ERR_NULL;
+  if (x && (row_bytes <= 0 || row_bytes % 16)) return GMM_ERR_SHAPE;
+  for (const void* ptr : {(const void*)expert_ids, x, (const void*)x_perm, (const void*)group_sizes,
+                          (const void*)row_of_slot, (const void*)slot_of_row, (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t ws_need = gmm_permute_workspace_size(T, k, G);
+  if (ws_need && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
+  const size_t ib = (size_t)n * 4, xb = x ? (size_t)T * row_bytes : 0,
+               pb = x ? (size_t)n * row_bytes : 0, gb = (size_t)G * 4;
+  // every output against every input and every other output
+  const struct { const void* p; size_t n; } outs[] = {
+      {x_perm, pb}, {group_sizes, gb}, {row_of_slot, ib}, {slot_of_row, ib}, {workspace, ws_need}};
+  for (size_t i = 0; i < 5; ++i) {
+    if (overlaps(outs[i].p, outs[i].n, expert_ids, ib) || overlaps(outs[i].p, outs[i].n, x, xb))
+      return GMM_ERR_ALIAS;
+    for (size_t j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return GMM_ERR_ALIAS;
+  }
+  trace("gmm_permute", T, k, row_bytes, G);
+  return launch_route(expert_ids, n, k, G, (int32_t*)workspace, group_sizes, row_of_slot,
+                      slot_of_row, x, row_bytes, x_perm, (hipStream_t)stream) == hipSuccess
+             ? GMM_OK
+             : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_unpermute(int64_t T, int32_t k, int64_t H, const void* y,
+                           const int32_t* row_of_slot, const float* weights, void* out,
+                           gmm_stream_t stream) {
+  if (T < 0 || k < 1 || k > 64 || H <= 0 || H % 8 || H > MAX_DIM) return GMM_ERR_SHAPE;
+  const int64_t n = T * k;
+  if (n >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  if (T == 0) return GMM_OK;
+  if (!y || !row_of_slot || !out) return GMM_ERR_NULL;
+  for (const void* ptr : {y, (const void*)row_of_slot, (const void*)weights, (const void*)out})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t ob = (size_t)T * H * 2;
+  if (overlaps(out, ob, y, (size_t)n * H * 2) || overlaps(out, ob, row_of_slot, (size_t)n * 4) ||
+      overlaps(out, ob, weights, weights ? (size_t)n * 4 : 0))
+    return GMM_ERR_ALIAS;
+  trace("gmm_unpermute", T, k, H, 1);
+  return launch_combine((const uint16_t*)y, T, k, H, n, row_of_slot, weights, (uint16_t*)out,
+                        (hipStream_t)stream) == hipSuccess
+             ? GMM_OK
+             : GMM_ERR_HIP;
 }
 
 gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu, void* d_gu,
@@ -329,11 +430,22 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
                        const void* lhs, float* lhs_scales, const void* grad,
                        float* grad_scales, const int32_t* group_sizes, void* drhs,
                        void* workspace, size_t workspace_bytes, gmm_stream_t stream) {
+  return tgmm_drhs_local(lhs_op, grad_op, out_dtype, M, K, N, G, 0, G, lhs, lhs_scales, grad,
+                         grad_scales, group_sizes, drhs, workspace, workspace_bytes, stream);
+}
+
+gmm_status_t tgmm_drhs_local(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
+                             int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G_total,
+                             int32_t group_offset, int32_t G, const void* lhs, float* lhs_scales,
+                             const void* grad, float* grad_scales, const int32_t* group_sizes,
+                             void* drhs, void* workspace, size_t workspace_bytes,
+                             gmm_stream_t stream) {
   gmm_status_t s;
   if ((s = check_operand(lhs_op)) != GMM_OK) return s;
   if ((s = check_operand(grad_op)) != GMM_OK) return s;
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
-  if ((s = check_shape(M, K, N, G)) != GMM_OK) return s;
+  if ((s = check_shape(M, K, N, G_total)) != GMM_OK) return s;
+  if (group_offset < 0 || G < 1 || group_offset > G_total - G) return GMM_ERR_SHAPE;
   // 32-bit tile numbers, and byte offsets inside a 256-row slice of a transposed segment
   if (((K + 255) / 256) * ((N + 255) / 256) * G >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
   if (256 * tgmm_segment_row_bytes(M, G) >= (int64_t(1) << 32)) return GMM_ERR_SHAPE;
@@ -355,7 +467,7 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
   const size_t grad_bytes = (size_t)M * N * (g_codes ? 1 : 2);
   const size_t sc_bytes = (size_t)nblocks(M) * 4;
   if (overlaps(drhs, out_bytes, lhs, lhs_bytes) || overlaps(drhs, out_bytes, grad, grad_bytes) ||
-      overlaps(drhs, out_bytes, group_sizes, (size_t)G * 4) ||
+      overlaps(drhs, out_bytes, group_sizes, (size_t)G_total * 4) ||
       overlaps(drhs, out_bytes, lhs_scales, sc_bytes) ||
       overlaps(drhs, out_bytes, grad_scales, sc_bytes) ||
       overlaps(workspace, wa + wb + wt, drhs, out_bytes) ||
@@ -364,7 +476,7 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
       overlaps(workspace, wa + wb + wt, lhs_scales, sc_bytes) ||
       overlaps(workspace, wa + wb + wt, grad_scales, sc_bytes))
     return GMM_ERR_ALIAS;
-  if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
+  if ((s = check_group_sizes(group_sizes, G_total, M, (hipStream_t)stream)) != GMM_OK) return s;
   trace("tgmm_drhs", M, K, N, G);
   hipStream_t st = (hipStream_t)stream;
 
@@ -379,6 +491,7 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
   p.Kout = (int32_t)K;
   p.Nout = (int32_t)N;
   p.G = G;
+  p.g_before = group_offset;
   p.out_f32 = out_dtype == GMM_OUT_F32;
   {
     uint8_t* base = (uint8_t*)workspace + wa + wb;

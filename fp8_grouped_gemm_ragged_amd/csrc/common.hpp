@@ -72,6 +72,18 @@ __device__ inline uint32_t cvt_pk(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
 }
 
+// An fp32 product and an fp32 sum, each rounded to nearest on its own: never contracted
+// into a fused multiply-add (HIP's __fmul_rn / __fadd_rn are plain operators, which the
+// compiler fuses under its default contraction).
+__device__ inline float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ inline float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
 // Inverse of a dynamic scale: RNE_f32(1/s), or 0 when s == 0 or 1/s is not finite.
 __device__ inline float inv_from_scale(float s) {
   const float r = __fdiv_rn(1.0f, s);

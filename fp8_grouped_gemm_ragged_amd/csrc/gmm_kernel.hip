@@ -26,6 +26,8 @@
 //     interleaved between the MFMAs, so vector ALU and matrix core run concurrently;
 //   * epilogue: (acc * s_A(m)) * s_B(n), RNE to bf16 (or f32), stored only for rows
 //     inside the group and columns inside N.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace gmm {
@@ -47,18 +49,31 @@ struct TileCoord {
   int g, row0, row_end, n0;
 };
 
-// Per-group prefix sums into LDS (first wave): s_tile_cum[g] = M-tiles of groups < g,
-// s_row_off[g] = rows of groups < g.  The caller synchronizes before reading them.
-__device__ inline void group_prefix(const int32_t* __restrict__ gs, int G, int* s_tile_cum,
-                                    int* s_row_off) {
+// Per-group prefix sums into LDS (first wave) over the window of G groups that starts
+// after g_before others: s_tile_cum[g] = M-tiles of window groups < g, s_row_off[g] = the
+// first row of window group g (rows of every group before it, inside or outside the
+// window).  The caller synchronizes before reading them.
+__device__ inline void group_prefix(const int32_t* __restrict__ gs, int g_before, int G,
+                                    int* s_tile_cum, int* s_row_off) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid < 64) {
-    int carry_t = 0, carry_r = 0;
+    // sizes outside the contract (negative) are read as 0, and rows past M are dropped
+    // by the tile coordinates, so no access ever leaves the tensors
+    int carry_r = 0;
+    for (int base = 0; base < g_before; base += 64) {
+      const int g = base + lane;
+      const int ir = wave_incl_scan(g < g_before ? max(gs[g], 0) : 0, lane);
+      carry_r += __shfl(ir, 63, 64);
+    }
+    const int32_t* __restrict__ wgs = gs + g_before;
+    int carry_t = 0;
+    if (lane == 0) {
+      s_tile_cum[0] = 0;
+      s_row_off[0] = carry_r;
+    }
     for (int base = 0; base < G; base += 64) {
       const int g = base + lane;
-      // sizes outside the contract (negative) are read as 0, and rows past M are
-      // dropped by the tile coordinates, so no access ever leaves the tensors
-      const int m = g < G ? max(gs[g], 0) : 0;
+      const int m = g < G ? max(wgs[g], 0) : 0;
       const int it = wave_incl_scan((m + BM - 1) / BM, lane);
       const int ir = wave_incl_scan(m, lane);
       if (g < G) {
@@ -67,10 +82,6 @@ __device__ inline void group_prefix(const int32_t* __restrict__ gs, int G, int* 
       }
       carry_t += __shfl(it, 63, 64);
       carry_r += __shfl(ir, 63, 64);
-    }
-    if (lane == 0) {
-      s_tile_cum[0] = 0;
-      s_row_off[0] = 0;
     }
   }
 }
@@ -103,10 +114,10 @@ __device__ inline bool tile_coord(int L, int total_mt, int n_ntiles, int G, int6
 // Expert-tile scheduler of the one-tile-per-workgroup kernel.  Returns false for a
 // workgroup without a tile.  The two LDS arrays alias the stage buffers: they are dead
 // once the tile is known.
-__device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int64_t M,
-                                     int n_ntiles, int* s_tile_cum, int* s_row_off,
+__device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int g_before, int G,
+                                     int64_t M, int n_ntiles, int* s_tile_cum, int* s_row_off,
                                      TileCoord& tc) {
-  group_prefix(gs, G, s_tile_cum, s_row_off);
+  group_prefix(gs, g_before, G, s_tile_cum, s_row_off);
   __syncthreads();
   const int total_mt = s_tile_cum[G];
   const int total = total_mt * n_ntiles;
@@ -128,13 +139,16 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int G, int6
 }
 
 // SwiGLU epilogue of a gate|up tile.  The product values x = (acc * s_A(m)) * s_B(n) are
-// the ones gmm_fwd stores (written to gu when given).  The up waves pass theirs through
-// LDS, in the lane order every wave's accumulators share, and each gate wave then stores
-// h = silu(g) * u = (g / (1 + exp(-g))) * u for its 128 x 128 block, all in fp32: in the
-// output dtype, or as fp8 codes fp8(clamp(RNE_f32(h * inv), +-qmax)) of a static scale.
+// the ones gmm_fwd stores (written to gu when given).  The gate and up waves of a row
+// half exchange half of their values through LDS, in the lane order every wave's
+// accumulators share, and each then stores h = silu(g) * u = (g / (1 + exp(-g))) * u for
+// 64 of the 128 rows, all in fp32: in the output dtype, or as fp8 codes
+// fp8(clamp(RNE_f32(h * inv), +-qmax)) of a static scale.
 __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc, int c0, int wr,
-                                       int wc, int lane, v16f (&acc)[4][4], uint8_t* sA0,
+                                       int wc, v16f (&acc)[4][4], uint8_t* sA0,
                                        uint8_t* sB0, uint8_t* sA1, uint8_t* sB1) {
+  // the lane id is recomputed here: cheaper than keeping it live across the main loop
+  const int lane = __lane_id();
   const int frow = lane & 31, fhalf = lane >> 5;
   const int I = p.Nout >> 1;
   const int cb = wc == 0 ? c0 : I + c0;  // this wave's first channel
@@ -157,7 +171,9 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
     for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
     return o;
   };
-  // chunk r = 16 i + 4 j + r4 of the up wave of row half wr, lane-interleaved
+  // chunk r = 16 i + 4 j + r4 of row half wr, lane-interleaved: the gate wave finishes
+  // rows i < 2 and hands over its chunks i >= 2 (region xb); the up wave finishes rows
+  // i >= 2 and hands over its chunks i < 2 (region xa)
   uint8_t* const xa = wr == 0 ? sA0 : sA1;
   uint8_t* const xb = wr == 0 ? sB0 : sB1;
   auto chunk = [&](int r) { return reinterpret_cast<v4f*>((r < 32 ? xa : xb) + ((r & 31) * 64 + lane) * 16); };
@@ -181,22 +197,22 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
             *reinterpret_cast<v2u*>((uint16_t*)p.gu + idx) = v;
           }
         }
-        if (wc == 1) *chunk(i * 16 + j * 4 + r4) = o;
+        if ((wc == 0) == (i >= 2)) *chunk(i * 16 + j * 4 + r4) = o;
       }
     }
   }
-  __syncthreads();  // the up values are in LDS
-  if (wc != 0) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  __syncthreads();  // the handed-over values are in LDS
+  auto finish = [&](int i) {
     const int m = tc.row0 + wr * 128 + i * 32 + frow;
-    if (m >= tc.row_end) continue;
+    if (m >= tc.row_end) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const v4f g = value(i, j, r4);
-        const v4f u = *chunk(i * 16 + j * 4 + r4);
+        const v4f mine = value(i, j, r4);
+        const v4f other = *chunk(i * 16 + j * 4 + r4);
+        const v4f g = wc == 0 ? mine : other;
+        const v4f u = wc == 0 ? other : mine;
         v4f h;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -216,6 +232,13 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
         }
       }
     }
+  };
+  if (wc == 0) {
+    finish(0);
+    finish(1);
+  } else {
+    finish(2);
+    finish(3);
   }
 }
 
@@ -239,7 +262,8 @@ void gmm_kernel(GemmParams p) {
 
   const int n_ntiles = SW ? (p.Nout >> 1) / 128 : (p.Nout + BN - 1) / BN;
   TileCoord tc;
-  if (!schedule_tile(p.group_sizes, p.G, p.M, n_ntiles, s_tile_cum, s_row_off, tc)) return;
+  if (!schedule_tile(p.group_sizes, p.g_before, p.G, p.M, n_ntiles, s_tile_cum, s_row_off, tc))
+    return;
   const int c0 = SW ? (tc.n0 >> 1) : 0;  // SW: first channel pair of the tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -473,7 +497,7 @@ void gmm_kernel(GemmParams p) {
   if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
 
   if constexpr (SW) {
-    swiglu_epilogue(p, tc, c0, wr, wc, lane, acc, sA0, sB0, sA1, sB1);
+    swiglu_epilogue(p, tc, c0, wr, wc, acc, sA0, sB0, sA1, sB1);
     return;
   }
 
@@ -526,6 +550,41 @@ void gmm_kernel(GemmParams p) {
   }
 }
 
+// Rows outside a group window: [0, first row of the window) and [its end, M), written
+// with zeros.  Every workgroup sums the group sizes itself (at most GMM_MAX_GROUPS).
+__global__ __launch_bounds__(256) void zero_rows_outside_kernel(uint8_t* __restrict__ out,
+                                                                int64_t M, int64_t row_bytes,
+                                                                const int32_t* __restrict__ gs,
+                                                                int g_before, int G) {
+  __shared__ int64_t s_part[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int64_t before = 0, inside = 0;
+  for (int g = tid; g < g_before + G; g += 256) {
+    const int64_t m = max(gs[g], 0);
+    if (g < g_before) before += m; else inside += m;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    before += __shfl_xor(before, d, 64);
+    inside += __shfl_xor(inside, d, 64);
+  }
+  if (lane == 0) {
+    s_part[0][w] = before;
+    s_part[1][w] = inside;
+  }
+  __syncthreads();
+  const int64_t lo = min(s_part[0][0] + s_part[0][1] + s_part[0][2] + s_part[0][3], M);
+  const int64_t hi = min(lo + s_part[1][0] + s_part[1][1] + s_part[1][2] + s_part[1][3], M);
+  const int64_t vecs = row_bytes / 16;
+  const int64_t total = (lo + (M - hi)) * vecs;
+  const v4u z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / vecs, v = i - r * vecs;
+    const int64_t row = r < lo ? r : hi + (r - lo);
+    *reinterpret_cast<v4u*>(out + row * row_bytes + v * 16) = z;
+  }
+}
+
 template <int A_FMT, int B_FMT, bool A_FP8, bool B_TRANS>
 hipError_t launch_one(const GemmParams& p, hipStream_t st) {
   // upper bound on M-tiles: sum ceil(m_g/BM) <= ceil(M/BM) + G
@@ -552,6 +611,16 @@ hipError_t launch_gemm_swiglu(int a_fmt, const GemmParams& p, hipStream_t st) {
                        dim3(NT), 0, st, p);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows_outside(void* out, int64_t M, int64_t row_bytes,
+                                   const int32_t* gs, int g_before, int G, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const int64_t pieces = M * (row_bytes / 16);
+  const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 256 * 16);
+  hipLaunchKernelGGL(zero_rows_outside_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (uint8_t*)out, M, row_bytes, gs, g_before, G);
   return hipGetLastError();
 }
 

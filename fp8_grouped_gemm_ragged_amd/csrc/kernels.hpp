@@ -10,6 +10,7 @@ namespace gmm {
 
 constexpr int AMAX_SPLIT = 8;    // row slices per 128-row block in the abs-max prepass
 constexpr int MAX_GROUPS = 1024;
+constexpr int ROUTE_CHUNK = 256;  // slots per chunk of the routing sort
 
 // Grouped GEMM: out[M, Nout] = A[M, Kc] x B(g) for the rows of group g.
 // B is either "contraction-contiguous" codes [G, Nout, Kc] (b_trans == 0) or
@@ -25,6 +26,7 @@ struct GemmParams {
   float a_scale_static;
   int64_t M;
   int32_t Kc, Nout, G;
+  int32_t g_before;          // group window: the G groups after the first g_before ones
   int32_t out_f32;
   // SwiGLU epilogue (gmm_fwd_swiglu): B holds the merged [W0 | W1] channels (Nout = 2 I),
   // out is h [M, I], gu (optional) the product itself [M, 2 I]
@@ -50,6 +52,7 @@ struct TgmmParams {
   float a_inv_static, a_scale_static, b_inv_static, b_scale_static;
   int64_t M;
   int32_t Kout, Nout, G;
+  int32_t g_before;          // group window: the G groups after the first g_before ones
   int32_t out_f32;
   int32_t a_codes, b_codes;  // the operand is fp8 codes quantized beforehand
 };
@@ -77,6 +80,18 @@ hipError_t launch_gemm_swiglu(int a_fmt, const GemmParams& p, hipStream_t st);
 // d_gu [M, 2 I] from dh [M, I] and gu [M, 2 I], all bf16
 hipError_t launch_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, uint16_t* d_gu, int64_t M,
                              int64_t I, hipStream_t st);
+// routing sort (counts: route_chunks(n) * (G + 1) ints of workspace) and the row gather
+int64_t route_chunks(int64_t n);
+hipError_t launch_route(const int32_t* ids, int64_t n, int k, int G, int32_t* counts,
+                        int32_t* gs, int32_t* row_of_slot, int32_t* slot_of_row,
+                        const void* x, int64_t row_bytes, void* x_perm, hipStream_t st);
+// weighted sum of every token's expert rows (w may be null: weights 1)
+hipError_t launch_combine(const uint16_t* y, int64_t T, int k, int64_t H, int64_t rows,
+                          const int32_t* row_of_slot, const float* w, uint16_t* out,
+                          hipStream_t st);
+// zeros into the rows of out [M, row_bytes] outside the window's rows
+hipError_t launch_zero_rows_outside(void* out, int64_t M, int64_t row_bytes,
+                                   const int32_t* gs, int g_before, int G, hipStream_t st);
 hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st);
 hipError_t launch_dynamic_scales(int fmt, const void* x, int64_t R, int64_t C,
                                  uint32_t* partial, float* scales_out, hipStream_t st);

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
         const float u = h ? bf16_hi(uv[k]) : bf16_lo(uv[k]);
         const float d = h ? bf16_hi(dv[k]) : bf16_lo(dv[k]);
         const float s = __fdiv_rn(1.0f, __fadd_rn(1.0f, expf(-g)));
-        const float grow = __fadd_rn(1.0f, __fmul_rn(g, __fsub_rn(1.0f, s)));
+        const float grow = add_rn(1.0f, mul_rn(g, __fsub_rn(1.0f, s)));
         dg[h] = __fmul_rn(__fmul_rn(__fmul_rn(d, u), s), grow);
         du[h] = __fmul_rn(d, __fmul_rn(g, s));
       }

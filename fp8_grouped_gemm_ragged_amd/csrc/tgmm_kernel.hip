@@ -112,7 +112,7 @@ __device__ inline int block_incl_scan(int v, int* tmp, Op op) {
 // segment block b of group g, and 1 at ratio[seg[g + 1] + g], just past the group's
 // blocks.
 __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
-    const int32_t* __restrict__ gs, int G, int64_t M, OpScale a_sc, OpScale b_sc,
+    const int32_t* __restrict__ gs, int g_before, int G, int64_t M, OpScale a_sc, OpScale b_sc,
     int32_t* __restrict__ plan, float* __restrict__ scprod, float* __restrict__ ratio) {
   __shared__ int s_tmp[PLAN_NT / 64];
   __shared__ int s_incl[PLAN_NT];
@@ -128,13 +128,20 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
   int32_t* wide = plan + 3 * G + 1;
   float* fin = reinterpret_cast<float*>(plan + 4 * G + 1);
 
-  // ---- groups: first row, rows, segment offset (sizes outside the contract are
-  // clamped so that no access leaves the tensors) ----
-  const int m = t < G ? min(max(gs[t], 0), Mi) : 0;
-  const int incl = block_incl_scan(m, s_tmp, [Mi](int x, int y) { return min(x + y, Mi); });
+  // ---- groups of the window (the G after the first g_before): first row, rows,
+  // segment offset (sizes outside the contract are clamped so that no access leaves the
+  // tensors) ----
+  auto add_clamped = [Mi](int x, int y) { return (int)min((int64_t)x + y, (int64_t)Mi); };
+  const int mb = t < g_before ? min(max(gs[t], 0), Mi) : 0;
+  s_incl[t] = block_incl_scan(mb, s_tmp, add_clamped);
+  __syncthreads();
+  const int rows_before = s_incl[PLAN_NT - 1];
+  __syncthreads();
+  const int m = t < G ? min(max(gs[g_before + t], 0), Mi) : 0;
+  const int incl = block_incl_scan(m, s_tmp, add_clamped);
   s_incl[t] = incl;
   __syncthreads();
-  const int o = t > 0 ? s_incl[t - 1] : 0;
+  const int o = add_clamped(rows_before, t > 0 ? s_incl[t - 1] : 0);
   const int c = min(m, Mi - o);
   const int nb = c > 0 ? (o + c - 1) / BLOCK_ROWS - o / BLOCK_ROWS + 1 : 0;
   const int bincl = block_incl_scan(nb, s_tmp, [](int x, int y) { return x + y; });
@@ -872,8 +879,8 @@ hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st
   const int64_t seg_row = tgmm_segment_row_bytes(p.M, p.G);
   const OpScale a_sc{p.a_scale_blk, p.a_scale_static, p.a_inv_static, p.a_codes};
   const OpScale b_sc{p.b_scale_blk, p.b_scale_static, p.b_inv_static, p.b_codes};
-  hipLaunchKernelGGL(tgmm_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p.group_sizes, p.G, p.M,
-                     a_sc, b_sc, p.plan, p.scprod, p.ratio);
+  hipLaunchKernelGGL(tgmm_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p.group_sizes, p.g_before,
+                     p.G, p.M, a_sc, b_sc, p.plan, p.scprod, p.ratio);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.M > 0) {

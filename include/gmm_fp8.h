@@ -184,6 +184,40 @@ gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t 
                       void* workspace, size_t workspace_bytes, gmm_stream_t stream);
 
 /*
+ * Local-expert window ("FP8 Megablox for batch split" follow-up, Description 3: the
+ * group_offset argument of the ragged products).  With experts sharded over devices,
+ * each device holds G_local of the G_total experts, from group_offset on; the rows stay
+ * sorted by global expert, so group_sizes has all G_total entries and only the rows of
+ * the local experts are computed.  rhs and rhs_scales hold the G_local local experts
+ * (group 0 = expert group_offset).  0 <= group_offset, 1 <= G_local,
+ * group_offset + G_local <= G_total <= GMM_MAX_GROUPS (else GMM_ERR_SHAPE).
+ *
+ * gmm_fwd_local / gmm_dlhs_local - as gmm_fwd / gmm_dlhs; out rows of groups outside the
+ * window are written with zeros.  sum(group_sizes) == M over all G_total groups.
+ * tgmm_drhs_local - as tgmm_drhs; drhs [G_local, K, N] for the local experts.  Its
+ * workspace is gmm_workspace_size(GMM_OP_TGMM, ..., G_local) bytes or more.
+ * With group_offset 0 and G_local == G_total each equals its plain entry point.
+ */
+gmm_status_t gmm_fwd_local(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                           int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G_total,
+                           int32_t group_offset, int32_t G_local, const void* lhs,
+                           float* lhs_scales, const uint8_t* rhs, const float* rhs_scales,
+                           const int32_t* group_sizes, void* out, void* workspace,
+                           size_t workspace_bytes, gmm_stream_t stream);
+gmm_status_t gmm_dlhs_local(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
+                            int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G_total,
+                            int32_t group_offset, int32_t G_local, const void* grad,
+                            float* grad_scales, const uint8_t* rhs, const float* rhs_scales,
+                            const int32_t* group_sizes, void* dlhs, void* workspace,
+                            size_t workspace_bytes, gmm_stream_t stream);
+gmm_status_t tgmm_drhs_local(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
+                             int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G_total,
+                             int32_t group_offset, int32_t G_local, const void* lhs,
+                             float* lhs_scales, const void* grad, float* grad_scales,
+                             const int32_t* group_sizes, void* drhs, void* workspace,
+                             size_t workspace_bytes, gmm_stream_t stream);
+
+/*
  * gmm_fwd_swiglu - the merged gate|up forward with SwiGLU in its epilogue ("FP8 Megablox
  * for batch split", Description (2): W0 | W1 merged along N, one call for both).
  *
@@ -248,6 +282,60 @@ gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
  */
 gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu, void* d_gu,
                             gmm_stream_t stream);
+
+/*
+ * Token routing around the grouped products: the MoE layer's permute before them and
+ * unpermute after them (the later commits of "add static LHS scaling support for GMM v2
+ * FWD": permute()/unpermute() in the MoE layer, activations quantized before the sort so
+ * it moves fp8, and the expert outputs gathered back and reduced over the top-k).
+ *
+ * Slot s = t * k + j is the j-th expert choice of token t (expert_ids int32 [T, k]).
+ * Permuted row order: the slots whose id is in [0, G), sorted by expert, slots of one
+ * expert in increasing slot order, then the slots with any other id, in slot order: those
+ * are dropped (capacity dropping, or a token routed to fewer than k experts).  Every
+ * output is fully written.
+ */
+
+/* Workspace bytes of gmm_permute (one int per expert, plus one, and chunk of 256 slots). */
+size_t gmm_permute_workspace_size(int64_t T, int32_t k, int32_t G);
+
+/*
+ * gmm_permute - sort token slots by expert and gather the rows.
+ *
+ * expert_ids   int32 [T, k], device.  0 <= T, 1 <= k <= 64, T * k < 2^31, 1 <= G <=
+ *              GMM_MAX_GROUPS (else GMM_ERR_SHAPE).
+ * group_sizes  OUTPUT int32 [G]: rows per expert, the group_sizes of the grouped
+ *              products on x_perm; their sum, the number of routed slots, stays on the
+ *              device.
+ * row_of_slot  OUTPUT int32 [T * k]: the permuted row of every slot, -1 if dropped.
+ * slot_of_row  OUTPUT int32 [T * k]: the slot of every permuted row (the routed rows
+ *              first, sum(group_sizes) of them, then the dropped slots).
+ * x, x_perm    optional (both or neither): x [T, row_bytes] bytes (bf16 values, fp8 codes
+ *              of a static scale, ...), x_perm [T * k, row_bytes]; x_perm[r] = x[slot / k]
+ *              for slot = slot_of_row[r].  row_bytes a positive multiple of 16.  A grouped
+ *              product over all T * k rows takes the dropped tail as one more group.
+ * workspace    gmm_permute_workspace_size(T, k, G) bytes; contents undefined after.
+ * Pointers 16-byte aligned; outputs must not overlap inputs or one another.
+ */
+gmm_status_t gmm_permute(int64_t T, int32_t k, int32_t G, const int32_t* expert_ids,
+                         int64_t row_bytes, const void* x, void* x_perm, int32_t* group_sizes,
+                         int32_t* row_of_slot, int32_t* slot_of_row, void* workspace,
+                         size_t workspace_bytes, gmm_stream_t stream);
+
+/*
+ * gmm_unpermute - gather every token's expert outputs back and reduce them:
+ *
+ *   out[t, c] = RNE_bf16( sum_{j = 0..k-1, row_of_slot[t k + j] >= 0}
+ *                         weights[t, j] * y[row_of_slot[t k + j], c] )
+ *
+ * summed in fp32 in increasing j from +0, each product and each sum rounded to nearest
+ * (a token whose slots are all dropped gets +0).  y bf16 [rows, H] (the products' output
+ * on the permuted rows, rows = T * k); weights f32 [T, k] or NULL (all 1: then this is the
+ * backward of gmm_permute's gather); out bf16 [T, H]; H a positive multiple of 8.
+ */
+gmm_status_t gmm_unpermute(int64_t T, int32_t k, int64_t H, const void* y,
+                           const int32_t* row_of_slot, const float* weights, void* out,
+                           gmm_stream_t stream);
 
 /*
  * tgmm_drhs - weight gradient, the transposed grouped matmul ("Support quantization for

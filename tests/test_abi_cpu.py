@@ -221,3 +221,52 @@ def test_swiglu_validation():
     assert lib.gmm_swiglu_bwd(256, 256, ptr(1), None, ptr(3), None) == 1
     assert lib.gmm_swiglu_bwd(256, 256, ptr(1), ptr(2), ptr(2), None) == 9
     assert lib.gmm_swiglu_bwd(0, 256, None, None, None, None) == 0
+
+
+def test_route_validation():
+    lib = g.load()
+    assert lib.gmm_permute_workspace_size(1000, 8, 64) == ((8000 + 255) // 256 * 65 * 4 + 255) // 256 * 256
+
+    def perm(T=100, k=2, G=8, ids=1, rb=64, x=2, xp=3, gs=4, ros=5, sor=6, ws=7, wsb=1 << 20):
+        P = lambda i: None if i is None else ptr(i)
+        return lib.gmm_permute(T, k, G, P(ids), rb, P(x), P(xp), P(gs), P(ros), P(sor), P(ws), wsb, None)
+
+    assert perm(T=-1) == 2 and perm(k=0) == 2 and perm(k=65) == 2 and perm(G=0) == 2
+    assert perm(G=1025) == 2 and perm(T=1 << 30, k=4) == 2
+    assert perm(rb=24) == 2 and perm(rb=0) == 2
+    assert perm(ids=None) == 1 and perm(gs=None) == 1 and perm(sor=None) == 1
+    assert perm(x=None) == 1  # x and x_perm come together
+    assert perm(ws=None) == 5 and perm(wsb=16) == 5
+    assert perm(xp=2) == 9 and perm(ros=6) == 9 and perm(ws=1) == 9
+    assert lib.gmm_permute(100, 2, 8, ctypes.c_void_p(FAKE + 4), 64, ptr(2), ptr(3), ptr(4), ptr(5),
+                           ptr(6), ptr(7), 1 << 20, None) == 6
+
+    def unperm(T=100, k=2, H=64, y=1, ros=2, w=3, out=4):
+        P = lambda i: None if i is None else ptr(i)
+        return lib.gmm_unpermute(T, k, H, P(y), P(ros), P(w), P(out), None)
+
+    assert unperm(H=12) == 2 and unperm(k=0) == 2 and unperm(T=-1) == 2
+    assert unperm(y=None) == 1 and unperm(out=None) == 1 and unperm(ros=None) == 1
+    assert unperm(out=1) == 9 and unperm(out=3) == 9
+    assert unperm(T=0) == 0
+
+
+def test_local_window_validation():
+    lib = g.load()
+    o = op(scaling=0, s=1.0)
+
+    def fwd_local(G_total=8, off=2, G_local=3, M=256):
+        return lib.gmm_fwd_local(ctypes.byref(o), 0, 1, 0, M, 256, 256, G_total, off, G_local,
+                                 ptr(1), None, ptr(3), ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20,
+                                 None)
+
+    assert fwd_local(M=0) == 0
+    assert fwd_local(off=-1) == 2 and fwd_local(G_local=0) == 2 and fwd_local(off=6) == 2
+    assert fwd_local(G_total=1025, off=0, G_local=1) == 2
+    assert lib.gmm_dlhs_local(ctypes.byref(o), 0, 0, 0, 0, 256, 256, 8, 5, 4, ptr(1), None, ptr(3),
+                              ptr(4), ptr(5), ptr(6), ptr(7), 1 << 20, None) == 2
+    a, b = op(fmt=0, scaling=0, s=1.0), op(fmt=1, scaling=0, s=1.0)
+    assert lib.tgmm_drhs_local(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 8, 7, 2, ptr(1),
+                               None, ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 26, None) == 2
+    assert lib.tgmm_drhs_local(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 8, 0, 0, ptr(1),
+                               None, ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 26, None) == 2

@@ -353,7 +353,7 @@ gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
 
 size_t gmm_permute_workspace_size(int64_t T, int32_t k, int32_t G) {
   if (T < 0 || k < 1 || G < 1) return 0;
-  return align256((size_t)route_chunks(T * k) * (G + 1) * 4);
+  return align256((size_t)route_chunks(T * k) * (G + 1) * 4) + align256((size_t)T * k * 4);
 }
 
 gmm_status_t gmm_permute(int64_t T, int32_t k, int32_t G, const int32_t* expert_ids,
@@ -384,7 +384,10 @@ gmm_status_t gmm_permute(int64_t T, int32_t k, int32_t G, const int32_t* expert_
       if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return GMM_ERR_ALIAS;
   }
   trace("gmm_permute", T, k, row_bytes, G);
-  return launch_route(expert_ids, n, k, G, (int32_t*)workspace, group_sizes, row_of_slot,
+  int32_t* counts = (int32_t*)workspace;
+  int32_t* dest_all =
+      n ? (int32_t*)((uint8_t*)workspace + align256((size_t)route_chunks(n) * (G + 1) * 4)) : nullptr;
+  return launch_route(expert_ids, n, k, G, counts, dest_all, group_sizes, row_of_slot,
                       slot_of_row, x, row_bytes, x_perm, (hipStream_t)stream) == hipSuccess
              ? GMM_OK
              : GMM_ERR_HIP;

@@ -80,11 +80,13 @@ hipError_t launch_gemm_swiglu(int a_fmt, const GemmParams& p, hipStream_t st);
 // d_gu [M, 2 I] from dh [M, I] and gu [M, 2 I], all bf16
 hipError_t launch_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, uint16_t* d_gu, int64_t M,
                              int64_t I, hipStream_t st);
-// routing sort (counts: route_chunks(n) * (G + 1) ints of workspace) and the row gather
+// routing sort (workspace: counts, route_chunks(n) * (G + 1) ints, and dest_all, the row
+// of every slot, n ints) and the row gather
 int64_t route_chunks(int64_t n);
 hipError_t launch_route(const int32_t* ids, int64_t n, int k, int G, int32_t* counts,
-                        int32_t* gs, int32_t* row_of_slot, int32_t* slot_of_row,
-                        const void* x, int64_t row_bytes, void* x_perm, hipStream_t st);
+                        int32_t* dest_all, int32_t* gs, int32_t* row_of_slot,
+                        int32_t* slot_of_row, const void* x, int64_t row_bytes, void* x_perm,
+                        hipStream_t st);
 // weighted sum of every token's expert rows (w may be null: weights 1)
 hipError_t launch_combine(const uint16_t* y, int64_t T, int k, int64_t H, int64_t rows,
                           const int32_t* row_of_slot, const float* w, uint16_t* out,

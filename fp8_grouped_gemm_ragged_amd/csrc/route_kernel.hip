@@ -12,7 +12,7 @@
 //   route_count_kernel   per-chunk histogram of the keys (LDS counters)
 //   route_scan_kernel    per key, an exclusive scan of its chunk counts; group_sizes
 //   route_rank_kernel    one wave per chunk: destination row of every slot, in slot order
-//   route_gather_kernel  x_perm[r] = x[slot_of_row[r] / k], 16-byte copies
+//   route_gather_kernel  x_perm[row of slot t k + j] = x[t]: each row read once, k stores
 //   route_combine_kernel out[t] = sum_j w[t, j] * y[row_of_slot[t k + j]] in fp32, in
 //                        j order, each product and sum rounded to nearest; bf16 out
 #include <algorithm>
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(64) void route_rank_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ gs,
                                                         int32_t* __restrict__ row_of_slot,
-                                                        int32_t* __restrict__ slot_of_row) {
+                                                        int32_t* __restrict__ slot_of_row,
+                                                        int32_t* __restrict__ dest_all) {
   __shared__ int run[MAX_GROUPS + 1];
   const int lane = threadIdx.x;
   // run[e] = first row of key e (exclusive prefix of group_sizes; key G starts after
@@ -104,23 +105,33 @@ __global__ __launch_bounds__(64) void route_rank_kernel(const int32_t* __restric
     }
     if (ok) {
       row_of_slot[s] = e < G ? dest : -1;
+      dest_all[s] = dest;
       if (dest >= 0 && dest < n) slot_of_row[dest] = (int32_t)s;
     }
   }
 }
 
-// One permuted row per workgroup and iteration, copied in 16-byte pieces.
+// GATHER_TOKENS tokens per workgroup and iteration: every 16-byte piece of a token's row
+// is read once and stored into the rows of its k slots (dest holds the row of every slot,
+// dropped ones included).
+constexpr int GATHER_TOKENS = 4;
+
 __global__ __launch_bounds__(256) void route_gather_kernel(const uint8_t* __restrict__ x,
-                                                           int64_t n, int k, int64_t row_bytes,
-                                                           const int32_t* __restrict__ slot_of_row,
+                                                           int64_t T, int k, int64_t row_bytes,
+                                                           const int32_t* __restrict__ dest,
                                                            uint8_t* __restrict__ xp) {
-  const int64_t vecs = row_bytes / 16;
-  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
-    const int s = slot_of_row[r];
-    if (s < 0 || s >= n) continue;
-    const v4u* src = reinterpret_cast<const v4u*>(x + (int64_t)(s / k) * row_bytes);
-    v4u* dst = reinterpret_cast<v4u*>(xp + r * row_bytes);
-    for (int64_t v = threadIdx.x; v < vecs; v += 256) dst[v] = src[v];
+  const int64_t vecs = row_bytes / 16, n = T * k;
+  for (int64_t t0 = (int64_t)blockIdx.x * GATHER_TOKENS; t0 < T;
+       t0 += (int64_t)gridDim.x * GATHER_TOKENS) {
+    const int64_t pieces = std::min<int64_t>(GATHER_TOKENS, T - t0) * vecs;
+    for (int64_t i = threadIdx.x; i < pieces; i += 256) {
+      const int64_t tt = i / vecs, c = i - tt * vecs, t = t0 + tt;
+      const v4u v = *reinterpret_cast<const v4u*>(x + t * row_bytes + c * 16);
+      for (int j = 0; j < k; ++j) {
+        const int d = dest[t * k + j];
+        if (d >= 0 && d < n) *reinterpret_cast<v4u*>(xp + (int64_t)d * row_bytes + c * 16) = v;
+      }
+    }
   }
 }
 
@@ -137,15 +148,27 @@ __global__ __launch_bounds__(256) void route_combine_kernel(const uint16_t* __re
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int r = row_of_slot[t * k + j];
-        if (r < 0 || r >= rows) continue;
-        const float wj = w ? w[t * k + j] : 1.0f;
-        const v4u q = *reinterpret_cast<const v4u*>(y + (int64_t)r * H + v * 8);
+      // four slots at a time: their loads are issued before the sums that use them
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        v4u q[4];
+        float wj[4];
+        bool live[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = add_rn(acc[2 * i], mul_rn(wj, bf16_lo(q[i])));
-          acc[2 * i + 1] = add_rn(acc[2 * i + 1], mul_rn(wj, bf16_hi(q[i])));
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + u;
+          const int r = j < k ? row_of_slot[t * k + j] : -1;
+          live[u] = r >= 0 && r < rows;
+          wj[u] = live[u] && w ? w[t * k + j] : 1.0f;
+          if (live[u]) q[u] = *reinterpret_cast<const v4u*>(y + (int64_t)r * H + v * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (!live[u]) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = add_rn(acc[2 * i], mul_rn(wj[u], bf16_lo(q[u][i])));
+            acc[2 * i + 1] = add_rn(acc[2 * i + 1], mul_rn(wj[u], bf16_hi(q[u][i])));
+          }
         }
       }
       v4u o;
@@ -161,8 +184,9 @@ __global__ __launch_bounds__(256) void route_combine_kernel(const uint16_t* __re
 int64_t route_chunks(int64_t n) { return (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK; }
 
 hipError_t launch_route(const int32_t* ids, int64_t n, int k, int G, int32_t* counts,
-                        int32_t* gs, int32_t* row_of_slot, int32_t* slot_of_row,
-                        const void* x, int64_t row_bytes, void* x_perm, hipStream_t st) {
+                        int32_t* dest_all, int32_t* gs, int32_t* row_of_slot,
+                        int32_t* slot_of_row, const void* x, int64_t row_bytes, void* x_perm,
+                        hipStream_t st) {
   const int64_t nblk = route_chunks(n);
   if (nblk == 0) {
     // no slots: every expert is empty
@@ -173,11 +197,12 @@ hipError_t launch_route(const int32_t* ids, int64_t n, int k, int G, int32_t* co
                      counts);
   hipLaunchKernelGGL(route_scan_kernel, dim3(G + 1), dim3(256), 0, st, counts, (int)nblk, G, gs);
   hipLaunchKernelGGL(route_rank_kernel, dim3((unsigned)nblk), dim3(64), 0, st, ids, n, G, counts,
-                     gs, row_of_slot, slot_of_row);
+                     gs, row_of_slot, slot_of_row, dest_all);
   if (x && x_perm) {
-    const int64_t blocks = std::min<int64_t>(n, 256 * 64);
+    const int64_t T = n / k;
+    const int64_t blocks = std::min<int64_t>((T + GATHER_TOKENS - 1) / GATHER_TOKENS, 256 * 16);
     hipLaunchKernelGGL(route_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const uint8_t*)x, n, k, row_bytes, slot_of_row, (uint8_t*)x_perm);
+                       (const uint8_t*)x, T, k, row_bytes, dest_all, (uint8_t*)x_perm);
   }
   return hipGetLastError();
 }

@@ -296,7 +296,8 @@ gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu
  * output is fully written.
  */
 
-/* Workspace bytes of gmm_permute (one int per expert, plus one, and chunk of 256 slots). */
+/* Workspace bytes of gmm_permute (one int per expert, plus one, and chunk of 256 slots,
+ * and one int per slot). */
 size_t gmm_permute_workspace_size(int64_t T, int32_t k, int32_t G);
 
 /*

@@ -225,7 +225,7 @@ def test_swiglu_validation():
 
 def test_route_validation():
     lib = g.load()
-    assert lib.gmm_permute_workspace_size(1000, 8, 64) == ((8000 + 255) // 256 * 65 * 4 + 255) // 256 * 256
+    assert lib.gmm_permute_workspace_size(1000, 8, 64) == ((8000 + 255) // 256 * 65 * 4 + 255) // 256 * 256 + 32000
 
     def perm(T=100, k=2, G=8, ids=1, rb=64, x=2, xp=3, gs=4, ros=5, sor=6, ws=7, wsb=1 << 20):
         P = lambda i: None if i is None else ptr(i)

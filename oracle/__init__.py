@@ -16,6 +16,8 @@ gmm    the three grouped products: gmm forward, gmm dlhs and the transposed tgmm
 swiglu SwiGLU of the merged gate|up product, forward and backward.
 route  token routing around the products: the stable sort by expert, the row gather and
        the weighted combine.
+blockwise  block-wise weight scales [G, K/bk, N] and sub-channel lhs scales [M, K/bk]: the
+       forward with a per-block promotion, and both quantizers.
 
 Sources (the MaxText pull-request pages this method is taken from):
   * "FP8 Megablox for batch split" (PR #3770), Description (1) and (2): fp8 recipes
@@ -56,4 +58,9 @@ from .gmm import (  # noqa: F401
     tgmm_ref,
 )
 from .route import gather_rows_ref, permute_ref, unpermute_ref  # noqa: F401
+from .blockwise import (  # noqa: F401
+    gmm_fwd_blockwise_ref,
+    quantize_rhs_blockwise,
+    quantize_subchannel,
+)
 from .swiglu import silu, swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref  # noqa: F401

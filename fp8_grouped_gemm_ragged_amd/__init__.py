@@ -20,6 +20,7 @@ __all__ = [
     "load", "library_path", "GmmError", "gmm_fwd", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
     "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8", "gmm_swiglu_bwd",
     "gmm_permute", "gmm_unpermute", "gmm_fwd_local", "gmm_dlhs_local", "tgmm_drhs_local",
+    "gmm_fwd_blockwise", "gmm_quantize_subchannel", "gmm_quantize_rhs_blockwise",
     "gmm_quantize_rhs", "gmm_static_scale_from_bound", "gmm_workspace_size",
     "gmm_status_string", "gmm_version", "E4M3", "E5M2", "STATIC", "DYNAMIC", "BLOCK_ROWS",
 ]
@@ -69,6 +70,9 @@ _SIGNATURES = {
     "gmm_fwd_swiglu_fp8": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _OPP, _P, _P, _SZ, _P],
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
     "gmm_permute_workspace_size": [_I64, _I32, _I32],
+    "gmm_fwd_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
+    "gmm_quantize_subchannel": [_I32, _I64, _I64, _I64, _P, _P, _P, _P],
+    "gmm_quantize_rhs_blockwise": [_I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _P],
     "gmm_fwd_local": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_dlhs_local": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "tgmm_drhs_local": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -564,4 +568,64 @@ def gmm_unpermute(y, row_of_slot, weights=None, out=None):
         _need(out, torch.bfloat16, "out", 2)
     _check(lib.gmm_unpermute(T, k, H, _ptr(y), _ptr(row_of_slot), _ptr(weights), _ptr(out),
                              _stream()), "gmm_unpermute")
+    return out
+
+
+def gmm_quantize_subchannel(x, bk=128, fmt="e4m3"):
+    """bf16 x [M, K] -> (uint8 codes [M, K], f32 scales [M, K / bk]): one dynamic scale per
+    row and block of bk columns (bk 128, 256 or 512)."""
+    import torch
+
+    lib = load()
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M, K // bk if bk else 0), dtype=torch.float32, device=x.device)
+    _check(lib.gmm_quantize_subchannel(_FMT[fmt], M, K, int(bk), _ptr(x), _ptr(codes), _ptr(scales),
+                                       _stream()), "gmm_quantize_subchannel")
+    return codes, scales
+
+
+def gmm_quantize_rhs_blockwise(w, bk=128, fmt="e4m3", layout="nk"):
+    """bf16 w [G, K, N] -> (uint8 codes [G, N, K] ("nk") or [G, K, N] ("kn"), f32 scales
+    [G, K / bk, N]): one dynamic scale per expert, block of bk contraction rows and column."""
+    import torch
+
+    lib = load()
+    _need(w, torch.bfloat16, "w", 3)
+    G, K, N = w.shape
+    lay = _LAYOUT[layout]
+    codes = torch.empty((G, N, K) if lay == RHS_NK else (G, K, N), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((G, K // bk if bk else 0, N), dtype=torch.float32, device=w.device)
+    _check(lib.gmm_quantize_rhs_blockwise(_FMT[fmt], lay, G, K, N, int(bk), _ptr(w), _ptr(codes),
+                                          _ptr(scales), _stream()), "gmm_quantize_rhs_blockwise")
+    return codes, scales
+
+
+def gmm_fwd_blockwise(lhs, lhs_scales, rhs, rhs_scales, group_sizes, bk=128, *,
+                      lhs_format="e4m3", out_dtype=None, out=None):
+    """Forward grouped matmul with block-wise scales: lhs uint8 codes [M, K] with
+    lhs_scales f32 [M, K / bk], rhs uint8 codes [G, N, K] with rhs_scales f32
+    [G, K / bk, N]; every block of bk contraction elements is scaled on its own."""
+    import torch
+
+    lib = load()
+    _need(lhs, torch.uint8, "lhs", 2)
+    _need(lhs_scales, torch.float32, "lhs_scales", 2)
+    _need(rhs, torch.uint8, "rhs", 3)
+    _need(rhs_scales, torch.float32, "rhs_scales", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = lhs.shape
+    G, N = rhs.shape[0], rhs.shape[1]
+    if rhs.shape[2] != K:
+        raise ValueError("rhs must be [G, N, K] codes matching the lhs width")
+    odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=odt, device=lhs.device)
+    else:
+        _need(out, odt, "out", 2)
+    _check(lib.gmm_fwd_blockwise(_FMT[lhs_format], OUT_F32 if odt == torch.float32 else OUT_BF16,
+                                 M, K, N, G, int(bk), _ptr(lhs), _ptr(lhs_scales), _ptr(rhs),
+                                 _ptr(rhs_scales), _ptr(group_sizes), _ptr(out), _stream()),
+           "gmm_fwd_blockwise")
     return out

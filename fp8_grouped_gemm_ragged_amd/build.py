@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgmm_fp8.so")
-SOURCES = ["api.hip", "quant_kernels.hip", "gmm_kernel.hip", "tgmm_kernel.hip", "swiglu_kernel.hip", "route_kernel.hip"]
+SOURCES = ["api.hip", "quant_kernels.hip", "gmm_kernel.hip", "tgmm_kernel.hip", "swiglu_kernel.hip", "route_kernel.hip",
+           "blockwise_kernel.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",

@@ -601,9 +601,90 @@ gmm_status_t gmm_quantize_rhs(int32_t format, int32_t channel_axis, int32_t layo
       overlaps(scales, (size_t)G * (channel_axis ? K : N) * 4, w, (size_t)G * K * N * 2) ||
       overlaps(scales, (size_t)G * (channel_axis ? K : N) * 4, codes, (size_t)G * K * N))
     return GMM_ERR_ALIAS;
-  return launch_quantize_rhs(format, channel_axis, layout == GMM_RHS_NK, G, K, N, w, codes,
+  return launch_quantize_rhs(format, channel_axis, layout == GMM_RHS_NK, G, K, N, K, w, codes,
                              scales, (hipStream_t)stream) == hipSuccess
              ? GMM_OK : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_quantize_rhs_blockwise(int32_t format, int32_t layout, int64_t G, int64_t K,
+                                        int64_t N, int64_t bk, const void* w, uint8_t* codes,
+                                        float* scales, gmm_stream_t stream) {
+  if (format != GMM_FP8_E4M3 && format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (layout != GMM_RHS_KN && layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  gmm_status_t s = check_shape(0, K, N, (int32_t)std::min<int64_t>(G, GMM_MAX_GROUPS + 1));
+  if (s != GMM_OK || G < 1 || G > 65535 || bk < 128 || bk % 128 || K % bk) return GMM_ERR_SHAPE;
+  if (!w || !codes || !scales) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)w, (const void*)codes, (const void*)scales})
+    if (!aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t sb = (size_t)G * (K / bk) * N * 4;
+  if (overlaps(codes, (size_t)G * K * N, w, (size_t)G * K * N * 2) ||
+      overlaps(scales, sb, w, (size_t)G * K * N * 2) || overlaps(scales, sb, codes, (size_t)G * K * N))
+    return GMM_ERR_ALIAS;
+  return launch_quantize_rhs(format, 0, layout == GMM_RHS_NK, G, K, N, bk, w, codes, scales,
+                             (hipStream_t)stream) == hipSuccess
+             ? GMM_OK : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_quantize_subchannel(int32_t format, int64_t M, int64_t K, int64_t bk,
+                                     const void* x, uint8_t* codes, float* scales,
+                                     gmm_stream_t stream) {
+  if (format != GMM_FP8_E4M3 && format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (M < 0 || M >= (int64_t(1) << 31) || K <= 0 || K > MAX_DIM) return GMM_ERR_SHAPE;
+  if ((bk != 128 && bk != 256 && bk != 512) || K % bk) return GMM_ERR_SHAPE;
+  if (M == 0) return GMM_OK;
+  if (!x || !codes || !scales) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)x, (const void*)codes, (const void*)scales})
+    if (!aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t xb = (size_t)M * K * 2, cb = (size_t)M * K, sb = (size_t)M * (K / bk) * 4;
+  if (overlaps(codes, cb, x, xb) || overlaps(scales, sb, x, xb) || overlaps(scales, sb, codes, cb))
+    return GMM_ERR_ALIAS;
+  trace("gmm_quantize_subchannel", M, K, bk, 1);
+  return launch_quantize_subchannel(format, x, M, K, (int)bk, codes, scales,
+                                    (hipStream_t)stream) == hipSuccess
+             ? GMM_OK : GMM_ERR_HIP;
+}
+
+gmm_status_t gmm_fwd_blockwise(int32_t lhs_format, int32_t out_dtype, int64_t M, int64_t K,
+                               int64_t N, int32_t G, int64_t bk, const uint8_t* lhs,
+                               const float* lhs_scales, const uint8_t* rhs,
+                               const float* rhs_scales, const int32_t* group_sizes, void* out,
+                               gmm_stream_t stream) {
+  if (lhs_format != GMM_FP8_E4M3 && lhs_format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
+  gmm_status_t s = check_shape(M, K, N, G);
+  if (s != GMM_OK) return s;
+  if (bk < 128 || bk % 128 || K % bk) return GMM_ERR_SHAPE;
+  if ((M / 128 + 1 + G) * (N / 128) >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
+  if (M > 0 && (!lhs || !lhs_scales || !out)) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)lhs, (const void*)lhs_scales, (const void*)rhs,
+                          (const void*)rhs_scales, (const void*)group_sizes, (const void*)out})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const int64_t nkb = K / bk;
+  const size_t ob = (size_t)M * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
+  if (overlaps(out, ob, lhs, (size_t)M * K) || overlaps(out, ob, lhs_scales, (size_t)M * nkb * 4) ||
+      overlaps(out, ob, rhs, (size_t)G * K * N) ||
+      overlaps(out, ob, rhs_scales, (size_t)G * nkb * N * 4) ||
+      overlaps(out, ob, group_sizes, (size_t)G * 4))
+    return GMM_ERR_ALIAS;
+  if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
+  trace("gmm_fwd_blockwise", M, K, N, G);
+  if (M == 0) return GMM_OK;
+  BsParams p{};
+  p.a = lhs;
+  p.b = rhs;
+  p.a_scale = lhs_scales;
+  p.b_scale = rhs_scales;
+  p.group_sizes = group_sizes;
+  p.out = out;
+  p.M = M;
+  p.K = (int32_t)K;
+  p.N = (int32_t)N;
+  p.G = G;
+  p.bk = (int32_t)bk;
+  p.out_f32 = out_dtype == GMM_OUT_F32;
+  return launch_gemm_blockwise(lhs_format, p, (hipStream_t)stream) == hipSuccess ? GMM_OK
+                                                                                 : GMM_ERR_HIP;
 }
 
 gmm_status_t gmm_static_scale_from_bound(float lo, float hi, int32_t format, float* scale) {

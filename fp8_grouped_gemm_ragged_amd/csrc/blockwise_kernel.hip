@@ -1,0 +1,284 @@
+// Forward grouped matmul with block-wise scales on gfx950 ("Support quantization for
+// tokamax gmm v2", review thread on the ops diff: a 3-D weight scale is block-wise
+// quantization; "add static LHS scaling support for GMM v2 FWD", review thread on the
+// lhs docstring: lhs scales of shape [M, num_blocks]).
+//
+// Block kb covers contraction elements [kb bk, (kb + 1) bk); the weight scale is
+// sB[g, kb, n] and the lhs scale sA[m, kb].  Because both vary along the contraction,
+// every block's partial sum is promoted on its own:
+//   out[m, n] = sum_kb RNE(RNE(partial_kb[m, n] * sA[m, kb]) * sB[g, kb, n])
+// in fp32 from +0 in increasing kb.
+//
+// gmm_bs_kernel: 128 x 128 output tiles, four waves of 64 x 64.  Each wave keeps a
+// partial accumulator (MFMA target) and an fp32 total; at the end of every block the
+// partial is scaled into the total and restarts from zero.  Operands are fp8 codes
+// staged through two LDS stages (one register stage ahead); the tile grid is the
+// expert-tile schedule of the other products with 128-row tiles.
+//
+// subchannel_quant_kernel: bf16 [M, K] -> codes and one dynamic scale per row and block
+// of bk columns (bk = 128, 256 or 512): bk / 8 lanes share a block and reduce its
+// abs-max with lane shuffles.
+#include <algorithm>
+
+#include "kernels.hpp"
+
+namespace gmm {
+
+namespace {
+
+constexpr int BS_BM = 128, BS_BN = 128, BS_BK = TILE_K, BS_NT = 256;
+constexpr int BS_TILE = BS_BM * BS_BK;  // bytes of one operand tile (A or B)
+constexpr int BS_BAND = 8;              // M-tiles per band of the tile order
+
+struct BsTile {
+  int g, row0, row_end, n0;
+};
+
+// Expert-tile schedule with BS_BM-row tiles (a tile never spans two groups), the tile
+// order in bands of BS_BAND M-tiles, XCD-aware: the workgroups of XCD x = wg % 8 take a
+// contiguous range of tiles.
+__device__ inline bool bs_schedule(const int32_t* __restrict__ gs, int G, int64_t M,
+                                   int n_ntiles, int* s_cum, int* s_off, BsTile& tc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    int carry_t = 0, carry_r = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + lane;
+      const int m = g < G ? max(gs[g], 0) : 0;
+      const int it = wave_incl_scan((m + BS_BM - 1) / BS_BM, lane);
+      const int ir = wave_incl_scan(m, lane);
+      if (g < G) {
+        s_cum[g + 1] = carry_t + it;
+        s_off[g + 1] = carry_r + ir;
+      }
+      carry_t += __shfl(it, 63, 64);
+      carry_r += __shfl(ir, 63, 64);
+    }
+    if (lane == 0) {
+      s_cum[0] = 0;
+      s_off[0] = 0;
+    }
+  }
+  __syncthreads();
+  const int total_mt = s_cum[G];
+  const int total = total_mt * n_ntiles;
+  const int wg = blockIdx.x;
+  bool ok = wg < total;
+  if (ok) {
+    const int xcd = wg & 7, j = wg >> 3, q = total >> 3, r = total & 7;
+    const int L = xcd * q + min(xcd, r) + j;
+    const int band = L / (BS_BAND * n_ntiles);
+    const int rem = L - band * BS_BAND * n_ntiles;
+    const int mt0 = band * BS_BAND;
+    const int gm = min(BS_BAND, total_mt - mt0);
+    const int nt = rem / gm;
+    const int mt = mt0 + (rem - nt * gm);
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cum[mid] <= mt) lo = mid; else hi = mid;
+    }
+    tc.g = lo;
+    tc.row0 = s_off[lo] + (mt - s_cum[lo]) * BS_BM;
+    tc.row_end = (int)min((int64_t)s_off[lo + 1], M);
+    tc.n0 = nt * BS_BN;
+    ok = tc.row0 < tc.row_end;
+  }
+  __syncthreads();  // the schedule arrays alias stage memory
+  tc.g = __builtin_amdgcn_readfirstlane(tc.g);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+  tc.n0 = __builtin_amdgcn_readfirstlane(tc.n0);
+  return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+}
+
+template <int A_FMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(BS_NT, BS_NT), amdgpu_waves_per_eu(2, 2)))
+void gmm_bs_kernel(BsParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BS_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BS_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BS_TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BS_TILE];
+  int* s_cum = reinterpret_cast<int*>(sA0);
+  int* s_off = reinterpret_cast<int*>(sB0);
+  static_assert((MAX_GROUPS + 1) * sizeof(int) <= BS_TILE, "schedule arrays fit a tile");
+
+  const int n_ntiles = p.N / BS_BN;
+  BsTile tc;
+  if (!bs_schedule(p.group_sizes, p.G, p.M, n_ntiles, s_cum, s_off, tc)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int K = p.K, nk = K / BS_BK, steps_per_block = p.bk / BS_BK, nkb = K / p.bk;
+  const int rows_here = min(tc.row_end - tc.row0, BS_BM);
+  // rows past the group's end and columns past N read zeros
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(p.a + (int64_t)tc.row0 * K, (uint32_t)rows_here * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rb =
+      make_rsrc(p.b + ((int64_t)tc.g * p.N + tc.n0) * K, (uint32_t)BS_BN * (uint32_t)K);
+
+  // staging: piece i of a tile = rows 32 i + tid / 8, 16 bytes at chunk tid % 8
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  v4u a_reg[4], b_reg[4];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (uint32_t)(i * 32 + lrow) * K + (uint32_t)kt * BS_BK + lchunk * 16;
+      a_reg[i] = buf_load16(ra, off);
+      b_reg[i] = buf_load16(rb, off);
+    }
+  };
+  auto store = [&](uint8_t* at, uint8_t* bt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<v4u*>(at + tile_off(i * 32 + lrow, lchunk)) = a_reg[i];
+      *reinterpret_cast<v4u*>(bt + tile_off(i * 32 + lrow, lchunk)) = b_reg[i];
+    }
+  };
+
+  // lane holds out[m = row0 + 64 wr + 32 i + frow][n = n0 + 64 wc + 32 j + 8 (r/4) +
+  // 4 fhalf + r%4] in register r of tile (i, j)
+  const int frow = lane & 31, fhalf = lane >> 5;
+  v16f part[2][2], total[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      part[i][j] = v16f{0};
+      total[i][j] = v16f{0};
+    }
+  // the lane's rows (clamped inside the group) and its columns' scale offsets
+  int64_t sa_row[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    sa_row[i] = (int64_t)max(min(tc.row0 + 64 * wr + 32 * i + frow, tc.row_end - 1), 0) * nkb;
+  const int64_t sb_base = (int64_t)tc.g * nkb * p.N + tc.n0 + 64 * wc + 4 * fhalf;
+
+  auto promote = [&](int kb) {
+    float sa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sa[i] = p.a_scale[sa_row[i] + kb];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      v4f sb[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        sb[r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          total[i][j][r] = add_rn(total[i][j][r], mul_rn(mul_rn(part[i][j][r], sa[i]), sb[r >> 2][r & 3]));
+        part[i][j] = v16f{0};
+      }
+    }
+  };
+
+  auto compute = [&](const uint8_t* at, const uint8_t* bt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8i af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = lds_read_frag(at, 64 * wr + 32 * i + frow, 4 * ks + 2 * fhalf);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = lds_read_frag(bt, 64 * wc + 32 * j + frow, 4 * ks + 2 * fhalf);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          part[i][j] = mfma32x32x64<FMT_E4M3, A_FMT>(bf[j], af[i], part[i][j]);
+    }
+  };
+
+  load(0);
+  store(sA0, sB0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool odd = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+    compute(odd ? sA1 : sA0, odd ? sB1 : sB0);
+    if ((kt + 1) % steps_per_block == 0) promote(kt / steps_per_block);
+    if (kt + 1 < nk) store(odd ? sA0 : sA1, odd ? sB0 : sB1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: rows of the group only ----
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = tc.row0 + 64 * wr + 32 * i + frow;
+    if (m >= tc.row_end) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = tc.n0 + 64 * wc + 32 * j + 8 * r4 + 4 * fhalf;
+        const int64_t idx = (int64_t)m * p.N + n;
+        const v4f o = {total[i][j][4 * r4], total[i][j][4 * r4 + 1], total[i][j][4 * r4 + 2],
+                       total[i][j][4 * r4 + 3]};
+        if (p.out_f32) {
+          *reinterpret_cast<v4f*>((float*)p.out + idx) = o;
+        } else {
+          v2u v;
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
+        }
+      }
+    }
+  }
+}
+
+// One thread per 8 consecutive elements of a row; the bk / 8 lanes of a block (aligned
+// within the wave) reduce its abs-max with xor shuffles, then each quantizes its 8.
+template <int FMT>
+__global__ __launch_bounds__(256) void subchannel_quant_kernel(const uint16_t* __restrict__ x,
+                                                               int64_t M, int64_t K, int bk,
+                                                               uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales) {
+  const int64_t per_row = K / 8, total = M * per_row;
+  const int lanes = bk / 8;  // 16, 32 or 64: divides both 64 and per_row
+  const int lane = threadIdx.x & 63;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * 256) {
+    const v4u w = *reinterpret_cast<const v4u*>(x + t * 8);
+    uint32_t m = absmax_bits16(w, 0u);
+    for (int d = lanes >> 1; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+    const float s = __fdiv_rn(__uint_as_float(m << 16), qmax<FMT>());
+    reinterpret_cast<v2u*>(codes)[t] = quant8<FMT>(w, inv_from_scale(s));
+    if ((lane & (lanes - 1)) == 0) {
+      const int64_t row = t / per_row, c8 = t - row * per_row;
+      scales[row * (K / bk) + c8 / lanes] = s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_blockwise(int a_fmt, const BsParams& p, hipStream_t st) {
+  const int64_t max_mt = (p.M + BS_BM - 1) / BS_BM + p.G;
+  const int64_t grid = max_mt * (p.N / BS_BN);
+  if (grid == 0 || p.M == 0) return hipSuccess;
+  if (a_fmt == FMT_E4M3)
+    hipLaunchKernelGGL(gmm_bs_kernel<FMT_E4M3>, dim3((unsigned)grid), dim3(BS_NT), 0, st, p);
+  else if (a_fmt == FMT_E5M2)
+    hipLaunchKernelGGL(gmm_bs_kernel<FMT_E5M2>, dim3((unsigned)grid), dim3(BS_NT), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_subchannel(int fmt, const void* x, int64_t M, int64_t K, int bk,
+                                      uint8_t* codes, float* scales, hipStream_t st) {
+  const int64_t total = M * (K / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  if (fmt == FMT_E4M3)
+    hipLaunchKernelGGL(subchannel_quant_kernel<FMT_E4M3>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const uint16_t*)x, M, K, bk, codes, scales);
+  else
+    hipLaunchKernelGGL(subchannel_quant_kernel<FMT_E5M2>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const uint16_t*)x, M, K, bk, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace gmm

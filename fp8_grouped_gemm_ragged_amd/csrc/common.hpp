@@ -72,6 +72,16 @@ __device__ inline uint32_t cvt_pk(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
 }
 
+// Abs-max of bf16 values through their bit patterns: for finite bf16, |x| orders like
+// the unsigned integer (bits & 0x7fff).  Returns the larger magnitude bits seen.
+__device__ inline uint32_t absmax_bits16(v4u w, uint32_t m) {
+  const uint32_t mask = 0x7fff7fffu;
+  uint32_t a = w.x & mask, b = w.y & mask, c = w.z & mask, d = w.w & mask;
+  uint32_t lo = max(max(a & 0xffffu, b & 0xffffu), max(c & 0xffffu, d & 0xffffu));
+  uint32_t hi = max(max(a >> 16, b >> 16), max(c >> 16, d >> 16));
+  return max(m, max(lo, hi));
+}
+
 // An fp32 product and an fp32 sum, each rounded to nearest on its own: never contracted
 // into a fused multiply-add (HIP's __fmul_rn / __fadd_rn are plain operators, which the
 // compiler fuses under its default contraction).

@@ -69,6 +69,20 @@ struct TgmmSegParams {
   int64_t seg_row;
 };
 
+// forward with block-wise scales: out[M, N] from fp8 A [M, K] (scales [M, K / bk]) and
+// fp8 B [G, N, K] (scales [G, K / bk, N])
+struct BsParams {
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* a_scale;
+  const float* b_scale;
+  const int32_t* group_sizes;
+  void* out;
+  int64_t M;
+  int32_t K, N, G, bk;
+  int32_t out_f32;
+};
+
 int64_t tgmm_segment_row_bytes(int64_t M, int G);
 // plan words: off, cnt, seg (G + 1), wide, final scale per group, one any-wide flag
 inline int64_t tgmm_plan_words(int G) { return 5 * (int64_t)G + 2; }
@@ -100,8 +114,13 @@ hipError_t launch_dynamic_scales(int fmt, const void* x, int64_t R, int64_t C,
 hipError_t launch_quantize_rows(int fmt, const void* x, int64_t R, int64_t C,
                                 const float* scale_blk, float inv_static, uint8_t* codes,
                                 hipStream_t st);
+// axis 0 scales every (g, block of kblk contraction rows, n): [G, K / kblk, N] (kblk = K is
+// per channel); axis 1 every (g, k): [G, K]
 hipError_t launch_quantize_rhs(int fmt, int axis, int layout_nk, int64_t G, int64_t K,
-                               int64_t N, const void* w, uint8_t* codes, float* scales,
-                               hipStream_t st);
+                               int64_t N, int64_t kblk, const void* w, uint8_t* codes,
+                               float* scales, hipStream_t st);
+hipError_t launch_gemm_blockwise(int a_fmt, const BsParams& p, hipStream_t st);
+hipError_t launch_quantize_subchannel(int fmt, const void* x, int64_t M, int64_t K, int bk,
+                                      uint8_t* codes, float* scales, hipStream_t st);
 
 }  // namespace gmm

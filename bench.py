@@ -350,6 +350,50 @@ def route_block(g, reps=10):
     return res
 
 
+def blockwise_block(g, reps=10):
+    """The forward with block-wise scales at the Mixtral gate|up shape (G=8, M=16384,
+    K=4096, N=28672): gmm_fwd_blockwise on sub-channel e4m3 lhs codes ([M, K/bk] scales)
+    and block-scaled e4m3 weights ([G, K/bk, N] scales) for bk 128 and 512, against the
+    fp8 MFMA peak; the lhs quantization timed apart.  HIP events on the current stream."""
+    import torch
+
+    from synth.workloads import WORKLOADS, normal_bf16
+
+    wl = WORKLOADS["mixtral_gate_up"]
+    G, M, K, N = wl.G, wl.M, wl.K, wl.N
+    gs = torch.tensor(wl.group_sizes(), dtype=torch.int32, device="cuda")
+    x = normal_bf16((M, K), 1.0, wl.seed * 100 + 11, "cuda")
+    w = normal_bf16((G, K, N), 0.02, wl.seed * 100 + 12, "cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    flop = 2.0 * M * K * N
+    res = {"workload": wl.name, "G": G, "M": M, "K": K, "N": N}
+    for bk in (128, 512):
+        codes, s = g.gmm_quantize_subchannel(x, bk)
+        wq, ws = g.gmm_quantize_rhs_blockwise(w, bk)
+        t = timed(lambda: g.gmm_fwd_blockwise(codes, s, wq, ws, gs, bk, out=out))
+        tq = timed(lambda: g.gmm_quantize_subchannel(x, bk))
+        res[f"bk{bk}"] = {"ms": round(t, 4), "TFLOP/s": round(flop / t / 1e9, 1),
+                          "frac_peak": round(flop / t / 1e9 / FP8_PEAK_TFLOPS, 4),
+                          "lhs_quantize_ms": round(tq, 4)}
+        del codes, s, wq, ws
+    del x, w, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(step, rows, cols):
     """Time the CPU oracle on a bounded sample: the first `rows` rows (with their group
     split), all K, the first `cols` columns of the merged weight; fwd + dlhs + tgmm."""
@@ -483,6 +527,7 @@ def main():
     if not args.no_swiglu:
         line["swiglu_block"] = swiglu_block(g)
         line["route_block"] = route_block(g)
+        line["blockwise_block"] = blockwise_block(g)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)
     print(json.dumps(line), flush=True)

@@ -6,8 +6,9 @@
 // Block kb covers contraction elements [kb bk, (kb + 1) bk); the weight scale is
 // sB[g, kb, n] and the lhs scale sA[m, kb].  Because both vary along the contraction,
 // every block's partial sum is promoted on its own:
-//   out[m, n] = sum_kb RNE(RNE(partial_kb[m, n] * sA[m, kb]) * sB[g, kb, n])
-// in fp32 from +0 in increasing kb.
+//   out[m, n] = sum_kb partial_kb[m, n] * sA[m, kb] * sB[g, kb, n]
+// in fp32 from +0 in increasing kb, each block added with one fused multiply-add by
+// RNE(sA * sB) (a rounding order of the same sum; the products are fp32-accurate).
 //
 // gmm_bs_kernel: 128 x 128 output tiles, four waves of 64 x 64.  Each wave keeps a
 // partial accumulator (MFMA target) and an fp32 total; at the end of every block the
@@ -167,6 +168,8 @@ void gmm_bs_kernel(BsParams p) {
       for (int r4 = 0; r4 < 4; ++r4)
         sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
   };
+  // total += partial * RNE(sA * sB): one fused multiply-add per value; the partial
+  // restarts from zero
   auto promote = [&]() {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -174,7 +177,8 @@ void gmm_bs_kernel(BsParams p) {
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          total[i][j][r] = add_rn(total[i][j][r], mul_rn(mul_rn(part[i][j][r], sa[i]), sb[j][r >> 2][r & 3]));
+          total[i][j][r] = __builtin_fmaf(part[i][j][r], mul_rn(sa[i], sb[j][r >> 2][r & 3]),
+                                          total[i][j][r]);
         part[i][j] = v16f{0};
       }
   };

@@ -291,11 +291,11 @@ gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu
  *
  * gmm_fwd_blockwise - forward grouped matmul with scales that vary along K:
  *
- *   out[m, n] = RNE_out( sum_kb RNE(RNE(partial_kb[m, n] * lhs_scales[m, kb])
- *                                   * rhs_scales[g, kb, n]) ),
+ *   out[m, n] = RNE_out( sum_kb partial_kb[m, n] * lhs_scales[m, kb] * rhs_scales[g, kb, n] ),
  *   partial_kb[m, n] = sum_{k in block kb} lhs[m, k] * rhs[g, n, k]   (fp32),
  *
- * the sum over kb in fp32 from +0 in increasing kb.
+ * the sum over kb in fp32 from +0 in increasing kb, each block added with one fused
+ * multiply-add by RNE(lhs_scales[m, kb] * rhs_scales[g, kb, n]).
  * lhs          fp8 codes [M, K] (lhs_format), lhs_scales f32 [M, K / bk] (from
  *              gmm_quantize_subchannel or any caller).
  * rhs          e4m3 codes [G, N, K] (contraction contiguous), rhs_scales f32

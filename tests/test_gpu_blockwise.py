@@ -99,3 +99,32 @@ def test_one_block_matches_gmm_fwd(lib):
     sync()
     R = to_np(ref).astype(np.float64) * to_np(s)[:, :1].astype(np.float64)
     assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL
+
+
+def test_blockwise_mixtral_full_size_sampled(lib):
+    """gmm_fwd_blockwise at the Mixtral gate|up shape with bk = 128, as the benchmark
+    launches it: sampled rows x sampled columns against the oracle (every scale depends
+    on its own row or column only, so the samples are quantized independently)."""
+    from synth.workloads import WORKLOADS
+    from tests.test_gpu_full import sample_cols, sample_rows, sampled_sizes
+
+    wl = WORKLOADS["mixtral_gate_up"]
+    G, M, K, N, bk = wl.G, wl.M, wl.K, wl.N, 128
+    sizes = wl.group_sizes()
+    x = normal_bf16((M, K), 1.0, wl.seed * 100 + 11, DEV)
+    w = normal_bf16((G, K, N), 0.02, wl.seed * 100 + 12, DEV)
+    codes, s = lib.gmm_quantize_subchannel(x, bk)
+    wq, ws = lib.gmm_quantize_rhs_blockwise(w, bk)
+    out = lib.gmm_fwd_blockwise(codes, s, wq, ws, gs_tensor(sizes), bk, out_dtype=torch.float32)
+    sync()
+    rng = np.random.default_rng(17)
+    rows = sample_rows(sizes, rng)
+    cols = sample_cols(N, rng, 48)
+    ri, ci = torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)
+    c_ref, s_ref = quantize_subchannel(bf16_to_bits(x[ri]), "e4m3", bk)
+    wc_ref, ws_ref = quantize_rhs_blockwise(bf16_to_bits(w[:, :, ci]), "e4m3", bk)
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_fwd_blockwise_ref(c_ref, "e4m3", s_ref, wc_ref, "e4m3", ws_ref, sub, bk)
+    err = group_rel_err(to_np(out[ri][:, ci]), R, group_row_ranges(sub))
+    print(f"sampled max group relative error {err:.3e}", flush=True)
+    assert err <= TOL, err

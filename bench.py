@@ -436,7 +436,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path runs "
-              "on a single MI355X and this build has no multi-GPU mode.", file=sys.stderr)
+              "on a single MI355X and the library has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
     import torch
 

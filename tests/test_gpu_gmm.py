@@ -5,7 +5,6 @@ import pytest
 import torch
 
 import oracle.ops as ops
-from oracle.gmm import gmm_fwd_ref
 from oracle.quant import quantize_rhs_per_channel
 from synth.workloads import WORKLOADS
 from tests.gpu_util import DEV, channel_varied, gen, gs_tensor, sync

@@ -12,7 +12,7 @@ from oracle.quant import (
     quantize_rowblock,
     quantize_static,
 )
-from tests.gpu_util import DEV, channel_varied, gen, gs_tensor, sync
+from tests.gpu_util import DEV, channel_varied, gen, gs_tensor
 from tests.parity import to_np
 
 pytestmark = pytest.mark.gpu

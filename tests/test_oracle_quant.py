@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.fp8 import bf16_bits_to_f32, decode_fp8, encode_fp8
+from oracle.fp8 import bf16_bits_to_f32, decode_fp8
 from oracle.quant import (
     dynamic_scale_from_amax,
     quantize_rhs_per_channel,

@@ -29,6 +29,8 @@ def ids_tensor(ids):
     (777, 8, 64, 0.05, 1408),    # top-8 with dropped choices, a ragged last chunk
     (3000, 6, 1024, 0.1, 72),    # the largest expert count
     (300, 4, 3, 0.9, 256),       # mostly dropped
+    (500, 3, 5, 0.2, 16),        # odd top-k, 32-byte rows
+    (40, 64, 128, 0.0, 64),      # the largest top-k
 ])
 def test_permute_matches_oracle(lib, T, k, G, drop, H):
     if G < k:  # fewer experts than choices: repeats allowed (random ids, some out of range)
@@ -54,8 +56,9 @@ def test_permute_matches_oracle(lib, T, k, G, drop, H):
 
 
 @pytest.mark.parametrize("weighted", [True, False])
-def test_unpermute_matches_oracle(lib, weighted):
-    T, k, G, H = 1500, 4, 16, 2048
+@pytest.mark.parametrize("k", [1, 3, 4, 6])
+def test_unpermute_matches_oracle(lib, weighted, k):
+    T, G, H = 1500, 16, 2048
     ids = topk_expert_ids(T, k, G, 1.2, 910, 0.1)
     _, ros, _ = lib.gmm_permute(ids_tensor(ids), G)
     _, ros_r, _ = permute_ref(ids, G)

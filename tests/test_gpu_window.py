@@ -93,3 +93,15 @@ def test_tgmm_local(lib, problem, a, b):
     for j in range(b):  # empty local experts: +0.0 slabs
         if SIZES[a + j] == 0:
             assert (to_np(out)[j].view(np.uint32) == 0).all()
+
+
+@pytest.mark.parametrize("a,b", [(2, 3), (7, 1)])
+def test_tgmm_local_bf16_is_the_rounded_f32(lib, problem, a, b):
+    """The window's bf16 slabs are the RNE of its f32 slabs, bit for bit."""
+    from oracle.fp8 import f32_to_bf16_bits
+
+    d = problem
+    o32 = lib.tgmm_drhs_local(d["x"], d["grad"], gs_tensor(SIZES), a, b, out_dtype=torch.float32)
+    o16 = lib.tgmm_drhs_local(d["x"], d["grad"], gs_tensor(SIZES), a, b)
+    sync()
+    assert np.array_equal(to_np(o16), f32_to_bf16_bits(to_np(o32)))

@@ -60,6 +60,7 @@ from .gmm import (  # noqa: F401
 from .route import gather_rows_ref, permute_ref, unpermute_ref  # noqa: F401
 from .blockwise import (  # noqa: F401
     gmm_fwd_blockwise_ref,
+    quantize_folded,
     quantize_rhs_blockwise,
     quantize_subchannel,
 )

@@ -22,9 +22,15 @@ recipe of ``quant`` (s = RNE(amax / qmax), inverse 0 when s is 0 or 1/s overflow
 clamp then round) with the abs-max taken over each block: a row's bk elements for the
 lhs, a column's bk elements of one expert for the weights.
 
+The dlhs can also run on the forward's weight copy, whose per-channel scales s[g, n]
+lie on the dlhs contraction: they are folded into the gradient before it is quantized
+(``quantize_folded``), and the product then takes unit output-channel scales.
+
 Parity: pinned by brute force with exact rationals on tiny inputs, by the one-block
 reduction to the per-channel forward, by block-constant scales factoring out, and by the
-quantizers' brute-force block abs-max (``tests/test_oracle_blockwise.py``).
+quantizers' brute-force block abs-max; the fold by unit and power-of-two scales
+(identical codes, scales multiplied exactly) and by the folded dlhs against the float64
+definition within the quantization bound (``tests/test_oracle_blockwise.py``).
 """
 
 import numpy as np
@@ -92,3 +98,25 @@ def gmm_fwd_blockwise_ref(a_codes, a_fmt, a_scale_kb, b_codes, b_fmt, b_scale_kb
             acc = (acc + v.astype(np.float32)).astype(np.float32)
         out[r0:r1] = acc
     return _finish(out, out_dtype)
+
+
+def quantize_folded(grad_bits, col_scales, group_sizes, fmt, block_rows=128):
+    """The dlhs variant that folds the forward's per-channel weight scales into the
+    gradient: y[m, n] = RNE_f32(grad[m, n] * s_fwd[g(m), n]) for the group g(m) of row m,
+    then the dynamic 128-row-block recipe on y (abs-max over the block's full width,
+    s = RNE(amax / qmax), inverse 0 when s is 0 or 1/s overflows, clamp then round).
+    Returns (codes [M, N], scales [ceil(M / block_rows)]).  The dlhs on these codes uses
+    the forward's codes with unit output-channel scales."""
+    x = bf16_bits_to_f32(np.asarray(grad_bits, np.uint16))
+    M, N = x.shape
+    off = group_offsets(group_sizes, M)
+    gid = np.repeat(np.arange(len(group_sizes)), np.diff(off))
+    y = (x * np.asarray(col_scales, np.float32)[gid]).astype(np.float32)
+    nb = -(-M // block_rows)
+    amax = np.zeros(nb, np.float32)
+    for b in range(nb):
+        blk = y[b * block_rows:(b + 1) * block_rows]
+        amax[b] = np.abs(blk).max() if blk.size else 0.0
+    s, inv = dynamic_scale_from_amax(amax, fmt)
+    codes = _quantize(y, np.repeat(inv, block_rows)[:M, None], fmt)
+    return codes, s.astype(np.float32)

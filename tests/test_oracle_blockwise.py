@@ -106,3 +106,44 @@ def test_quantizers_block_absmax_brute_force(bk):
                 assert ws[g, kb, n] == np.float32(amax / np.float32(57344.0))
     # the largest element of every block maps to +-qmax
     assert np.all(np.isin((codes & 0x7F).reshape(M, K // bk, bk).max(axis=2), [0x7E, 0x00]))
+
+
+def test_fold_by_unit_and_power_of_two_scales():
+    """Folding scales of 1 is the plain dynamic quantization; folding 2^e multiplies exactly,
+    so the codes stay and the block scales gain the factor 2^e exactly."""
+    from oracle.blockwise import quantize_folded
+    from oracle.quant import quantize_rowblock
+
+    rng = np.random.default_rng(34)
+    M, N, G = 300, 256, 3
+    gs = np.array([100, 0, 200], np.int32)
+    gb = bits(rng, (M, N), 1e-3)
+    c1, s1 = quantize_folded(gb, np.ones((G, N), np.float32), gs, "e5m2")
+    c0, s0, _ = quantize_rowblock(gb, "e5m2")
+    assert np.array_equal(c1, c0) and np.array_equal(s1, s0)
+    c2, s2 = quantize_folded(gb, np.full((G, N), 2.0 ** 7, np.float32), gs, "e5m2")
+    assert np.array_equal(c2, c0) and np.array_equal(s2, s0 * np.float32(2.0 ** 7))
+
+
+def test_folded_dlhs_matches_the_definition():
+    """dlhs through the fold (one weight copy, per-n forward scales) against the float64
+    sum_n grad[m, n] W[g, k, n] s[g, n], within the e5m2 and e4m3 rounding of the operands."""
+    from oracle.blockwise import quantize_folded
+    from oracle.gmm import gmm_dlhs_ref, row_scales
+
+    rng = np.random.default_rng(35)
+    M, N, K, G = 256, 512, 128, 2
+    gs = np.array([150, 106], np.int32)
+    gb = bits(rng, (M, N), 1e-3)
+    wb = bits(rng, (G, K, N), 0.02)
+    wq, ws = quantize_rhs_per_channel(wb, "e4m3", "n")  # the forward copy: s[g, n]
+    codes, s = quantize_folded(gb, ws, gs, "e5m2")
+    R = gmm_dlhs_ref(codes, "e5m2", row_scales(s, M), wq, "e4m3", np.ones((G, K), np.float32), gs)
+    x = bf16_bits_to_f32(gb).astype(np.float64)
+    W = tdec(wq, "e4m3") * ws[:, None, :].astype(np.float64)
+    gid = np.repeat(np.arange(G), gs)
+    exact = np.stack([W[gid[m]] @ x[m] for m in range(M)])
+    absum = np.stack([np.abs(W[gid[m]]) @ np.abs(x[m]) for m in range(M)])
+    # e5m2 relative rounding 2^-3 per gradient element (plus its subnormal floor)
+    assert np.all(np.abs(R - exact) <= absum * 2.0 ** -3 + 1e-12)
+    assert np.abs(R - exact).max() < 0.1 * np.abs(exact).max()

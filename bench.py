@@ -354,7 +354,9 @@ def blockwise_block(g, reps=10):
     """The forward with block-wise scales at the Mixtral gate|up shape (G=8, M=16384,
     K=4096, N=28672): gmm_fwd_blockwise on sub-channel e4m3 lhs codes ([M, K/bk] scales)
     and block-scaled e4m3 weights ([G, K/bk, N] scales) for bk 128 and 512, against the
-    fp8 MFMA peak; the lhs quantization timed apart.  HIP events on the current stream."""
+    fp8 MFMA peak; the lhs quantization timed apart; and the one-weight-copy dlhs (the
+    gradient folded with the forward's scales, then the fp8-A dlhs on the forward's
+    codes).  HIP events on the current stream."""
     import torch
 
     from synth.workloads import WORKLOADS, normal_bf16
@@ -389,7 +391,19 @@ def blockwise_block(g, reps=10):
                           "frac_peak": round(flop / t / 1e9 / FP8_PEAK_TFLOPS, 4),
                           "lhs_quantize_ms": round(tq, 4)}
         del codes, s, wq, ws
-    del x, w, out
+    # the one-weight-copy dlhs: the gradient folded with the forward's per-channel scales,
+    # then the fp8-A dlhs on the forward's codes ([G, K, N]) with unit output scales
+    grad = normal_bf16((M, N), 1e-3, wl.seed * 100 + 13, "cuda")
+    wq, ws = g.gmm_quantize_rhs(w, "e4m3", 0, "kn")
+    ones = torch.ones((G, K), dtype=torch.float32, device="cuda")
+    dl = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    codes, s = g.gmm_quantize_folded(grad, ws, gs)
+    tq = timed(lambda: g.gmm_quantize_folded(grad, ws, gs))
+    td = timed(lambda: g.gmm_dlhs(codes, wq, ones, gs, grad_scaling="dynamic", grad_scales=s,
+                                  rhs_layout="kn", out=dl))
+    res["folded_dlhs"] = {"quantize_ms": round(tq, 4), "dlhs_ms": round(td, 4),
+                          "dlhs_TFLOP/s": round(flop / td / 1e9, 1)}
+    del x, w, out, grad, wq, ws, ones, dl, codes, s
     torch.cuda.empty_cache()
     return res
 

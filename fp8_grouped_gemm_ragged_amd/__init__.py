@@ -21,6 +21,7 @@ __all__ = [
     "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8", "gmm_swiglu_bwd",
     "gmm_permute", "gmm_unpermute", "gmm_fwd_local", "gmm_dlhs_local", "tgmm_drhs_local",
     "gmm_fwd_blockwise", "gmm_quantize_subchannel", "gmm_quantize_rhs_blockwise",
+    "gmm_quantize_folded",
     "gmm_quantize_rhs", "gmm_static_scale_from_bound", "gmm_workspace_size",
     "gmm_status_string", "gmm_version", "E4M3", "E5M2", "STATIC", "DYNAMIC", "BLOCK_ROWS",
 ]
@@ -73,6 +74,7 @@ _SIGNATURES = {
     "gmm_fwd_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
     "gmm_quantize_subchannel": [_I32, _I64, _I64, _I64, _P, _P, _P, _P],
     "gmm_quantize_rhs_blockwise": [_I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _P],
+    "gmm_quantize_folded": [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_fwd_local": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_dlhs_local": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "tgmm_drhs_local": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -629,3 +631,28 @@ def gmm_fwd_blockwise(lhs, lhs_scales, rhs, rhs_scales, group_sizes, bk=128, *,
                                  _ptr(rhs_scales), _ptr(group_sizes), _ptr(out), _stream()),
            "gmm_fwd_blockwise")
     return out
+
+
+def gmm_quantize_folded(grad, col_scales, group_sizes, fmt="e5m2"):
+    """The folded gradient of the one-weight-copy dlhs: codes and 128-row-block scales of
+    RNE_f32(grad[m, n] * col_scales[g(m), n]).  grad bf16 [M, N], col_scales f32 [G, N]
+    (the forward's per-channel weight scales).  Feed the result to gmm_dlhs with
+    grad_scales=scales, the forward's codes laid out [G, K, N] and all-one rhs_scales."""
+    import torch
+
+    lib = load()
+    _need(grad, torch.bfloat16, "grad", 2)
+    _need(col_scales, torch.float32, "col_scales", 2)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, N = grad.shape
+    G = group_sizes.shape[0]
+    if tuple(col_scales.shape) != (G, N):
+        raise ValueError("col_scales must be [G, N]")
+    codes = torch.empty((M, N), dtype=torch.uint8, device=grad.device)
+    scales = torch.empty(_nblocks(M), dtype=torch.float32, device=grad.device)
+    ws_n = _nblocks(M) * 32
+    ws = _workspace(ws_n, grad.device)
+    _check(lib.gmm_quantize_folded(_FMT[fmt], M, N, G, _ptr(grad), _ptr(col_scales),
+                                   _ptr(group_sizes), _ptr(codes), _ptr(scales), _ptr(ws), ws_n,
+                                   _stream()), "gmm_quantize_folded")
+    return codes, scales

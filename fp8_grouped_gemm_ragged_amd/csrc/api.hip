@@ -644,6 +644,39 @@ gmm_status_t gmm_quantize_subchannel(int32_t format, int64_t M, int64_t K, int64
              ? GMM_OK : GMM_ERR_HIP;
 }
 
+gmm_status_t gmm_quantize_folded(int32_t format, int64_t M, int64_t N, int32_t G,
+                                 const void* grad, const float* col_scales,
+                                 const int32_t* group_sizes, uint8_t* codes, float* scales,
+                                 void* workspace, size_t workspace_bytes, gmm_stream_t stream) {
+  if (format != GMM_FP8_E4M3 && format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  gmm_status_t s = check_shape(M, 128, N, G);
+  if (s != GMM_OK) return s;
+  if (M == 0) return GMM_OK;
+  if (!grad || !col_scales || !group_sizes || !codes || !scales) return GMM_ERR_NULL;
+  for (const void* ptr : {grad, (const void*)col_scales, (const void*)group_sizes,
+                          (const void*)codes, (const void*)scales, (const void*)workspace})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const size_t ws_need = (size_t)nblocks(M) * AMAX_SPLIT * 4;
+  if (!workspace || workspace_bytes < ws_need) return GMM_ERR_WORKSPACE;
+  const size_t gb = (size_t)M * N * 2, cb = (size_t)M * N, sb = (size_t)nblocks(M) * 4,
+               csb = (size_t)G * N * 4, gsb = (size_t)G * 4;
+  const struct { const void* p; size_t n; } outs[] = {{codes, cb}, {scales, sb}, {workspace, ws_need}};
+  for (size_t i = 0; i < 3; ++i) {
+    if (overlaps(outs[i].p, outs[i].n, grad, gb) || overlaps(outs[i].p, outs[i].n, col_scales, csb) ||
+        overlaps(outs[i].p, outs[i].n, group_sizes, gsb))
+      return GMM_ERR_ALIAS;
+    for (size_t j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return GMM_ERR_ALIAS;
+  }
+  if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
+  trace("gmm_quantize_folded", M, N, 0, G);
+  return launch_quantize_folded(format, grad, M, N, col_scales, group_sizes, G,
+                                (uint32_t*)workspace, scales, codes,
+                                (hipStream_t)stream) == hipSuccess
+             ? GMM_OK
+             : GMM_ERR_HIP;
+}
+
 gmm_status_t gmm_fwd_blockwise(int32_t lhs_format, int32_t out_dtype, int64_t M, int64_t K,
                                int64_t N, int32_t G, int64_t bk, const uint8_t* lhs,
                                const float* lhs_scales, const uint8_t* rhs,

@@ -263,6 +263,119 @@ __global__ __launch_bounds__(256) void subchannel_quant_kernel(const uint16_t* _
   }
 }
 
+// ---- the folded gradient of the one-weight-copy dlhs ----
+// y[m, n] = RNE(grad[m, n] * s[g(m), n]); its 128-row-block abs-max (as fp32 bits) over
+// AMAX_SPLIT row slices per block, then the codes of y.  Every workgroup builds the
+// group row offsets in LDS and looks each row's group up once.
+__device__ inline void fold_offsets(const int32_t* __restrict__ gs, int G, int* s_off) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int carry = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + lane;
+      const int incl = wave_incl_scan(g < G ? max(gs[g], 0) : 0, lane);
+      if (g < G) s_off[g + 1] = carry + incl;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_off[0] = 0;
+  }
+  __syncthreads();
+}
+
+// group of row r: the last g with s_off[g] <= r (rows past every group: the last group)
+__device__ inline int fold_group(const int* s_off, int G, int64_t r) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_off[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// 8 consecutive bf16 gradient values times their columns' scales, each product rounded
+__device__ inline void fold8(v4u w, const float* __restrict__ sc, float (&y)[8]) {
+  const v4f s0 = *reinterpret_cast<const v4f*>(sc);
+  const v4f s1 = *reinterpret_cast<const v4f*>(sc + 4);
+  y[0] = mul_rn(bf16_lo(w.x), s0[0]); y[1] = mul_rn(bf16_hi(w.x), s0[1]);
+  y[2] = mul_rn(bf16_lo(w.y), s0[2]); y[3] = mul_rn(bf16_hi(w.y), s0[3]);
+  y[4] = mul_rn(bf16_lo(w.z), s1[0]); y[5] = mul_rn(bf16_hi(w.z), s1[1]);
+  y[6] = mul_rn(bf16_lo(w.w), s1[2]); y[7] = mul_rn(bf16_hi(w.w), s1[3]);
+}
+
+__global__ __launch_bounds__(256) void fold_amax_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t M, int64_t N,
+                                                        const float* __restrict__ col_scales,
+                                                        const int32_t* __restrict__ gs, int G,
+                                                        uint32_t* __restrict__ partial) {
+  __shared__ int s_off[MAX_GROUPS + 1];
+  __shared__ uint32_t red[4];
+  fold_offsets(gs, G, s_off);
+  const int b = blockIdx.x, sl = blockIdx.y;
+  constexpr int rows_per = BLOCK_ROWS / AMAX_SPLIT;
+  const int64_t r0 = (int64_t)b * BLOCK_ROWS + (int64_t)sl * rows_per;
+  const int64_t r1 = min(r0 + rows_per, M);
+  uint32_t m = 0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const float* sc = col_scales + (int64_t)fold_group(s_off, G, r) * N;
+    for (int64_t j = threadIdx.x; j < N / 8; j += 256) {
+      float y[8];
+      fold8(reinterpret_cast<const v4u*>(x + r * N)[j], sc + j * 8, y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(y[e]) & 0x7fffffffu);
+    }
+  }
+  // block maximum
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partial[b * AMAX_SPLIT + sl] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+template <int FMT>
+__global__ void fold_scales_kernel(const uint32_t* __restrict__ partial, int nb,
+                                   float* __restrict__ scales) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nb) return;
+  uint32_t m = 0;
+#pragma unroll
+  for (int s = 0; s < AMAX_SPLIT; ++s) m = max(m, partial[b * AMAX_SPLIT + s]);
+  scales[b] = __fdiv_rn(__uint_as_float(m), qmax<FMT>());
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void fold_quantize_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t M, int64_t N,
+                                                            const float* __restrict__ col_scales,
+                                                            const int32_t* __restrict__ gs, int G,
+                                                            const float* __restrict__ scales,
+                                                            uint8_t* __restrict__ codes) {
+  __shared__ int s_off[MAX_GROUPS + 1];
+  fold_offsets(gs, G, s_off);
+  const int b = blockIdx.x, sl = blockIdx.y;
+  constexpr int rows_per = BLOCK_ROWS / AMAX_SPLIT;
+  const int64_t r0 = (int64_t)b * BLOCK_ROWS + (int64_t)sl * rows_per;
+  const int64_t r1 = min(r0 + rows_per, M);
+  const float inv = inv_from_scale(scales[b]);
+  for (int64_t r = r0; r < r1; ++r) {
+    const float* sc = col_scales + (int64_t)fold_group(s_off, G, r) * N;
+    for (int64_t j = threadIdx.x; j < N / 8; j += 256) {
+      float y[8];
+      fold8(reinterpret_cast<const v4u*>(x + r * N)[j], sc + j * 8, y);
+      uint32_t d0 = cvt_pk<FMT, false>(quant_prep<FMT>(y[0], inv), quant_prep<FMT>(y[1], inv), 0u);
+      d0 = cvt_pk<FMT, true>(quant_prep<FMT>(y[2], inv), quant_prep<FMT>(y[3], inv), d0);
+      uint32_t d1 = cvt_pk<FMT, false>(quant_prep<FMT>(y[4], inv), quant_prep<FMT>(y[5], inv), 0u);
+      d1 = cvt_pk<FMT, true>(quant_prep<FMT>(y[6], inv), quant_prep<FMT>(y[7], inv), d1);
+      v2u o;
+      o.x = d0;
+      o.y = d1;
+      reinterpret_cast<v2u*>(codes + r * N)[j] = o;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_blockwise(int a_fmt, const BsParams& p, hipStream_t st) {
@@ -289,6 +402,32 @@ hipError_t launch_quantize_subchannel(int fmt, const void* x, int64_t M, int64_t
   else
     hipLaunchKernelGGL(subchannel_quant_kernel<FMT_E5M2>, dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)x, M, K, bk, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace gmm
+
+namespace gmm {
+
+hipError_t launch_quantize_folded(int fmt, const void* x, int64_t M, int64_t N,
+                                  const float* col_scales, const int32_t* gs, int G,
+                                  uint32_t* partial, float* scales, uint8_t* codes,
+                                  hipStream_t st) {
+  const int nb = (int)((M + BLOCK_ROWS - 1) / BLOCK_ROWS);
+  if (nb == 0) return hipSuccess;
+  const uint16_t* xp = (const uint16_t*)x;
+  hipLaunchKernelGGL(fold_amax_kernel, dim3(nb, AMAX_SPLIT), dim3(256), 0, st, xp, M, N,
+                     col_scales, gs, G, partial);
+  const unsigned fb = (unsigned)((nb + 255) / 256);
+  if (fmt == FMT_E4M3) {
+    hipLaunchKernelGGL(fold_scales_kernel<FMT_E4M3>, dim3(fb), dim3(256), 0, st, partial, nb, scales);
+    hipLaunchKernelGGL(fold_quantize_kernel<FMT_E4M3>, dim3(nb, AMAX_SPLIT), dim3(256), 0, st, xp,
+                       M, N, col_scales, gs, G, scales, codes);
+  } else {
+    hipLaunchKernelGGL(fold_scales_kernel<FMT_E5M2>, dim3(fb), dim3(256), 0, st, partial, nb, scales);
+    hipLaunchKernelGGL(fold_quantize_kernel<FMT_E5M2>, dim3(nb, AMAX_SPLIT), dim3(256), 0, st, xp,
+                       M, N, col_scales, gs, G, scales, codes);
+  }
   return hipGetLastError();
 }
 

@@ -120,6 +120,12 @@ hipError_t launch_quantize_rhs(int fmt, int axis, int layout_nk, int64_t G, int6
                                int64_t N, int64_t kblk, const void* w, uint8_t* codes,
                                float* scales, hipStream_t st);
 hipError_t launch_gemm_blockwise(int a_fmt, const BsParams& p, hipStream_t st);
+// the folded gradient: codes and 128-row-block scales of grad * s[g(m), n]
+// (partial: ceil(M / 128) * AMAX_SPLIT words of workspace)
+hipError_t launch_quantize_folded(int fmt, const void* x, int64_t M, int64_t N,
+                                  const float* col_scales, const int32_t* gs, int G,
+                                  uint32_t* partial, float* scales, uint8_t* codes,
+                                  hipStream_t st);
 hipError_t launch_quantize_subchannel(int fmt, const void* x, int64_t M, int64_t K, int bk,
                                       uint8_t* codes, float* scales, hipStream_t st);
 

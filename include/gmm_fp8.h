@@ -311,6 +311,26 @@ gmm_status_t gmm_fwd_blockwise(int32_t lhs_format, int32_t out_dtype, int64_t M,
                                gmm_stream_t stream);
 
 /*
+ * gmm_quantize_folded - the gradient of the dlhs that runs on the forward's weight copy
+ * ("Support quantization for tokamax gmm v2", review threads on the ops diff: per-channel
+ * weight scales; the dlhs is a gmm against the transposed rhs).  The forward's scales
+ * s[g, n] lie on the dlhs contraction, so they are folded into the gradient first:
+ *
+ *   y[m, n] = RNE_f32(grad[m, n] * col_scales[g(m), n])       (g(m): the group of row m)
+ *
+ * then y gets the dynamic 128-row-block recipe (abs-max over the block's full width,
+ * s = RNE(amax / qmax), inverse 0 when s is 0 or 1/s overflows, clamp then RNE).
+ * grad bf16 [M, N], col_scales f32 [G, N], codes uint8 [M, N], scales f32 [ceil(M/128)].
+ * gmm_dlhs on (codes, DYNAMIC_GIVEN-style block scales) with the forward's codes laid out
+ * [G, K, N] and all-one rhs_scales [G, K] then computes the lhs gradient.  N a positive
+ * multiple of 128; workspace ceil(M/128) * 32 bytes.
+ */
+gmm_status_t gmm_quantize_folded(int32_t format, int64_t M, int64_t N, int32_t G,
+                                 const void* grad, const float* col_scales,
+                                 const int32_t* group_sizes, uint8_t* codes, float* scales,
+                                 void* workspace, size_t workspace_bytes, gmm_stream_t stream);
+
+/*
  * gmm_quantize_subchannel - dynamic quantization of bf16 x [M, K] with one scale per row
  * and block of bk columns (bk = 128, 256 or 512, dividing K; else GMM_ERR_SHAPE):
  * s = RNE(amax / qmax) over the block, codes as gmm_quantize's dynamic recipe with that

@@ -294,3 +294,18 @@ def test_blockwise_validation():
     assert lib.gmm_quantize_rhs_blockwise(0, 1, 2, 512, 256, 192, ptr(1), ptr(2), ptr(3), None) == 2
     assert lib.gmm_quantize_rhs_blockwise(0, 5, 2, 512, 256, 128, ptr(1), ptr(2), ptr(3), None) == 4
     assert lib.gmm_quantize_rhs_blockwise(0, 1, 2, 512, 256, 128, ptr(1), ptr(2), ptr(2), None) == 9
+
+
+def test_folded_quantizer_validation():
+    lib = g.load()
+
+    def fold(fmt=1, M=256, N=256, G=4, grad=1, cs=2, gs=3, codes=4, sc=5, ws=6, wsb=1 << 20):
+        P = lambda i: None if i is None else ptr(i)
+        return lib.gmm_quantize_folded(fmt, M, N, G, P(grad), P(cs), P(gs), P(codes), P(sc), P(ws),
+                                       wsb, None)
+
+    assert fold(M=0) == 0
+    assert fold(N=200) == 2 and fold(G=0) == 2 and fold(fmt=3) == 4
+    assert fold(cs=None) == 1 and fold(codes=None) == 1
+    assert fold(ws=None) == 5 and fold(wsb=8) == 5
+    assert fold(codes=1) == 9 and fold(sc=4) == 9 and fold(ws=2) == 9

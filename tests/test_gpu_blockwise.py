@@ -128,3 +128,31 @@ def test_blockwise_mixtral_full_size_sampled(lib):
     err = group_rel_err(to_np(out[ri][:, ci]), R, group_row_ranges(sub))
     print(f"sampled max group relative error {err:.3e}", flush=True)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("sizes", [[300, 0, 212, 1], [640]])
+def test_folded_dlhs(lib, sizes):
+    """The one-weight-copy dlhs: the gradient folded with the forward's per-channel scales
+    (codes and scales byte for byte), then gmm_dlhs on the forward's codes with unit
+    output-channel scales, against the oracle."""
+    from oracle.blockwise import quantize_folded
+    from oracle.gmm import gmm_dlhs_ref, row_scales
+    from oracle.quant import quantize_rhs_per_channel
+
+    G, M, K, N = len(sizes), sum(sizes), 256, 512
+    gr, grb = gen((M, N), 1e-3, 741)
+    w, wb = gen((G, K, N), 0.02, 742)
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w, "e4m3", 0, "kn")  # the forward copy: [G, K, N], s[g, n]
+    codes, s = lib.gmm_quantize_folded(gr, ws, gs)
+    ones = torch.ones((G, K), dtype=torch.float32, device=gr.device)
+    out = lib.gmm_dlhs(codes, wq, ones, gs, grad_scaling="dynamic", grad_scales=s,
+                       rhs_layout="kn", out_dtype=torch.float32)
+    sync()
+    wq_ref, ws_ref = quantize_rhs_per_channel(wb, "e4m3", "n")
+    c_ref, s_ref = quantize_folded(grb, ws_ref, sizes, "e5m2")
+    assert np.array_equal(to_np(codes), c_ref)
+    assert np.array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    R = gmm_dlhs_ref(c_ref, "e5m2", row_scales(s_ref, M), wq_ref, "e4m3",
+                     np.ones((G, K), np.float32), sizes)
+    assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL

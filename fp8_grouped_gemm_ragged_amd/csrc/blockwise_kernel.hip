@@ -266,7 +266,8 @@ __global__ __launch_bounds__(256) void subchannel_quant_kernel(const uint16_t* _
 // ---- the folded gradient of the one-weight-copy dlhs ----
 // y[m, n] = RNE(grad[m, n] * s[g(m), n]); its 128-row-block abs-max (as fp32 bits) over
 // AMAX_SPLIT row slices per block, then the codes of y.  Every workgroup builds the
-// group row offsets in LDS and looks each row's group up once.
+// group row offsets in LDS and looks each row's group up once; a thread walks its
+// columns and, for each, the slice's rows, so a column's scales are read once per group.
 __device__ inline void fold_offsets(const int32_t* __restrict__ gs, int G, int* s_off) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) {
@@ -293,9 +294,7 @@ __device__ inline int fold_group(const int* s_off, int G, int64_t r) {
 }
 
 // 8 consecutive bf16 gradient values times their columns' scales, each product rounded
-__device__ inline void fold8(v4u w, const float* __restrict__ sc, float (&y)[8]) {
-  const v4f s0 = *reinterpret_cast<const v4f*>(sc);
-  const v4f s1 = *reinterpret_cast<const v4f*>(sc + 4);
+__device__ inline void fold8(v4u w, v4f s0, v4f s1, float (&y)[8]) {
   y[0] = mul_rn(bf16_lo(w.x), s0[0]); y[1] = mul_rn(bf16_hi(w.x), s0[1]);
   y[2] = mul_rn(bf16_lo(w.y), s0[2]); y[3] = mul_rn(bf16_hi(w.y), s0[3]);
   y[4] = mul_rn(bf16_lo(w.z), s1[0]); y[5] = mul_rn(bf16_hi(w.z), s1[1]);
@@ -314,14 +313,35 @@ __global__ __launch_bounds__(256) void fold_amax_kernel(const uint16_t* __restri
   constexpr int rows_per = BLOCK_ROWS / AMAX_SPLIT;
   const int64_t r0 = (int64_t)b * BLOCK_ROWS + (int64_t)sl * rows_per;
   const int64_t r1 = min(r0 + rows_per, M);
+  __shared__ int s_grp[BLOCK_ROWS / AMAX_SPLIT];
+  if ((int)threadIdx.x < r1 - r0) s_grp[threadIdx.x] = fold_group(s_off, G, r0 + threadIdx.x);
+  __syncthreads();
   uint32_t m = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const float* sc = col_scales + (int64_t)fold_group(s_off, G, r) * N;
-    for (int64_t j = threadIdx.x; j < N / 8; j += 256) {
-      float y[8];
-      fold8(reinterpret_cast<const v4u*>(x + r * N)[j], sc + j * 8, y);
+  const int64_t chunks = N / 8;
+  const int nrows = (int)(r1 - r0);
+  // columns outer, the slice's rows inner: a chunk's 8 scales are loaded once per group
+  for (int64_t j = threadIdx.x; j < chunks; j += 256) {
+    int gcur = -1;
+    v4f s0, s1;
+    for (int i0 = 0; i0 < nrows; i0 += 4) {
+      v4u w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(y[e]) & 0x7fffffffu);
+      for (int u = 0; u < 4; ++u)
+        w[u] = reinterpret_cast<const v4u*>(x + (r0 + min(i0 + u, nrows - 1)) * N)[j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u >= nrows) break;
+        const int gr = s_grp[i0 + u];
+        if (gr != gcur) {
+          gcur = gr;
+          s0 = *reinterpret_cast<const v4f*>(col_scales + (int64_t)gr * N + j * 8);
+          s1 = *reinterpret_cast<const v4f*>(col_scales + (int64_t)gr * N + j * 8 + 4);
+        }
+        float y[8];
+        fold8(w[u], s0, s1, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(y[e]) & 0x7fffffffu);
+      }
     }
   }
   // block maximum
@@ -359,19 +379,39 @@ __global__ __launch_bounds__(256) void fold_quantize_kernel(const uint16_t* __re
   const int64_t r0 = (int64_t)b * BLOCK_ROWS + (int64_t)sl * rows_per;
   const int64_t r1 = min(r0 + rows_per, M);
   const float inv = inv_from_scale(scales[b]);
-  for (int64_t r = r0; r < r1; ++r) {
-    const float* sc = col_scales + (int64_t)fold_group(s_off, G, r) * N;
-    for (int64_t j = threadIdx.x; j < N / 8; j += 256) {
-      float y[8];
-      fold8(reinterpret_cast<const v4u*>(x + r * N)[j], sc + j * 8, y);
-      uint32_t d0 = cvt_pk<FMT, false>(quant_prep<FMT>(y[0], inv), quant_prep<FMT>(y[1], inv), 0u);
-      d0 = cvt_pk<FMT, true>(quant_prep<FMT>(y[2], inv), quant_prep<FMT>(y[3], inv), d0);
-      uint32_t d1 = cvt_pk<FMT, false>(quant_prep<FMT>(y[4], inv), quant_prep<FMT>(y[5], inv), 0u);
-      d1 = cvt_pk<FMT, true>(quant_prep<FMT>(y[6], inv), quant_prep<FMT>(y[7], inv), d1);
-      v2u o;
-      o.x = d0;
-      o.y = d1;
-      reinterpret_cast<v2u*>(codes + r * N)[j] = o;
+  __shared__ int s_grp[BLOCK_ROWS / AMAX_SPLIT];
+  if ((int)threadIdx.x < r1 - r0) s_grp[threadIdx.x] = fold_group(s_off, G, r0 + threadIdx.x);
+  __syncthreads();
+  const int64_t chunks = N / 8;
+  const int nrows = (int)(r1 - r0);
+  for (int64_t j = threadIdx.x; j < chunks; j += 256) {
+    int gcur = -1;
+    v4f s0, s1;
+    for (int i0 = 0; i0 < nrows; i0 += 4) {
+      v4u w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        w[u] = reinterpret_cast<const v4u*>(x + (r0 + min(i0 + u, nrows - 1)) * N)[j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u >= nrows) break;
+        const int gr = s_grp[i0 + u];
+        if (gr != gcur) {
+          gcur = gr;
+          s0 = *reinterpret_cast<const v4f*>(col_scales + (int64_t)gr * N + j * 8);
+          s1 = *reinterpret_cast<const v4f*>(col_scales + (int64_t)gr * N + j * 8 + 4);
+        }
+        float y[8];
+        fold8(w[u], s0, s1, y);
+        uint32_t d0 = cvt_pk<FMT, false>(quant_prep<FMT>(y[0], inv), quant_prep<FMT>(y[1], inv), 0u);
+        d0 = cvt_pk<FMT, true>(quant_prep<FMT>(y[2], inv), quant_prep<FMT>(y[3], inv), d0);
+        uint32_t d1 = cvt_pk<FMT, false>(quant_prep<FMT>(y[4], inv), quant_prep<FMT>(y[5], inv), 0u);
+        d1 = cvt_pk<FMT, true>(quant_prep<FMT>(y[6], inv), quant_prep<FMT>(y[7], inv), d1);
+        v2u o;
+        o.x = d0;
+        o.y = d1;
+        reinterpret_cast<v2u*>(codes + (r0 + i0 + u) * N)[j] = o;
+      }
     }
   }
 }

@@ -11,6 +11,19 @@
  *   gmm_dlhs   dlhs[m, :]  = grad[m, :] . rhs[g]^T       (the gmm against rhs transposed)
  *   tgmm_drhs  drhs[g]     = lhs_g^T . grad_g            (one [K, N] slab per group)
  *
+ * and the steps around them in the same MoE layer:
+ *
+ *   gmm_fwd_swiglu / gmm_fwd_swiglu_fp8 / gmm_swiglu_bwd   SwiGLU of the merged
+ *              gate|up product in the forward's epilogue (h in bf16/f32 or fp8 codes),
+ *              and its backward
+ *   gmm_fwd_local / gmm_dlhs_local / tgmm_drhs_local   the products over a window of
+ *              local experts (group_offset)
+ *   gmm_fwd_blockwise, gmm_quantize_subchannel, gmm_quantize_rhs_blockwise,
+ *   gmm_quantize_folded   block-wise weight scales, sub-channel lhs scales, and the
+ *              dlhs on the forward's weight copy
+ *   gmm_permute / gmm_unpermute   token routing: the sort of top-k choices by expert
+ *              and the weighted combine back
+ *
  * Rows of lhs / grad are sorted by group: group g owns rows [off_g, off_g + m_g) with
  * off_0 = 0 and off_{g+1} = off_g + m_g, m_g = group_sizes[g].
  *

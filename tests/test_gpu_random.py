@@ -104,3 +104,75 @@ def test_random_fwd_dlhs_tgmm(lib, i):
     for g in range(G):  # empty experts: +0.0 slabs
         if sizes[g] == 0:
             assert (to_np(dr)[g].view(np.uint32) == 0).all()
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_windows(lib, i):
+    """Random local-expert windows of random groupings: fwd, dlhs and tgmm (dynamic bf16
+    operands) against the oracle's windows; rows outside the window are zero."""
+    from oracle.gmm import gmm_dlhs_local_ref, gmm_fwd_local_ref, group_offsets, tgmm_local_ref
+
+    rng = np.random.default_rng(5000 + i)
+    G = int(rng.integers(2, 20))
+    sizes = [int(v) for v in rng.multinomial(int(rng.integers(1, 1500)), np.ones(G) / G)]
+    sizes = [0 if rng.random() < 0.2 else v for v in sizes]
+    M = sum(sizes)
+    a = int(rng.integers(0, G))
+    b = int(rng.integers(1, G - a + 1))
+    K, N = int(rng.choice([128, 384])), int(rng.choice([256, 640]))
+    print(f"window config {i}: G={G} sizes={sizes} window=({a}, {b}) K={K} N={N}", flush=True)
+    x, xb = gen((M, K), 1.0, 6000 + i)
+    w, wb = gen((G, K, N), 0.02, 7000 + i)
+    gr, grb = gen((M, N), 1e-3, 8000 + i)
+    gs = gs_tensor(sizes)
+    wq, ws = lib.gmm_quantize_rhs(w[a:a + b].contiguous(), "e4m3", 0, "nk")
+    out = lib.gmm_fwd_local(x, wq, ws, gs, a, out_dtype=torch.float32)
+    wk, sk = lib.gmm_quantize_rhs(w[a:a + b].contiguous(), "e4m3", 1, "kn")
+    dl = lib.gmm_dlhs_local(gr, wk, sk, gs, a, out_dtype=torch.float32)
+    dr = lib.tgmm_drhs_local(x, gr, gs, a, b, out_dtype=torch.float32)
+    sync()
+    aq, sa = ops.quantize_operand(xb, "e4m3", "dynamic")
+    gq, sg = ops.quantize_operand(grb, "e5m2", "dynamic")
+    c_ref, s_ref = quantize_rhs_per_channel(wb[a:a + b], "e4m3", "n")
+    ck_ref, sk_ref = quantize_rhs_per_channel(wb[a:a + b], "e4m3", "k")
+    off = group_offsets(sizes)
+    win = [(int(off[g]), int(off[g + 1])) for g in range(a, a + b)]
+    outside = np.ones(M, bool)
+    outside[off[a]:off[a + b]] = False
+    R = gmm_fwd_local_ref(aq, "e4m3", np.repeat(sa, 128)[:M], c_ref, "e4m3", s_ref, sizes, a)
+    Y = to_np(out)
+    assert not Y[outside].any() and group_rel_err(Y, R, win) <= TOL
+    Rd = gmm_dlhs_local_ref(gq, "e5m2", np.repeat(sg, 128)[:M], ck_ref, "e4m3", sk_ref, sizes, a)
+    D = to_np(dl)
+    assert not D[outside].any() and group_rel_err(D, Rd, win) <= TOL
+    Rt = tgmm_local_ref(aq, "e4m3", sa, gq, "e5m2", sg, sizes, a, b)
+    assert slab_rel_err(to_np(dr), Rt) <= TOL
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_blockwise(lib, i):
+    """Random shapes and block sizes of the block-wise forward against the oracle."""
+    from oracle.blockwise import gmm_fwd_blockwise_ref, quantize_rhs_blockwise, quantize_subchannel
+
+    rng = np.random.default_rng(9000 + i)
+    G = int(rng.integers(1, 9))
+    sizes = [int(v) for v in rng.multinomial(int(rng.integers(0, 900)), np.ones(G) / G)]
+    M = sum(sizes)
+    bk = int(rng.choice([128, 256, 512]))
+    K = bk * int(rng.integers(1, 5))
+    N = 128 * int(rng.integers(1, 5))
+    fmt = str(rng.choice(["e4m3", "e5m2"]))
+    print(f"block-wise config {i}: sizes={sizes} K={K} N={N} bk={bk} {fmt}", flush=True)
+    x, xb = gen((M, K), 1.0, 9100 + i)
+    w, wb = gen((G, K, N), 0.02, 9200 + i)
+    codes, s = lib.gmm_quantize_subchannel(x, bk, fmt)
+    wq, ws = lib.gmm_quantize_rhs_blockwise(w, bk)
+    out = lib.gmm_fwd_blockwise(codes, s, wq, ws, gs_tensor(sizes), bk, lhs_format=fmt,
+                                out_dtype=torch.float32)
+    sync()
+    if M == 0:
+        return
+    c_ref, s_ref = quantize_subchannel(xb, fmt, bk)
+    wc_ref, ws_ref = quantize_rhs_blockwise(wb, "e4m3", bk)
+    R = gmm_fwd_blockwise_ref(c_ref, fmt, s_ref, wc_ref, "e4m3", ws_ref, sizes, bk)
+    assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL

@@ -176,3 +176,32 @@ def test_random_blockwise(lib, i):
     wc_ref, ws_ref = quantize_rhs_blockwise(wb, "e4m3", bk)
     R = gmm_fwd_blockwise_ref(c_ref, fmt, s_ref, wc_ref, "e4m3", ws_ref, sizes, bk)
     assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_routing(lib, i):
+    """Random routings: permute (indices, group sizes, gathered rows) and the weighted
+    combine, bit for bit against the oracle."""
+    from oracle.fp8 import bf16_bits_to_f32
+    from oracle.route import gather_rows_ref, permute_ref, unpermute_ref
+
+    rng = np.random.default_rng(9500 + i)
+    T = int(rng.integers(0, 3000))
+    k = int(rng.integers(1, 17))
+    G = int(rng.integers(1, 300))
+    H = 8 * int(rng.integers(1, 300))
+    ids = rng.integers(-1, G + 2, (T, k)).astype(np.int32)  # repeats and dropped ids
+    print(f"routing config {i}: T={T} k={k} G={G} H={H}", flush=True)
+    x, xb = gen((T, H), 1.0, 9600 + i)
+    idt = torch.as_tensor(ids, device=x.device)
+    xp, gs, ros, sor = lib.gmm_permute(idt, G, x)
+    wts = rng.random((T, k)).astype(np.float32)
+    y, yb = gen((T * k, H), 1.0, 9700 + i)
+    out = lib.gmm_unpermute(y, ros, torch.as_tensor(wts, device=x.device))
+    sync()
+    gs_r, ros_r, sor_r = permute_ref(ids, G)
+    assert np.array_equal(to_np(gs), gs_r) and np.array_equal(to_np(ros), ros_r)
+    assert np.array_equal(to_np(sor), sor_r)
+    assert np.array_equal(to_np(xp), gather_rows_ref(xb, sor_r, k))
+    _, bits = unpermute_ref(bf16_bits_to_f32(yb), ros_r, wts)
+    assert np.array_equal(to_np(out), bits)

@@ -522,6 +522,45 @@ void gmm_kernel(GemmParams p) {
         sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + n_ok +
                                                   j * 32 + 8 * r4 + 4 * fhalf);
   }
+  if (!p.out_f32) {
+    // bf16: each wave puts its 128 x 128 sub-tile into its own 32 KB of LDS ([row][256 B],
+    // 16-byte chunk c of row r at c ^ (r & 15)), then stores whole rows, 16 lanes per row
+    // and 16 bytes per lane: every store instruction writes 8 full 128-byte lines instead
+    // of 16-byte pieces of 32 rows.  The last step ended with a workgroup barrier after
+    // every wave's last LDS access, so the stage memory is free.
+    uint8_t* const wl = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + frow;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
+          v2u v;
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
+          const int chunk = (4 * j + r4) ^ (row & 15);
+          *reinterpret_cast<v2u*>(wl + row * 256 + chunk * 16 + fhalf * 8) = v;
+        }
+      }
+    }
+    // this wave's LDS writes are done before its own reads (no other wave touches wl)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bool cols_ok = tc.n0 + wc * 128 < p.Nout;  // N is a multiple of 128
+    const int c = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int row = q * 4 + (lane >> 4);
+      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 256 + ((c ^ (row & 15)) << 4));
+      const int m = tc.row0 + wr * 128 + row;
+      if (cols_ok && m < tc.row_end)
+        *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.Nout + tc.n0 + wc * 128 + c * 8) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = tc.row0 + wr * 128 + i * 32 + frow;
@@ -535,16 +574,8 @@ void gmm_kernel(GemmParams p) {
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
-        const int64_t idx = (int64_t)m * p.Nout + n;
-        if (p.out_f32) {
-          v4f v = {o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
-        } else {
-          v2u v;
-          v.x = pack_bf16x2(o[0], o[1]);
-          v.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
-        }
+        v4f v = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<v4f*>((float*)p.out + (int64_t)m * p.Nout + n) = v;
       }
     }
   }

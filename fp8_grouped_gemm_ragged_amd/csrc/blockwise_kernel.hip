@@ -214,6 +214,37 @@ void gmm_bs_kernel(BsParams p) {
   }
 
   // ---- epilogue: rows of the group only ----
+  if (!p.out_f32) {
+    // bf16: each wave puts its 64 x 64 sub-tile into its own 16 KB stage tile
+    // ([row][128 B], 16-byte chunk c of row r at c ^ (r & 7)) and stores whole 128-byte
+    // rows, 8 lanes per row: full lines instead of 16-byte pieces of 32 rows.  The loop
+    // ended with a barrier after every wave's last LDS access.
+    uint8_t* const wl = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 32 * i + frow;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          v2u v;
+          v.x = pack_bf16x2(total[i][j][4 * r4], total[i][j][4 * r4 + 1]);
+          v.y = pack_bf16x2(total[i][j][4 * r4 + 2], total[i][j][4 * r4 + 3]);
+          *reinterpret_cast<v2u*>(wl + row * 128 + (((4 * j + r4) ^ (row & 7)) << 4) + fhalf * 8) = v;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane & 7;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = q * 8 + (lane >> 3);
+      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 128 + ((c ^ (row & 7)) << 4));
+      const int m = tc.row0 + 64 * wr + row;
+      if (m < tc.row_end)
+        *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.N + tc.n0 + 64 * wc + c * 8) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = tc.row0 + 64 * wr + 32 * i + frow;
@@ -226,14 +257,7 @@ void gmm_bs_kernel(BsParams p) {
         const int64_t idx = (int64_t)m * p.N + n;
         const v4f o = {total[i][j][4 * r4], total[i][j][4 * r4 + 1], total[i][j][4 * r4 + 2],
                        total[i][j][4 * r4 + 3]};
-        if (p.out_f32) {
-          *reinterpret_cast<v4f*>((float*)p.out + idx) = o;
-        } else {
-          v2u v;
-          v.x = pack_bf16x2(o[0], o[1]);
-          v.y = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
-        }
+        *reinterpret_cast<v4f*>((float*)p.out + idx) = o;
       }
     }
   }

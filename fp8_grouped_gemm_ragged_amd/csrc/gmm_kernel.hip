@@ -25,7 +25,8 @@
 //     and the quantization of the next step (about 14 VALU instructions per MFMA) is
 //     interleaved between the MFMAs, so vector ALU and matrix core run concurrently;
 //   * epilogue: (acc * s_A(m)) * s_B(n), RNE to bf16 (or f32), stored only for rows
-//     inside the group and columns inside N.
+//     inside the group and columns inside N; bf16 rows are staged through LDS so that
+//     every store instruction writes whole 128-byte lines.
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -202,43 +203,83 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
     }
   }
   __syncthreads();  // the handed-over values are in LDS
-  auto finish = [&](int i) {
-    const int m = tc.row0 + wr * 128 + i * 32 + frow;
-    if (m >= tc.row_end) return;
+  // This wave finishes rows i0 .. i0 + 1 of its row half (64 rows x 128 channels), 32
+  // rows (one ii) at a time.  Rows of ii come from the 16 KB half ii of the LDS region
+  // this wave reads (no other wave touches it now); once read, that half stages the
+  // rows' outputs as [32 rows][RB bytes], 16-byte chunk c of row r at c ^ (r & 15), which
+  // are then stored as whole rows: every store instruction writes full lines.
+  const int i0 = wc == 0 ? 0 : 2;
+  uint8_t* const wl = wc == 0 ? xa : xb;
+  const bool codes = p.h_codes != 0;
+  const int RB = codes ? 128 : 256;             // bytes per staged row (bf16 or codes)
+  const int lanes_per_row = RB / 16;            // 16 or 8
+  const int rows_per_op = 64 / lanes_per_row;   // 4 or 8
+  const int c = lane % lanes_per_row;
+  const int swz = codes ? 7 : 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+  for (int ii = 0; ii < 2; ++ii) {
+    v4f hv[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const v4f mine = value(i, j, r4);
-        const v4f other = *chunk(i * 16 + j * 4 + r4);
+        // accumulator rows by constant index only (a computed index would move the
+        // accumulators to scratch memory)
+        v4f mine, other;
+        if (wc == 0) {
+          mine = value(ii, j, r4);
+          other = *chunk(ii * 16 + j * 4 + r4);
+        } else {
+          mine = value(2 + ii, j, r4);
+          other = *chunk((2 + ii) * 16 + j * 4 + r4);
+        }
         const v4f g = wc == 0 ? mine : other;
         const v4f u = wc == 0 ? other : mine;
-        v4f h;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          h[e] = __fmul_rn(__fdiv_rn(g[e], __fadd_rn(1.0f, expf(-g[e]))), u[e]);
-        const int64_t idx = (int64_t)m * I + c0 + j * 32 + 8 * r4 + 4 * fhalf;
-        if (p.h_codes) {
+          hv[j][r4][e] = __fmul_rn(__fdiv_rn(g[e], __fadd_rn(1.0f, expf(-g[e]))), u[e]);
+      }
+    const int mrow = tc.row0 + wr * 128 + (i0 + ii) * 32;  // first row of these 32
+    if (p.out_f32 && !codes) {
+      const int m = mrow + frow;
+      if (m < tc.row_end) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<v4f*>((float*)p.out + (int64_t)m * I + c0 + j * 32 + 8 * r4 + 4 * fhalf) =
+                hv[j][r4];
+      }
+      continue;
+    }
+    uint8_t* const st = wl + ii * 16384;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this half's reads are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const v4f h = hv[j][r4];
+        if (codes) {
           // fp8 codes of h under a static scale, the lhs of the down projection
-          *reinterpret_cast<uint32_t*>((uint8_t*)p.out + idx) =
+          const uint32_t q =
               p.h_codes == 1 + FMT_E4M3 ? quant4<FMT_E4M3>(h, p.h_inv) : quant4<FMT_E5M2>(h, p.h_inv);
-        } else if (p.out_f32) {
-          *reinterpret_cast<v4f*>((float*)p.out + idx) = h;
+          const int byte = j * 32 + 8 * r4 + 4 * fhalf;
+          *reinterpret_cast<uint32_t*>(st + frow * 128 + ((((byte >> 4) ^ frow) & 7) << 4) + (byte & 15)) = q;
         } else {
           v2u v;
           v.x = pack_bf16x2(h[0], h[1]);
           v.y = pack_bf16x2(h[2], h[3]);
-          *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
+          *reinterpret_cast<v2u*>(st + frow * 256 + (((4 * j + r4) ^ (frow & 15)) << 4) + fhalf * 8) = v;
         }
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int q = 0; q < 32 / rows_per_op; ++q) {
+      const int row = q * rows_per_op + lane / lanes_per_row;
+      const v4u v = *reinterpret_cast<const v4u*>(st + row * RB + ((c ^ (row & swz)) << 4));
+      const int m = mrow + row;
+      if (m < tc.row_end)
+        *reinterpret_cast<v4u*>((uint8_t*)p.out + ((int64_t)m * I + c0) * (RB / 128) + c * 16) = v;
     }
-  };
-  if (wc == 0) {
-    finish(0);
-    finish(1);
-  } else {
-    finish(2);
-    finish(3);
   }
 }
 

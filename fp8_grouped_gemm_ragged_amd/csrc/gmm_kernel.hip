@@ -147,25 +147,24 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int g_befor
 // fp8(clamp(RNE_f32(h * inv), +-qmax)) of a static scale.
 __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc, int c0, int wr,
                                        int wc, v16f (&acc)[4][4], uint8_t* sA0,
-                                       uint8_t* sB0, uint8_t* sA1, uint8_t* sB1) {
+                                       uint8_t* sB0, uint8_t* sA1, uint8_t* sB1,
+                                       const float* s_sa, const float* s_sb) {
   // the lane id is recomputed here: cheaper than keeping it live across the main loop
   const int lane = __lane_id();
   const int frow = lane & 31, fhalf = lane >> 5;
   const int I = p.Nout >> 1;
   const int cb = wc == 0 ? c0 : I + c0;  // this wave's first channel
+  // the tile's row scales and its gate (0..127) and up (128..255) channel scales, put
+  // into LDS by the prologue
   float sa[4];
   v4f sb[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = max(min(tc.row0 + wr * 128 + i * 32 + frow, tc.row_end - 1), 0);
-    sa[i] = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
-  }
+  for (int i = 0; i < 4; ++i) sa[i] = s_sa[wr * 128 + i * 32 + frow];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + cb + j * 32 +
-                                                8 * r4 + 4 * fhalf);
+      sb[j][r4] = *reinterpret_cast<const v4f*>(s_sb + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf);
   auto value = [&](int i, int j, int r4) {
     v4f o;
 #pragma unroll
@@ -297,6 +296,9 @@ void gmm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_TILE];
+  // the tile's row and column scales (beside the 128 KB of stages: 160 KB of LDS)
+  __shared__ float s_sa[BM];
+  __shared__ float s_sb[BN];
   int* s_tile_cum = reinterpret_cast<int*>(sA0);
   int* s_row_off = s_tile_cum + (MAX_GROUPS + 1);
   static_assert(2 * (MAX_GROUPS + 1) * sizeof(int) <= A_TILE, "scheduler arrays fit a tile");
@@ -513,11 +515,25 @@ void gmm_kernel(GemmParams p) {
     stage_barrier();
   };
 
-  // ---- prologue: step 0 into stage 0, step 1 into registers ----
+  // ---- prologue: the tile's scales, step 0 into stage 0, step 1 into registers ----
+  // The epilogue scales are loaded first (thread t: row row0 + t, column n0 + t) and put
+  // into LDS once they land, so the epilogue reads them there instead of waiting for
+  // global loads after the last step.
+  // (SW: columns 0..127 are the gate channels c0.., 128..255 the up channels I + c0..)
+  float sa_t, sb_t;
+  {
+    const int m = max(min(tc.row0 + tid, tc.row_end - 1), 0);
+    sa_t = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
+    const int n = SW ? (tid < 128 ? c0 + tid : (p.Nout >> 1) + c0 + tid - 128)
+                     : min(tc.n0 + tid, p.Nout - 1);
+    sb_t = p.b_scale[(int64_t)tc.g * p.Nout + n];
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) { load_a_piece(0, i); load_bk_piece(0, i); }
   load_b_block(0, 0);
   load_b_block(0, 1);
+  s_sa[tid] = sa_t;
+  s_sb[tid] = sb_t;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { store_a_piece(sA0, i); store_bk_piece(sB0, i); }
   store_b_block(sB0, 0);
@@ -538,31 +554,24 @@ void gmm_kernel(GemmParams p) {
   if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
 
   if constexpr (SW) {
-    swiglu_epilogue(p, tc, c0, wr, wc, acc, sA0, sB0, sA1, sB1);
+    swiglu_epilogue(p, tc, c0, wr, wc, acc, sA0, sB0, sA1, sB1, s_sa, s_sb);
     return;
   }
 
   // ---- epilogue ----
   // lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) + 4*(lane/32) + r%4].
-  // Every scale is loaded before the first store: a load issued after a store waits for
-  // that store too (the vector-memory counter retires in order), and the compiler cannot
-  // keep scales across stores to a buffer it must assume they alias.
+  // The scales come from LDS, filled in the prologue (a global load issued here would
+  // also wait for every store issued before it: the vector-memory counter retires in
+  // order).  Columns past N only ever scale values that are not stored.
   float sa[4];
   v4f sb[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = max(min(tc.row0 + wr * 128 + i * 32 + frow, tc.row_end - 1), 0);
-    sa[i] = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
-  }
-  {
-    const int n_ok = min(tc.n0 + wc * 128, p.Nout - 128);  // a column block inside N
+  for (int i = 0; i < 4; ++i) sa[i] = s_sa[wr * 128 + i * 32 + frow];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + n_ok +
-                                                  j * 32 + 8 * r4 + 4 * fhalf);
-  }
+    for (int r4 = 0; r4 < 4; ++r4)
+      sb[j][r4] = *reinterpret_cast<const v4f*>(s_sb + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf);
   if (!p.out_f32) {
     // bf16: each wave puts its 128 x 128 sub-tile into its own 32 KB of LDS ([row][256 B],
     // 16-byte chunk c of row r at c ^ (r & 15)), then stores whole rows, 16 lanes per row

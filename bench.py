@@ -12,14 +12,16 @@ routing), inputs resident in HBM:
   4. gmm_dlhs  dlhs[M, K]     = q(grad) . rhs[g]^T     (hybrid: fp8 codes of step 3)
   5. tgmm_drhs drhs[G, K, N]  = q(lhs)_g^T . q(grad)_g  (scales of steps 1 and 3 reused)
 
-value = 3 * 2*M*K*N / step time (TFLOP/s).  Every call is timed with HIP events on the
-stream it runs on.  gmm_fwd is a quantize kernel and the product kernel; gmm_dlhs is
+value = 3 * 2*M*K*N / step time (TFLOP/s), with steps 4 and 5 (independent of each other)
+on two HIP streams so that tgmm fills the CUs dlhs leaves idle in its short last round of
+tiles; the per-op figures come from the same step on one stream, where every call is
+timed with HIP events on the stream it runs on.  gmm_fwd is a quantize kernel and the product kernel; gmm_dlhs is
 one kernel launch; tgmm_drhs is a plan
 kernel, two quantize-transpose kernels, the fp8 tgmm kernel and its wide-range fallback
 (which exits at once here), and its window holds all five.  The slowest product window is reported against the dense FP8 MFMA peak (5.0
 PFLOP/s).  The CPU oracle is timed on a bounded sample of the same workload (N=1).
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline] [--no-overlap]
 """
 
 import argparse
@@ -74,6 +76,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="mixtral_gate_up")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="time the step on one stream only (ms_per_step is then the serial step)")
     p.add_argument("--no-swiglu", action="store_true",
                    help="skip the SwiGLU block measurement (moe_swiglu shape)")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
@@ -166,6 +170,27 @@ class Step:
         chk(lib.tgmm_drhs(self.r_l8, self.r_g8, self.g.OUT_BF16, M, K, N, G, p["lhs_q"], p["s_lhs"],
                           p["grad_q"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
         rec(5)
+
+    def run_overlapped(self, s, s2, e_fork, e_join):
+        """Enqueue one step with the backward products on two streams: after the grad
+        quantizer, dlhs runs on `s` and tgmm on `s2` (torch streams; default priority), so
+        that tgmm's workgroups take the CUs dlhs leaves idle in its short last round of
+        tiles.  The two read the same grad codes and write separate outputs."""
+        lib, p = self.lib, self.p
+        M, K, N, G = self.M, self.K, self.N, self.G
+        chk, sp, sp2 = self._chk, s.cuda_stream, s2.cuda_stream
+        chk(lib.gmm_quantize(self.r_lq, M, K, p["lhs"], p["lhs_q"], p["s_lhs"], p["ws"], self.ws_n, sp))
+        chk(lib.gmm_fwd(self.r_l8, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
+                        p["lhs_q"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"], None, 0, sp))
+        chk(lib.gmm_quantize(self.r_gq, M, N, p["grad"], p["grad_q"], p["s_grad"], p["ws"], self.ws_n, sp))
+        e_fork.record(s)
+        s2.wait_event(e_fork)
+        chk(lib.gmm_dlhs(self.r_g8, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
+                         p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, sp))
+        chk(lib.tgmm_drhs(self.r_l8, self.r_g8, self.g.OUT_BF16, M, K, N, G, p["lhs_q"], p["s_lhs"],
+                          p["grad_q"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, sp2))
+        e_join.record(s2)
+        s.wait_event(e_join)
 
     def fused_fwd(self, stream):
         """The forward with the lhs quantized inside the product kernel (no workspace)."""
@@ -484,7 +509,20 @@ def main():
     names = ["quantize_lhs", "gmm_fwd", "quantize_grad", "gmm_dlhs", "tgmm_drhs"]
     per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
            for j, n in enumerate(names)}
-    ms_step = wall * 1000.0 / args.steps
+    ms_serial = wall * 1000.0 / args.steps
+    # The same steps with dlhs and tgmm on two streams: value and ms_per_step.
+    ms_step = ms_serial
+    if not args.no_overlap:
+        s2 = torch.cuda.Stream()
+        forks = [(torch.cuda.Event(), torch.cuda.Event()) for _ in range(args.steps)]
+        for _ in range(args.warmup):
+            step.run_overlapped(stream, s2, *forks[0])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step.run_overlapped(stream, s2, *forks[i])
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
     # the in-kernel quantization route of the forward, timed on its own after the steps
     fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     step.fused_fwd(s)
@@ -519,6 +557,11 @@ def main():
                    "rhs": "e4m3 per-channel", "out": "bf16",
                    "step": "lhs quantize + fwd + grad quantize + hybrid dlhs + tgmm; each tensor "
                            "quantized once, its codes used by every product"},
+        "serial_ms_per_step": round(ms_serial, 4),
+        "overlap": None if args.no_overlap else
+                   "the backward products dlhs and tgmm run on two HIP streams (ms_per_step, "
+                   "value); ops, prep_ms and roofline come from the same step run on one stream "
+                   "(serial_ms_per_step)",
         "ops": ops,
         "fwd_in_kernel_quantization": {"ms": round(fused_ms, 4),
                                        "TFLOP/s": round(flop_op / (fused_ms / 1000) / 1e12, 1),

@@ -53,6 +53,27 @@ def test_fused_swiglu_forward(lib, lhs_kind):
     assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
 
 
+def test_fused_swiglu_forward_saturated_gates(lib):
+    """Gate values spread over about +-130: e^-g overflows fp32 for g below about -88 and
+    underflows for large g, where the sigmoid saturates to 0 and 1; h stays finite and
+    within the parity metric of the float64 definition."""
+    sizes = [0, 300, 133, 457]
+    G, M, K, I = len(sizes), sum(sizes), 256, 256
+    x, xb = gen((M, K), 100.0, 531)
+    w, wb = gen((G, K, 2 * I), 0.02, 532)
+    wq, ws = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    gs = gs_tensor(sizes)
+    a_codes, s_blk = ops.quantize_operand(xb, "e4m3", "dynamic")
+    b_codes, b_s = quantize_rhs_per_channel(wb, "e4m3", "n")
+    R = gmm_fwd_ref(a_codes, "e4m3", row_scales(s_blk, M), b_codes, "e4m3", b_s, sizes)
+    assert R[:, :I].min() < -100 and R[:, :I].max() > 100  # both saturations occur
+    h = to_np(lib.gmm_fwd_swiglu(x, wq, ws, gs, out_dtype=torch.float32))
+    assert np.isfinite(h).all()
+    err = group_rel_err(h, swiglu_ref(R, I), group_row_ranges(sizes))
+    print(f"max group relative error of h {err:.3e}")
+    assert err <= TOL, err
+
+
 def test_swiglu_backward(lib):
     M, I = 777, 384
     dh, dhb = gen((M, I), 1e-3, 511)

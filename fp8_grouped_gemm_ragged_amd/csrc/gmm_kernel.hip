@@ -39,12 +39,7 @@ constexpr int BM = 256, BN = 256, BK = TILE_K;
 constexpr int NT = 256;
 constexpr int A_TILE = BM * BK;                // bytes of one fp8 A tile
 constexpr int B_TILE = BN * BK;
-constexpr int STAGE = A_TILE + B_TILE;         // 64 KB
 constexpr int BAND = 8;                        // M-tiles per band of the tile order
-
-// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100,
-              SG_DS_WR = 0x200;
 
 struct TileCoord {
   int g, row0, row_end, n0;

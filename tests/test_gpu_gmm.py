@@ -290,3 +290,35 @@ def test_quantize_once_route_writes_the_codes_into_the_workspace(lib):
     assert torch.equal(ws.view(M, K), xq)
     ref = lib.gmm_fwd(x, codes, scales, gs, lhs_scaling="static", static_scale=S_4_448, fused=True)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("op", ["fwd", "dlhs"])
+def test_more_tiles_than_cus_is_bit_identical(lib, op):
+    """More output tiles than the device has compute units (a full round of workgroups
+    and a short last one): the fp8-codes route is bit for bit equal to the in-kernel
+    quantization route."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sizes = [256 * 3 + 100, 0, 256 + 7]          # 4 + 0 + 2 = 6 M-tiles of 256 rows
+    n_nt = -(-(cus + cus // 8) // 6)             # about 9/8 of the CUs in tiles
+    M = sum(sizes)
+    gs = gs_tensor(sizes)
+    if op == "fwd":
+        K, N = 256, 256 * n_nt
+        x, _ = gen((M, K), 1.0, 171)
+        w, _ = channel_varied((len(sizes), K, N), 0.02, 172, 0)
+        codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+        ref, sc = lib.gmm_fwd(x, codes, scales, gs, out_dtype=torch.float32, return_scales=True,
+                              fused=True)
+        xq, _ = lib.gmm_quantize(x, "e4m3", "dynamic_given", scales=sc)
+        got = lib.gmm_fwd(xq, codes, scales, gs, lhs_scaling="dynamic_given", lhs_scales=sc,
+                          out_dtype=torch.float32)
+    else:
+        K, N = 256 * n_nt, 256                   # dlhs output tiles are 256 columns of K
+        gr, _ = gen((M, N), 1e-3, 173)
+        w, _ = channel_varied((len(sizes), K, N), 0.02, 174, 1)
+        codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 1, "kn")
+        ref = lib.gmm_dlhs(gr, codes, scales, gs, out_dtype=torch.float32, fused=True)
+        gq, gsc = lib.gmm_quantize(gr, "e5m2", "dynamic")
+        got = lib.gmm_dlhs(gq, codes, scales, gs, grad_scales=gsc, out_dtype=torch.float32)
+    sync()
+    assert torch.equal(ref.view(torch.int32), got.view(torch.int32))

@@ -449,8 +449,10 @@ gmm_status_t tgmm_drhs_local(const gmm_operand_t* lhs_op, const gmm_operand_t* g
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, K, N, G_total)) != GMM_OK) return s;
   if (group_offset < 0 || G < 1 || group_offset > G_total - G) return GMM_ERR_SHAPE;
-  // 32-bit tile numbers, and byte offsets inside a 256-row slice of a transposed segment
-  if (((K + 255) / 256) * ((N + 255) / 256) * G >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  // 32-bit workgroup numbers (each group's tiles rounded up to a multiple of 8), and byte
+  // offsets inside a 256-row slice of a transposed segment
+  if ((((K + 255) / 256) * ((N + 255) / 256) + 7) / 8 * 8 * G >= (int64_t(1) << 31))
+    return GMM_ERR_SHAPE;
   if (256 * tgmm_segment_row_bytes(M, G) >= (int64_t(1) << 32)) return GMM_ERR_SHAPE;
   if (!group_sizes || !drhs) return GMM_ERR_NULL;
   if (M > 0 && (!lhs || !grad)) return GMM_ERR_NULL;

@@ -85,7 +85,7 @@ struct BsParams {
 
 int64_t tgmm_segment_row_bytes(int64_t M, int G);
 // plan words: off, cnt, seg (G + 1), wide, final scale per group, one any-wide flag
-inline int64_t tgmm_plan_words(int G) { return 5 * (int64_t)G + 2; }
+inline int64_t tgmm_plan_words(int G) { return 6 * (int64_t)G + 2; }
 
 hipError_t launch_gemm(int a_fmt, int b_fmt, bool a_fp8, bool b_trans, const GemmParams& p,
                        hipStream_t st);

@@ -63,10 +63,11 @@ struct Plan {  // views of the plan words (see plan_words)
   const int32_t* wide;
   const float* fin;
   const int32_t* any_wide;
+  const int32_t* order;
 };
 __device__ inline Plan plan_view(const int32_t* w, int G) {
   return Plan{w, w + G, w + 2 * G, w + 3 * G + 1, reinterpret_cast<const float*>(w + 4 * G + 1),
-              w + 5 * G + 1};
+              w + 5 * G + 1, w + 5 * G + 2};
 }
 
 // Operand scaling as the plan sees it: per-block scales (blk) or a static scale and
@@ -107,7 +108,7 @@ __device__ inline int block_incl_scan(int v, int* tmp, Op op) {
 }
 
 // One workgroup.  Plan words: off[G], cnt[G], seg[G + 1], wide[G], fin[G] (float),
-// any_wide;
+// any_wide, order[G] (the groups by segment blocks, most first; ties by index);
 // scprod[c] per 128-row block (0 for a block that adds nothing); ratio[b + g] for
 // segment block b of group g, and 1 at ratio[seg[g + 1] + g], just past the group's
 // blocks.
@@ -168,6 +169,18 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
     scprod[cb] = dead ? 0.0f : sc;
   }
   __syncthreads();
+
+  // ---- the order in which the rescaling kernel walks the groups: most segment blocks
+  // first, ties by group index (each group's rank counts the groups that go before it) ----
+  if (t < G) {
+    const int nb_t = s_seg[t + 1] - s_seg[t];
+    int rank = 0;
+    for (int h = 0; h < G; ++h) {
+      const int nb_h = s_seg[h + 1] - s_seg[h];
+      rank += (nb_h > nb_t || (nb_h == nb_t && h < t)) ? 1 : 0;
+    }
+    plan[5 * G + 2 + rank] = t;
+  }
 
   // ---- per segment block ratios: each thread walks a contiguous chunk ----
   const int S = s_seg[G];
@@ -397,36 +410,25 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
 
   const int n_kt = (p.Kout + RBM - 1) / RBM;
   const int n_nt = (p.Nout + RBN - 1) / RBN;
-  const int total = n_kt * n_nt * p.G;
-  const int wg = blockIdx.x;
-  if (wg >= total) return;
-  // Workgroup i runs on XCD i % 8 and each XCD owns a contiguous range of the tile
-  // order.  That order is made of 32-tile super-tiles (the workgroups one XCD runs at a
-  // time), cycling over the groups so that every XCD holds an equal share of every
-  // group's work (a tile's work grows with its group's row count).  Inside a group,
-  // tiles run in bands of ST_K k-tiles, k-tile fastest, so one super-tile is ST_K k-tiles
-  // x 32/ST_K n-tiles: each A block it reads is shared by 32/ST_K workgroups and each
-  // B block by ST_K of them while they sit together in the XCD's L2.  Tiles past the
-  // last whole super-tile of each group follow, group-fastest.
-  const int xcd = wg & 7, jx = wg >> 3, qx = total >> 3, rx = total & 7;
-  const int L = xcd * qx + min(xcd, rx) + jx;
-  const int T = n_kt * n_nt, T32 = T & ~31;
-  int g, t;
-  if (L < p.G * T32) {
-    const int S = L >> 5;
-    g = S % p.G;
-    t = (S / p.G) * 32 + (L & 31);
-  } else {
-    const int r = L - p.G * T32;
-    g = r % p.G;
-    t = T32 + r / p.G;
-  }
+  // Workgroup i runs on XCD i % 8.  A tile's work grows with its group's row count, and
+  // one group may hold a third of the rows, so every group's T tiles are split into 8
+  // chunks of csize = ceil(T / 8) consecutive tiles, chunk x on XCD x: every XCD holds an
+  // equal share of every group's work.  Each XCD walks its chunks group by group in the
+  // plan's order, most blocks first, so the longest tiles start first.  Inside a group,
+  // tiles run in bands of ST_K k-tiles, k-tile fastest, so the 32 workgroups an XCD runs
+  // together form ST_K k-tiles x 32/ST_K n-tiles: each A block they read is shared by
+  // 32/ST_K workgroups and each B block by ST_K of them in the XCD's L2.
+  const int T = n_kt * n_nt, csize = (T + 7) / 8;
+  const int wg = blockIdx.x, xcd = wg & 7, jx = wg >> 3;
+  const int o = jx / csize, t = xcd * csize + (jx - o * csize);
+  if (o >= p.G || t >= T) return;
+  const Plan pl = plan_view(p.plan, p.G);
+  const int g = __builtin_amdgcn_readfirstlane(pl.order[o]);
   const int kt_base = t / (ST_K * n_nt) * ST_K;
   const int band_rows = min(ST_K, n_kt - kt_base);
   const int rt = t - kt_base * n_nt;
   const int kt = kt_base + rt % band_rows, nt = rt / band_rows;
 
-  const Plan pl = plan_view(p.plan, p.G);
   if (pl.wide[g]) return;  // tgmm_promote takes this group
   const int k0 = kt * RBM, n0 = nt * RBN;
   const int seg0 = __builtin_amdgcn_readfirstlane(pl.seg[g]);
@@ -856,7 +858,9 @@ hipError_t launch_qt(int fmt, bool codes, const void* x, int64_t M, int64_t C,
 
 template <int A_FMT, int B_FMT>
 hipError_t launch_tgmm_fp8(const TgmmSegParams& p, hipStream_t st) {
-  const int64_t tiles = (int64_t)((p.Kout + RBM - 1) / RBM) * ((p.Nout + RBN - 1) / RBN) * p.G;
+  // per group T tiles in 8 chunks of ceil(T / 8), one per XCD
+  const int64_t T = (int64_t)((p.Kout + RBM - 1) / RBM) * ((p.Nout + RBN - 1) / RBN);
+  const int64_t tiles = 8 * ((T + 7) / 8) * p.G;
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((tgmm_ratio_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(RNT), 0, st, p,
                      p.ratio);

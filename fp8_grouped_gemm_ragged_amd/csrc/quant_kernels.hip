@@ -28,6 +28,7 @@ __device__ inline uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
 
 // grid (nb, AMAX_SPLIT), 256 threads.  WG (b, s) covers rows
 // [b*128 + s*rows_per, +rows_per) of the block and all columns.
+template <bool NT>
 __global__ __launch_bounds__(256) void absmax_partial_kernel(const uint16_t* __restrict__ x,
                                                              int64_t R, int64_t C,
                                                              uint32_t* __restrict__ partial) {
@@ -36,23 +37,33 @@ __global__ __launch_bounds__(256) void absmax_partial_kernel(const uint16_t* __r
   constexpr int rows_per = BLOCK_ROWS / AMAX_SPLIT;
   const int64_t r0 = (int64_t)b * BLOCK_ROWS + (int64_t)s * rows_per;
   const int64_t r1 = min(r0 + rows_per, R);
-  const int64_t chunks = C / 8;  // 16-byte chunks per row (C % 8 == 0)
+  // rows r0 .. r1 - 1 are one contiguous range of 16-byte pieces (C % 8 == 0): walked as
+  // one range, four loads in flight per thread whatever the row width.  NT: non-temporal
+  // loads for a tensor too large to stay in the last-level cache; a smaller one is read
+  // normally, so that it is still there when the quantizing pass reads it again.
+  const int64_t pieces = r1 > r0 ? (r1 - r0) * (C / 8) : 0;
+  const v4u* slice = reinterpret_cast<const v4u*>(x + r0 * C);
   uint32_t m = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const v4u* row = reinterpret_cast<const v4u*>(x + r * C);
-    int64_t j = threadIdx.x;
-    for (; j + 768 < chunks; j += 1024) {
-      v4u w0 = __builtin_nontemporal_load(row + j);
-      v4u w1 = __builtin_nontemporal_load(row + j + 256);
-      v4u w2 = __builtin_nontemporal_load(row + j + 512);
-      v4u w3 = __builtin_nontemporal_load(row + j + 768);
-      m = absmax_bits16(w0, m);
-      m = absmax_bits16(w1, m);
-      m = absmax_bits16(w2, m);
-      m = absmax_bits16(w3, m);
+  int64_t j = threadIdx.x;
+  for (; j + 768 < pieces; j += 1024) {
+    v4u w0, w1, w2, w3;
+    if constexpr (NT) {
+      w0 = __builtin_nontemporal_load(slice + j);
+      w1 = __builtin_nontemporal_load(slice + j + 256);
+      w2 = __builtin_nontemporal_load(slice + j + 512);
+      w3 = __builtin_nontemporal_load(slice + j + 768);
+    } else {
+      w0 = slice[j];
+      w1 = slice[j + 256];
+      w2 = slice[j + 512];
+      w3 = slice[j + 768];
     }
-    for (; j < chunks; j += 256) m = absmax_bits16(row[j], m);
+    m = absmax_bits16(w0, m);
+    m = absmax_bits16(w1, m);
+    m = absmax_bits16(w2, m);
+    m = absmax_bits16(w3, m);
   }
+  for (; j < pieces; j += 256) m = absmax_bits16(slice[j], m);
   m = block_reduce_max(m, red);
   if (threadIdx.x == 0) partial[b * AMAX_SPLIT + s] = m;
 }
@@ -208,8 +219,13 @@ hipError_t launch_dynamic_scales(int fmt, const void* x, int64_t R, int64_t C,
                                  uint32_t* partial, float* scales_out, hipStream_t st) {
   const int nb = (int)((R + BLOCK_ROWS - 1) / BLOCK_ROWS);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(absmax_partial_kernel, dim3(nb, AMAX_SPLIT), dim3(256), 0, st,
-                     (const uint16_t*)x, R, C, partial);
+  // tensors above 128 MiB do not stay in the 256 MB last-level cache until the second pass
+  if ((int64_t)R * C * 2 > (int64_t(128) << 20))
+    hipLaunchKernelGGL(absmax_partial_kernel<true>, dim3(nb, AMAX_SPLIT), dim3(256), 0, st,
+                       (const uint16_t*)x, R, C, partial);
+  else
+    hipLaunchKernelGGL(absmax_partial_kernel<false>, dim3(nb, AMAX_SPLIT), dim3(256), 0, st,
+                       (const uint16_t*)x, R, C, partial);
   const int thr = 256, blocks = (nb + thr - 1) / thr;
   if (fmt == FMT_E4M3)
     hipLaunchKernelGGL(finalize_scales_kernel<FMT_E4M3>, dim3(blocks), dim3(thr), 0, st,

@@ -57,13 +57,12 @@ DynWs carve(void* base, int64_t rows) {
 
 // The call runs the abs-max prepass itself (and needs workspace) only for a bf16
 // operand with GMM_SCALE_DYNAMIC.
-// tgmm: plan words, per-block scale products, per-segment-block ratios and the two
-// quantized, transposed segment buffers.
-size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int32_t G) {
-  const size_t seg_row = (size_t)tgmm_segment_row_bytes(M, G);
+// tgmm: plan words, per-block scale products, per-segment-block ratios, and the row-major
+// codes of each operand that arrives as bf16 (quantized once by the call).
+size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int32_t G, bool a_codes, bool b_codes) {
   return align256((size_t)tgmm_plan_words(G) * 4) + align256((size_t)nblocks(M) * 4) +
-         align256((size_t)(nblocks(M) + 2 * G) * 4) + align256((size_t)K * seg_row) +
-         align256((size_t)N * seg_row);
+         align256((size_t)(nblocks(M) + 2 * G) * 4) + (a_codes ? 0 : align256((size_t)M * K)) +
+         (b_codes ? 0 : align256((size_t)M * N));
 }
 
 bool needs_dyn_ws(const gmm_operand_t* op) {
@@ -449,11 +448,9 @@ gmm_status_t tgmm_drhs_local(const gmm_operand_t* lhs_op, const gmm_operand_t* g
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, K, N, G_total)) != GMM_OK) return s;
   if (group_offset < 0 || G < 1 || group_offset > G_total - G) return GMM_ERR_SHAPE;
-  // 32-bit workgroup numbers (each group's tiles rounded up to a multiple of 8), and byte
-  // offsets inside a 256-row slice of a transposed segment
+  // 32-bit workgroup numbers (each group's tiles rounded up to a multiple of 8)
   if ((((K + 255) / 256) * ((N + 255) / 256) + 7) / 8 * 8 * G >= (int64_t(1) << 31))
     return GMM_ERR_SHAPE;
-  if (256 * tgmm_segment_row_bytes(M, G) >= (int64_t(1) << 32)) return GMM_ERR_SHAPE;
   if (!group_sizes || !drhs) return GMM_ERR_NULL;
   if (M > 0 && (!lhs || !grad)) return GMM_ERR_NULL;
   if (M > 0 && ((scales_are_input(lhs_op) && !lhs_scales) || (scales_are_input(grad_op) && !grad_scales)))
@@ -464,10 +461,10 @@ gmm_status_t tgmm_drhs_local(const gmm_operand_t* lhs_op, const gmm_operand_t* g
     if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
   const size_t wa = needs_dyn_ws(lhs_op) ? dyn_ws_bytes(M) : 0;
   const size_t wb = needs_dyn_ws(grad_op) ? dyn_ws_bytes(M) : 0;
-  const size_t wt = tgmm_ws_bytes(M, K, N, G);
+  const bool a_codes = lhs_op->kind == GMM_OPERAND_FP8, g_codes = grad_op->kind == GMM_OPERAND_FP8;
+  const size_t wt = tgmm_ws_bytes(M, K, N, G, a_codes, g_codes);
   if (!workspace || workspace_bytes < wa + wb + wt) return GMM_ERR_WORKSPACE;
   const size_t out_bytes = (size_t)G * K * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
-  const bool a_codes = lhs_op->kind == GMM_OPERAND_FP8, g_codes = grad_op->kind == GMM_OPERAND_FP8;
   const size_t lhs_bytes = (size_t)M * K * (a_codes ? 1 : 2);
   const size_t grad_bytes = (size_t)M * N * (g_codes ? 1 : 2);
   const size_t sc_bytes = (size_t)nblocks(M) * 4;
@@ -500,12 +497,12 @@ gmm_status_t tgmm_drhs_local(const gmm_operand_t* lhs_op, const gmm_operand_t* g
   p.out_f32 = out_dtype == GMM_OUT_F32;
   {
     uint8_t* base = (uint8_t*)workspace + wa + wb;
-    const size_t seg_row = (size_t)tgmm_segment_row_bytes(M, G);
     p.plan = (int32_t*)base;
     p.scprod = (float*)(base + align256((size_t)tgmm_plan_words(G) * 4));
     p.ratio = (float*)((uint8_t*)p.scprod + align256((size_t)nblocks(M) * 4));
-    p.a_seg = (uint8_t*)p.ratio + align256((size_t)(nblocks(M) + 2 * G) * 4);
-    p.b_seg = p.a_seg + align256((size_t)K * seg_row);
+    uint8_t* codes = (uint8_t*)p.ratio + align256((size_t)(nblocks(M) + 2 * G) * 4);
+    p.a_q = a_codes ? nullptr : codes;
+    p.b_q = g_codes ? nullptr : codes + (a_codes ? 0 : align256((size_t)M * K));
   }
   if (M > 0) {
     Scaling sa, sg;
@@ -540,7 +537,8 @@ gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_op
     if (!b) return GMM_ERR_NULL;
     if ((s = check_operand(b)) != GMM_OK) return s;
     n += needs_dyn_ws(b) ? dyn_ws_bytes(rows) : 0;
-    n += tgmm_ws_bytes(rows, cols_a, cols_b, G);
+    n += tgmm_ws_bytes(rows, cols_a, cols_b, G, a->kind == GMM_OPERAND_FP8,
+                       b->kind == GMM_OPERAND_FP8);
   } else if (op != GMM_OP_FWD && op != GMM_OP_DLHS && op != GMM_OP_FWD_FUSED &&
              op != GMM_OP_DLHS_FUSED && op != GMM_OP_QUANTIZE && op != GMM_OP_FWD_SWIGLU) {
     return GMM_ERR_RECIPE;

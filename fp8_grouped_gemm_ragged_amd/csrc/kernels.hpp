@@ -45,8 +45,8 @@ struct TgmmParams {
   int32_t* plan;             // workspace: tgmm_plan_words(G) words
   float* scprod;             // workspace: one scale product per 128-row block
   float* ratio;              // workspace: ceil(M / 128) + 2 G floats
-  uint8_t* a_seg;            // workspace: Kout x tgmm_segment_row_bytes(M, G)
-  uint8_t* b_seg;            // workspace: Nout x tgmm_segment_row_bytes(M, G)
+  uint8_t* a_q;              // workspace (bf16 a only): its codes, row-major [M, Kout]
+  uint8_t* b_q;              // workspace (bf16 b only): its codes, row-major [M, Nout]
   const float* a_scale_blk;  // dynamic: per-block scales; null -> static
   const float* b_scale_blk;
   float a_inv_static, a_scale_static, b_inv_static, b_scale_static;
@@ -55,18 +55,6 @@ struct TgmmParams {
   int32_t g_before;          // group window: the G groups after the first g_before ones
   int32_t out_f32;
   int32_t a_codes, b_codes;  // the operand is fp8 codes quantized beforehand
-};
-
-// the fp8 tgmm on quantized, transposed segments
-struct TgmmSegParams {
-  const uint8_t* a_seg;
-  const uint8_t* b_seg;
-  const int32_t* plan;
-  const float* scprod;
-  const float* ratio;
-  void* out;
-  int32_t Kout, Nout, G, out_f32;
-  int64_t seg_row;
 };
 
 // forward with block-wise scales: out[M, N] from fp8 A [M, K] (scales [M, K / bk]) and
@@ -83,7 +71,6 @@ struct BsParams {
   int32_t out_f32;
 };
 
-int64_t tgmm_segment_row_bytes(int64_t M, int G);
 // plan words: off, cnt, seg (G + 1), wide, final scale per group, one any-wide flag
 inline int64_t tgmm_plan_words(int G) { return 6 * (int64_t)G + 2; }
 

@@ -1,56 +1,53 @@
 // Transposed grouped matmul on gfx950: the kernels behind tgmm_drhs ("Support
 // quantization for tokamax gmm v2", PR #4451, What this does: drhs_tgmm2).
 //
-//   drhs[g, k, n] = sum over 128-row blocks c meeting group g of
-//                   RNE( P_c[k, n] * RNE(s_lhs[c] * s_grad[c]) ),
-//   P_c[k, n]     = sum_{m in c, m in g} q(lhs)[m, k] * q(grad)[m, n]   (fp32 MFMA sums)
+//   drhs[g, k, n] = sum over 128-row blocks c meeting group g of  P_c[k, n] * sc_c,
+//   P_c[k, n]     = sum_{m in c, m in g} q(lhs)[m, k] * q(grad)[m, n]   (fp32 MFMA sums),
+//   sc_c          = RNE(s_lhs[c] * s_grad[c])
 //
-// The contraction runs over the rows of a group, and both operands are stored with
-// that axis strided.  The path therefore has four kernels:
-//   1. tgmm_plan: per group the first row, the row count and the offset of its
-//      "segment" (the 128-row blocks the group meets, laid end to end); per block the
-//      scale product sc_c; per segment block the ratio of scale products used below.
-//   2. quant_transpose (once per operand): every element quantized exactly once (with
-//      its block's scale), or taken as it is when the operand arrives as fp8 codes, and
-//      written transposed into the segment, so that each group's rows start on a block
-//      boundary and rows of other groups inside a shared block are zero codes.  Columns are stored in pairs: block b of columns 2p, 2p + 1 is 256
-//      bytes, [2p: m 0..63][2p + 1: m 0..63][2p: m 64..127][2p + 1: m 64..127], so a
-//      half block of two columns is one 128-byte line.
-//   3. tgmm_ratio: per (group, 256 k x 256 n) tile, one contraction step per block of
-//      the group's segment.  Instead of scaling each block's partial sum and adding it
+// The contraction runs over the rows of a group, and both operands are stored row-major
+// with that axis strided.  The kernels read the row-major fp8 codes directly: a tile of
+// 128 rows x 256 columns is copied into LDS as it lies in memory (whole 128-byte lines
+// from global memory), and gfx950's transposing LDS read (ds_read_b64_tr_b8) hands every
+// lane the 8 rows of one column that an MFMA operand needs, so no transposed copy of
+// either operand is made.  A bf16 operand is quantized once, row-major, into the
+// workspace by the stand-alone quantizer (its codes are those every other product uses).
+//
+//   1. tgmm_plan: per group the first row, the row count and the index of its first
+//      "segment block" (the 128-row blocks the group meets, numbered end to end over
+//      the groups); per block the scale product sc_c (0 for a block that adds nothing);
+//      per segment block the ratio of scale products used below.
+//   2. tgmm_main: per (group, 256 k x 256 n) tile, one contraction step per 128-row
+//      block of the group.  Instead of scaling each block's partial sum and adding it
 //      (two vector ops per value per block), the fp32 accumulators are kept in units of
 //      the current block's scale product: MFMA adds P_c straight into them, and between
-//      blocks each value is multiplied once by sc_prev / sc_next.  The last block's
-//      scale product is applied in the epilogue.  A group without rows stores +0.0.
-//   4. tgmm_promote: the exact per-block promotion (fresh MFMA partial, then
-//      acc += partial * sc_c), for the rare groups whose scale products span more than
-//      2^60, where the rescaled accumulators could leave the fp32 range.
+//      blocks each value is multiplied once by sc_prev / sc_next.  The last block's scale
+//      product is applied in the epilogue.  A group without rows stores +0.0.
+//   3. tgmm_promote: the per-block promotion as the method states it (fresh MFMA
+//      partial P_c, then acc = RNE(acc + RNE(P_c * sc_c))), for the rare groups whose
+//      scale products span more than 2^60, where the rescaled accumulators could leave
+//      the fp32 range.
 //
 // A block whose scale product is zero (an all-zero block, a scale whose inverse is not
-// finite, or a product that underflows) adds nothing in the method; its codes are
-// written as zeros and it keeps the accumulator units unchanged.  For an operand given
-// as codes only a zero product counts: its codes are used as they are.
+// finite, or a product that underflows) adds nothing in the method: its rows are read
+// as zeros and it leaves the accumulator units unchanged.  For an operand given as codes
+// only a zero product counts: its codes are used as they are.
 #include "kernels.hpp"
 
 namespace gmm {
 
 namespace {
 
-// tgmm_promote tile
-constexpr int TBM = 256;   // k rows of a slab tile
-constexpr int TBN = 128;   // n columns of a slab tile
-constexpr int NT = 256;
-constexpr int A_TILE = TBM * TILE_K;  // [256 k][128 m] fp8
-constexpr int B_TILE = TBN * TILE_K;  // [128 n][128 m] fp8
-// tgmm_ratio tile
-constexpr int RBM = 256;   // k rows
-constexpr int RBN = 256;   // n columns
-constexpr int RNT = 512;   // 8 waves: 2 (k) x 4 (n), 128 x 64 each
-constexpr int RA_TILE = RBM * TILE_K;
-constexpr int RB_TILE = RBN * TILE_K;
-constexpr int ST_K = 4;    // k-tiles per band of the tile order
+constexpr int MBK = 256;    // k rows of a tgmm_main tile
+constexpr int MBN = 256;    // n columns of a tgmm_main tile
+constexpr int MNT = 512;    // 8 waves: 2 (k) x 4 (n), 128 k x 64 n each (two per SIMD)
+constexpr int ROWB = 256;   // bytes of one LDS row: 256 k (lhs) or 256 n (grad) codes
+constexpr int OPB = BLOCK_ROWS * ROWB;  // one operand's 128-row stage tile: 32 KB
+constexpr int ST_K = 4;     // k-tiles per band of the tile order
+constexpr int PBK = 128;    // tgmm_promote tile: 128 k x 128 n, 4 waves of 64 x 64
+constexpr int PNT = 256;
+constexpr int PROWB = 128;  // bytes of one promote LDS row
 constexpr int PLAN_NT = 1024;
-constexpr int PAIR_BLOCK = 2 * BLOCK_ROWS;  // bytes of one block of a column pair
 static_assert(MAX_GROUPS <= PLAN_NT, "one plan thread per group");
 // widest spread of nonzero scale products in a group that the rescaled accumulators
 // take: with |P_c| <= 128 * 57344^2 and at most 2^15 blocks the values stay below 2^114
@@ -268,156 +265,95 @@ __global__ __launch_bounds__(PLAN_NT) void tgmm_plan_kernel(
   if (t == 0) plan[5 * G + 1] = any;
 }
 
-// Quantize an 8 (rows) x 8 (cols) bf16 block held as 8 row vectors into 8 column
-// vectors of 8 codes each (rows 0..3 in .x, rows 4..7 in .y): the paired conversion
-// packs two rows of one column per instruction, so the transposition is free.
-template <int FMT>
-__device__ inline void quant_transpose8(const v4u in[8], float inv, v2u out[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float v[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t d = c < 2 ? in[r].x : c < 4 ? in[r].y : c < 6 ? in[r].z : in[r].w;
-      v[r] = quant_prep<FMT>((c & 1) ? bf16_hi(d) : bf16_lo(d), inv);
-    }
-    uint32_t lo = cvt_pk<FMT, false>(v[0], v[1], __float_as_uint(v[0]));
-    lo = cvt_pk<FMT, true>(v[2], v[3], lo);
-    uint32_t hi = cvt_pk<FMT, false>(v[4], v[5], __float_as_uint(v[4]));
-    hi = cvt_pk<FMT, true>(v[6], v[7], hi);
-    out[c].x = lo;
-    out[c].y = hi;
-  }
+// ---------------------------------------------------------------------------------
+// LDS tiles of row-major codes and their transposing reads.
+//
+// A stage tile is [128 rows m][R bytes] (R = 256 in tgmm_main, 128 in tgmm_promote).
+// 16-byte chunk c of row m sits at chunk position c ^ key(m): the 8 rows that one
+// 16-lane group of a transposing read touches land on distinct 16-byte bank groups.
+//
+// ds_read_b64_tr_b8 (measured lane layout): within each group of 16 lanes, lane j
+// receives byte b from the address of lane 2b + (j >> 3), plus (j & 7).  So if lane
+// 2b + h addresses row m0 + b at column col0 + 8h, lane j receives column col0 + j of
+// rows m0 .. m0 + 7, one byte per row: 8 contraction bytes of one MFMA operand row.
+// ---------------------------------------------------------------------------------
+typedef int32_t v2i __attribute__((ext_vector_type(2)));
+
+__device__ inline v2i lds_read_tr8(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
 }
 
-// grid (segment blocks upper bound, ceil(C / CW)).  Workgroup (b, ct): segment block b
-// (a pair (group g, 128-row block c)) and columns [CW ct, CW ct + CW).  A block whose
-// scale product is zero gets zero codes.  x holds bf16 values, quantized here with the
-// block's scale (CW = 128: 8 rows x 8 columns per thread), or (CODES) fp8 codes quantized
-// beforehand, which are only transposed (CW = 256: 8 rows x 16 columns per thread, so a
-// load reads 16 bytes of a row).
-template <int FMT, bool CODES>
-__global__ __launch_bounds__(256) void quant_transpose_kernel(
-    const void* __restrict__ x, int64_t C, const int32_t* __restrict__ plan, int G,
-    const float* __restrict__ scale_blk, float inv_static, const float* __restrict__ scprod,
-    uint8_t* __restrict__ seg, int64_t seg_row) {
-  constexpr int ES = CODES ? 1 : 2;     // bytes per element of x
-  constexpr int CW = CODES ? 256 : 128;  // columns per workgroup
-  const int32_t* off = plan;
-  const int32_t* cnt = plan + G;
-  const int32_t* sg = plan + 2 * G;
-  const int b = blockIdx.x;
-  if (b >= sg[G]) return;
-  int lo = 0, hi = G;  // sg[lo] <= b < sg[lo + 1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (sg[mid] <= b) lo = mid; else hi = mid;
+// One 32 x 64 MFMA operand from a stage tile: operand row r (0..31) is tile column
+// R0 + r, and its 64 contraction bytes are tile rows m0 .. m0 + 63.  Lane l holds row
+// l % 32 and contraction bytes 8 q + b = tile row m0 + 32 (l / 32) + 8 q + b: the same
+// assignment for both operands of an MFMA, so the products pair up.  `lo` is the lane's
+// address of its first read (row part and swizzled column, see tr_lane_offset).
+template <int R>
+__device__ inline v8i frag_tr8(const uint8_t* lo) {
+  v8i f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v2i v = lds_read_tr8(lo + q * 8 * R);
+    f[2 * q] = v.x;
+    f[2 * q + 1] = v.y;
   }
-  const int g = __builtin_amdgcn_readfirstlane(lo);
-  const int o = __builtin_amdgcn_readfirstlane(off[g]);
-  const int n = __builtin_amdgcn_readfirstlane(cnt[g]);
-  const int c = o / BLOCK_ROWS + (b - __builtin_amdgcn_readfirstlane(sg[g]));
-  const int r_lo = max(o, c * BLOCK_ROWS), r_hi = min(o + n, (c + 1) * BLOCK_ROWS);
-  const int rel = r_lo - c * BLOCK_ROWS;  // first row of the block that belongs to g
-  const int64_t col0 = (int64_t)blockIdx.y * CW;
-  // rows [r_lo, r_hi) from column col0 on: later rows read as zero
-  const __amdgpu_buffer_rsrc_t r =
-      make_rsrc((const uint8_t*)x + ((int64_t)r_lo * C + col0) * ES,
-                (uint32_t)(((int64_t)(r_hi - r_lo) * C - col0) * ES));
-  const bool dead = scprod[c] == 0.0f;
-  const int t = threadIdx.x;
-  const int rb = t & 15, cb = t >> 4;  // 8-row block; 8- (bf16) or 16-column (codes) block
-  // segment layout by column pairs: pair p, block b holds 256 bytes, [col 2p, m 0..63]
-  // [col 2p + 1, m 0..63] [col 2p, m 64..127] [col 2p + 1, m 64..127]
-  auto store8 = [&](int64_t col, const v2u (&q)[8]) {
-    uint8_t* dst = seg + col * seg_row + (int64_t)b * PAIR_BLOCK + (rb >> 3) * 128 + (rb & 7) * 8;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
-      *reinterpret_cast<v2u*>(dst + (cc >> 1) * 2 * seg_row + (cc & 1) * 64) = q[cc];
-  };
-  if constexpr (CODES) {
-    if (col0 + cb * 16 >= C) return;  // C is a multiple of 128: whole 16-column blocks
-    v4u in[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = rb * 8 + e - rel;  // relative to the first row of g in the block
-      uint32_t voff = (uint32_t)row * (uint32_t)C + cb * 16;
-      if (row < 0 || dead) voff = 0xfffffff0u;  // previous group's rows, or a dead block: zeros
-      in[e] = buf_load16(r, voff);
-    }
-    v2u lo8[8], hi8[8], q[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo8[e].x = in[e].x; lo8[e].y = in[e].y;
-      hi8[e].x = in[e].z; hi8[e].y = in[e].w;
-    }
-    transpose8x8(lo8, q);
-    store8(col0 + cb * 16, q);
-    transpose8x8(hi8, q);
-    store8(col0 + cb * 16 + 8, q);
-  } else {
-    const float inv = dead ? 0.0f : scale_blk ? inv_from_scale(scale_blk[c]) : inv_static;
-    v4u in[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = rb * 8 + e - rel;
-      uint32_t voff = (uint32_t)row * (uint32_t)(C * 2) + cb * 16;
-      if (row < 0) voff = 0xfffffff0u;  // rows of the previous group: zero codes
-      in[e] = buf_load16(r, voff);
-    }
-    v2u q[8];
-    quant_transpose8<FMT>(in, inv, q);
-    store8(col0 + cb * 8, q);
-  }
+  return f;
 }
 
-// One wave fills 8 rows (1 KB) of a swizzled [rows][128 B] tile from global memory.
-__device__ inline void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_rows,
-                                        uint32_t goff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_rows, 16, goff, 0, 0, 0);
+// The lane's address (from the tile's start, for m0 = 0) of operand rows R0 .. R0 + 31
+// (R0 a multiple of 32) in a tile of R-byte rows whose chunk position is c ^ key(m):
+// lane l = 16 g16 + j addresses row 32 (g16 >> 1) + (j >> 1) (+ 8 q per read), column
+// R0 + 16 (g16 & 1) + 8 (j & 1).  key(m) depends on m & 7 = (j >> 1) only.
+template <int R>
+__device__ inline uint32_t tr_lane_offset(int lane, int R0) {
+  const int g16 = lane >> 4, j = lane & 15;
+  const int row = 32 * (g16 >> 1) + (j >> 1);
+  const int chunk = (R0 >> 4) + (g16 & 1);
+  const int key = R == 256 ? 2 * (j >> 1) : (j >> 1);
+  return (uint32_t)(row * R + ((chunk ^ key) << 4) + 8 * (j & 1));
 }
 
-// Half-block stage of the rescaling kernel: [256 rows][64 contraction bytes] per operand.
-// 16-byte chunk c of row r sits at chunk position c ^ (((r >> 1) ^ (r >> 3)) & 3): the
-// rows one phase of a fragment read touches (8 rows over 32 banks, or 16 over 64) then
-// fall on distinct 16-byte bank groups.
-constexpr int HROW = 64;
-constexpr int RH_TILE = RBM * HROW;  // 16 KB
+// Row range of block c inside the group [off, off + cnt).
+__device__ inline void block_rows(int c, int off, int cnt, int& lo, int& hi) {
+  lo = max(off, c * BLOCK_ROWS);
+  hi = min(off + cnt, c * BLOCK_ROWS + BLOCK_ROWS);
+}
 
-// One (group, 256 k x 256 n) tile per workgroup of 8 waves, each wave 128 k x 64 n
-// (2 x 4 waves; two waves per SIMD, so one wave's vector work overlaps the other's
-// MFMAs).  The contraction runs in half-blocks of 64 rows through a ring of 4 LDS
-// stages: half-step h's fp8 tiles are loaded into one of two register staging sets
-// three half-steps ahead and written into stage h % 4 two half-steps ahead, and
-// half-step h + 1's fragments are read into registers while half-step h's MFMAs run,
-// so no step waits on LDS reads when it starts.
+struct TgmmCodesParams {
+  const uint8_t* a;      // lhs codes [M, Kout]
+  const uint8_t* b;      // grad codes [M, Nout]
+  const int32_t* plan;
+  const float* scprod;
+  const float* ratio;
+  void* out;             // [G, Kout, Nout] bf16 or f32
+  int32_t Kout, Nout, G, out_f32;
+};
+
+// One (group, 256 k x 256 n) tile per workgroup of 8 waves, each 128 k x 64 n (2 x 4
+// waves; two per SIMD, so one wave's vector work overlaps the other's MFMAs).  Step s
+// contracts the group's rows in its block c_lo + s: two LDS stages of [128 rows][256 B]
+// per operand (128 KB), filled from registers that were loaded two steps ahead; one
+// barrier per step.
 template <int A_FMT, int B_FMT>
-__global__ __attribute__((amdgpu_flat_work_group_size(RNT, RNT), amdgpu_waves_per_eu(2, 2)))
-void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
-  // one array for the 4 stages (A tile, then B tile, per stage): every LDS address is
-  // then a per-lane register plus a constant that fits the instruction's offset field
-  // (two base registers in all), instead of one register per stage and operand
-  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[8 * RH_TILE];
+__global__ __attribute__((amdgpu_flat_work_group_size(MNT, MNT), amdgpu_waves_per_eu(2, 2)))
+void tgmm_main_kernel(TgmmCodesParams p) {
+  // stage x: A tile at 2 x OPB, B tile at 2 x OPB + OPB
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[4 * OPB];
   uint8_t* const sA0 = s_lds;
-  uint8_t* const sB0 = s_lds + RH_TILE;
-  uint8_t* const sA1 = s_lds + 2 * RH_TILE;
-  uint8_t* const sB1 = s_lds + 3 * RH_TILE;
-  uint8_t* const sA2 = s_lds + 4 * RH_TILE;
-  uint8_t* const sB2 = s_lds + 5 * RH_TILE;
-  uint8_t* const sA3 = s_lds + 6 * RH_TILE;
-  uint8_t* const sB3 = s_lds + 7 * RH_TILE;
+  uint8_t* const sB0 = s_lds + OPB;
+  uint8_t* const sA1 = s_lds + 2 * OPB;
+  uint8_t* const sB1 = s_lds + 3 * OPB;
 
-  const int n_kt = (p.Kout + RBM - 1) / RBM;
-  const int n_nt = (p.Nout + RBN - 1) / RBN;
+  const int n_kt = (p.Kout + MBK - 1) / MBK;
+  const int n_nt = (p.Nout + MBN - 1) / MBN;
   // Workgroup i runs on XCD i % 8.  A tile's work grows with its group's row count, and
   // one group may hold a third of the rows, so every group's T tiles are split into 8
   // chunks of csize = ceil(T / 8) consecutive tiles, chunk x on XCD x: every XCD holds an
   // equal share of every group's work.  Each XCD walks its chunks group by group in the
   // plan's order, most blocks first, so the longest tiles start first.  Inside a group,
   // tiles run in bands of ST_K k-tiles, k-tile fastest, so the 32 workgroups an XCD runs
-  // together form ST_K k-tiles x 32/ST_K n-tiles: each A block they read is shared by
-  // 32/ST_K workgroups and each B block by ST_K of them in the XCD's L2.
+  // together form ST_K k-tiles x 32/ST_K n-tiles that share lhs and grad rows in its L2.
   const int T = n_kt * n_nt, csize = (T + 7) / 8;
   const int wg = blockIdx.x, xcd = wg & 7, jx = wg >> 3;
   const int o = jx / csize, t = xcd * csize + (jx - o * csize);
@@ -430,7 +366,7 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
   const int kt = kt_base + rt % band_rows, nt = rt / band_rows;
 
   if (pl.wide[g]) return;  // tgmm_promote takes this group
-  const int k0 = kt * RBM, n0 = nt * RBN;
+  const int k0 = kt * MBK, n0 = nt * MBN;
   const int seg0 = __builtin_amdgcn_readfirstlane(pl.seg[g]);
   const int nblk = __builtin_amdgcn_readfirstlane(pl.seg[g + 1]) - seg0;
 
@@ -438,166 +374,159 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
   const int wr = wave >> 2, wc = wave & 3;  // wave sub-tile: 128 (k) x 64 (n)
   const int frow = lane & 31, fhalf = lane >> 5;
 
-  v16f acc[8];
+  v16f acc[8];  // acc[2 i + j]: k rows wr 128 + 32 i.., n columns wc 64 + 32 j..
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[b] = v16f{0};
   float fin = 1.0f;
 
   if (nblk > 0) {
     fin = pl.fin[g];
-    const int H = 2 * nblk;  // half-steps
-    const uint32_t seg_row = (uint32_t)p.seg_row;
-    const int krows = min(p.Kout - k0, RBM), nrows = min(p.Nout - n0, RBN);
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
-                  (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
-                  (uint32_t)((int64_t)nrows * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
-    // The ratio half-step h applies: block (h + 1) / 2's (the tail of the move into
-    // block h / 2 for even h, the head of the move into block h / 2 + 1 for odd h).  The
-    // group's ratios are followed by a 1 (for the move past its last block); the index
-    // stops there.  A uniform read through a restrict pointer: a scalar load, outside
-    // the vector-load count the pipeline waits on.
-    const float* gratio = ratio + seg0 + g;
-    auto ratio_of = [&](int h) -> float { return gratio[min((h + 1) >> 1, nblk)]; };
+    const int off = __builtin_amdgcn_readfirstlane(pl.off[g]);
+    const int cnt = __builtin_amdgcn_readfirstlane(pl.cnt[g]);
+    const int c_lo = off / BLOCK_ROWS;
+    const int K = p.Kout, N = p.Nout;
+    // ratio(t): the factor of the move into the group's block t (a 1 follows the last)
+    const float* gratio = p.ratio + seg0 + g;
 
-    // Half-step X of both tiles goes through registers: thread t holds 16-byte chunks t
-    // and t + 512 of each tile (row idx / 4, logical chunk idx % 4); in the column-pair
-    // layout 8 consecutive threads cover one 128-byte line (rows 2p, 2p + 1).  Past the
-    // last half-step the offsets leave the ranges and the loads return zeros.
-    auto gload = [&](int X, v4u (&sa)[2], v4u (&sb)[2]) {
-      const uint32_t hoff =
-          X < H ? (uint32_t)(X >> 1) * PAIR_BLOCK + (uint32_t)(X & 1) * 128 : 0x80000000u;
+    // Global loads: thread t moves 16-byte chunk t & 15 of rows (t >> 4) + 32 q of the
+    // step's 128 rows (q = 0..3), of both operands: 16 threads read one row's 256
+    // contiguous bytes (two whole lines).  Offsets are relative to the step's first row
+    // of the group; rows before it wrap around to offsets past the range and read zeros.
+    const int lrow = tid >> 4, lch = tid & 15;
+    uint32_t a_off[4], b_off[4];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = q * RNT + tid, row = idx >> 2;
-        const uint32_t go = (uint32_t)(row >> 1) * 2 * seg_row + (uint32_t)(row & 1) * 64 + hoff +
-                            (uint32_t)(idx & 3) * 16;
-        sa[q] = buf_load16(ra, go);
-        sb[q] = buf_load16(rb, go);
-      }
-    };
-    uint32_t wo[2];  // the chunks' places in a stage tile
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = q * RNT + tid, row = idx >> 2;
-      wo[q] = (uint32_t)row * HROW + ((uint32_t)((idx & 3) ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+    for (int q = 0; q < 4; ++q) {
+      a_off[q] = (uint32_t)(lrow + 32 * q) * (uint32_t)K + lch * 16;
+      b_off[q] = (uint32_t)(lrow + 32 * q) * (uint32_t)N + lch * 16;
     }
-    auto lwrite = [&](uint8_t* t, const v4u (&sv)[2]) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(t + wo[q]) = sv[q];
+    const uint32_t wofs = (uint32_t)lrow * ROWB + ((uint32_t)(lch ^ (2 * (lrow & 7))) << 4);
+    v4u sa[4], sb[4];  // staging registers of step s + 2
+    // Step x's loads into the staging registers: block c_lo + x's rows of the group;
+    // past the group, or in a block whose scale product is zero, everything reads zero.
+    auto gload = [&](int x, bool live, int q) {
+      int lo, hi;
+      block_rows(c_lo + x, off, cnt, lo, hi);
+      live = live && x < nblk;
+      const __amdgpu_buffer_rsrc_t ra =
+          make_rsrc(p.a + (int64_t)lo * K + k0, live ? (uint32_t)((hi - lo) * K - k0) : 0u);
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(p.b + (int64_t)lo * N + n0, live ? (uint32_t)((hi - lo) * N - n0) : 0u);
+      const int skip = lo - (c_lo + x) * BLOCK_ROWS;  // rows of the block before the group
+      sa[q] = buf_load16(ra, a_off[q] - (uint32_t)(skip * K));
+      sb[q] = buf_load16(rb, b_off[q] - (uint32_t)(skip * N));
     };
-    uint32_t fo[2];
-    {
-      const uint32_t f0 = (uint32_t)(((frow >> 1) ^ (frow >> 3)) & 3);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) fo[e] = (uint32_t)frow * HROW + ((((uint32_t)(2 * fhalf + e)) ^ f0) << 4);
-    }
-    auto frag = [&](const uint8_t* tile, int base_row, int i) -> v8i {
-      const uint8_t* p0 = tile + (base_row + i * 32) * HROW;
-      const v4u lo = *reinterpret_cast<const v4u*>(p0 + fo[0]);
-      const v4u hi = *reinterpret_cast<const v4u*>(p0 + fo[1]);
-      v8i f;
-      f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-      f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-      return f;
+    // whether block c_lo + x adds anything (read one step before its loads are issued)
+    auto live_of = [&](int x) -> bool {
+      return p.scprod[c_lo + min(x, nblk - 1)] != 0.0f;
     };
-    auto rescale = [&](int b, int half, float r) {
+    auto lwrite = [&](uint8_t* at, uint8_t* bt, int q) {
+      *reinterpret_cast<v4u*>(at + q * 32 * ROWB + wofs) = sa[q];
+      *reinterpret_cast<v4u*>(bt + q * 32 * ROWB + wofs) = sb[q];
+    };
+    // fragment addresses: A operand rows wr 128 + 32 i (k), B operand rows wc 64 + 32 j (n)
+    uint32_t fa[4], fb[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[b][half * 8 + e] *= r;
+    for (int i = 0; i < 4; ++i) fa[i] = tr_lane_offset<ROWB>(lane, wr * 128 + 32 * i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = tr_lane_offset<ROWB>(lane, wc * 64 + 32 * j);
+    auto fragA = [&](const uint8_t* at, int i, int ks) { return frag_tr8<ROWB>(at + fa[i] + ks * 64 * ROWB); };
+    auto fragB = [&](const uint8_t* bt, int j, int ks) { return frag_tr8<ROWB>(bt + fb[j] + ks * 64 * ROWB); };
+    auto rescale = [&](int v, int h, float r) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[v][h * 8 + e] *= r;
     };
 
-    // Half-step h on stage (at, bt).  Unit u: MFMA on sub-block u = 2 i + j (acc[u] holds
-    // A rows 32 i.., B rows 32 j..).  B fragments stay in bf for the whole half-step; A
-    // fragment i is read into slot i % 2 two units before its first use.  After the
-    // first MFMA: this wave's LDS writes of stage h + 1 (made during h - 1) and its reads
-    // are done; then the workgroup barrier, after which all of stage h + 1 may be read.
-    // Then: the loads of half-step h + 3 into staging set (la, lb); at units 4 and 5
-    // staging set (wa, wb), loaded during h - 1, written to stage h + 2 (the four loads
-    // of h + 3 may stay in flight); at units 6 and 7 half-step h + 1's first fragments
-    // from stage h + 1 (bf[0] and A fragment 0 after the last uses here, bf[1] last).
-    // Rescales: the accumulators hold units of the last live block's scale product; the
-    // move into block c + 1 multiplies acc[u] by ratio[c + 1] in two halves, at units
-    // u + 10 and u + 13 counted from block c's first half-step (after its last MFMA of
-    // block c, before its first of block c + 1).  The ratio register r serves
-    // half-steps h, h + 4, ...: it is reloaded after its last use here.
-    v8i af[2], bf[2];
-    auto half = [&](int h, const uint8_t* at, const uint8_t* an, const uint8_t* bn, uint8_t* aw,
-                    uint8_t* bw, v4u (&la)[2], v4u (&lb)[2], const v4u (&wa)[2],
-                    const v4u (&wb)[2], float& r) {
-      const bool second = h & 1;
-      float rn = 1.0f;
+    // Step s on stage (at, bt); (an, bn) is the next stage.  Unit u issues MFMA
+    // (ks = u / 8, i = (u / 2) % 4, j = u % 2) on acc[2 i + j], with the A fragment of
+    // linear index L = 4 ks + i in register slot L % 2.  Alongside:
+    //   * units 0..3: staging chunk q = u (step s + 1) is written to the next stage and
+    //     refilled with step s + 2's loads;
+    //   * after odd unit u <= 11, A fragment L = (u + 3) / 2 is read into the slot unit u
+    //     has just finished with (two MFMAs before its first use); the ks = 1 B
+    //     fragments are read after unit 3;
+    //   * before unit 14: this wave's LDS work is done, the workgroup barrier, after which
+    //     the next stage is complete and the next step's first fragments are read while
+    //     units 14 and 15 (whose fragments are in registers) keep the matrix core busy;
+    //     the next step's A fragment 1 follows unit 15;
+    //   * the move into block s + 1 multiplies acc[v] by r_next in two halves, half 0 at
+    //     unit 10 + v and half 1 at unit 14 + v (two MFMAs after acc[v]'s last one of the
+    //     block at unit 8 + v); the halves past unit 15 run in units 0..5 of the next step,
+    //     with the same ratio (r_prev there), before acc[v]'s first MFMA at unit v.
+    v8i af[2], bf0[2], bf1[2];
+    auto step = [&](int s, const uint8_t* at, const uint8_t* bt, uint8_t* an, uint8_t* bn,
+                    float r_prev, float r_next, bool live2) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = u >> 1, j = u & 1;
-        acc[u] = mfma32x32x64<B_FMT, A_FMT>(bf[j], af[i & 1], acc[u]);
-        if (u == 0) {
-          __builtin_amdgcn_sched_barrier(0);  // the first MFMA goes out before the wait
+      for (int u = 0; u < 16; ++u) {
+        const int ks = u >> 3, i = (u >> 1) & 3, j = u & 1;
+        if (u == 14) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
-          // this half-step's ratio, loaded long ago: taken into a fresh register here,
-          // where nothing else is pending, so its uses below wait for nothing
-          asm volatile("s_mov_b32 %0, %1" : "=s"(rn) : "s"(r));
-          gload(h + 3, la, lb);
+          __builtin_amdgcn_sched_barrier(0);
+          bf0[0] = fragB(bn, 0, 0);
+          bf0[1] = fragB(bn, 1, 0);
+          af[0] = fragA(an, 0, 0);
         }
-        if (!(u & 1) && u < 6) af[(i + 1) & 1] = frag(at, wr * 128, i + 1);
-        if (u == 4) {
-          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-          lwrite(aw, wa);
+        acc[2 * i + j] = mfma32x32x64<B_FMT, A_FMT>(ks == 0 ? bf0[j] : bf1[j], af[i & 1], acc[2 * i + j]);
+        if (u < 4) {
+          // the chunk leaves its registers before they are reloaded (one staging set)
+          lwrite(an, bn, u);
+          __builtin_amdgcn_sched_barrier(0);
+          gload(s + 2, live2, u);
         }
-        if (u == 5) lwrite(bw, wb);
-        if (u == 6) {
-          bf[0] = frag(bn, wc * 64, 0);
-          af[0] = frag(an, wr * 128, 0);
+        if (u == 3) {
+          bf1[0] = fragB(bt, 0, 1);
+          bf1[1] = fragB(bt, 1, 1);
         }
-        if (u == 7) bf[1] = frag(bn, wc * 64, 1);
-        if (!second) {
-          if (u == 0) { rescale(6, 0, rn); rescale(3, 1, rn); }
-          if (u == 1) { rescale(7, 0, rn); rescale(4, 1, rn); }
-          if (u == 2) rescale(5, 1, rn);
-          if (u == 3) rescale(6, 1, rn);
-          if (u == 4) rescale(7, 1, rn);
-        } else {
-          if (u >= 2) rescale(u - 2, 0, rn);
-          if (u >= 5) rescale(u - 5, 1, rn);
+        if ((u & 1) && u <= 11) {
+          const int L = (u + 3) >> 1;
+          af[L & 1] = fragA(at, L & 3, L >> 2);
         }
-        if (u == 7) r = ratio_of(h + 4);
+        if (u == 15) af[1] = fragA(an, 1, 0);
+        // the tail of the move into this block
+        if (u == 0) { rescale(2, 1, r_prev); rescale(6, 0, r_prev); }
+        if (u == 1) { rescale(3, 1, r_prev); rescale(7, 0, r_prev); }
+        if (u >= 2 && u <= 5) rescale(u + 2, 1, r_prev);
+        // the head of the move into the next block
+        if (u >= 10) rescale(u - 10, 0, r_next);
+        if (u >= 14) rescale(u - 14, 1, r_next);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // prologue: half-steps 0 and 1 into stages 0 and 1, half-step 2 loaded; stage 0's
-    // first fragments
-    v4u s0a[2], s0b[2], s1a[2], s1b[2];
-    gload(0, s0a, s0b);
-    gload(1, s1a, s1b);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    lwrite(sA0, s0a);
-    lwrite(sB0, s0b);
-    gload(2, s0a, s0b);
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    lwrite(sA1, s1a);
-    lwrite(sB1, s1b);
-    float r0 = ratio_of(0), r1 = ratio_of(1), r2 = ratio_of(2), r3 = ratio_of(3);
+    // prologue: step 0 into stage 0, step 1 into the staging registers, the first
+    // fragments of stage 0
+    bool live0 = live_of(0), live1 = live_of(1), live2 = live_of(2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload(0, live0, q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lwrite(sA0, sB0, q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload(1, live1, q);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    af[0] = frag(sA0, wr * 128, 0);
-    bf[0] = frag(sB0, wc * 64, 0);
-    bf[1] = frag(sB0, wc * 64, 1);
-    int h = 0;
-    for (; h + 4 <= H; h += 4) {
-      half(h, sA0, sA1, sB1, sA2, sB2, s1a, s1b, s0a, s0b, r0);
-      half(h + 1, sA1, sA2, sB2, sA3, sB3, s0a, s0b, s1a, s1b, r1);
-      half(h + 2, sA2, sA3, sB3, sA0, sB0, s1a, s1b, s0a, s0b, r2);
-      half(h + 3, sA3, sA0, sB0, sA1, sB1, s0a, s0b, s1a, s1b, r3);
+    bf0[0] = fragB(sB0, 0, 0);
+    bf0[1] = fragB(sB0, 1, 0);
+    af[0] = fragA(sA0, 0, 0);
+    af[1] = fragA(sA0, 1, 0);
+    float r_prev = 1.0f, r_next = gratio[min(1, nblk)];
+    int s = 0;
+    for (; s + 1 < nblk; s += 2) {
+      bool live3 = live_of(s + 3);
+      float r_n2 = gratio[min(s + 2, nblk)];
+      step(s, sA0, sB0, sA1, sB1, r_prev, r_next, live2);
+      r_prev = r_next;
+      r_next = r_n2;
+      live2 = live3;
+      live3 = live_of(s + 4);
+      r_n2 = gratio[min(s + 3, nblk)];
+      step(s + 1, sA1, sB1, sA0, sB0, r_prev, r_next, live2);
+      r_prev = r_next;
+      r_next = r_n2;
+      live2 = live3;
     }
-    if (h < H) {  // H is even: two half-steps remain
-      half(h, sA0, sA1, sB1, sA2, sB2, s1a, s1b, s0a, s0b, r0);
-      half(h + 1, sA1, sA2, sB2, sA3, sB3, s0a, s0b, s1a, s1b, r1);
-    }
-    // the halves still owed to a next block would multiply by 1
+    if (s < nblk) step(s, sA0, sB0, sA1, sB1, r_prev, r_next, live2);
+    // the halves still owed to the move past the last block would multiply by 1
   }
 
   // ---- store: lane holds out[k = base + lane%32][n = base + 8*(r/4) + 4*(lane/32) + r%4]
@@ -605,7 +534,7 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
   if (!p.out_f32) {
     // bf16: each wave puts its 128 x 64 sub-tile into its own 16 KB of LDS ([row][128 B],
     // 16-byte chunk c of row r at c ^ (r & 7)), then stores whole 128-byte rows, 16 bytes
-    // per lane: full lines instead of 16-byte pieces of 32 rows per store.
+    // per lane: full lines instead of 16-byte pieces of 32 rows.
     __syncthreads();  // every wave is done with the stage tiles
     uint8_t* const wl = s_lds + wave * (128 * 128);
 #pragma unroll
@@ -621,6 +550,7 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
         *reinterpret_cast<v2u*>(wl + row * 128 + ((((col >> 4) ^ (row & 7)) << 4) | (col & 15))) = v;
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's region only
     const bool cols_ok = n0 + wc * 64 < p.Nout;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -650,184 +580,112 @@ void tgmm_ratio_kernel(TgmmSegParams p, const float* __restrict__ ratio) {
   }
 }
 
-// Exact per-block promotion for the groups the plan marks wide.  A grid-stride loop
-// over all (group, 256 k x 128 n) tiles that skips every other group, so that the
-// launch costs next to nothing when no group is wide.
+// The per-block promotion for the groups the plan marks wide: for each block, a fresh
+// MFMA partial P_c, then acc = RNE(acc + RNE(P_c * sc_c)), each rounding on its own.  A
+// grid-stride loop over all (group, 128 k x 128 n) tiles that skips every other group,
+// so that the launch costs next to nothing when no group is wide.  One LDS stage,
+// loaded and consumed in turn: a rare fallback, kept simple.
 template <int A_FMT, int B_FMT>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
-void tgmm_promote_kernel(TgmmSegParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_TILE];
-
+__global__ __attribute__((amdgpu_flat_work_group_size(PNT, PNT), amdgpu_waves_per_eu(1, 1)))
+void tgmm_promote_kernel(TgmmCodesParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[BLOCK_ROWS * PROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[BLOCK_ROWS * PROWB];
   const Plan pl = plan_view(p.plan, p.G);
   if (*pl.any_wide == 0) return;
-  const int n_kt = (p.Kout + TBM - 1) / TBM;
-  const int n_nt = p.Nout / TBN;
+  const int n_kt = p.Kout / PBK, n_nt = p.Nout / PBK;
   const int total = n_kt * n_nt * p.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;  // wave sub-tile: 64 (k) x 64 (n)
+  const int frow = lane & 31, fhalf = lane >> 5;
+  uint32_t fa[2], fb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    fa[i] = tr_lane_offset<PROWB>(lane, wr * 64 + 32 * i);
+    fb[i] = tr_lane_offset<PROWB>(lane, wc * 64 + 32 * i);
+  }
+  // thread t moves 16-byte chunk t & 7 of rows (t >> 3) + 32 q (q = 0..3)
+  const int lrow = tid >> 3, lch = tid & 7;
+  const uint32_t wofs = (uint32_t)lrow * PROWB + ((uint32_t)(lch ^ (lrow & 7)) << 4);
   for (int L = blockIdx.x; L < total; L += gridDim.x) {
     const int g = L % p.G;
     if (pl.wide[g] == 0) continue;
-    const int t = L / p.G;
-    const int kt = t / n_nt, nt = t - kt * n_nt;
-    const int k0 = kt * TBM, n0 = nt * TBN;
-    const int32_t* off = p.plan;
-    const int32_t* sg = p.plan + 2 * p.G;
-    const int seg0 = __builtin_amdgcn_readfirstlane(sg[g]);
-    const int nblk = __builtin_amdgcn_readfirstlane(sg[g + 1]) - seg0;
-    const int c0 = __builtin_amdgcn_readfirstlane(off[g]) / BLOCK_ROWS;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;  // wave sub-tile: 128 (k) x 64 (n)
-    const int frow = lane & 31, fhalf = lane >> 5;
-
-    v16f acc[8];
-  #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = v16f{0};
-
-    if (nblk > 0) {
-      const uint32_t seg_row = (uint32_t)p.seg_row;
-      const int krows = min(p.Kout - k0, TBM);
+    const int tt = L / p.G;
+    const int k0 = (tt / n_nt) * PBK, n0 = (tt % n_nt) * PBK;
+    const int off = __builtin_amdgcn_readfirstlane(pl.off[g]);
+    const int cnt = __builtin_amdgcn_readfirstlane(pl.cnt[g]);
+    const int seg0 = __builtin_amdgcn_readfirstlane(pl.seg[g]);
+    const int nblk = __builtin_amdgcn_readfirstlane(pl.seg[g + 1]) - seg0;
+    const int c_lo = off / BLOCK_ROWS;
+    v16f acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = v16f{0};
+    for (int s = 0; s < nblk; ++s) {
+      const int c = c_lo + s;
+      const float sc = p.scprod[c];
+      int lo, hi;
+      block_rows(c, off, cnt, lo, hi);
+      const bool live = sc != 0.0f;
       const __amdgpu_buffer_rsrc_t ra =
-          make_rsrc(p.a_seg + (int64_t)k0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
-                    (uint32_t)((int64_t)krows * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
+          make_rsrc(p.a + (int64_t)lo * p.Kout + k0, live ? (uint32_t)((hi - lo) * p.Kout - k0) : 0u);
       const __amdgpu_buffer_rsrc_t rb =
-          make_rsrc(p.b_seg + (int64_t)n0 * p.seg_row + (int64_t)seg0 * PAIR_BLOCK,
-                    (uint32_t)((int64_t)TBN * p.seg_row - (int64_t)seg0 * PAIR_BLOCK));
-
-      // direct loads of segment block s: A rows 64w..64w+63 (8 per wave-load),
-      // B rows 32w..32w+31
-      // byte of (row, logical 16-byte chunk c of the block) from the block's start in the
-      // column-pair layout
-      auto pair_off = [&](int row, uint32_t c) -> uint32_t {
-        return (uint32_t)(row >> 1) * 2 * seg_row + (c >> 2) * 128 + (uint32_t)(row & 1) * 64 +
-               (c & 3) * 16;
-      };
-      auto issue = [&](int s, uint8_t* at, uint8_t* bt) {
-        const uint32_t koff = (uint32_t)s * PAIR_BLOCK;
-  #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int row = wave * 64 + q * 8 + (lane >> 3);
-          const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
-          load_rows_to_lds(ra, at + (wave * 64 + q * 8) * TILE_K, pair_off(row, c) + koff);
-        }
-  #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wave * 32 + q * 8 + (lane >> 3);
-          const uint32_t c = (uint32_t)((lane & 7) ^ (row & 7) ^ ((row >> 3) & 7));
-          load_rows_to_lds(rb, bt + (wave * 32 + q * 8) * TILE_K, pair_off(row, c) + koff);
-        }
-      };
-      // fragment addressing, as in the grouped GEMM: two per-lane offsets per half block
-      uint32_t fo[2][2];
-      {
-        const uint32_t f0 = (uint32_t)((frow & 7) ^ (frow >> 3));
-  #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-  #pragma unroll
-          for (int e = 0; e < 2; ++e)
-            fo[tt][e] = (uint32_t)frow * TILE_K + ((((uint32_t)(2 * fhalf + e)) ^ f0 ^ (4u * tt)) << 4);
+          make_rsrc(p.b + (int64_t)lo * p.Nout + n0, live ? (uint32_t)((hi - lo) * p.Nout - n0) : 0u);
+      const int skip = lo - c * BLOCK_ROWS;
+      v4u va[4], vb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t r = (uint32_t)(lrow + 32 * q - skip);  // wraps for rows before the group
+        va[q] = buf_load16(ra, r * (uint32_t)p.Kout + lch * 16);
+        vb[q] = buf_load16(rb, r * (uint32_t)p.Nout + lch * 16);
       }
-      auto frag = [&](const uint8_t* tile, int base_row, int i, int ks) -> v8i {
-        const int tt = ks ^ (i & 1);
-        const uint8_t* p0 = tile + base_row * TILE_K + i * 32 * TILE_K;
-        const v4u lo = *reinterpret_cast<const v4u*>(p0 + fo[tt][0]);
-        const v4u hi = *reinterpret_cast<const v4u*>(p0 + fo[tt][1]);
-        v8i f;
-        f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-        f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-        return f;
-      };
-      auto barrier = [&]() {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      };
-
-      // Partial sums of the current block, one 32x32 sub-block per entry, in block-major
-      // MFMA order: unit u = 2b + ks issues half step ks of sub-block b (the two halves are
-      // chained accumulations).  Sub-block b is complete after unit 2b + 1; its promotion
-      // acc += part * sc runs three units later, 8 values per unit, so every unit pairs
-      // one MFMA with 16 VALU instructions, and units 0..2 finish the previous block.
-      v16f part[8];
-  #pragma unroll
-      for (int b = 0; b < 8; ++b) part[b] = v16f{0};
-      float sc_prev = 0.0f;
-      // scale product of the block a step will multiply, loaded one step ahead so that
-      // waiting for it never waits for the direct loads issued after it
-      float sc_next = p.scprod[c0];
-
-      auto promote = [&](int b, int half, float sc) {
-  #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[b][half * 8 + e] = __builtin_fmaf(part[b][half * 8 + e], sc, acc[b][half * 8 + e]);
-      };
-
-      auto step = [&](int s, const uint8_t* at, const uint8_t* bt, uint8_t* an, uint8_t* bn) {
-        const float sc_cur = sc_next;
-        sc_next = p.scprod[c0 + min(s + 1, nblk - 1)];
-        issue(s + 1, an, bn);
-        v8i bf[2][2], af[2][2];  // [j or i parity][ks]
-  #pragma unroll
-        for (int j = 0; j < 2; ++j)
-  #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) bf[j][ks] = frag(bt, wc * 64, j, ks);
-  #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) af[0][ks] = frag(at, wr * 128, 0, ks);
-  #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int b = u >> 1, ks = u & 1, i = b >> 1, j = b & 1;
-          part[b] = mfma32x32x64<B_FMT, A_FMT>(bf[j][ks], af[i & 1][ks], ks == 0 ? v16f{0} : part[b]);
-          // next A fragments once the previous pair of sub-blocks has used its registers
-          if (u == 1 || u == 5 || u == 9) {
-  #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) af[(i + 1) & 1][k2] = frag(at, wr * 128, i + 1, k2);
-          }
-          const int v = (u + 13) & 15;  // promotion slot: unit u handles value-half v
-          if (u < 3) promote(v >> 1, v & 1, sc_prev);
-          else promote(v >> 1, v & 1, sc_cur);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        sc_prev = sc_cur;
-        barrier();
-      };
-
-      issue(0, sA0, sB0);
-      barrier();
-      int s = 0;
-      for (; s + 1 < nblk; s += 2) {
-        step(s, sA0, sB0, sA1, sB1);
-        step(s + 1, sA1, sB1, sA0, sB0);
+      __syncthreads();  // the previous block's fragment reads are done
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<v4u*>(sA + q * 32 * PROWB + wofs) = va[q];
+        *reinterpret_cast<v4u*>(sB + q * 32 * PROWB + wofs) = vb[q];
       }
-      if (s < nblk) step(s, sA0, sB0, sA1, sB1);
-      // the last block's sub-blocks 6 (second half) and 7 are still unpromoted
-      promote(6, 1, sc_prev);
-      promote(7, 0, sc_prev);
-      promote(7, 1, sc_prev);
+      __syncthreads();
+      v16f part[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) part[b] = v16f{0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v8i a2[2], b2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          a2[i] = frag_tr8<PROWB>(sA + fa[i] + ks * 64 * PROWB);
+          b2[i] = frag_tr8<PROWB>(sB + fb[i] + ks * 64 * PROWB);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            part[2 * i + j] = mfma32x32x64<B_FMT, A_FMT>(b2[j], a2[i], part[2 * i + j]);
+      }
+      if (live) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][e] = add_rn(acc[b][e], mul_rn(part[b][e], sc));
+      }
     }
-
-    // ---- store: lane holds out[k = base + lane%32][n = base + 8*(r/4) + 4*(lane/32) + r%4]
+    __syncthreads();  // the next tile's LDS writes wait for this tile's reads
+    // store: lane holds out[k = base + lane%32][n = base + 8*(r/4) + 4*(lane/32) + r%4]
     const int64_t slab = (int64_t)g * p.Kout * p.Nout;
-  #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
       const int i = blk >> 1, j = blk & 1;
-      const int k = k0 + wr * 128 + i * 32 + frow;
-      if (k >= p.Kout) continue;
-  #pragma unroll
+      const int k = k0 + wr * 64 + i * 32 + frow;
+#pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int n = n0 + wc * 64 + j * 32 + 8 * r4 + 4 * fhalf;
         const int64_t idx = slab + (int64_t)k * p.Nout + n;
-        float o[4];
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = acc[blk][4 * r4 + e];
         if (p.out_f32) {
-          v4f v = {o[0], o[1], o[2], o[3]};
+          v4f v = {acc[blk][4 * r4], acc[blk][4 * r4 + 1], acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]};
           *reinterpret_cast<v4f*>((float*)p.out + idx) = v;
         } else {
           v2u v;
-          v.x = pack_bf16x2(o[0], o[1]);
-          v.y = pack_bf16x2(o[2], o[3]);
+          v.x = pack_bf16x2(acc[blk][4 * r4], acc[blk][4 * r4 + 1]);
+          v.y = pack_bf16x2(acc[blk][4 * r4 + 2], acc[blk][4 * r4 + 3]);
           *reinterpret_cast<v2u*>((uint16_t*)p.out + idx) = v;
         }
       }
@@ -835,78 +693,50 @@ void tgmm_promote_kernel(TgmmSegParams p) {
   }
 }
 
-// The transposing quantizer for one operand (bf16 values, or fp8 codes when `codes`).
-hipError_t launch_qt(int fmt, bool codes, const void* x, int64_t M, int64_t C,
-                     const int32_t* plan, int G, const float* scale_blk, float inv_static,
-                     const float* scprod, uint8_t* seg, int64_t seg_row, hipStream_t st) {
-  const int64_t max_blocks = (M + BLOCK_ROWS - 1) / BLOCK_ROWS + G;
-  const int64_t cw = codes ? 256 : 128;
-  dim3 grid((unsigned)max_blocks, (unsigned)((C + cw - 1) / cw));
-#define GMM_QT(F, CD)                                                                     \
-  if (fmt == F && codes == CD) {                                                          \
-    hipLaunchKernelGGL((quant_transpose_kernel<F, CD>), grid, dim3(256), 0, st, x, C, plan, \
-                       G, scale_blk, inv_static, scprod, seg, seg_row);                   \
-    return hipGetLastError();                                                             \
-  }
-  GMM_QT(FMT_E4M3, false)
-  GMM_QT(FMT_E5M2, false)
-  GMM_QT(FMT_E4M3, true)
-  GMM_QT(FMT_E5M2, true)
-#undef GMM_QT
-  return hipErrorInvalidValue;
-}
-
 template <int A_FMT, int B_FMT>
-hipError_t launch_tgmm_fp8(const TgmmSegParams& p, hipStream_t st) {
+hipError_t launch_tgmm_fp8(const TgmmCodesParams& p, hipStream_t st) {
   // per group T tiles in 8 chunks of ceil(T / 8), one per XCD
-  const int64_t T = (int64_t)((p.Kout + RBM - 1) / RBM) * ((p.Nout + RBN - 1) / RBN);
+  const int64_t T = (int64_t)((p.Kout + MBK - 1) / MBK) * ((p.Nout + MBN - 1) / MBN);
   const int64_t tiles = 8 * ((T + 7) / 8) * p.G;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((tgmm_ratio_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(RNT), 0, st, p,
-                     p.ratio);
+  hipLaunchKernelGGL((tgmm_main_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(MNT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ptiles = (int64_t)((p.Kout + TBM - 1) / TBM) * (p.Nout / TBN) * p.G;
+  const int64_t ptiles = (int64_t)(p.Kout / PBK) * (p.Nout / PBK) * p.G;
   hipLaunchKernelGGL((tgmm_promote_kernel<A_FMT, B_FMT>), dim3((unsigned)(ptiles < 1024 ? ptiles : 1024)),
-                     dim3(NT), 0, st, p);
+                     dim3(PNT), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t tgmm_segment_row_bytes(int64_t M, int G) {
-  // every group's rows start on a block boundary: at most ceil(M/128) + G blocks
-  return ((M + BLOCK_ROWS - 1) / BLOCK_ROWS + G) * BLOCK_ROWS;
-}
-
 hipError_t launch_tgmm(int a_fmt, int b_fmt, const TgmmParams& p, hipStream_t st) {
-  const int64_t seg_row = tgmm_segment_row_bytes(p.M, p.G);
   const OpScale a_sc{p.a_scale_blk, p.a_scale_static, p.a_inv_static, p.a_codes};
   const OpScale b_sc{p.b_scale_blk, p.b_scale_static, p.b_inv_static, p.b_codes};
   hipLaunchKernelGGL(tgmm_plan_kernel, dim3(1), dim3(PLAN_NT), 0, st, p.group_sizes, p.g_before,
                      p.G, p.M, a_sc, b_sc, p.plan, p.scprod, p.ratio);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.M > 0) {
-    e = launch_qt(a_fmt, p.a_codes != 0, p.a, p.M, p.Kout, p.plan, p.G, p.a_scale_blk,
-                  p.a_inv_static, p.scprod, p.a_seg, seg_row, st);
-    if (e != hipSuccess) return e;
-    e = launch_qt(b_fmt, p.b_codes != 0, p.b, p.M, p.Nout, p.plan, p.G, p.b_scale_blk,
-                  p.b_inv_static, p.scprod, p.b_seg, seg_row, st);
+  // a bf16 operand is quantized once, row-major, into the workspace
+  if (p.M > 0 && !p.a_codes) {
+    e = launch_quantize_rows(a_fmt, p.a, p.M, p.Kout, p.a_scale_blk, p.a_inv_static, p.a_q, st);
     if (e != hipSuccess) return e;
   }
-  TgmmSegParams q{};
-  q.a_seg = p.a_seg;
-  q.b_seg = p.b_seg;
+  if (p.M > 0 && !p.b_codes) {
+    e = launch_quantize_rows(b_fmt, p.b, p.M, p.Nout, p.b_scale_blk, p.b_inv_static, p.b_q, st);
+    if (e != hipSuccess) return e;
+  }
+  TgmmCodesParams q{};
+  q.a = p.a_codes ? (const uint8_t*)p.a : p.a_q;
+  q.b = p.b_codes ? (const uint8_t*)p.b : p.b_q;
   q.plan = p.plan;
-  q.out = p.out;
   q.scprod = p.scprod;
   q.ratio = p.ratio;
+  q.out = p.out;
   q.Kout = p.Kout;
   q.Nout = p.Nout;
   q.G = p.G;
   q.out_f32 = p.out_f32;
-  q.seg_row = seg_row;
   if (a_fmt == FMT_E4M3 && b_fmt == FMT_E5M2) return launch_tgmm_fp8<FMT_E4M3, FMT_E5M2>(q, st);
   if (a_fmt == FMT_E4M3 && b_fmt == FMT_E4M3) return launch_tgmm_fp8<FMT_E4M3, FMT_E4M3>(q, st);
   if (a_fmt == FMT_E5M2 && b_fmt == FMT_E5M2) return launch_tgmm_fp8<FMT_E5M2, FMT_E5M2>(q, st);

@@ -435,12 +435,12 @@ gmm_status_t gmm_unpermute(int64_t T, int32_t k, int64_t H, const void* y,
  * lhs_scales / grad_scales: as gmm_fwd's lhs_scales (outputs for DYNAMIC + BF16, may be
  * NULL; inputs for DYNAMIC_GIVEN and for DYNAMIC + FP8).
  * drhs [G, K, N] bf16 or f32.  A group with m_g == 0 gets a slab of +0.0.
- * Limits beyond the common ones: ceil(M / 128) + G <= 131071 (its transposed copies are
- * addressed with 32-bit offsets inside 256-row slices; about 16.7 million rows), and
- * ceil(K / 256) * ceil(N / 256) * G < 2^31; otherwise GMM_ERR_SHAPE.
+ * Limits beyond the common ones: ceil(K / 256) * ceil(N / 256) * G < 2^31; otherwise
+ * GMM_ERR_SHAPE.
  * workspace    required: gmm_workspace_size(GMM_OP_TGMM, lhs_op, grad_op, M, K, N, G)
- *              bytes.  It holds each operand quantized once and transposed so that the
- *              rows of every group start on a 128-row block boundary.
+ *              bytes: the plan of the call (per-group offsets, per-block scale products
+ *              and their ratios) and, for an operand given as bf16, its codes quantized
+ *              once, row-major.  Operands given as fp8 codes are read where they are.
  */
 gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op,
                        int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
@@ -459,9 +459,10 @@ gmm_status_t tgmm_drhs(const gmm_operand_t* lhs_op, const gmm_operand_t* grad_op
  * GMM_OP_QUANTIZE: gmm_quantize / gmm_dynamic_scales on `a` [rows, cols_a].
  * GMM_OP_FWD_SWIGLU: gmm_fwd_swiglu, `a` the lhs, `rows` M, `cols_a` K; a bf16 lhs always
  *   gets room for its codes (the SwiGLU epilogue reads fp8 codes).
- * GMM_OP_TGMM: `a` is the lhs and `b` the grad; tgmm always needs workspace for its
- *   quantized, transposed copies of both operands (about (K + N) x (M + 128 G) bytes).
- *   `rows` is M, `cols_a` / `cols_b` the row widths (K and N), G the number of groups.
+ * GMM_OP_TGMM: `a` is the lhs and `b` the grad; tgmm always needs workspace for its plan
+ *   (a few bytes per group and per 128-row block), plus rows x cols bytes of codes for
+ *   each operand given as bf16.  `rows` is M, `cols_a` / `cols_b` the row widths (K and
+ *   N), G the number of groups.
  * Sets *bytes. */
 gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_operand_t* b,
                                 int64_t rows, int64_t cols_a, int64_t cols_b, int32_t G,

@@ -63,14 +63,18 @@ def test_workspace_sizes():
     assert n >= nb * (8 + 2) * 4 and n % 256 == 0
     t = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "dynamic", 1000, 256, 384, b_fmt="e5m2",
                              b_scaling="dynamic", groups=5)
-    seg = (8 + 5) * 128  # bytes per transposed row: ceil(1000/128) + G blocks
     plan = 256  # 5 G + 2 words, aligned
     sc = 256  # one float per 128-row block, aligned
     ratio = 256  # ceil(1000/128) + 2 G floats, aligned
-    assert t == 2 * n + plan + sc + ratio + 256 * seg + 384 * seg
+    codes = 256000 + 384000  # row-major codes of both bf16 operands, each aligned to 256
+    assert t == 2 * n + plan + sc + ratio + codes
     s = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "static", 1000, 256, 384, b_scaling="static",
                              static_scale=0.5, groups=5)
-    assert s == plan + sc + ratio + 256 * seg + 384 * seg
+    assert s == plan + sc + ratio + codes
+    # operands handed over as codes need no room for codes
+    c = g.gmm_workspace_size(g.OP_TGMM, "e4m3", "static", 1000, 256, 384, b_scaling="static",
+                             static_scale=0.5, groups=5, a_kind=g.KIND_FP8)
+    assert c == plan + sc + ratio + 384000
 
 
 # ---- validation: fake but aligned device pointers; nothing is dereferenced -------------
@@ -149,10 +153,9 @@ def test_dlhs_and_tgmm_validation():
 def test_size_limits():
     lib = g.load()
     a, b = op(fmt=0, scaling=0, s=1.0), op(fmt=1, scaling=0, s=1.0)
-    # tgmm: ceil(M/128) + G <= 131071 (32-bit offsets inside 256-row segment slices)
-    M = (131071 - 2) * 128
-    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, M + 1, 256, 256, 2, ptr(1), None,
-                         ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 40, None) == 2
+    # tgmm: M below 2^31 rows
+    assert lib.tgmm_drhs(ctypes.byref(a), ctypes.byref(b), 0, 1 << 31, 256, 256, 2, ptr(1), None,
+                         ptr(3), None, ptr(5), ptr(6), ptr(7), 1 << 50, None) == 2
     # gmm: fewer than 2^31 output tiles
     assert call_fwd(M=(1 << 31) - 1, K=128, N=(1 << 22), G=1, o=op(scaling=0, s=1.0)) == 2
 

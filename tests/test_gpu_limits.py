@@ -166,14 +166,14 @@ def test_most_rows_forward(lib):
     assert group_rel_err(to_np(out[ri]), R, group_row_ranges(sub)) <= TOL
 
 
-def test_tgmm_at_its_row_limit(lib):
-    # ceil(M/128) + G = 131071, the most tgmm_drhs accepts: its transposed copies are
-    # then 2^32 - 2^15 bytes per 256-row slice, the edge of their 32-bit offsets
+def test_tgmm_tall(lib):
+    # 16.7 million rows in two groups: the row offsets of the operands pass 2^32 bytes
+    # (M * K = 2^32 - 2^15 for the lhs), which every 128-row step rebases away
     G = 2
     M = (131071 - G) * 128
     sizes = np.array([M // 2 + 77, M - M // 2 - 77], np.int32)
-    K, N = 256, 128  # a full 256-row slice of the lhs copy: 2^32 - 2^15 bytes
-    print(f"tgmm row limit: M={M}", flush=True)
+    K, N = 256, 128
+    print(f"tall tgmm: M={M}", flush=True)
     x = normal_bf16((M, K), 1.0, 71, DEV)
     gr = normal_bf16((M, N), 1e-3, 72, DEV)
     dw = lib.tgmm_drhs(x, gr, gs_tensor(sizes), lhs_scaling="static", lhs_static_scale=S_LHS,

@@ -1,27 +1,38 @@
 """Benchmark of the FP8 grouped (ragged) matmul hot path on one MI355X.
 
-One step is the whole path over one batch of the Mixtral-shaped merged gate|up expert
-layer (G=8 experts, K=4096, N=2x14336=28672, M=16384 rows = 8192 tokens x top-2, Zipf(1.1)
-routing), inputs resident in HBM:
+One step is the whole path over one batch of an MoE expert layer, inputs resident in HBM
+(default workload: the Mixtral-shaped merged gate|up layer, G=8 experts, K=4096,
+N=2x14336=28672, M=16384 rows = 8192 tokens x top-2, Zipf(1.1) routing):
 
-  1. block scales of lhs  (abs-max prepass, e4m3, 128 rows x K)
-  2. gmm_fwd   out[M, N]      = q(lhs) . rhs[g]        (bf16 lhs; the call quantizes it
-                                                         once into its workspace, then
-                                                         runs the fp8 product)
-  3. quantize grad once       (e5m2 codes [M, N] + 128-row block scales)
-  4. gmm_dlhs  dlhs[M, K]     = q(grad) . rhs[g]^T     (hybrid: fp8 codes of step 3)
-  5. tgmm_drhs drhs[G, K, N]  = q(lhs)_g^T . q(grad)_g  (scales of steps 1 and 3 reused)
+  1. quantize lhs once           e4m3 codes [M, K]: dynamic 128-row block scales (abs-max
+                                  prepass + codes), or a static per-tensor scale 4/448 when
+                                  the workload's forward recipe is static (no prepass)
+  2. gmm_fwd   out[M, N]       = q(lhs) . rhs[g]          (the codes of step 1)
+  3. quantize grad once          e5m2 codes [M, N] + 128-row block scales
+  4. gmm_dlhs  dlhs[M, K]      = q(grad) . rhs[g]^T       (hybrid: the codes of step 3)
+  5. tgmm_drhs drhs[G, K, N]   = q(lhs)_g^T . q(grad)_g   (the codes of steps 1 and 3)
 
 value = 3 * 2*M*K*N / step time (TFLOP/s), with steps 4 and 5 (independent of each other)
 on two HIP streams so that tgmm fills the CUs dlhs leaves idle in its short last round of
-tiles; the per-op figures come from the same step on one stream, where every call is
-timed with HIP events on the stream it runs on.  gmm_fwd is a quantize kernel and the product kernel; gmm_dlhs is
-one kernel launch; tgmm_drhs is a plan
-kernel, two quantize-transpose kernels, the fp8 tgmm kernel and its wide-range fallback
-(which exits at once here), and its window holds all five.  The slowest product window is reported against the dense FP8 MFMA peak (5.0
-PFLOP/s).  The CPU oracle is timed on a bounded sample of the same workload (N=1).
+tiles.  The per-op figures come from the same step on one stream, every call timed with HIP
+events on the stream it runs on.  The slowest product is reported against the dense FP8
+MFMA peak (5.0 PFLOP/s).
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline] [--no-overlap]
+Also reported (each timed with HIP events on the current stream):
+  * protocol: per op and for the whole step, the median and the minimum of `--reps` runs
+    after 5 warm-up runs, warm, and cold (a 512 MiB device write between runs flushes the
+    4 MB L2 of every XCD and the 256 MB last-level cache);
+  * static_vs_dynamic: the workload's forward with a static per-tensor lhs scale and with
+    dynamic 128-row block scales, both with the lhs quantized by the call and on
+    pre-quantized codes (the pages say static scaling is slightly faster);
+  * ffn_chain: the MoE SwiGLU feed-forward block (G=64, M=65536, hidden 2048,
+    intermediate 1408), forward and backward as one timed chain, in pure mode (every
+    product quantizes its own bf16 operands) and hybrid mode (each gradient quantized once,
+    its codes feeding dlhs and tgmm), each with static and dynamic forward lhs scaling;
+  * the SwiGLU, routing and block-wise blocks, and the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
+       [--no-cpu-baseline] [--no-overlap] [--no-extras] [--no-clock] [--reps 50]
 """
 
 import argparse
@@ -38,10 +49,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 GMM TFLOP/s (fwd/dlhs/drhs) and % of MI355X FP8 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0
+STATIC_SCALE = float(np.float32(4.0) / np.float32(448.0))  # the pages' bound 4 over e4m3's 448
 
 
 def kernel_source_hash():
-    """sha256 (first 16 hex) over the HIP sources, as recorded with the HBM counters."""
+    """sha256 (first 16 hex) over the HIP sources, as recorded with the counter summaries."""
     import hashlib
 
     h = hashlib.sha256()
@@ -54,19 +69,31 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(op, workload):
-    """HBM bytes per launch of `op` from the committed FETCH_SIZE / WRITE_SIZE summary,
-    or None when there is none for this workload or the kernels changed since."""
+def _summary(path, workload):
+    """A committed counter summary for this workload, or None when there is none or the
+    kernels changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
     if t.get("workload") != workload or t.get("source_hash") != kernel_source_hash():
         return None
-    entry = t.get("ops", {}).get(op)
+    return t
+
+
+def measured_traffic(op, workload):
+    """L2-to-fabric bytes per launch of `op` (FETCH_SIZE + WRITE_SIZE, scaled by a copy of
+    known size) from the committed summary, or None."""
+    t = _summary(TRAFFIC_FILE, workload)
+    entry = t.get("ops", {}).get(op) if t else None
     return int(entry["traffic_bytes"]) if entry else None
-FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+
+
+def measured_counters(workload):
+    """Per-op MFMA-busy fractions and L2 hit rates from the committed counter summary."""
+    t = _summary(COUNTER_FILE, workload)
+    return t.get("ops") if t else None
 
 
 def parse():
@@ -75,17 +102,45 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="mixtral_gate_up")
+    p.add_argument("--reps", type=int, default=50, help="timed runs per op for median / min")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-overlap", action="store_true",
                    help="time the step on one stream only (ms_per_step is then the serial step)")
-    p.add_argument("--no-swiglu", action="store_true",
-                   help="skip the SwiGLU block measurement (moe_swiglu shape)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the timed steps: no protocol, static/dynamic, FFN chain or blocks")
+    p.add_argument("--no-clock", action="store_true", help="skip the GFX clock reading")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=2048, help="at most 4096")
     p.add_argument("--copy-calibration", action="store_true",
                    help="copy 1 GiB device-to-device once before the steps (a known-size "
                         "transfer for scaling HBM byte counters)")
     return p.parse_args()
+
+
+def _median_min(ts):
+    ts = sorted(ts)
+    return {"median_ms": round(float(np.median(ts)), 4), "min_ms": round(float(ts[0]), 4)}
+
+
+def event_times(fn, reps, warmup=5, cold=None):
+    """ms of each of `reps` calls of fn() (HIP events on the current stream around each),
+    after `warmup` untimed calls; with `cold` (a uint8 tensor) every timed call follows a
+    full write of it."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        if cold is not None:
+            cold.fill_(i & 0xFF)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
 
 
 class Step:
@@ -96,12 +151,13 @@ class Step:
 
         from synth.workloads import normal_bf16
 
-        self.g, self.torch = g, torch
+        self.g, self.torch, self.wl = g, torch, wl
         lib = g.load()
         self.lib = lib
         dev = "cuda"
         G, M, K, N = wl.G, wl.M, wl.K, wl.N
         self.G, self.M, self.K, self.N = G, M, K, N
+        self.static = wl.lhs_scaling == "static"
         self.sizes = wl.group_sizes()
         self.gs = torch.tensor(self.sizes, dtype=torch.int32, device=dev)
         self.lhs = normal_bf16((M, K), 1.0, seed, dev)
@@ -128,47 +184,61 @@ class Step:
                                          max(K, N), 0, 1, ctypes.byref(n)))
         self.ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
         self.ws_n = n.value
-        # each tensor is quantized once (dynamic 128-row blocks) and its codes feed every
-        # product that uses it: lhs codes -> fwd and tgmm, grad codes -> dlhs and tgmm
-        self.op_lq = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC, 0.0)     # lhs quantizer recipe
-        self.op_l8 = g.Operand(g.KIND_FP8, g.E4M3, g.DYNAMIC, 0.0)      # its codes
-        self.op_gq = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC, 0.0)     # grad quantizer recipe
-        self.op_g8 = g.Operand(g.KIND_FP8, g.E5M2, g.DYNAMIC, 0.0)      # its codes
+        # each tensor is quantized once and its codes feed every product that uses it: lhs
+        # codes -> fwd and tgmm (the workload's forward recipe), grad codes -> dlhs and tgmm
+        lmode, ls = (g.STATIC, STATIC_SCALE) if self.static else (g.DYNAMIC, 0.0)
+        self.op_lq = g.Operand(g.KIND_BF16, g.E4M3, lmode, ls)      # lhs quantizer recipe
+        self.op_l8 = g.Operand(g.KIND_FP8, g.E4M3, lmode, ls)       # its codes
+        self.op_gq = g.Operand(g.KIND_BF16, g.E5M2, g.DYNAMIC, 0.0)  # grad quantizer recipe
+        self.op_g8 = g.Operand(g.KIND_FP8, g.E5M2, g.DYNAMIC, 0.0)   # its codes
         self._chk(lib.gmm_workspace_size(g.OP_TGMM, ctypes.byref(self.op_l8), ctypes.byref(self.op_g8),
                                          M, K, N, G, ctypes.byref(n)))
         self.ws_t = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
         self.ws_t_n = n.value
-        # the forward with in-kernel quantization of the bf16 lhs (timed outside the step)
-        self.op_lhs = g.Operand(g.KIND_BF16, g.E4M3, g.DYNAMIC_GIVEN, 0.0)
-        self.r_lhs = ctypes.byref(self.op_lhs)
         self.r_lq, self.r_l8 = ctypes.byref(self.op_lq), ctypes.byref(self.op_l8)
         self.r_gq, self.r_g8 = ctypes.byref(self.op_gq), ctypes.byref(self.op_g8)
         P = lambda t: t.data_ptr()
         self.p = {k: P(getattr(self, k)) for k in
                   ("lhs", "grad", "lhs_q", "grad_q", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs",
                    "drhs", "s_lhs", "s_grad", "ws", "ws_t", "gs")}
+        # a static lhs has no block scales
+        self.p_sl = None if self.static else self.p["s_lhs"]
         torch.cuda.synchronize()
+
+    # the five calls of a step, each on stream s
+    def q_lhs(self, s):
+        self._chk(self.lib.gmm_quantize(self.r_lq, self.M, self.K, self.p["lhs"], self.p["lhs_q"],
+                                        self.p_sl, self.p["ws"], self.ws_n, s))
+
+    def fwd(self, s):
+        g, p = self.g, self.p
+        self._chk(self.lib.gmm_fwd(self.r_l8, g.E4M3, g.RHS_NK, g.OUT_BF16, self.M, self.K, self.N,
+                                   self.G, p["lhs_q"], self.p_sl, p["w_fwd"], p["s_fwd"], p["gs"],
+                                   p["out"], None, 0, s))
+
+    def q_grad(self, s):
+        self._chk(self.lib.gmm_quantize(self.r_gq, self.M, self.N, self.p["grad"], self.p["grad_q"],
+                                        self.p["s_grad"], self.p["ws"], self.ws_n, s))
+
+    def dlhs_(self, s):
+        g, p = self.g, self.p
+        self._chk(self.lib.gmm_dlhs(self.r_g8, g.E4M3, g.RHS_KN, g.OUT_BF16, self.M, self.K, self.N,
+                                    self.G, p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"],
+                                    p["gs"], p["dlhs"], None, 0, s))
+
+    def tgmm(self, s):
+        p = self.p
+        self._chk(self.lib.tgmm_drhs(self.r_l8, self.r_g8, self.g.OUT_BF16, self.M, self.K, self.N,
+                                     self.G, p["lhs_q"], self.p_sl, p["grad_q"], p["s_grad"],
+                                     p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
 
     def run(self, stream, ev=None):
         """Enqueue one step; ev (6 events) brackets: lhs quantize, fwd, grad quantize, dlhs,
         tgmm."""
-        lib, p, s = self.lib, self.p, stream
-        M, K, N, G = self.M, self.K, self.N, self.G
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
-        chk = self._chk
-        rec(0)
-        chk(lib.gmm_quantize(self.r_lq, M, K, p["lhs"], p["lhs_q"], p["s_lhs"], p["ws"], self.ws_n, s))
-        rec(1)
-        chk(lib.gmm_fwd(self.r_l8, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
-                        p["lhs_q"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"], None, 0, s))
-        rec(2)
-        chk(lib.gmm_quantize(self.r_gq, M, N, p["grad"], p["grad_q"], p["s_grad"], p["ws"], self.ws_n, s))
-        rec(3)
-        chk(lib.gmm_dlhs(self.r_g8, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
-                         p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, s))
-        rec(4)
-        chk(lib.tgmm_drhs(self.r_l8, self.r_g8, self.g.OUT_BF16, M, K, N, G, p["lhs_q"], p["s_lhs"],
-                          p["grad_q"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, s))
+        for i, op in enumerate((self.q_lhs, self.fwd, self.q_grad, self.dlhs_, self.tgmm)):
+            rec(i)
+            op(stream)
         rec(5)
 
     def run_overlapped(self, s, s2, e_fork, e_join):
@@ -176,32 +246,240 @@ class Step:
         quantizer, dlhs runs on `s` and tgmm on `s2` (torch streams; default priority), so
         that tgmm's workgroups take the CUs dlhs leaves idle in its short last round of
         tiles.  The two read the same grad codes and write separate outputs."""
-        lib, p = self.lib, self.p
-        M, K, N, G = self.M, self.K, self.N, self.G
-        chk, sp, sp2 = self._chk, s.cuda_stream, s2.cuda_stream
-        chk(lib.gmm_quantize(self.r_lq, M, K, p["lhs"], p["lhs_q"], p["s_lhs"], p["ws"], self.ws_n, sp))
-        chk(lib.gmm_fwd(self.r_l8, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, M, K, N, G,
-                        p["lhs_q"], p["s_lhs"], p["w_fwd"], p["s_fwd"], p["gs"], p["out"], None, 0, sp))
-        chk(lib.gmm_quantize(self.r_gq, M, N, p["grad"], p["grad_q"], p["s_grad"], p["ws"], self.ws_n, sp))
+        sp = s.cuda_stream
+        self.q_lhs(sp)
+        self.fwd(sp)
+        self.q_grad(sp)
         e_fork.record(s)
         s2.wait_event(e_fork)
-        chk(lib.gmm_dlhs(self.r_g8, self.g.E4M3, self.g.RHS_KN, self.g.OUT_BF16, M, K, N, G,
-                         p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"], p["gs"], p["dlhs"], None, 0, sp))
-        chk(lib.tgmm_drhs(self.r_l8, self.r_g8, self.g.OUT_BF16, M, K, N, G, p["lhs_q"], p["s_lhs"],
-                          p["grad_q"], p["s_grad"], p["gs"], p["drhs"], p["ws_t"], self.ws_t_n, sp2))
+        self.dlhs_(sp)
+        self.tgmm(s2.cuda_stream)
         e_join.record(s2)
         s.wait_event(e_join)
-
-    def fused_fwd(self, stream):
-        """The forward with the lhs quantized inside the product kernel (no workspace)."""
-        p = self.p
-        self._chk(self.lib.gmm_fwd(self.r_lhs, self.g.E4M3, self.g.RHS_NK, self.g.OUT_BF16, self.M,
-                                   self.K, self.N, self.G, p["lhs"], p["s_lhs"], p["w_fwd"],
-                                   p["s_fwd"], p["gs"], p["out"], None, 0, stream))
 
     def _chk(self, status):
         if status != 0:
             raise RuntimeError(f"library call failed: {self.g.gmm_status_string(status)}")
+
+
+def protocol(step, reps):
+    """Median and minimum of `reps` runs per op and per step (one stream), warm and cold."""
+    import torch
+
+    s = torch.cuda.current_stream().cuda_stream
+    cold = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ops = {"quantize_lhs": step.q_lhs, "gmm_fwd": step.fwd, "quantize_grad": step.q_grad,
+           "gmm_dlhs": step.dlhs_, "tgmm_drhs": step.tgmm}
+    ops["step"] = lambda st: step.run(st)
+    res = {}
+    for name, fn in ops.items():
+        r = reps if name != "step" else max(reps // 2, 10)
+        warm = event_times(lambda: fn(s), r)
+        cld = event_times(lambda: fn(s), r, warmup=1, cold=cold)
+        e = _median_min(warm)
+        c = _median_min(cld)
+        e.update({"cold_median_ms": c["median_ms"], "cold_min_ms": c["min_ms"], "runs": r})
+        res[name] = e
+    del cold
+    torch.cuda.empty_cache()
+    return res
+
+
+def static_vs_dynamic(g, step, reps):
+    """The workload's forward with a static per-tensor lhs scale (4/448) and with dynamic
+    128-row block scales: (a) the bf16 lhs handed to gmm_fwd, which quantizes it itself
+    (dynamic: abs-max prepass first), and (b) gmm_quantize, then gmm_fwd on the codes.
+    Medians of `reps` runs."""
+    import torch
+
+    lhs, w, ws, gs = step.lhs, step.w_fwd, step.s_fwd, step.gs
+    out = step.out
+    res = {}
+    for mode in ("static", "dynamic"):
+        kw = dict(lhs_scaling="static", static_scale=STATIC_SCALE) if mode == "static" else {}
+        t_call = event_times(lambda: g.gmm_fwd(lhs, w, ws, gs, out=out, **kw), reps)
+        codes = {}
+
+        def two_calls():
+            if mode == "static":
+                q, _ = g.gmm_quantize(lhs, "e4m3", "static", static_scale=STATIC_SCALE)
+                g.gmm_fwd(q, w, ws, gs, out=out, **kw)
+            else:
+                q, sc = g.gmm_quantize(lhs, "e4m3", "dynamic")
+                g.gmm_fwd(q, w, ws, gs, out=out, lhs_scales=sc)
+
+        t_two = event_times(two_calls, reps)
+        res[mode] = {"gmm_fwd_bf16_lhs": _median_min(t_call), "quantize_then_fwd": _median_min(t_two)}
+        del codes
+    a = res["static"]["gmm_fwd_bf16_lhs"]["median_ms"]
+    b = res["dynamic"]["gmm_fwd_bf16_lhs"]["median_ms"]
+    res["static_over_dynamic"] = round(a / b, 4)
+    res["note"] = ("same shape and inputs; the dynamic recipe adds the abs-max prepass over the "
+                   "lhs (2 M K bytes) and per-row-block scales in the epilogue")
+    torch.cuda.empty_cache()
+    return res
+
+
+def dense_ceiling(wl, reps):
+    """Context only: the vendor library's dense FP8 GEMM (torch._scaled_mm, hipBLASLt) at the
+    workload's M x K x N with one group, e4m3 operands and unit scales, bf16 out: what a
+    tuned dense FP8 GEMM reaches on this chip at the same shape.  Nothing of the path uses
+    it.  None when the call is unavailable."""
+    import torch
+
+    M, K, N = wl.M, wl.K, wl.N
+    try:
+        gen = torch.Generator(device="cuda").manual_seed(17)
+        a = (torch.randn((M, K), device="cuda", generator=gen) * 0.5).to(torch.float8_e4m3fn)
+        b = (torch.randn((N, K), device="cuda", generator=gen) * 0.5).to(torch.float8_e4m3fn).t()
+        one = torch.tensor(1.0, device="cuda")
+        ts = event_times(lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one,
+                                                  out_dtype=torch.bfloat16), reps)
+    except Exception as e:  # pragma: no cover
+        return {"error": repr(e)[:200]}
+    r = _median_min(ts)
+    r["TFLOP/s"] = round(2.0 * M * K * N / r["median_ms"] / 1e9, 1)
+    r["frac_peak"] = round(r["TFLOP/s"] / FP8_PEAK_TFLOPS, 4)
+    r["what"] = ("torch._scaled_mm (hipBLASLt), dense [M, K] x [K, N] e4m3, random data, "
+                 "bf16 out; context for the grouped products, not part of the path")
+    del a, b
+    torch.cuda.empty_cache()
+    return r
+
+
+def ffn_chain(g, reps=10):
+    """The MoE SwiGLU feed-forward block (moe_swiglu shape: G=64, M=65536, hidden 2048,
+    intermediate 1408), forward and backward as one chain, timed per op and in total:
+
+      gate|up gmm with SwiGLU in its epilogue (h, and gu for the backward), the down gmm on
+      h, dlhs of the down weight (dh), the SwiGLU backward (d_gu), dlhs of the gate|up
+      weight (dx), tgmm of both weights.
+
+    pure: every product takes bf16 operands and quantizes them itself.  hybrid: each
+    gradient (grad_y, d_gu) is quantized once (e5m2, dynamic) and its codes feed both its
+    dlhs and its tgmm.  static: the forward lhs (x, h) uses the static scale 4/448 (h comes
+    out of the gate|up epilogue as e4m3 codes); dynamic: 128-row block scales."""
+    import torch
+
+    from synth.workloads import WORKLOADS, normal_bf16
+
+    wl = WORKLOADS["moe_swiglu"]
+    G, M, H, I = wl.G, wl.M, wl.K, wl.extra["intermediate"]
+    seed = wl.seed * 100
+    dev = "cuda"
+    gs = torch.tensor(wl.group_sizes(), dtype=torch.int32, device=dev)
+    x = normal_bf16((M, H), 1.0, seed, dev)
+    w_gu = normal_bf16((G, H, 2 * I), 0.02, seed + 1, dev)
+    w_dn = normal_bf16((G, I, H), 0.02, seed + 2, dev)
+    grad_y = normal_bf16((M, H), 1e-3, seed + 3, dev)
+    wgu_q, wgu_s = g.gmm_quantize_rhs(w_gu, "e4m3", 0, "nk")
+    wgu_k, wgu_sk = g.gmm_quantize_rhs(w_gu, "e4m3", 1, "kn")
+    wdn_q, wdn_s = g.gmm_quantize_rhs(w_dn, "e4m3", 0, "nk")
+    wdn_k, wdn_sk = g.gmm_quantize_rhs(w_dn, "e4m3", 1, "kn")
+    del w_gu, w_dn
+    bf = torch.bfloat16
+    h = torch.empty((M, I), dtype=bf, device=dev)
+    hq = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=bf, device=dev)
+    dh = torch.empty((M, I), dtype=bf, device=dev)
+    d_gu = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    dx = torch.empty((M, H), dtype=bf, device=dev)
+    dwd = torch.empty((G, I, H), dtype=bf, device=dev)
+    dwg = torch.empty((G, H, 2 * I), dtype=bf, device=dev)
+    S = STATIC_SCALE
+    names = ["fwd_gate_up_swiglu", "fwd_down", "dlhs_down", "swiglu_bwd", "dlhs_gate_up",
+             "tgmm_down", "tgmm_gate_up"]
+
+    def chain(mode, scaling, ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        if scaling == "static":
+            _, gu = g.gmm_fwd_swiglu_fp8(x, wgu_q, wgu_s, gs, S, lhs_scaling="static",
+                                         static_scale=S, out=hq, gu=True)
+            rec(1)
+            g.gmm_fwd(hq, wdn_q, wdn_s, gs, lhs_scaling="static", static_scale=S, out=y)
+            h_lhs, h_kw = hq, dict(lhs_scaling="static", lhs_static_scale=S)
+            x_kw = dict(lhs_scaling="static", lhs_static_scale=S)
+        else:
+            _, gu = g.gmm_fwd_swiglu(x, wgu_q, wgu_s, gs, out=h, gu=True)
+            rec(1)
+            g.gmm_fwd(h, wdn_q, wdn_s, gs, out=y)
+            h_lhs, h_kw, x_kw = h, {}, {}
+        rec(2)
+        if mode == "hybrid":
+            gyq, sgy = g.gmm_quantize(grad_y, "e5m2", "dynamic")
+            g.gmm_dlhs(gyq, wdn_k, wdn_sk, gs, grad_scales=sgy, out=dh)
+            rec(3)
+            g.gmm_swiglu_bwd(dh, gu, out=d_gu)
+            rec(4)
+            dgq, sdg = g.gmm_quantize(d_gu, "e5m2", "dynamic")
+            g.gmm_dlhs(dgq, wgu_k, wgu_sk, gs, grad_scales=sdg, out=dx)
+            rec(5)
+            g.tgmm_drhs(h_lhs, gyq, gs, grad_scales=sgy, out=dwd, **h_kw)
+            rec(6)
+            g.tgmm_drhs(x, dgq, gs, grad_scales=sdg, out=dwg, **x_kw)
+        else:
+            g.gmm_dlhs(grad_y, wdn_k, wdn_sk, gs, out=dh)
+            rec(3)
+            g.gmm_swiglu_bwd(dh, gu, out=d_gu)
+            rec(4)
+            g.gmm_dlhs(d_gu, wgu_k, wgu_sk, gs, out=dx)
+            rec(5)
+            g.tgmm_drhs(h_lhs, grad_y, gs, out=dwd, **h_kw)
+            rec(6)
+            g.tgmm_drhs(x, d_gu, gs, out=dwg, **x_kw)
+        rec(7)
+
+    two = 2.0 * M * H * I
+    flops = {"fwd_gate_up_swiglu": 2 * two, "fwd_down": two, "dlhs_down": two, "swiglu_bwd": 0.0,
+             "dlhs_gate_up": 2 * two, "tgmm_down": two, "tgmm_gate_up": 2 * two}
+    # algorithmic bytes of the fused path (bf16 operands read, fp8 weights, bf16 outputs)
+    nbytes = {"fwd_down": 2 * M * I + G * I * H + 2 * M * H,
+              "dlhs_down": 2 * M * H + G * I * H + 2 * M * I,
+              "swiglu_bwd": 10 * M * I,
+              "tgmm_down": 2 * M * I + 2 * M * H + 2 * G * I * H,
+              "tgmm_gate_up": 2 * M * H + 4 * M * I + 4 * G * H * I}
+    total_flop = 18.0 * M * H * I
+    res = {"workload": wl.name, "G": G, "M": M, "hidden": H, "intermediate": I,
+           "flop_per_chain": total_flop, "runs": reps}
+    for mode in ("pure", "hybrid"):
+        for scaling in ("static", "dynamic"):
+            for _ in range(3):
+                chain(mode, scaling)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(reps)]
+            torch.cuda.synchronize()
+            for i in range(reps):
+                chain(mode, scaling, evs[i])
+            torch.cuda.synchronize()
+            tot = [e[0].elapsed_time(e[7]) for e in evs]
+            per = {}
+            for j, n in enumerate(names):
+                t = float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                d = {"ms": round(t, 4)}
+                if flops[n]:
+                    d["TFLOP/s"] = round(flops[n] / t / 1e9, 1)
+                    d["frac_peak"] = round(flops[n] / t / 1e9 / FP8_PEAK_TFLOPS, 4)
+                if n in nbytes:
+                    d["GB/s"] = round(nbytes[n] / t / 1e6, 1)
+                    d["frac_hbm"] = round(nbytes[n] / t / 1e6 / HBM_PEAK_GBS, 4)
+                per[n] = d
+            mt = _median_min(tot)
+            res[f"{mode}_{scaling}"] = {"chain": mt,
+                                        "TFLOP/s": round(total_flop / mt["median_ms"] / 1e9, 1),
+                                        "ops": per}
+    res["hybrid_over_pure"] = {s: round(res[f"hybrid_{s}"]["chain"]["median_ms"] /
+                                        res[f"pure_{s}"]["chain"]["median_ms"], 4)
+                               for s in ("static", "dynamic")}
+    res["static_over_dynamic"] = {m: round(res[f"{m}_static"]["chain"]["median_ms"] /
+                                           res[f"{m}_dynamic"]["chain"]["median_ms"], 4)
+                                  for m in ("pure", "hybrid")}
+    res["note"] = ("hybrid timings include the stand-alone gradient quantizers inside the dlhs "
+                   "ops; GB/s on algorithmic bytes of the fused path for the ops the roofline "
+                   "calls HBM-bound")
+    del x, grad_y, wgu_q, wgu_s, wgu_k, wgu_sk, wdn_q, wdn_s, wdn_k, wdn_sk
+    del h, hq, y, dh, d_gu, dx, dwd, dwg
+    torch.cuda.empty_cache()
+    return res
 
 
 def gfx_clock_during(run, seconds=1.0):
@@ -281,20 +559,11 @@ def swiglu_block(g, reps=10):
     d_gu = torch.empty_like(gu)
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return float(np.median(event_times(fn, reps, warmup=3)))
 
     t_plain = timed(lambda: g.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out=gu))
     t_fused = timed(lambda: g.gmm_fwd_swiglu(xq, wq, ws, gs, lhs_scales=sx, out=h))
-    s_h = 4.0 / 448.0  # a static scale for h (its value does not change the work)
+    s_h = STATIC_SCALE  # a static scale for h (its value does not change the work)
     t_fp8 = timed(lambda: g.gmm_fwd_swiglu_fp8(xq, wq, ws, gs, s_h, lhs_scales=sx, out=hq))
     down = dict(lhs_scaling="static", static_scale=s_h, out=y)
     t_down_codes = timed(lambda: g.gmm_fwd(hq, wdq, wds, gs, **down))
@@ -312,7 +581,7 @@ def swiglu_block(g, reps=10):
         "down_on_h_codes_ms": round(t_down_codes, 4),
         "down_on_bf16_h_ms": round(t_down_bf16, 4),
         "swiglu_bwd": {"ms": round(t_bwd, 4), "GB/s": round(bwd_bytes / t_bwd / 1e6, 1),
-                       "frac_hbm": round(bwd_bytes / t_bwd / 1e6 / 8000.0, 4)},
+                       "frac_hbm": round(bwd_bytes / t_bwd / 1e6 / HBM_PEAK_GBS, 4)},
         "note": "fwd_swiglu writes h [M, I] only; the unfused path would add a bf16 [M, 2I] "
                 "write and read around an elementwise SwiGLU",
     }
@@ -335,23 +604,14 @@ def route_block(g, reps=10):
     T = wl.M // k
     ids = torch.as_tensor(topk_expert_ids(T, k, G, wl.zipf_s, wl.seed), device="cuda")
     x = normal_bf16((T, H), 1.0, wl.seed * 100 + 7, "cuda")
-    codes, _ = g.gmm_quantize(x, "e4m3", "static", static_scale=4.0 / 448.0)
+    codes, _ = g.gmm_quantize(x, "e4m3", "static", static_scale=STATIC_SCALE)
     xp, gs, ros, sor = g.gmm_permute(ids, G, x)
     cp = torch.empty((T * k, H), dtype=torch.uint8, device="cuda")
     w = torch.rand((T, k), device="cuda")
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return float(np.median(event_times(fn, reps, warmup=3)))
 
     t_perm = timed(lambda: g.gmm_permute(ids, G, x, xp))
     t_perm8 = timed(lambda: g.gmm_permute(ids, G, codes, cp))
@@ -365,7 +625,7 @@ def route_block(g, reps=10):
 
     def rate(b, t):
         return {"ms": round(t, 4), "GB/s": round(b / t / 1e6, 1),
-                "frac_hbm": round(b / t / 1e6 / 8000.0, 4)}
+                "frac_hbm": round(b / t / 1e6 / HBM_PEAK_GBS, 4)}
 
     res = {"workload": wl.name, "tokens": T, "top_k": k, "G": G, "hidden": H,
            "permute_bf16": rate(perm_b, t_perm), "permute_e4m3": rate(perm8_b, t_perm8),
@@ -394,16 +654,7 @@ def blockwise_block(g, reps=10):
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
     def timed(fn):
-        for _ in range(3):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return float(np.median(event_times(fn, reps, warmup=3)))
 
     flop = 2.0 * M * K * N
     res = {"workload": wl.name, "G": G, "M": M, "K": K, "N": N}
@@ -454,12 +705,14 @@ def cpu_baseline(step, rows, cols):
     lhs = bits(step.lhs[:M].to("cpu"))
     grad = bits(step.grad[:M, :cols].to("cpu"))
     w = bits(step.w_sample[:, :, :cols].contiguous())
+    lmode = "static" if step.static else "dynamic"
+    s = np.float32(STATIC_SCALE) if step.static else None
     t0 = time.perf_counter()
     wq_n, ws_n = quantize_rhs_per_channel(w, "e4m3", "n")
     wq_k, ws_k = quantize_rhs_per_channel(w, "e4m3", "k")
-    ops.fwd(lhs, wq_n, ws_n, sizes, "e4m3", "dynamic", None, "e4m3", "bf16")
+    ops.fwd(lhs, wq_n, ws_n, sizes, "e4m3", lmode, s, "e4m3", "bf16")
     ops.dlhs(grad, wq_k, ws_k, sizes, "e5m2", "dynamic", None, "e4m3", "bf16")
-    ops.tgmm(lhs, grad, sizes, out_dtype="bf16")
+    ops.tgmm(lhs, grad, sizes, "e4m3", lmode, s, out_dtype="bf16")
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * M * K * cols
     return {
@@ -523,18 +776,9 @@ def main():
             step.run_overlapped(stream, s2, *forks[i])
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
-    # the in-kernel quantization route of the forward, timed on its own after the steps
-    fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    step.fused_fwd(s)
-    fe[0].record()
-    for _ in range(3):
-        step.fused_fwd(s)
-    fe[1].record()
-    torch.cuda.synchronize()
-    fused_ms = fe[0].elapsed_time(fe[1]) / 3
     # the GFX clock the chip holds under this load (FP8 MFMA work draws enough power to
     # keep it well below the 2.4 GHz the published peak assumes)
-    clock_mhz = gfx_clock_during(lambda: [step.run(s) for _ in range(8)])
+    clock_mhz = None if args.no_clock else gfx_clock_during(lambda: [step.run(s) for _ in range(8)])
     flop_op = 2.0 * wl.M * wl.K * wl.N
     value = 3 * flop_op / (ms_step / 1000.0) / 1e12
     ops = {n: {"ms": round(per[n], 4), "TFLOP/s": round(flop_op / (per[n] / 1000) / 1e12, 1),
@@ -544,16 +788,19 @@ def main():
     ach = flop_op / (per[dom] / 1000.0) / 1e12
     kern = {"gmm_fwd": "gmm_kernel<e4m3,e4m3,fp8 A,contraction-contiguous B>",
             "gmm_dlhs": "gmm_kernel<e5m2,e4m3,fp8 A,contraction-contiguous B>",
-            "tgmm_drhs": "tgmm_plan + quant_transpose<e4m3 codes> + quant_transpose<e5m2 codes> + "
-                         "tgmm_ratio_kernel<e4m3,e5m2> + tgmm_promote_kernel (exits: no wide group)"}[dom]
+            "tgmm_drhs": "tgmm_plan_kernel + tgmm_main_kernel<e4m3,e5m2> + tgmm_promote_kernel "
+                         "(exits at once: no wide-range group)"}[dom]
+    lhs_desc = ("bf16 -> e4m3 static per-tensor 4/448" if step.static
+                else "bf16 -> e4m3 dynamic 128-row blocks")
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": wl.name, "G": wl.G, "M": wl.M, "K": wl.K, "N": wl.N,
-                   "routing": f"zipf{wl.zipf_s}", "group_sizes": [int(x) for x in wl.group_sizes()],
-                   "lhs": "bf16 -> e4m3 dynamic 128-row blocks", "grad": "bf16 -> e5m2 dynamic 128-row blocks",
+                   "routing": f"zipf{wl.zipf_s}" if wl.routing == "zipf" else wl.routing,
+                   "group_sizes": [int(x) for x in wl.group_sizes()],
+                   "lhs": lhs_desc, "grad": "bf16 -> e5m2 dynamic 128-row blocks",
                    "rhs": "e4m3 per-channel", "out": "bf16",
                    "step": "lhs quantize + fwd + grad quantize + hybrid dlhs + tgmm; each tensor "
                            "quantized once, its codes used by every product"},
@@ -563,10 +810,6 @@ def main():
                    "value); ops, prep_ms and roofline come from the same step run on one stream "
                    "(serial_ms_per_step)",
         "ops": ops,
-        "fwd_in_kernel_quantization": {"ms": round(fused_ms, 4),
-                                       "TFLOP/s": round(flop_op / (fused_ms / 1000) / 1e12, 1),
-                                       "note": "gmm_fwd without workspace (lhs quantized inside "
-                                               "the product kernel); not part of the step"},
         "prep_ms": {"lhs_quantize": round(per["quantize_lhs"], 4),
                     "grad_quantize": round(per["quantize_grad"], 4)},
         "roofline": {"kernel": kern, "op": dom, "bound": "mfma", "achieved": round(ach, 1),
@@ -578,15 +821,24 @@ def main():
                                    "of back-to-back steps after the timed region; peak_at_clock = "
                                    "256 CUs x 8192 FP8 FLOP/clk x clock",
                      "traffic": measured_traffic(dom, wl.name),
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
-                                     "1 GiB copy; null once the kernel sources changed)"},
+                     "traffic_unit": "L2-to-fabric bytes per launch (FETCH_SIZE + WRITE_SIZE, "
+                                     "scaled by a 1 GiB copy; last-level-cache hits count as "
+                                     "fabric traffic); null once the kernel sources changed"},
+        "counters": measured_counters(wl.name),
     }
-    if not args.no_swiglu:
+    if not args.no_extras:
+        line["protocol"] = protocol(step, args.reps)
+        line["static_vs_dynamic"] = static_vs_dynamic(g, step, max(args.reps // 2, 10))
+        line["dense_fp8_ceiling"] = dense_ceiling(wl, max(args.reps // 2, 10))
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)
+    del step
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        line["ffn_chain"] = ffn_chain(g)
         line["swiglu_block"] = swiglu_block(g)
         line["route_block"] = route_block(g)
         line["blockwise_block"] = blockwise_block(g)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_rows, args.cpu_sample_cols)
     print(json.dumps(line), flush=True)
 
 

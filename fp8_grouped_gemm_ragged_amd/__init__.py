@@ -158,6 +158,27 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions")
 
 
+def _shape(t, shape, name):
+    """Reject a tensor whose shape differs from the one the call reads or writes: the C ABI
+    sees only pointers, so an undersized buffer would be accessed past its end."""
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(d) for d in shape)}, got {tuple(t.shape)}")
+
+
+def _block_scales(t, rows, name):
+    """Per-128-row-block scales: a 1-D f32 tensor with at least ceil(rows / 128) entries."""
+    import torch
+
+    _need(t, torch.float32, name, 1)
+    if t.shape[0] < _nblocks(rows):
+        raise ValueError(f"{name} needs {_nblocks(rows)} block scales for {rows} rows, got {t.shape[0]}")
+
+
+def _group_sizes(gs, G, name="group_sizes"):
+    if gs.shape[0] != G:
+        raise ValueError(f"{name} must hold one size per expert ({G}), got {gs.shape[0]}")
+
+
 def gmm_static_scale_from_bound(lo, hi, fmt="e4m3"):
     """Per-tensor scale of a fixed symmetric range [lo, hi] = [-b, b]: RNE(b / qmax)."""
     out = _F()
@@ -209,10 +230,16 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
         raise ValueError("operand width does not match the rhs contraction dimension")
     odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
     n_out = N if out_cols == "N" else K
+    _shape(rhs_scales, (G, n_out), "rhs_scales")
+    if group_offset is None:
+        _group_sizes(group_sizes, G)
+    elif not 0 <= int(group_offset) <= group_sizes.shape[0] - G:
+        raise ValueError("the local window group_offset .. group_offset + G must lie inside group_sizes")
     if out is None:
         out = torch.empty((M, n_out), dtype=odt, device=a.device)
     else:
         _need(out, odt, "out", 2)
+        _shape(out, (M, n_out), "out")
     op = _operand(KIND_FP8 if prequant else KIND_BF16, fmt, scaling, static_scale)
     mode = _SCALING[scaling]
     if mode != STATIC and a_scales is None:
@@ -220,7 +247,7 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
             raise ValueError("this recipe needs the operand's block scales as an input")
         a_scales = torch.empty(_nblocks(M), dtype=torch.float32, device=a.device)
     if a_scales is not None:
-        _need(a_scales, torch.float32, "scales", 1)
+        _block_scales(a_scales, M, "scales")
     ws_n = _SZ()
     if cname == "gmm_fwd":
         wop = OP_FWD_FUSED if fused else OP_FWD
@@ -321,21 +348,27 @@ def tgmm_drhs(lhs, grad, group_sizes, *, lhs_format="e4m3", lhs_scaling="dynamic
     N = grad.shape[1]
     G_total = group_sizes.shape[0]
     offset, G = _window if _window else (0, G_total)
+    if not (G >= 1 and 0 <= offset <= G_total - G):
+        raise ValueError("the local window group_offset .. group_offset + num_local must lie inside group_sizes")
     odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((G, K, N), dtype=odt, device=lhs.device)
     else:
         _need(out, odt, "out", 3)
+        _shape(out, (G, K, N), "out")
     aop = _operand(KIND_FP8 if a_codes else KIND_BF16, lhs_format, lhs_scaling, lhs_static_scale)
     bop = _operand(KIND_FP8 if g_codes else KIND_BF16, grad_format, grad_scaling, grad_static_scale)
     def scales_for(mode, given, codes):
         if _SCALING[mode] == DYNAMIC_GIVEN or (codes and _SCALING[mode] == DYNAMIC):
             if given is None:
                 raise ValueError("this recipe needs the operand's block scales as an input")
-            _need(given, torch.float32, "scales", 1)
+            _block_scales(given, M, "scales")
             return given
         if _SCALING[mode] == DYNAMIC:
-            return given if given is not None else torch.empty(_nblocks(M), dtype=torch.float32, device=lhs.device)
+            if given is not None:
+                _block_scales(given, M, "scales")
+                return given
+            return torch.empty(_nblocks(M), dtype=torch.float32, device=lhs.device)
         return None
 
     sa = scales_for(lhs_scaling, lhs_scales, a_codes)
@@ -399,12 +432,15 @@ def _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling, stat
     if rhs.shape[2] != K or N2 % 2:
         raise ValueError("rhs must be [G, 2I, K] codes matching the lhs width")
     I = N2 // 2
+    _shape(rhs_scales, (G, N2), "rhs_scales")
+    _group_sizes(group_sizes, G)
     odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
     hdt = torch.uint8 if h_fp8 else odt
     if out is None:
         out = torch.empty((M, I), dtype=hdt, device=lhs.device)
     else:
         _need(out, hdt, "out", 2)
+        _shape(out, (M, I), "out")
     x = torch.empty((M, N2), dtype=odt, device=lhs.device) if gu else None
     op = _operand(KIND_FP8 if prequant else KIND_BF16, lhs_format, lhs_scaling, static_scale)
     mode = _SCALING[lhs_scaling]
@@ -413,7 +449,7 @@ def _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling, stat
             raise ValueError("this recipe needs the operand's block scales as an input")
         lhs_scales = torch.empty(_nblocks(M), dtype=torch.float32, device=lhs.device)
     if lhs_scales is not None:
-        _need(lhs_scales, torch.float32, "scales", 1)
+        _block_scales(lhs_scales, M, "scales")
     ws_n = _SZ()
     _check(lib.gmm_workspace_size(OP_FWD_SWIGLU, ctypes.byref(op), ctypes.byref(op), M, K, N2, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
@@ -448,6 +484,7 @@ def gmm_swiglu_bwd(dh, gu, out=None):
         out = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dh.device)
     else:
         _need(out, torch.bfloat16, "out", 2)
+        _shape(out, (M, 2 * I), "out")
     _check(lib.gmm_swiglu_bwd(M, I, _ptr(dh), _ptr(gu), _ptr(out), _stream()), "gmm_swiglu_bwd")
     return out
 
@@ -486,6 +523,8 @@ def gmm_quantize(x, fmt="e4m3", scaling="dynamic", static_scale=None, scales=Non
         raise ValueError("dynamic_given needs the block scales")
     if mode == DYNAMIC and scales is None:
         scales = torch.empty(_nblocks(R), dtype=torch.float32, device=x.device)
+    if scales is not None and mode != STATIC:
+        _block_scales(scales, R, "scales")
     ws_n = _SZ()
     _check(lib.gmm_workspace_size(OP_QUANTIZE, ctypes.byref(op), ctypes.byref(op), R, C, 0, 1,
                                   ctypes.byref(ws_n)), "gmm_workspace_size")
@@ -568,6 +607,7 @@ def gmm_unpermute(y, row_of_slot, weights=None, out=None):
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     else:
         _need(out, torch.bfloat16, "out", 2)
+        _shape(out, (T, H), "out")
     _check(lib.gmm_unpermute(T, k, H, _ptr(y), _ptr(row_of_slot), _ptr(weights), _ptr(out),
                              _stream()), "gmm_unpermute")
     return out
@@ -621,11 +661,17 @@ def gmm_fwd_blockwise(lhs, lhs_scales, rhs, rhs_scales, group_sizes, bk=128, *,
     G, N = rhs.shape[0], rhs.shape[1]
     if rhs.shape[2] != K:
         raise ValueError("rhs must be [G, N, K] codes matching the lhs width")
+    if bk <= 0 or K % bk:
+        raise ValueError("bk must be a positive divisor of K")
+    _shape(lhs_scales, (M, K // bk), "lhs_scales")
+    _shape(rhs_scales, (G, K // bk, N), "rhs_scales")
+    _group_sizes(group_sizes, G)
     odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((M, N), dtype=odt, device=lhs.device)
     else:
         _need(out, odt, "out", 2)
+        _shape(out, (M, N), "out")
     _check(lib.gmm_fwd_blockwise(_FMT[lhs_format], OUT_F32 if odt == torch.float32 else OUT_BF16,
                                  M, K, N, G, int(bk), _ptr(lhs), _ptr(lhs_scales), _ptr(rhs),
                                  _ptr(rhs_scales), _ptr(group_sizes), _ptr(out), _stream()),

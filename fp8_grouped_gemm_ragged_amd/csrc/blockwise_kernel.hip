@@ -40,26 +40,9 @@ struct BsTile {
 // contiguous range of tiles.
 __device__ inline bool bs_schedule(const int32_t* __restrict__ gs, int G, int64_t M,
                                    int n_ntiles, int* s_cum, int* s_off, BsTile& tc) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  if (tid < 64) {
-    int carry_t = 0, carry_r = 0;
-    for (int base = 0; base < G; base += 64) {
-      const int g = base + lane;
-      const int m = g < G ? max(gs[g], 0) : 0;
-      const int it = wave_incl_scan((m + BS_BM - 1) / BS_BM, lane);
-      const int ir = wave_incl_scan(m, lane);
-      if (g < G) {
-        s_cum[g + 1] = carry_t + it;
-        s_off[g + 1] = carry_r + ir;
-      }
-      carry_t += __shfl(it, 63, 64);
-      carry_r += __shfl(ir, 63, 64);
-    }
-    if (lane == 0) {
-      s_cum[0] = 0;
-      s_off[0] = 0;
-    }
-  }
+  const int tid = threadIdx.x;
+  // sizes outside the contract are clamped: no tile leaves rows [0, M)
+  if (tid < 64) group_tiles_prefix<BS_BM>(gs, G, (uint32_t)M, 0u, s_cum, s_off);
   __syncthreads();
   const int total_mt = s_cum[G];
   const int total = total_mt * n_ntiles;

@@ -191,4 +191,63 @@ __device__ inline int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// Wave-level inclusive prefix sum that saturates at cap: every value lies in [0, cap]
+// and cap < 2^31, so no partial sum wraps.
+__device__ inline uint32_t wave_incl_scan_sat(uint32_t v, int lane, uint32_t cap) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v = min(v + o, cap);
+  }
+  return v;
+}
+
+// Expert-tile prefix sums, computed by one whole wave.  Groups 0 .. G-1 with sizes gs[g]
+// follow `rows_before` rows (<= M).  Every size is read as clamp(gs[g], 0, M) and every
+// row offset is clamped to M, so sizes that break the contract (negative, or summing past
+// M) can never place a tile outside rows [0, M).  Writes row_off[0 .. G] (row_off[g] =
+// first row of group g, row_off[G] = end of the last) and tile_cum[0 .. G] (BM-row tiles
+// of the groups before g, each group's count taken from its clamped row range).
+template <int BM>
+__device__ inline void group_tiles_prefix(const int32_t* __restrict__ gs, int G, uint32_t M,
+                                          uint32_t rows_before, int* tile_cum, int* row_off) {
+  const int lane = threadIdx.x & 63;
+  uint32_t carry_r = rows_before;
+  int carry_t = 0;
+  if (lane == 0) {
+    tile_cum[0] = 0;
+    row_off[0] = (int)rows_before;
+  }
+  for (int base = 0; base < G; base += 64) {
+    const int g = base + lane;
+    const uint32_t m = g < G ? (uint32_t)min(max(gs[g], 0), (int)M) : 0u;
+    const uint32_t ir = wave_incl_scan_sat(m, lane, M);
+    // the shuffle runs on every lane (a lane reads another lane's value only while that
+    // lane is active), then lane 0 takes 0
+    const uint32_t up = (uint32_t)__shfl_up(ir, 1, 64);
+    const uint32_t ex = lane == 0 ? 0u : up;
+    const uint32_t end = min(carry_r + ir, M), start = min(carry_r + ex, M);
+    const int it = wave_incl_scan((int)((end - start + BM - 1) / BM), lane);
+    if (g < G) {
+      tile_cum[g + 1] = carry_t + it;
+      row_off[g + 1] = (int)end;
+    }
+    carry_t += __shfl(it, 63, 64);
+    carry_r = min(carry_r + (uint32_t)__shfl(ir, 63, 64), M);
+  }
+}
+
+// Rows of the first n groups, clamped as in group_tiles_prefix (one whole wave).
+__device__ inline uint32_t rows_of_groups(const int32_t* __restrict__ gs, int n, uint32_t M) {
+  const int lane = threadIdx.x & 63;
+  uint32_t carry = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int g = base + lane;
+    const uint32_t m = g < n ? (uint32_t)min(max(gs[g], 0), (int)M) : 0u;
+    const uint32_t ir = wave_incl_scan_sat(m, lane, M);
+    carry = min(carry + (uint32_t)__shfl(ir, 63, 64), M);
+  }
+  return carry;
+}
+
 }  // namespace gmm

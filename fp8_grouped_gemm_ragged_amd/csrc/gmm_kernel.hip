@@ -48,37 +48,14 @@ struct TileCoord {
 // Per-group prefix sums into LDS (first wave) over the window of G groups that starts
 // after g_before others: s_tile_cum[g] = M-tiles of window groups < g, s_row_off[g] = the
 // first row of window group g (rows of every group before it, inside or outside the
-// window).  The caller synchronizes before reading them.
-__device__ inline void group_prefix(const int32_t* __restrict__ gs, int g_before, int G,
+// window), both clamped so that sizes outside the contract never place a tile outside
+// rows [0, M).  The caller synchronizes before reading them.
+__device__ inline void group_prefix(const int32_t* __restrict__ gs, int g_before, int G, int64_t M,
                                     int* s_tile_cum, int* s_row_off) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  if (tid < 64) {
-    // sizes outside the contract (negative) are read as 0, and rows past M are dropped
-    // by the tile coordinates, so no access ever leaves the tensors
-    int carry_r = 0;
-    for (int base = 0; base < g_before; base += 64) {
-      const int g = base + lane;
-      const int ir = wave_incl_scan(g < g_before ? max(gs[g], 0) : 0, lane);
-      carry_r += __shfl(ir, 63, 64);
-    }
-    const int32_t* __restrict__ wgs = gs + g_before;
-    int carry_t = 0;
-    if (lane == 0) {
-      s_tile_cum[0] = 0;
-      s_row_off[0] = carry_r;
-    }
-    for (int base = 0; base < G; base += 64) {
-      const int g = base + lane;
-      const int m = g < G ? max(wgs[g], 0) : 0;
-      const int it = wave_incl_scan((m + BM - 1) / BM, lane);
-      const int ir = wave_incl_scan(m, lane);
-      if (g < G) {
-        s_tile_cum[g + 1] = carry_t + it;
-        s_row_off[g + 1] = carry_r + ir;
-      }
-      carry_t += __shfl(it, 63, 64);
-      carry_r += __shfl(ir, 63, 64);
-    }
+  if (threadIdx.x < 64) {
+    const uint32_t Mu = (uint32_t)M;  // M < 2^31
+    group_tiles_prefix<BM>(gs + g_before, G, Mu, rows_of_groups(gs, g_before, Mu), s_tile_cum,
+                           s_row_off);
   }
 }
 
@@ -113,7 +90,7 @@ __device__ inline bool tile_coord(int L, int total_mt, int n_ntiles, int G, int6
 __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int g_before, int G,
                                      int64_t M, int n_ntiles, int* s_tile_cum, int* s_row_off,
                                      TileCoord& tc) {
-  group_prefix(gs, g_before, G, s_tile_cum, s_row_off);
+  group_prefix(gs, g_before, G, M, s_tile_cum, s_row_off);
   __syncthreads();
   const int total_mt = s_tile_cum[G];
   const int total = total_mt * n_ntiles;

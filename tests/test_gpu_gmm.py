@@ -158,6 +158,42 @@ def test_rows_written_exactly_once_with_canaries(lib):
     assert torch.isnan(buf[:pad * N]).all() and torch.isnan(buf[(pad + M) * N:]).all()
 
 
+def test_sizes_outside_the_contract_stay_inside_the_output(lib):
+    # group sizes that break the contract (one near INT_MAX, a negative one, a sum past M)
+    # are clamped by the schedulers: every kernel still writes only inside its output
+    # (NaN canaries on both sides stay), whatever it writes there
+    M, K, N, G = 556, 256, 384, 5
+    sizes = [300, 2147483000, 45, -5, 211]
+    x, _ = gen((M, K), 1.0, 163)
+    gr, _ = gen((M, N), 1e-3, 164)
+    w, _ = gen((G, K, N), 0.02, 165)
+    codes, scales = lib.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+    wk, sk = lib.gmm_quantize_rhs(w, "e4m3", 1, "kn")
+    gs = gs_tensor(sizes)
+    pad = 64
+
+    def canaried(rows, cols):
+        buf = torch.full(((rows + 2 * pad) * cols,), float("nan"), dtype=torch.float32, device=DEV)
+        return buf, buf[pad * cols:(pad + rows) * cols].view(rows, cols)
+
+    def intact(buf, rows, cols):
+        return bool(torch.isnan(buf[:pad * cols]).all() and torch.isnan(buf[(pad + rows) * cols:]).all())
+
+    b1, o1 = canaried(M, N)
+    lib.gmm_fwd(x, codes, scales, gs, lhs_scaling="static", static_scale=S_4_448,
+                out_dtype=torch.float32, out=o1)
+    b2, o2 = canaried(M, K)
+    lib.gmm_dlhs(gr, wk, sk, gs, out_dtype=torch.float32, out=o2)
+    xq, sx = lib.gmm_quantize_subchannel(x, 128)
+    wb, wbs = lib.gmm_quantize_rhs_blockwise(w, 128)
+    b3, o3 = canaried(M, N)
+    lib.gmm_fwd_blockwise(xq, sx, wb, wbs, gs, 128, out_dtype=torch.float32, out=o3)
+    b4, o4 = canaried(G * K, N)
+    lib.tgmm_drhs(x, gr, gs, out_dtype=torch.float32, out=o4.view(G, K, N))
+    sync()
+    assert intact(b1, M, N) and intact(b2, M, K) and intact(b3, M, N) and intact(b4, G * K, N)
+
+
 def compositions(M, G):
     import itertools
 

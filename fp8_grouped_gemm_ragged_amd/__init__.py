@@ -7,7 +7,7 @@ the library.  There is no fallback: if the shared library is missing, ``load()``
 raises, and so does every call.
 
 Functions (same names as the C ABI):
-  gmm_fwd, gmm_dlhs, tgmm_drhs, gmm_dynamic_scales, gmm_quantize, gmm_quantize_rhs,
+  gmm_fwd, gmm_fwd_noalloc, gmm_dlhs, tgmm_drhs, gmm_dynamic_scales, gmm_quantize, gmm_quantize_rhs,
   gmm_static_scale_from_bound, gmm_workspace_size, gmm_status_string, gmm_version.
 
 fp8 codes travel as ``torch.uint8`` tensors; bf16 values as ``torch.bfloat16``.
@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "load", "library_path", "GmmError", "gmm_fwd", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
+    "load", "library_path", "GmmError", "gmm_fwd", "gmm_fwd_noalloc", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
     "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8", "gmm_swiglu_bwd",
     "gmm_permute", "gmm_unpermute", "gmm_fwd_local", "gmm_dlhs_local", "tgmm_drhs_local",
     "gmm_fwd_blockwise", "gmm_quantize_subchannel", "gmm_quantize_rhs_blockwise",
@@ -65,6 +65,7 @@ _OPP = ctypes.POINTER(Operand)
 
 _SIGNATURES = {
     "gmm_fwd": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "gmm_fwd_noalloc": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P],
     "gmm_dlhs": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "tgmm_drhs": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_fwd_swiglu": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -287,6 +288,49 @@ def gmm_fwd(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3", lhs_scaling
     o, s = _gemm("gmm_fwd", lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
                  static_scale, lhs_scales, rhs_layout, out_dtype, out, "K", "N", fused)
     return (o, s) if return_scales else o
+
+
+def gmm_fwd_noalloc(lhs, rhs, rhs_scales, group_sizes, *, lhs_format="e4m3",
+                    lhs_scaling="dynamic", static_scale=None, lhs_scales=None, rhs_layout="nk",
+                    out_dtype=None, out=None):
+    """gmm_fwd without a workspace: the library's device scratch array holds the dynamic
+    scales' abs-max partials (M <= GMM_NOALLOC_MAX_ROWS).  With `out` (and `lhs_scales`
+    when the recipe needs or returns them) given, nothing is allocated here either."""
+    import torch
+
+    lib = load()
+    prequant = lhs.dtype == torch.uint8
+    _need(lhs, torch.uint8 if prequant else torch.bfloat16, "lhs", 2)
+    _need(rhs, torch.uint8, "rhs", 3)
+    _need(rhs_scales, torch.float32, "rhs_scales", 2)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, K = lhs.shape
+    G = rhs.shape[0]
+    if _LAYOUT[rhs_layout] == RHS_KN:
+        Kw, N = rhs.shape[1], rhs.shape[2]
+    else:
+        N, Kw = rhs.shape[1], rhs.shape[2]
+    if Kw != K:
+        raise ValueError("operand width does not match the rhs contraction dimension")
+    _shape(rhs_scales, (G, N), "rhs_scales")
+    _group_sizes(group_sizes, G)
+    odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=odt, device=lhs.device)
+    else:
+        _need(out, odt, "out", 2)
+        _shape(out, (M, N), "out")
+    mode = _SCALING[lhs_scaling]
+    if mode != STATIC and (prequant or mode == DYNAMIC_GIVEN) and lhs_scales is None:
+        raise ValueError("this recipe needs the operand's block scales as an input")
+    if lhs_scales is not None:
+        _block_scales(lhs_scales, M, "scales")
+    op = _operand(KIND_FP8 if prequant else KIND_BF16, lhs_format, lhs_scaling, static_scale)
+    _check(lib.gmm_fwd_noalloc(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout],
+                               OUT_F32 if odt == torch.float32 else OUT_BF16, M, K, N, G,
+                               _ptr(lhs), _ptr(lhs_scales), _ptr(rhs), _ptr(rhs_scales),
+                               _ptr(group_sizes), _ptr(out), _stream()), "gmm_fwd_noalloc")
+    return out
 
 
 def gmm_fwd_local(lhs, rhs, rhs_scales, group_sizes, group_offset, *, lhs_format="e4m3",

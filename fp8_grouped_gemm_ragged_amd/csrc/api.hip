@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/gmm_fp8.h"
@@ -268,6 +269,34 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   return e == hipSuccess ? GMM_OK : GMM_ERR_HIP;
 }
 
+// ---- the scratch array of gmm_fwd_noalloc ----
+// Its workspace is the dynamic-scale workspace of GMM_NOALLOC_MAX_ROWS rows: abs-max
+// partials, then the block scales.
+constexpr size_t NOALLOC_SCRATCH_BYTES =
+    (size_t((GMM_NOALLOC_MAX_ROWS + BLOCK_ROWS - 1) / BLOCK_ROWS) * AMAX_SPLIT * 4 + 255) / 256 * 256 +
+    (size_t((GMM_NOALLOC_MAX_ROWS + BLOCK_ROWS - 1) / BLOCK_ROWS) * 4 + 255) / 256 * 256;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of the current device's copy of `scratch`, looked up on the first
+// call with that device current.  In host code the array's name is only a stand-in: the
+// kernels are handed this address.
+gmm_status_t noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return GMM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GMM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +311,23 @@ gmm_status_t gmm_fwd(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rh
   return grouped_gemm("gmm_fwd", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN, out_dtype, M, K,
                       N, G, 0, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes, out, workspace,
                       workspace_bytes, (hipStream_t)stream);
+}
+
+gmm_status_t gmm_fwd_noalloc(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                             int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                             const void* lhs, float* lhs_scales, const uint8_t* rhs,
+                             const float* rhs_scales, const int32_t* group_sizes, void* out,
+                             gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  if (M > GMM_NOALLOC_MAX_ROWS) return GMM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  gmm_status_t s = noalloc_scratch(&ws);
+  if (s != GMM_OK) return s;
+  // only the dynamic-scale workspace fits: a bf16 lhs is quantized inside the product kernel
+  const size_t ws_bytes = needs_dyn_ws(lhs_op) ? dyn_ws_bytes(M) : 0;
+  return grouped_gemm("gmm_fwd_noalloc", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN, out_dtype,
+                      M, K, N, G, 0, G, lhs, lhs_scales, rhs, rhs_scales, group_sizes, out,
+                      ws_bytes ? ws : nullptr, ws_bytes, (hipStream_t)stream);
 }
 
 gmm_status_t gmm_fwd_local(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,

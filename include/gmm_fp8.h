@@ -90,6 +90,7 @@ typedef struct ihipStream_t* gmm_stream_t;
 
 #define GMM_BLOCK_ROWS 128   /* rows per dynamic-scale block */
 #define GMM_MAX_GROUPS 1024  /* largest supported number of groups (experts) */
+#define GMM_NOALLOC_MAX_ROWS (1 << 20)  /* largest M that gmm_fwd_noalloc accepts */
 
 typedef enum gmm_status {
   GMM_OK = 0,
@@ -176,6 +177,27 @@ gmm_status_t gmm_fwd(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rh
                      const void* lhs, float* lhs_scales, const uint8_t* rhs,
                      const float* rhs_scales, const int32_t* group_sizes, void* out,
                      void* workspace, size_t workspace_bytes, gmm_stream_t stream);
+
+/*
+ * gmm_fwd_noalloc - gmm_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace: the one scratch buffer the forward needs (the abs-max partials of a dynamic
+ * bf16 lhs and, when lhs_scales is NULL, its block scales) is a file-scope device array of
+ * the library, about 288 KiB, which each GPU the library runs on holds until the process
+ * ends.  Its address is looked up once per device (hipGetSymbolAddress), on the first call
+ * with that device current; the call itself makes no allocation.
+ * Arguments, outputs and errors as gmm_fwd; a bf16 lhs is quantized inside the product
+ * kernel (the codes and outputs equal gmm_fwd's).  M <= GMM_NOALLOC_MAX_ROWS, else
+ * GMM_ERR_WORKSPACE.  Every call on one GPU shares that GPU's scratch array, which keeps
+ * the last call's contents (the call writes every byte it reads): calls that overlap on
+ * one GPU (concurrent streams, or host threads) race, and must be serialized by the
+ * caller.  The current device must be the stream's device.
+ */
+gmm_status_t gmm_fwd_noalloc(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,
+                             int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,
+                             const void* lhs, float* lhs_scales, const uint8_t* rhs,
+                             const float* rhs_scales, const int32_t* group_sizes, void* out,
+                             gmm_stream_t stream);
 
 /*
  * gmm_dlhs - lhs gradient: a gmm of grad against rhs transposed ("Support quantization

@@ -3,9 +3,13 @@
 Floating-point outputs (the reading of "max relative error 1e-3 after identical
 quantization"): per group, max |Y - R| / max |R| <= tol, where R is the oracle's
 fp32-accumulated result and Y the library's f32 output.  A group whose reference is
-all zero must be exactly zero.  bf16 outputs cannot meet 1e-3 against an fp32
-reference (half a bf16 ulp is up to 2^-8 relative), so for them every element must be
-RNE_bf16(R) or one of its two bf16 neighbours.
+all zero must be exactly zero.  Beside that metric, f32 outputs are also held element
+by element to the rounding bound of their sums (assert_rounding_bound), which a wrong
+term in a single output would break.
+bf16 outputs cannot meet 1e-3 against an fp32 reference (half a bf16 ulp is up to 2^-8
+relative), so for them (assert_bf16_close) every element must lie between
+RNE_bf16(R - d) and RNE_bf16(R + d), d = tol * max|R| of its group, and at least 95% of
+the elements must equal RNE_bf16(R) exactly.
 Codes and scales: byte-exact.
 """
 
@@ -72,6 +76,34 @@ def assert_bf16_close(Ybits, R, ranges=None, tol=TOL, min_exact=0.95):
     frac = float(1.0 - exact.mean())
     assert 1.0 - frac >= min_exact, f"only {1 - frac:.4f} of bf16 outputs equal RNE(oracle)"
     return frac
+
+
+U = 2.0 ** -24  # unit roundoff of float32
+
+
+def magnitudes(codes):
+    """fp8 codes of |value|: the sign bit cleared (finite codes stay finite)."""
+    return np.asarray(codes, np.uint8) & np.uint8(0x7F)
+
+
+def assert_rounding_bound(Y, R, absR, n_terms):
+    """f32 outputs, element by element: |Y - R| <= 2 (n + 8) u absR + 4 u |R| + 2^-126.
+
+    absR holds the same product computed on the codes' magnitudes (sum |a| |b| times the
+    positive scales); n_terms is the contraction length (broadcast against Y: for tgmm the
+    rows of each group).  Y and R sum the same exact products in two fp32 orders (the
+    oracle's sequential sum; the MFMA's 64-term blocks, the rescaling between tgmm's row
+    blocks), each within (n + 8) u absR of the exact sum, and round the scale products of
+    the epilogue twice each; 2^-126 absorbs subnormal results."""
+    Y = np.asarray(Y, np.float64)
+    R = np.asarray(R, np.float64)
+    A = np.asarray(absR, np.float64)
+    n = np.asarray(n_terms, np.float64)
+    bound = 2.0 * (n + 8.0) * U * A + 4.0 * U * np.abs(R) + 2.0 ** -126
+    excess = np.abs(Y - R) - bound
+    bad = excess > 0
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} outputs outside their rounding "
+                           f"bound (worst excess {float(excess.max()):.3e})")
 
 
 def group_row_ranges(group_sizes):

@@ -19,7 +19,8 @@ from oracle.quant import (block_amax, dynamic_scale_from_amax, quantize_rhs_per_
                           quantize_with_inv, static_inv)
 from synth.workloads import WORKLOADS, bf16_to_bits, normal_bf16
 from tests.gpu_util import DEV, gs_tensor, sync
-from tests.parity import TOL, assert_bf16_close, group_rel_err, group_row_ranges, to_np
+from tests.parity import (TOL, assert_bf16_close, assert_rounding_bound, group_rel_err,
+                          group_row_ranges, magnitudes, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,11 +61,13 @@ def dynamic_block_scales(x_bits, fmt):
     return dynamic_scale_from_amax(block_amax(x_bits, 128), fmt)
 
 
-def check_sampled(Ybf, Y32, R, sub_sizes):
+def check_sampled(Ybf, Y32, R, sub_sizes, absR=None, n_terms=None):
     ranges = group_row_ranges(sub_sizes)
     err = group_rel_err(Y32, R, ranges)
     print(f"sampled max group relative error {err:.3e} over {R.size} outputs", flush=True)
     assert err <= TOL, err
+    if absR is not None:
+        assert_rounding_bound(Y32, R, absR, n_terms)
     assert_bf16_close(Ybf, R, ranges)
 
 
@@ -94,8 +97,10 @@ def test_mixtral_gate_up_forward(lib):
     assert np.array_equal(np.transpose(to_np(wq[:, ci, :]), (0, 2, 1)), b_codes)
     sub = sampled_sizes(rows, sizes)
     R = gmm_fwd_ref(a_codes, "e4m3", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    absR = gmm_fwd_ref(magnitudes(a_codes), "e4m3", s_ref[rows // 128], magnitudes(b_codes),
+                       "e4m3", b_s, sub)
     ri = torch.as_tensor(rows, device=DEV)
-    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub)
+    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub, absR, K)
 
 
 @pytest.fixture(scope="module")
@@ -130,8 +135,10 @@ def test_deepseek_local_forward_static(lib, deepseek):
     sub = sampled_sizes(rows, sizes)
     R = gmm_fwd_ref(a_codes, "e4m3", np.full(len(rows), S_4_448, np.float32), b_codes, "e4m3",
                     b_s, sub)
+    absR = gmm_fwd_ref(magnitudes(a_codes), "e4m3", np.full(len(rows), S_4_448, np.float32),
+                       magnitudes(b_codes), "e4m3", b_s, sub)
     ri, ci = torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)
-    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub)
+    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub, absR, a_codes.shape[1])
 
 
 @pytest.mark.parametrize("route", ["hybrid", "fused"])
@@ -163,8 +170,10 @@ def test_deepseek_local_dlhs(lib, deepseek, route):
     assert np.array_equal(to_np(wk[:, ki, :]), b_codes)
     sub = sampled_sizes(rows, sizes)
     R = gmm_dlhs_ref(g_codes, "e5m2", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    absR = gmm_dlhs_ref(magnitudes(g_codes), "e5m2", s_ref[rows // 128], magnitudes(b_codes),
+                        "e4m3", b_s, sub)
     ri = torch.as_tensor(rows, device=DEV)
-    check_sampled(to_np(out[ri][:, ki]), to_np(out32[ri][:, ki]), R, sub)
+    check_sampled(to_np(out[ri][:, ki]), to_np(out32[ri][:, ki]), R, sub, absR, g_codes.shape[1])
 
 
 def test_deepseek_local_tgmm(lib, deepseek):
@@ -199,6 +208,9 @@ def test_deepseek_local_tgmm(lib, deepseek):
     err = group_rel_err(Y32, R, ranges)
     print(f"sampled max slab relative error {err:.3e}", flush=True)
     assert err <= TOL, err
+    absR = tgmm_ref(magnitudes(a_codes), "e4m3", sa_ref, magnitudes(g_codes), "e5m2", sg_ref,
+                    np.asarray(sizes))
+    assert_rounding_bound(Y32, R, absR, np.asarray(sizes)[:, None, None])
     assert_bf16_close(Ybf, R, ranges)
 
 
@@ -224,8 +236,9 @@ def _check_fwd(lib, lhs, scaling, s_gpu, w_bits_cols, wq, ws, cols, sizes, out, 
     assert np.array_equal(np.transpose(to_np(wq[:, ci, :]), (0, 2, 1)), b_codes)
     sub = sampled_sizes(rows, sizes)
     R = gmm_fwd_ref(a_codes, "e4m3", s_row, b_codes, "e4m3", b_s, sub)
+    absR = gmm_fwd_ref(magnitudes(a_codes), "e4m3", s_row, magnitudes(b_codes), "e4m3", b_s, sub)
     ri = torch.as_tensor(rows, device=DEV)
-    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub)
+    check_sampled(to_np(out[ri][:, ci]), to_np(out32[ri][:, ci]), R, sub, absR, a_codes.shape[1])
 
 
 def _check_dlhs(grad, s_gpu, w_bits_krows, wk, sk, kcols, sizes, out, out32, rng):
@@ -240,8 +253,10 @@ def _check_dlhs(grad, s_gpu, w_bits_krows, wk, sk, kcols, sizes, out, out32, rng
     assert np.array_equal(to_np(wk[:, ki, :]), b_codes)
     sub = sampled_sizes(rows, sizes)
     R = gmm_dlhs_ref(g_codes, "e5m2", s_ref[rows // 128], b_codes, "e4m3", b_s, sub)
+    absR = gmm_dlhs_ref(magnitudes(g_codes), "e5m2", s_ref[rows // 128], magnitudes(b_codes),
+                        "e4m3", b_s, sub)
     ri = torch.as_tensor(rows, device=DEV)
-    check_sampled(to_np(out[ri][:, ki]), to_np(out32[ri][:, ki]), R, sub)
+    check_sampled(to_np(out[ri][:, ki]), to_np(out32[ri][:, ki]), R, sub, absR, g_codes.shape[1])
 
 
 def _check_tgmm(lhs, grad, sa, sg, sizes, out, out32, rng):
@@ -257,11 +272,14 @@ def _check_tgmm(lhs, grad, sa, sg, sizes, out, out32, rng):
     a_codes = quantize_with_inv(bf16_bits_to_f32(lb[:, ks]), ia[rb], "e4m3")
     g_codes = quantize_with_inv(bf16_bits_to_f32(gb[:, ns]), ig[rb], "e5m2")
     R = tgmm_ref(a_codes, "e4m3", sa_ref, g_codes, "e5m2", sg_ref, np.asarray(sizes))
+    absR = tgmm_ref(magnitudes(a_codes), "e4m3", sa_ref, magnitudes(g_codes), "e5m2", sg_ref,
+                    np.asarray(sizes))
     ki, ni = torch.as_tensor(ks, device=DEV), torch.as_tensor(ns, device=DEV)
     ranges = [(g, g + 1) for g in range(len(sizes))]
     err = group_rel_err(to_np(out32[:, ki][:, :, ni]), R, ranges)
     print(f"sampled max slab relative error {err:.3e}", flush=True)
     assert err <= TOL, err
+    assert_rounding_bound(to_np(out32[:, ki][:, :, ni]), R, absR, np.asarray(sizes)[:, None, None])
     assert_bf16_close(to_np(out[:, ki][:, :, ni]), R, ranges)
 
 

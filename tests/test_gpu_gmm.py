@@ -5,14 +5,17 @@ import pytest
 import torch
 
 import oracle.ops as ops
+from oracle.gmm import gmm_dlhs_ref, gmm_fwd_ref, row_scales
 from oracle.quant import quantize_rhs_per_channel
 from synth.workloads import WORKLOADS
 from tests.gpu_util import DEV, channel_varied, gen, gs_tensor, sync
 from tests.parity import (
     TOL,
     assert_bf16_close,
+    assert_rounding_bound,
     group_rel_err,
     group_row_ranges,
+    magnitudes,
     to_np,
 )
 
@@ -33,10 +36,14 @@ def run_fwd(lib, x, xbits, w, wbits, sizes, scaling, layout, out_dtype, s=S_4_44
     out, sc = lib.gmm_fwd(x, codes, scales, gs_tensor(sizes), lhs_format="e4m3",
                           lhs_scaling=scaling, static_scale=s, rhs_layout=layout,
                           out_dtype=out_dtype, return_scales=True)
-    R, _, s_blk = ops.fwd(xbits, c_ref, s_ref, np.asarray(sizes), "e4m3", scaling,
-                          np.float32(s), "e4m3", "f32")
+    R, a_codes, s_blk = ops.fwd(xbits, c_ref, s_ref, np.asarray(sizes), "e4m3", scaling,
+                                np.float32(s), "e4m3", "f32")
     if scaling == "dynamic":
         assert np.array_equal(to_np(sc).view(np.uint32), s_blk.view(np.uint32))
+    if out_dtype == torch.float32 and xbits.shape[0]:
+        absR = gmm_fwd_ref(magnitudes(a_codes), "e4m3", row_scales(s_blk, xbits.shape[0]),
+                           magnitudes(c_ref), "e4m3", s_ref, np.asarray(sizes))
+        assert_rounding_bound(to_np(out), R, absR, xbits.shape[1])
     return to_np(out), R
 
 
@@ -86,13 +93,16 @@ def test_dlhs_ragged_medium(lib, layout, out_dtype):
     out, sc = lib.gmm_dlhs(gr, codes, scales, gs_tensor(sizes), grad_format="e5m2",
                            grad_scaling="dynamic", rhs_layout=layout, out_dtype=out_dtype,
                            return_scales=True)
-    R, _, s_blk = ops.dlhs(gb, c_ref, s_ref, np.asarray(sizes))
+    R, g_codes, s_blk = ops.dlhs(gb, c_ref, s_ref, np.asarray(sizes))
     assert np.array_equal(to_np(sc).view(np.uint32), s_blk.view(np.uint32))
     Y = to_np(out)
     if out_dtype == torch.float32:
         err = group_rel_err(Y, R, group_row_ranges(sizes))
         print(f"max group relative error {err:.3e}")
         assert err <= TOL, err
+        absR = gmm_dlhs_ref(magnitudes(g_codes), "e5m2", row_scales(s_blk, M), magnitudes(c_ref),
+                            "e4m3", s_ref, np.asarray(sizes))
+        assert_rounding_bound(Y, R, absR, N)
     else:
         assert_bf16_close(Y, R, group_row_ranges(sizes))
 

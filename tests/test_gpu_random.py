@@ -10,7 +10,9 @@ import torch
 import oracle.ops as ops
 from oracle.quant import quantize_rhs_per_channel
 from tests.gpu_util import gen, gs_tensor, sync
-from tests.parity import TOL, group_rel_err, group_row_ranges, slab_rel_err, to_np
+from oracle.gmm import gmm_dlhs_ref, gmm_fwd_ref, row_scales, tgmm_ref
+from tests.parity import (TOL, assert_rounding_bound, group_rel_err, group_row_ranges,
+                          magnitudes, slab_rel_err, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,10 +64,13 @@ def test_random_fwd_dlhs_tgmm(lib, i):
         lhs = x
     out = lib.gmm_fwd(lhs, wq, ws, gs, rhs_layout=layout, out_dtype=torch.float32,
                       fused=fused and kind == "bf16", **kw)
-    R, _, _ = ops.fwd(xb, c_ref, s_ref, np.asarray(sizes), "e4m3", scaling,
-                             np.float32(S), "e4m3", "f32")
+    R, a_codes, a_s = ops.fwd(xb, c_ref, s_ref, np.asarray(sizes), "e4m3", scaling,
+                              np.float32(S), "e4m3", "f32")
     if M:
         assert group_rel_err(to_np(out), R, ranges) <= TOL
+        absR = gmm_fwd_ref(magnitudes(a_codes), "e4m3", row_scales(a_s, M), magnitudes(c_ref),
+                           "e4m3", s_ref, np.asarray(sizes))
+        assert_rounding_bound(to_np(out), R, absR, K)
 
     # dlhs (the rhs quantized per k)
     wk, sk = lib.gmm_quantize_rhs(w, "e4m3", 1, "kn" if layout == "nk" else "nk")
@@ -79,10 +84,13 @@ def test_random_fwd_dlhs_tgmm(lib, i):
         grad = gr
     dl = lib.gmm_dlhs(grad, wk, sk, gs, rhs_layout="kn" if layout == "nk" else "nk",
                       out_dtype=torch.float32, fused=fused and kind == "bf16", **gkw)
-    Rd, _, _ = ops.dlhs(grb, ck_ref, sk_ref, np.asarray(sizes), "e5m2", scaling,
+    Rd, g_codes, g_s = ops.dlhs(grb, ck_ref, sk_ref, np.asarray(sizes), "e5m2", scaling,
                                 np.float32(S), "e4m3", "f32")
     if M:
         assert group_rel_err(to_np(dl), Rd, group_row_ranges(sizes)) <= TOL
+        absD = gmm_dlhs_ref(magnitudes(g_codes), "e5m2", row_scales(g_s, M), magnitudes(ck_ref),
+                            "e4m3", sk_ref, np.asarray(sizes))
+        assert_rounding_bound(to_np(dl), Rd, absD, N)
 
     # tgmm (bf16 operands, or the codes just made)
     if kind == "codes" and M:
@@ -101,6 +109,10 @@ def test_random_fwd_dlhs_tgmm(lib, i):
     Rt, _, _ = ops.tgmm(xb, grb, np.asarray(sizes), "e4m3", scaling, np.float32(S), "e5m2",
                         scaling, np.float32(S), "f32")
     assert slab_rel_err(to_np(dr), Rt) <= TOL
+    if M:
+        absT = tgmm_ref(magnitudes(a_codes), "e4m3", a_s, magnitudes(g_codes), "e5m2", g_s,
+                        np.asarray(sizes))
+        assert_rounding_bound(to_np(dr), Rt, absT, np.asarray(sizes)[:, None, None])
     for g in range(G):  # empty experts: +0.0 slabs
         if sizes[g] == 0:
             assert (to_np(dr)[g].view(np.uint32) == 0).all()

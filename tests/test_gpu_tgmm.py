@@ -6,7 +6,9 @@ import torch
 
 import oracle.ops as ops
 from tests.gpu_util import DEV, gen, gs_tensor, sync
-from tests.parity import TOL, assert_bf16_close, slab_rel_err, to_np
+from oracle.gmm import tgmm_ref
+from tests.parity import (TOL, assert_bf16_close, assert_rounding_bound, magnitudes,
+                          slab_rel_err, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +39,11 @@ def test_tgmm_ragged_medium(lib, out_dtype, lhs_scaling):
         err = slab_rel_err(Y, R)
         print(f"max slab relative error {err:.3e}")
         assert err <= TOL, err
+        a_codes, _ = ops.quantize_operand(xb, "e4m3", lhs_scaling, np.float32(S_4_448))
+        g_codes, _ = ops.quantize_operand(gb, "e5m2", "dynamic")
+        absR = tgmm_ref(magnitudes(a_codes), "e4m3", sa_ref, magnitudes(g_codes), "e5m2", sg_ref,
+                        np.asarray(sizes))
+        assert_rounding_bound(Y, R, absR, np.asarray(sizes)[:, None, None])
     else:
         assert_bf16_close(Y, R, [(g, g + 1) for g in range(len(sizes))])
 

@@ -77,9 +77,9 @@ def _summary(path, workload):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash():
         return None
-    return t
+    return t.get("workloads", {}).get(workload)
 
 
 def measured_traffic(op, workload):

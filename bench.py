@@ -195,12 +195,21 @@ class Step:
                                          M, K, N, G, ctypes.byref(n)))
         self.ws_t = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
         self.ws_t_n = n.value
+        # the products' own workspace: on large calls, the tail split's partial sums
+        self._chk(lib.gmm_workspace_size(g.OP_FWD, ctypes.byref(self.op_l8), ctypes.byref(self.op_l8),
+                                         M, K, N, G, ctypes.byref(n)))
+        self.ws_f = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+        self.ws_f_n = n.value
+        self._chk(lib.gmm_workspace_size(g.OP_DLHS, ctypes.byref(self.op_g8), ctypes.byref(self.op_g8),
+                                         M, N, K, G, ctypes.byref(n)))
+        self.ws_d = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+        self.ws_d_n = n.value
         self.r_lq, self.r_l8 = ctypes.byref(self.op_lq), ctypes.byref(self.op_l8)
         self.r_gq, self.r_g8 = ctypes.byref(self.op_gq), ctypes.byref(self.op_g8)
         P = lambda t: t.data_ptr()
         self.p = {k: P(getattr(self, k)) for k in
                   ("lhs", "grad", "lhs_q", "grad_q", "w_fwd", "s_fwd", "w_dlhs", "s_dlhs", "out", "dlhs",
-                   "drhs", "s_lhs", "s_grad", "ws", "ws_t", "gs")}
+                   "drhs", "s_lhs", "s_grad", "ws", "ws_t", "ws_f", "ws_d", "gs")}
         # a static lhs has no block scales
         self.p_sl = None if self.static else self.p["s_lhs"]
         torch.cuda.synchronize()
@@ -214,7 +223,7 @@ class Step:
         g, p = self.g, self.p
         self._chk(self.lib.gmm_fwd(self.r_l8, g.E4M3, g.RHS_NK, g.OUT_BF16, self.M, self.K, self.N,
                                    self.G, p["lhs_q"], self.p_sl, p["w_fwd"], p["s_fwd"], p["gs"],
-                                   p["out"], None, 0, s))
+                                   p["out"], p["ws_f"], self.ws_f_n, s))
 
     def q_grad(self, s):
         self._chk(self.lib.gmm_quantize(self.r_gq, self.M, self.N, self.p["grad"], self.p["grad_q"],
@@ -224,7 +233,7 @@ class Step:
         g, p = self.g, self.p
         self._chk(self.lib.gmm_dlhs(self.r_g8, g.E4M3, g.RHS_KN, g.OUT_BF16, self.M, self.K, self.N,
                                     self.G, p["grad_q"], p["s_grad"], p["w_dlhs"], p["s_dlhs"],
-                                    p["gs"], p["dlhs"], None, 0, s))
+                                    p["gs"], p["dlhs"], p["ws_d"], self.ws_d_n, s))
 
     def tgmm(self, s):
         p = self.p

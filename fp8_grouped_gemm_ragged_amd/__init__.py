@@ -254,8 +254,8 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
         wop = OP_FWD_FUSED if fused else OP_FWD
     else:
         wop = OP_DLHS_FUSED if fused else OP_DLHS
-    _check(lib.gmm_workspace_size(wop, ctypes.byref(op), ctypes.byref(op), M, K_or_N, n_out, 1,
-                                  ctypes.byref(ws_n)), "gmm_workspace_size")
+    _check(lib.gmm_workspace_size(wop, ctypes.byref(op), ctypes.byref(op), M, K_or_N, n_out,
+                                  G, ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, a.device)
     odt_code = OUT_F32 if odt == torch.float32 else OUT_BF16
     if group_offset is None:

@@ -156,6 +156,18 @@ size_t quant_once_bytes(int64_t M, int64_t Kc) { return align256((size_t)M * Kc)
 
 bool quant_once_applies(int64_t Nout) { return Nout <= 0 || (Nout + 255) / 256 >= QUANT_ONCE_MIN_TILES; }
 
+// The tail split of gmm_dlhs (partial sums of the last round's tiles) needs SPLIT_SLOTS
+// fp32 tiles of workspace.  It can occur when the call has more 256 x 256 tiles than 8
+// XCDs x SPLIT_CUS CUs take in one round and a contraction long enough for the split to
+// save SPLIT_MIN_SAVED steps (with SPLIT_MAX slices); without that workspace the call
+// runs unsplit.
+size_t split_ws_bytes(int64_t M, int64_t Kc, int64_t Nout, int32_t G) {
+  const int64_t max_tiles = ((M + 255) / 256 + G) * ((Nout + 255) / 256);
+  const int64_t nk = Kc / 128;
+  return max_tiles > SPLIT_SLOTS && nk - nk / SPLIT_MAX >= SPLIT_MIN_SAVED
+             ? SPLIT_SLOTS * SPLIT_SLOT_BYTES : 0;
+}
+
 // Shared body of gmm_fwd / gmm_dlhs: out[M, Nout] = A[M, Kc] x B.
 // The products run over the window of G groups that follows the first g_before of the
 // G_total in group_sizes; output rows outside the window are zero-filled.
@@ -194,11 +206,20 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
     if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
   const size_t ws_need = needs_dyn_ws(aop) ? dyn_ws_bytes(M) : 0;
   if (ws_need && (!workspace || workspace_bytes < ws_need)) return GMM_ERR_WORKSPACE;
+  // Workspace, in order: the dynamic scales' pass, the tail split's partial tiles (dlhs
+  // only: a forward stays bit-identical to the SwiGLU forward's product half, whose tiles
+  // pair gate and up channels differently), the quantize-once codes.  The split takes
+  // its room first, so that the sizes of both routes (GMM_OP_DLHS, GMM_OP_DLHS_FUSED)
+  // give both the same split.
+  const bool is_dlhs = std::strncmp(name, "gmm_dlhs", 8) == 0;
+  const size_t split_need = is_dlhs ? split_ws_bytes(M, Kc, Nout, G) : 0;
+  const bool split = split_need && workspace && workspace_bytes >= ws_need + split_need;
+  const size_t ws_base = ws_need + (split ? split_need : 0);
   const bool quant_once = !a_fp8 && (swiglu || quant_once_applies(Nout)) && workspace &&
-                          workspace_bytes >= ws_need + quant_once_bytes(M, Kc);
+                          workspace_bytes >= ws_base + quant_once_bytes(M, Kc);
   // the SwiGLU epilogue exists on the fp8-A route only: a bf16 lhs is quantized once
   if (swiglu && !a_fp8 && !quant_once) return GMM_ERR_WORKSPACE;
-  const size_t ws_used = ws_need + (quant_once ? quant_once_bytes(M, Kc) : 0);
+  const size_t ws_used = ws_base + (quant_once ? quant_once_bytes(M, Kc) : 0);
   const size_t a_bytes = (size_t)M * Kc * (a_fp8 ? 1 : 2);
   const size_t esize = out_dtype == GMM_OUT_F32 ? 4 : 2;
   const size_t out_bytes = (size_t)M * (swiglu ? Nout / 2 : Nout) * (h_op ? 1 : esize);
@@ -246,6 +267,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.g_before = g_before;
   p.out_f32 = out_dtype == GMM_OUT_F32;
   p.gu = gu;
+  p.split_ws = split ? (float*)((uint8_t*)workspace + ws_need) : nullptr;
   if (h_op) {
     p.h_codes = 1 + h_op->format;
     p.h_inv = 1.0f / h_op->static_scale;  // IEEE division on the host: RNE(1/s)
@@ -257,7 +279,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.a_inv_static = sc.inv;
   bool a_codes = a_fp8;
   if (quant_once) {
-    uint8_t* codes = (uint8_t*)workspace + ws_need;
+    uint8_t* codes = (uint8_t*)workspace + ws_base;
     if (launch_quantize_rows(aop->format, (const uint16_t*)a, M, Kc, sc.blk, sc.inv, codes, st) !=
         hipSuccess)
       return GMM_ERR_HIP;
@@ -578,6 +600,7 @@ gmm_status_t gmm_workspace_size(int32_t op, const gmm_operand_t* a, const gmm_op
   if ((op == GMM_OP_FWD || op == GMM_OP_DLHS) && a->kind == GMM_OPERAND_BF16 &&
       quant_once_applies(cols_b))
     n += quant_once_bytes(rows, cols_a);
+  if (op == GMM_OP_DLHS || op == GMM_OP_DLHS_FUSED) n += split_ws_bytes(rows, cols_a, cols_b, G);
   if (op == GMM_OP_FWD_SWIGLU && a->kind == GMM_OPERAND_BF16) n += quant_once_bytes(rows, cols_a);
   if (op == GMM_OP_TGMM) {
     if (!b) return GMM_ERR_NULL;

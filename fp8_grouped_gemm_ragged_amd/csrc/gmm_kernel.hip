@@ -16,6 +16,9 @@
 //     are remapped to give each XCD a contiguous range of tiles, ordered in bands of 8
 //     M-tiles sweeping the N-tiles: the 32 concurrent tiles of one XCD share A rows and
 //     B columns in that XCD's L2;
+//   * tail split (with its workspace): when an XCD's last round of tiles is partly
+//     empty, those tiles are cut along the contraction into slices run by the idle CUs,
+//     and gmm_split_fixup adds the fp32 partial sums in slice order;
 //   * K-loop over 128-byte contraction steps with two LDS stages (2 x 64 KB).  Every
 //     operand is prefetched two steps ahead into registers with range-checked 16-byte
 //     buffer loads (rows past the group end read as zero) and stored into the swizzled
@@ -84,31 +87,177 @@ __device__ inline bool tile_coord(int L, int total_mt, int n_ntiles, int G, int6
   return tc.row0 < tc.row_end;
 }
 
+// The tail split.  Each XCD works through its range of the tile order in rounds of
+// SPLIT_CUS tiles (its CUs).  When at least one round is full and the last one is not,
+// the last round's tiles are cut along the contraction into s slices each (s = the most
+// that fit the round, at most SPLIT_MAX, at least 2 steps per slice), one workgroup per
+// slice: the CUs that would idle through the last round share its work instead.  Only
+// when that shortens the round by SPLIT_MIN_SAVED steps or more.  Slices
+// store fp32 partial sums, and gmm_split_fixup adds them in slice order and finishes
+// the tiles.  The split depends on the shapes and group sizes only, never on the
+// device, so every call of a shape gives the same bits.
+struct XcdSplit {
+  int lo, len;    // the XCD's range of the tile order
+  int full;       // tiles in whole rounds (run uncut)
+  int tail, s;    // tiles in the last round and slices per tile (s = 1: no split)
+};
+
+__device__ inline XcdSplit xcd_split(int total, int xcd, int nk, bool split) {
+  XcdSplit x;
+  const int q = total >> 3, r = total & 7;
+  x.lo = xcd * q + min(xcd, r);
+  x.len = q + (xcd < r ? 1 : 0);
+  x.full = x.len;
+  x.tail = 0;
+  x.s = 1;
+  if (split && x.len > SPLIT_CUS && x.len % SPLIT_CUS != 0) {
+    const int tail = x.len % SPLIT_CUS;
+    const int s = min(min(SPLIT_CUS / tail, SPLIT_MAX), nk / 2);
+    if (s >= 2 && nk - nk / s >= SPLIT_MIN_SAVED) {
+      x.full = x.len - tail;
+      x.tail = tail;
+      x.s = s;
+    }
+  }
+  return x;
+}
+
+// The contraction slice [kb, ke) (of nk steps) of slice `slice` out of s.
+__device__ inline void slice_steps(int slice, int s, int nk, int& kb, int& ke) {
+  kb = slice * nk / s;
+  ke = (slice + 1) * nk / s;
+}
+
 // Expert-tile scheduler of the one-tile-per-workgroup kernel.  Returns false for a
-// workgroup without a tile.  The two LDS arrays alias the stage buffers: they are dead
-// once the tile is known.
+// workgroup without work.  Otherwise tc is its tile, [kb, ke) its contraction steps and
+// slot the partial-sum slot it stores (-1: the whole contraction, finished here).  The
+// two LDS arrays alias the stage buffers: they are dead once the work is known.
 __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int g_before, int G,
-                                     int64_t M, int n_ntiles, int* s_tile_cum, int* s_row_off,
-                                     TileCoord& tc) {
+                                     int64_t M, int n_ntiles, int nk, bool split,
+                                     int* s_tile_cum, int* s_row_off, TileCoord& tc, int& kb,
+                                     int& ke, int& slot) {
   group_prefix(gs, g_before, G, M, s_tile_cum, s_row_off);
   __syncthreads();
   const int total_mt = s_tile_cum[G];
   const int total = total_mt * n_ntiles;
-  const int wg = blockIdx.x;
-  bool ok = wg < total;
-  if (ok) {
-    // XCD-aware remap: workgroups of XCD x = wg % 8 take a contiguous range of tiles.
-    const int xcd = wg & 7, j = wg >> 3, q = total >> 3, r = total & 7;
-    ok = tile_coord(xcd * q + min(xcd, r) + j, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
+  // XCD-aware remap: workgroups of XCD x = wg % 8 take a contiguous range of tiles
+  const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
+  const XcdSplit x = xcd_split(total, xcd, nk, split);
+  bool ok = false;
+  kb = 0;
+  ke = nk;
+  slot = -1;
+  if (j < x.full) {
+    ok = tile_coord(x.lo + j, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
+  } else if (j - x.full < x.tail * x.s) {
+    const int t = j - x.full;
+    ok = tile_coord(x.lo + x.full + t / x.s, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
+    slice_steps(t % x.s, x.s, nk, kb, ke);
+    slot = xcd * SPLIT_CUS + t;
   }
   __syncthreads();  // the scheduler arrays alias stage memory
-  // every lane computed the same tile: make that visible to the compiler, so the buffer
+  // every lane computed the same work: make that visible to the compiler, so the buffer
   // resources built from it live in scalar registers
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);
   tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
   tc.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
   tc.n0 = __builtin_amdgcn_readfirstlane(tc.n0);
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  ke = __builtin_amdgcn_readfirstlane(ke);
+  slot = __builtin_amdgcn_readfirstlane(slot);
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
+}
+
+// Thread t's epilogue scales of a tile: row row0 + t and column n0 + t (SW: columns
+// 0..127 are the gate channels c0.., 128..255 the up channels I + c0..).
+template <bool SW>
+__device__ __forceinline__ void tile_scales(const GemmParams& p, const TileCoord& tc, int tid, float& sa_t,
+                                   float& sb_t) {
+  const int m = max(min(tc.row0 + tid, tc.row_end - 1), 0);
+  sa_t = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
+  const int c0 = tc.n0 >> 1;
+  const int n = SW ? (tid < 128 ? c0 + tid : (p.Nout >> 1) + c0 + tid - 128)
+                   : min(tc.n0 + tid, p.Nout - 1);
+  sb_t = p.b_scale[(int64_t)tc.g * p.Nout + n];
+}
+
+// Epilogue of a 256 x 256 tile: out = RNE((acc * s_A(m)) * s_B(n)), rows inside the group
+// and columns inside N only.  lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) +
+// 4*(lane/32) + r%4].  The scales come from LDS (a global load issued here would also
+// wait for every store issued before it: the vector-memory counter retires in order).
+// bf16: each wave puts its 128 x 128 sub-tile into its own 32 KB of LDS (`wl`, [row][256
+// B], 16-byte chunk c of row r at c ^ (r & 15)), then stores whole rows, 16 lanes per row
+// and 16 bytes per lane: every store instruction writes 8 full 128-byte lines instead of
+// 16-byte pieces of 32 rows.  Nothing else may touch wl meanwhile.
+__device__ __forceinline__ void store_tile(const GemmParams& p, const TileCoord& tc, v16f (&acc)[4][4],
+                                  const float* s_sa, const float* s_sb, uint8_t* wl) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1, frow = lane & 31, fhalf = lane >> 5;
+  float sa[4];
+  v4f sb[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sa[i] = s_sa[wr * 128 + i * 32 + frow];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      sb[j][r4] = *reinterpret_cast<const v4f*>(s_sb + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf);
+  if (!p.out_f32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + frow;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
+          v2u v;
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
+          const int chunk = (4 * j + r4) ^ (row & 15);
+          *reinterpret_cast<v2u*>(wl + row * 256 + chunk * 16 + fhalf * 8) = v;
+        }
+      }
+    }
+    // this wave's LDS writes are done before its own reads (no other wave touches wl)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bool cols_ok = tc.n0 + wc * 128 < p.Nout;  // N is a multiple of 128
+    const int c = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int row = q * 4 + (lane >> 4);
+      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 256 + ((c ^ (row & 15)) << 4));
+      const int m = tc.row0 + wr * 128 + row;
+      if (cols_ok && m < tc.row_end)
+        *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.Nout + tc.n0 + wc * 128 + c * 8) = v;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = tc.row0 + wr * 128 + i * 32 + frow;
+    if (m >= tc.row_end) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = tc.n0 + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf;
+        if (n >= p.Nout) continue;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
+        v4f v = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<v4f*>((float*)p.out + (int64_t)m * p.Nout + n) = v;
+      }
+    }
+  }
+}
+
+// A partial-sum slot: one 256 x 256 fp32 tile, [row][column].
+__device__ inline float* split_slot(const GemmParams& p, int slot) {
+  return p.split_ws + (size_t)slot * (BM * BN);
 }
 
 // SwiGLU epilogue of a gate|up tile.  The product values x = (acc * s_A(m)) * s_B(n) are
@@ -283,15 +432,17 @@ void gmm_kernel(GemmParams p) {
   static_assert(2 * (MAX_GROUPS + 1) * sizeof(int) <= A_TILE, "scheduler arrays fit a tile");
 
   const int n_ntiles = SW ? (p.Nout >> 1) / 128 : (p.Nout + BN - 1) / BN;
+  const int Kc = p.Kc;
+  const int nk = Kc / BK;
   TileCoord tc;
-  if (!schedule_tile(p.group_sizes, p.g_before, p.G, p.M, n_ntiles, s_tile_cum, s_row_off, tc))
+  int kb, ke, slot;  // contraction steps [kb, ke); slot >= 0: a slice of a split tile
+  if (!schedule_tile(p.group_sizes, p.g_before, p.G, p.M, n_ntiles, nk, !SW && p.split_ws,
+                     s_tile_cum, s_row_off, tc, kb, ke, slot))
     return;
   const int c0 = SW ? (tc.n0 >> 1) : 0;  // SW: first channel pair of the tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int Kc = p.Kc;
-  const int nk = Kc / BK;
 
   // ---- operand resources (range-checked) ----
   constexpr int AES = A_FP8 ? 1 : 2;  // bytes per A element
@@ -494,23 +645,16 @@ void gmm_kernel(GemmParams p) {
     stage_barrier();
   };
 
-  // ---- prologue: the tile's scales, step 0 into stage 0, step 1 into registers ----
+  // ---- prologue: the tile's scales, step kb into stage 0, step kb + 1 into registers ----
   // The epilogue scales are loaded first (thread t: row row0 + t, column n0 + t) and put
   // into LDS once they land, so the epilogue reads them there instead of waiting for
   // global loads after the last step.
-  // (SW: columns 0..127 are the gate channels c0.., 128..255 the up channels I + c0..)
-  float sa_t, sb_t;
-  {
-    const int m = max(min(tc.row0 + tid, tc.row_end - 1), 0);
-    sa_t = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
-    const int n = SW ? (tid < 128 ? c0 + tid : (p.Nout >> 1) + c0 + tid - 128)
-                     : min(tc.n0 + tid, p.Nout - 1);
-    sb_t = p.b_scale[(int64_t)tc.g * p.Nout + n];
-  }
+  float sa_t = 1.0f, sb_t = 1.0f;  // (a slice of a split tile stores unscaled sums)
+  if (slot < 0) tile_scales<SW>(p, tc, tid, sa_t, sb_t);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { load_a_piece(0, i); load_bk_piece(0, i); }
-  load_b_block(0, 0);
-  load_b_block(0, 1);
+  for (int i = 0; i < 8; ++i) { load_a_piece(kb, i); load_bk_piece(kb, i); }
+  load_b_block(kb, 0);
+  load_b_block(kb, 1);
   s_sa[tid] = sa_t;
   s_sb[tid] = sb_t;
 #pragma unroll
@@ -518,94 +662,101 @@ void gmm_kernel(GemmParams p) {
   store_b_block(sB0, 0);
   store_b_block(sB0, 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { load_a_piece(1, i); load_bk_piece(1, i); }
-  load_b_block(1, 0);
-  load_b_block(1, 1);
+  for (int i = 0; i < 8; ++i) { load_a_piece(kb + 1, i); load_bk_piece(kb + 1, i); }
+  load_b_block(kb + 1, 0);
+  load_b_block(kb + 1, 1);
   stage_barrier();
 
   // two steps per trip so that every LDS access names a fixed stage object; past the
   // last step the loads read zeros or in-range bytes that are never used
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
+  int kt = kb;
+  for (; kt + 1 < ke; kt += 2) {
     step(kt, sA0, sB0, sA1, sB1);
     step(kt + 1, sA1, sB1, sA0, sB0);
   }
-  if (kt < nk) step(kt, sA0, sB0, sA1, sB1);
+  if (kt < ke) step(kt, sA0, sB0, sA1, sB1);
 
   if constexpr (SW) {
     swiglu_epilogue(p, tc, c0, wr, wc, acc, sA0, sB0, sA1, sB1, s_sa, s_sb);
-    return;
+  } else {
+    // A slice of a split tile stores its fp32 partial sums unscaled (its LDS scales are
+    // 1) as a plain [256][256] tile in its slot, for gmm_split_fixup to finish.  The
+    // last step ended with a workgroup barrier after every wave's last LDS access, so
+    // all stage memory is free: 32 KB per wave.
+    GemmParams q = p;
+    TileCoord t = tc;
+    if (slot >= 0) {
+      q.out = split_slot(p, slot);
+      q.Nout = BN;
+      q.out_f32 = 1;
+      t.row0 = 0;
+      t.row_end = BM;
+      t.n0 = 0;
+    }
+    store_tile(q, t, acc, s_sa, s_sb, wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1);
   }
+}
 
-  // ---- epilogue ----
-  // lane holds out[m = base_m + lane%32][n = base_n + 8*(r/4) + 4*(lane/32) + r%4].
-  // The scales come from LDS, filled in the prologue (a global load issued here would
-  // also wait for every store issued before it: the vector-memory counter retires in
-  // order).  Columns past N only ever scale values that are not stored.
-  float sa[4];
-  v4f sb[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sa[i] = s_sa[wr * 128 + i * 32 + frow];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      sb[j][r4] = *reinterpret_cast<const v4f*>(s_sb + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf);
-  if (!p.out_f32) {
-    // bf16: each wave puts its 128 x 128 sub-tile into its own 32 KB of LDS ([row][256 B],
-    // 16-byte chunk c of row r at c ^ (r & 15)), then stores whole rows, 16 lanes per row
-    // and 16 bytes per lane: every store instruction writes 8 full 128-byte lines instead
-    // of 16-byte pieces of 32 rows.  The last step ended with a workgroup barrier after
-    // every wave's last LDS access, so the stage memory is free.
-    uint8_t* const wl = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = i * 32 + frow;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
-          v2u v;
-          v.x = pack_bf16x2(o[0], o[1]);
-          v.y = pack_bf16x2(o[2], o[3]);
-          const int chunk = (4 * j + r4) ^ (row & 15);
-          *reinterpret_cast<v2u*>(wl + row * 256 + chunk * 16 + fhalf * 8) = v;
-        }
-      }
-    }
-    // this wave's LDS writes are done before its own reads (no other wave touches wl)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const bool cols_ok = tc.n0 + wc * 128 < p.Nout;  // N is a multiple of 128
-    const int c = lane & 15;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const int row = q * 4 + (lane >> 4);
-      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 256 + ((c ^ (row & 15)) << 4));
-      const int m = tc.row0 + wr * 128 + row;
-      if (cols_ok && m < tc.row_end)
-        *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.Nout + tc.n0 + wc * 128 + c * 8) = v;
-    }
+// Finishes the tiles that the tail split cut into slices.  Workgroup (xcd, t, part) takes
+// rows 32 part .. 32 part + 31 of tile t of that XCD's last round: it recomputes the split
+// from group_sizes exactly as gmm_kernel did, adds the slices' partial sums in slice
+// order, and applies the epilogue's arithmetic (RNE((sum * s_A(m)) * s_B(n)), rows of the
+// group and columns inside N only), element by element: thread (r, c) takes 8 consecutive
+// columns 8c.. of rows r, r + 8, .., so that every load and store is a contiguous run.
+constexpr int FIX_PARTS = BM / 32;
+
+__global__ __launch_bounds__(NT) void gmm_split_fixup_kernel(GemmParams p) {
+  __shared__ int s_tile_cum[MAX_GROUPS + 1];
+  __shared__ int s_row_off[MAX_GROUPS + 1];
+  const int n_ntiles = (p.Nout + BN - 1) / BN;
+  const int nk = p.Kc / BK;
+  group_prefix(p.group_sizes, p.g_before, p.G, p.M, s_tile_cum, s_row_off);
+  __syncthreads();
+  const int total_mt = s_tile_cum[p.G];
+  const int part = blockIdx.x % FIX_PARTS, tx = blockIdx.x / FIX_PARTS;
+  const int xcd = tx & 7, t = tx >> 3;
+  const XcdSplit x = xcd_split(total_mt * n_ntiles, xcd, nk, true);
+  if (__builtin_amdgcn_readfirstlane((int)(t < x.tail)) == 0) return;
+  TileCoord tc;
+  if (!tile_coord(x.lo + x.full + t, total_mt, n_ntiles, p.G, p.M, s_tile_cum, s_row_off, tc))
     return;
-  }
+  const int tid = threadIdx.x, c = tid & 31;
+  const int n = tc.n0 + 8 * c;
+  if (n >= p.Nout) return;
+  v4f sb[2];
+  sb[0] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + n);
+  sb[1] = *reinterpret_cast<const v4f*>(p.b_scale + (int64_t)tc.g * p.Nout + n + 4);
+  const int slot0 = xcd * SPLIT_CUS + t * x.s;
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = part * 32 + rr * 8 + (tid >> 5);  // row of the tile
+    const int m = tc.row0 + row;
+    if (m >= tc.row_end) break;
+    float v[8];
+    for (int k = 0; k < x.s; ++k) {
+      const float* const src = split_slot(p, slot0 + k) + row * BN + 8 * c;
+      const v4f lo = *reinterpret_cast<const v4f*>(src);
+      const v4f hi = *reinterpret_cast<const v4f*>(src + 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = tc.row0 + wr * 128 + i * 32 + frow;
-    if (m >= tc.row_end) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = tc.n0 + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf;
-        if (n >= p.Nout) continue;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = __fmul_rn(__fmul_rn(acc[i][j][4 * r4 + e], sa[i]), sb[j][r4][e]);
-        v4f v = {o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<v4f*>((float*)p.out + (int64_t)m * p.Nout + n) = v;
+      for (int e = 0; e < 4; ++e) {
+        v[e] = k == 0 ? lo[e] : __fadd_rn(v[e], lo[e]);
+        v[4 + e] = k == 0 ? hi[e] : __fadd_rn(v[4 + e], hi[e]);
       }
+    }
+    const float sa = p.a_scale_blk ? p.a_scale_blk[m / BLOCK_ROWS] : p.a_scale_static;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = __fmul_rn(__fmul_rn(v[e], sa), sb[e >> 2][e & 3]);
+    if (p.out_f32) {
+      float* const dst = (float*)p.out + (int64_t)m * p.Nout + n;
+      *reinterpret_cast<v4f*>(dst) = v4f{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<v4f*>(dst + 4) = v4f{o[4], o[5], o[6], o[7]};
+    } else {
+      v4u w;
+      w.x = pack_bf16x2(o[0], o[1]);
+      w.y = pack_bf16x2(o[2], o[3]);
+      w.z = pack_bf16x2(o[4], o[5]);
+      w.w = pack_bf16x2(o[6], o[7]);
+      *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.Nout + n) = w;
     }
   }
 }
@@ -650,10 +801,16 @@ hipError_t launch_one(const GemmParams& p, hipStream_t st) {
   // upper bound on M-tiles: sum ceil(m_g/BM) <= ceil(M/BM) + G
   const int64_t max_mt = (p.M + BM - 1) / BM + p.G;
   const int64_t n_nt = (p.Nout + BN - 1) / BN;
-  const int64_t grid = max_mt * n_nt;
-  if (grid == 0 || p.M == 0) return hipSuccess;
+  const int64_t tiles = max_mt * n_nt;
+  if (tiles == 0 || p.M == 0) return hipSuccess;
+  // with the tail split, each XCD's slices of its last round may reach SPLIT_CUS - 1
+  // workgroups past the end of its range
+  const int64_t grid = tiles + (p.split_ws ? SPLIT_SLOTS : 0);
   hipLaunchKernelGGL((gmm_kernel<A_FMT, B_FMT, A_FP8, B_TRANS>), dim3((unsigned)grid), dim3(NT),
                      0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.split_ws) return e;
+  hipLaunchKernelGGL(gmm_split_fixup_kernel, dim3(SPLIT_SLOTS * FIX_PARTS), dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 

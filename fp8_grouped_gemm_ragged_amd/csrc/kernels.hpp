@@ -34,7 +34,19 @@ struct GemmParams {
   // h as fp8 codes (1 + format; 0: h in the output dtype) under a static scale's inverse
   int32_t h_codes;
   float h_inv;
+  // workspace of SPLIT_SLOTS partial tiles (the tail split of gmm_kernel), or null: no split
+  float* split_ws;
 };
+
+// The tail split of the grouped GEMM: CUs per XCD that one round of tiles fills, the most
+// slices per tile, and the partial-sum slots (one 256 x 256 fp32 tile each) it can use.
+constexpr int SPLIT_CUS = 32;
+constexpr int SPLIT_MAX = 8;
+// a tile is cut only when that saves its CU at least this many 128-deep steps: below it,
+// the partial sums' stores and the fixup pass cost about what the cut saves
+constexpr int SPLIT_MIN_SAVED = 48;
+constexpr int SPLIT_SLOTS = 8 * SPLIT_CUS;
+constexpr size_t SPLIT_SLOT_BYTES = size_t(256) * 256 * 4;
 
 // tgmm: out[g] = A_g^T [Kout, m] x B_g [m, Nout], contraction over the rows of group g.
 struct TgmmParams {

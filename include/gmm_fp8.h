@@ -166,9 +166,9 @@ typedef enum gmm_op {
  *              gmm_workspace_size(GMM_OP_FWD, ...) bytes, a bf16 lhs feeding 4 or more
  *              256-column output tiles is quantized once into the workspace and the
  *              product reads the codes; with at least gmm_workspace_size(
- *              GMM_OP_FWD_FUSED, ...) bytes (0 unless the call computes dynamic block
- *              scales; then NULL is allowed) every workgroup quantizes its lhs tile in
- *              registers.  Both routes produce the same codes and the same outputs.
+ *              GMM_OP_FWD_FUSED, ...) bytes every workgroup quantizes its lhs tile in
+ *              registers (0 bytes unless the call computes dynamic block scales; then
+ *              NULL is allowed).  Both routes produce the same codes and outputs.
  * Merged gate|up: pass rhs = concat(W0, W1) along N with concatenated scales; one call
  * produces [gate | up] ("FP8 Megablox for batch split", Description (2)).
  */
@@ -211,6 +211,16 @@ gmm_status_t gmm_fwd_noalloc(const gmm_operand_t* lhs_op, int32_t rhs_format, in
  *              channel k: rhs_scales f32 [G, K].
  * dlhs         [M, K] bf16 or f32.
  * workspace    as gmm_fwd's (GMM_OP_DLHS / GMM_OP_DLHS_FUSED; output tiles of 256 k).
+ *              Both sizes include, for calls of more than 256 output tiles of 256 x 256
+ *              and at least 6912 contraction columns, the 64 MiB of the tail split: when
+ *              the last round of tiles on the GPU's 8 x 32 CUs is partly empty, its
+ *              tiles are cut along the contraction, run by the CUs that would idle,
+ *              and their fp32 partial sums added in slice order (only where that saves
+ *              48 or more 128-deep steps per tile).  The split takes its room first
+ *              (so both sizes give the same split), a bf16 grad's codes what is left; a
+ *              smaller workspace runs the call unsplit.  The split depends on the shapes,
+ *              group sizes and workspace only; it reorders the fp32 additions of the
+ *              tiles it cuts.
  */
 gmm_status_t gmm_dlhs(const gmm_operand_t* grad_op, int32_t rhs_format, int32_t rhs_layout,
                       int32_t out_dtype, int64_t M, int64_t K, int64_t N, int32_t G,

@@ -312,3 +312,22 @@ def test_folded_quantizer_validation():
     assert fold(cs=None) == 1 and fold(codes=None) == 1
     assert fold(ws=None) == 5 and fold(wsb=8) == 5
     assert fold(codes=1) == 9 and fold(sc=4) == 9 and fold(ws=2) == 9
+
+
+def test_split_workspace_for_dlhs_only():
+    """gmm_dlhs's workspace holds the tail split's 256 partial tiles (64 MiB) once a call can
+    have more than 256 output tiles and a contraction of 54 steps of 128 or more (a cut
+    into 8 slices then saves 48 steps); gmm_fwd's never does."""
+    M, G, C = 4352, 4, 54 * 128
+    fwd = g.gmm_workspace_size(g.OP_FWD, "e4m3", "dynamic", M, C, 4096, a_kind=g.KIND_FP8,
+                               groups=G)
+    dl = g.gmm_workspace_size(g.OP_DLHS, "e5m2", "dynamic", M, C, 4096, a_kind=g.KIND_FP8,
+                              groups=G)
+    dlf = g.gmm_workspace_size(g.OP_DLHS_FUSED, "e5m2", "dynamic", M, C, 4096, groups=G)
+    assert fwd == 0 and dl == 256 * 256 * 256 * 4
+    assert dlf == dl + g.gmm_workspace_size(g.OP_QUANTIZE, "e5m2", "dynamic", M, C)
+    # too few tiles (one round) or too short a contraction: no split
+    assert g.gmm_workspace_size(g.OP_DLHS, "e5m2", "dynamic", 1000, C, 4096,
+                                a_kind=g.KIND_FP8, groups=G) == 0
+    assert g.gmm_workspace_size(g.OP_DLHS, "e5m2", "dynamic", M, C - 128, 4096,
+                                a_kind=g.KIND_FP8, groups=G) == 0

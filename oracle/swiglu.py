@@ -15,16 +15,24 @@ With h emitted as fp8 codes for the down projection (its lhs, quantized with a f
 per-tensor scale as in "add static LHS scaling support for GMM v2 FWD", Description), the
 codes are those of the static quantization O2/O3 applied to the float32 h:
 code = encode(clip(RNE_f32(h * RNE_f32(1/s)), -qmax, qmax)).
+With dynamic scales instead, h takes the sub-channel layout that the same page's review
+thread on the lhs docstring names ([M, num_blocks] scales): per row and block of bk
+channels, s = RNE(amax / qmax) over the block's float32 |h|, inverse 0 when s is 0 or
+1/s overflows, and the codes as above with that block's inverse (the dynamic recipe O4
+with the abs-max taken over the block).
 
 Parity: pinned by closed forms (sigmoid(ln 3) = 3/4), the identity silu(v) - silu(-v) = v,
 the large-|v| limits, and central finite differences of the forward for the backward;
 the fp8 codes of h by a brute-force nearest search over all 256 codes, saturation and
-signed zeros (``tests/test_oracle_swiglu.py``).
+signed zeros; the sub-channel codes by a hand-worked example, by agreement with the
+static codes under each block's own scale, and by all-zero blocks
+(``tests/test_oracle_swiglu.py``).
 """
 
 import numpy as np
 
-from .quant import quantize_with_inv, static_inv
+from .fp8 import encode_fp8
+from .quant import dynamic_scale_from_amax, qmax_of, quantize_with_inv, static_inv
 
 
 def silu(v):
@@ -64,3 +72,18 @@ def swiglu_fp8_ref(x, I, s, fmt):
     h = swiglu_ref(x, I)
     inv = static_inv(s)
     return quantize_with_inv(h, np.full(h.shape[0], inv, np.float32), fmt), h
+
+
+def swiglu_fp8_subchannel_ref(x, I, fmt, bk=128):
+    """x [M, 2I] (the merged product) -> (codes uint8 [M, I], scales float32 [M, I/bk],
+    h float32 [M, I]): h as in swiglu_ref, then one dynamic scale per row and block of bk
+    channels of the float32 h."""
+    h = swiglu_ref(x, I)
+    M = h.shape[0]
+    assert I % bk == 0
+    amax = np.abs(h).reshape(M, I // bk, bk).max(axis=2).astype(np.float32)
+    s, inv = dynamic_scale_from_amax(amax, fmt)
+    y = (h * np.repeat(inv, bk, axis=1)).astype(np.float32)
+    q = qmax_of(fmt)
+    codes = encode_fp8(np.minimum(np.maximum(y, -q), q), fmt)
+    return codes, s.astype(np.float32), h

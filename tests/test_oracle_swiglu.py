@@ -5,7 +5,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle.swiglu import silu, swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref
+from oracle.swiglu import (silu, swiglu_bwd_ref, swiglu_fp8_ref, swiglu_fp8_subchannel_ref,
+                           swiglu_ref)
 
 
 def test_silu_closed_forms_and_limits():
@@ -137,3 +138,46 @@ def test_fp8_band_check_accepts_the_oracle_and_catches_a_one_step_error():
         except AssertionError:
             caught += 1
     assert caught >= 40, caught
+
+
+def test_subchannel_codes_hand_worked():
+    """g = 20 makes silu(g) round to 20.0 in float32, so h = 20 u exactly for these u: the
+    first block of row 0 holds 20, 10, -5 and zeros, its scale is RNE(20 / 448) and its
+    codes are e4m3 448, 224 and -112; the second block is all zero: scale 0, codes 0."""
+    I, bk = 256, 128
+    x = np.zeros((2, 2 * I), np.float32)
+    x[0, :I] = 20.0
+    x[0, I:I + 3] = [1.0, 0.5, -0.25]
+    x[1, :I] = np.linspace(-3.0, 3.0, I)
+    x[1, I:] = np.linspace(1.0, -2.0, I)
+    codes, scales, h = swiglu_fp8_subchannel_ref(x, I, "e4m3", bk)
+    assert scales.shape == (2, 2) and scales.dtype == np.float32
+    assert h[0, 0] == 20.0 and h[0, 1] == 10.0 and h[0, 2] == -5.0
+    assert scales[0, 0] == np.float32(0.044642857142857144)  # 20 / 448 rounded to float32
+    assert list(codes[0, :4]) == [0x7E, 0x76, 0xEE, 0x00]
+    assert np.all(codes[0, 4:bk] == 0)
+    assert scales[0, 1] == 0.0 and np.all(codes[0, bk:] == 0)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_subchannel_codes_are_the_static_codes_of_each_block(fmt):
+    """Each (row, block) of the dynamic sub-channel recipe equals the static recipe (pinned
+    above by a brute-force nearest-code search) applied to that block with its own scale,
+    and that scale is the block's largest |h| over qmax, rounded to float32."""
+    rng = np.random.default_rng(21)
+    M, I, bk = 6, 384, 128
+    x = rng.normal(0.0, 2.0, (M, 2 * I)).astype(np.float32)
+    x[2, :bk] = 0.0  # a block of h = 0: scale 0
+    codes, scales, h = swiglu_fp8_subchannel_ref(x, I, fmt, bk)
+    qmax = 448.0 if fmt == "e4m3" else 57344.0
+    for r in range(M):
+        for b in range(I // bk):
+            cols = slice(b * bk, (b + 1) * bk)
+            amax = np.float32(np.abs(swiglu_ref(x[r:r + 1], I)[0, cols]).max())
+            assert scales[r, b] == np.float32(amax / np.float32(qmax))
+            if scales[r, b] == 0:
+                assert np.all(codes[r, cols] == 0) or np.all((codes[r, cols] & 0x7F) == 0)
+                continue
+            xb = np.concatenate([x[r:r + 1, :I][:, cols], x[r:r + 1, I:][:, cols]], axis=1)
+            ref, _ = swiglu_fp8_ref(xb, bk, scales[r, b], fmt)
+            assert np.array_equal(codes[r, cols], ref[0])

@@ -542,7 +542,9 @@ def swiglu_block(g, reps=10):
     """The SwiGLU steps of an MoE feed-forward block at the moe_swiglu shape (G=64,
     M=65536, hidden 2048, intermediate 1408): gmm_fwd_swiglu (merged gate|up product with
     SwiGLU in its epilogue) against gmm_fwd alone, the same with h written as static-scale
-    e4m3 codes, the down projection on those codes against the same on the bf16 h, and
+    e4m3 codes, the down projection on those codes against the same on the bf16 h, h as
+    codes with dynamic scales per row and 128 channels (against bf16 h then the
+    sub-channel quantizer) with the block-wise down projection on them, and
     gmm_swiglu_bwd, each timed with HIP events on the current stream; synthetic inputs as
     the workload's."""
     import torch
@@ -559,6 +561,7 @@ def swiglu_block(g, reps=10):
     xq, sx = g.gmm_quantize(x, "e4m3", "dynamic")
     wd = normal_bf16((G, I, K), 0.02, wl.seed * 100 + 2, "cuda")
     wdq, wds = g.gmm_quantize_rhs(wd, "e4m3", 0, "nk")
+    wdbq, wdbs = g.gmm_quantize_rhs_blockwise(wd, 128, "e4m3", "nk")
     del wd
     dh = normal_bf16((M, I), 1e-3, wl.seed * 100 + 3, "cuda")
     h = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
@@ -577,6 +580,14 @@ def swiglu_block(g, reps=10):
     down = dict(lhs_scaling="static", static_scale=s_h, out=y)
     t_down_codes = timed(lambda: g.gmm_fwd(hq, wdq, wds, gs, **down))
     t_down_bf16 = timed(lambda: g.gmm_fwd(h, wdq, wds, gs, **down))
+    # h with dynamic scales per row and 128 channels, from the epilogue, and the
+    # block-wise down projection on it; against SwiGLU to bf16 h then the quantizer
+    hs = torch.empty((M, I // 128), dtype=torch.float32, device="cuda")
+    t_fp8_dyn = timed(lambda: g.gmm_fwd_swiglu_fp8_subchannel(xq, wq, ws, gs, lhs_scales=sx,
+                                                              out=hq, h_scales=hs))
+    t_down_dyn = timed(lambda: g.gmm_fwd_blockwise(hq, hs, wdbq, wdbs, gs, 128, out=y))
+    t_unfused_dyn = timed(lambda: (g.gmm_fwd_swiglu(xq, wq, ws, gs, lhs_scales=sx, out=h),
+                                   g.gmm_quantize_subchannel(h, 128)))
     g.gmm_fwd(xq, wq, ws, gs, lhs_scales=sx, out=gu)
     t_bwd = timed(lambda: g.gmm_swiglu_bwd(dh, gu, out=d_gu))
     flop = 2.0 * M * K * 2 * I
@@ -589,12 +600,15 @@ def swiglu_block(g, reps=10):
         "fwd_swiglu_fp8_h_ms": round(t_fp8, 4),
         "down_on_h_codes_ms": round(t_down_codes, 4),
         "down_on_bf16_h_ms": round(t_down_bf16, 4),
+        "fwd_swiglu_fp8_h_subchannel_ms": round(t_fp8_dyn, 4),
+        "fwd_swiglu_bf16_h_then_quantize_subchannel_ms": round(t_unfused_dyn, 4),
+        "down_blockwise_on_subchannel_h_ms": round(t_down_dyn, 4),
         "swiglu_bwd": {"ms": round(t_bwd, 4), "GB/s": round(bwd_bytes / t_bwd / 1e6, 1),
                        "frac_hbm": round(bwd_bytes / t_bwd / 1e6 / HBM_PEAK_GBS, 4)},
         "note": "fwd_swiglu writes h [M, I] only; the unfused path would add a bf16 [M, 2I] "
                 "write and read around an elementwise SwiGLU",
     }
-    del x, xq, wq, ws, wdq, wds, dh, h, hq, y, gu, d_gu
+    del x, xq, wq, ws, wdq, wds, wdbq, wdbs, dh, h, hq, hs, y, gu, d_gu
     torch.cuda.empty_cache()
     return res
 

@@ -18,7 +18,8 @@ import os
 
 __all__ = [
     "load", "library_path", "GmmError", "gmm_fwd", "gmm_fwd_noalloc", "gmm_dlhs", "tgmm_drhs", "gmm_quantize",
-    "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8", "gmm_swiglu_bwd",
+    "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8",
+    "gmm_fwd_swiglu_fp8_subchannel", "gmm_swiglu_bwd",
     "gmm_permute", "gmm_unpermute", "gmm_fwd_local", "gmm_dlhs_local", "tgmm_drhs_local",
     "gmm_fwd_blockwise", "gmm_quantize_subchannel", "gmm_quantize_rhs_blockwise",
     "gmm_quantize_folded",
@@ -70,6 +71,8 @@ _SIGNATURES = {
     "tgmm_drhs": [_OPP, _OPP, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_fwd_swiglu": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "gmm_fwd_swiglu_fp8": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _OPP, _P, _P, _SZ, _P],
+    "gmm_fwd_swiglu_fp8_subchannel": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P,
+                                      _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
     "gmm_permute_workspace_size": [_I64, _I32, _I32],
     "gmm_fwd_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
@@ -461,8 +464,31 @@ def gmm_fwd_swiglu_fp8(lhs, rhs, rhs_scales, group_sizes, h_scale, *, h_format="
                        (h_format, h_scale))
 
 
+def gmm_fwd_swiglu_fp8_subchannel(lhs, rhs, rhs_scales, group_sizes, *, h_format="e4m3",
+                                  lhs_format="e4m3", lhs_scaling="dynamic", static_scale=None,
+                                  lhs_scales=None, gu_dtype=None, out=None, h_scales=None,
+                                  gu=False, return_scales=False):
+    """gmm_fwd_swiglu with h returned as uint8 fp8 codes [M, I] under dynamic scales f32
+    [M, I/128], one per row and block of 128 channels (s = RNE(amax / qmax) over the
+    block's float32 |h|).  Returns (h_codes, h_scales[, gu][, lhs_scales]).  The pair
+    feeds gmm_fwd_blockwise(h_codes, h_scales, ..., bk=128) as its sub-channel lhs."""
+    import torch
+
+    I = rhs.shape[1] // 2
+    if h_scales is None:
+        h_scales = torch.empty((lhs.shape[0], I // 128), dtype=torch.float32, device=lhs.device)
+    else:
+        _need(h_scales, torch.float32, "h_scales", 2)
+        _shape(h_scales, (lhs.shape[0], I // 128), "h_scales")
+    res = _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling,
+                      static_scale, lhs_scales, gu_dtype, out, gu, return_scales,
+                      (h_format, None), h_scales)
+    res = res if isinstance(res, tuple) else (res,)
+    return (res[0], h_scales) + res[1:]
+
+
 def _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling, static_scale,
-                lhs_scales, out_dtype, out, gu, return_scales, h_fp8):
+                lhs_scales, out_dtype, out, gu, return_scales, h_fp8, h_scales=None):
     import torch
 
     lib = load()
@@ -501,7 +527,11 @@ def _swiglu_fwd(lhs, rhs, rhs_scales, group_sizes, lhs_format, lhs_scaling, stat
     odt_code = OUT_F32 if odt == torch.float32 else OUT_BF16
     head = (ctypes.byref(op), E4M3, RHS_NK, odt_code, M, K, I, G, _ptr(lhs), _ptr(lhs_scales),
             _ptr(rhs), _ptr(rhs_scales), _ptr(group_sizes), _ptr(x))
-    if h_fp8:
+    if h_scales is not None:
+        _check(lib.gmm_fwd_swiglu_fp8_subchannel(*head, _FMT[h_fp8[0]], _ptr(out), _ptr(h_scales),
+                                                 _ptr(ws), ws_n.value, _stream()),
+               "gmm_fwd_swiglu_fp8_subchannel")
+    elif h_fp8:
         hop = _operand(KIND_FP8, h_fp8[0], "static", h_fp8[1])
         _check(lib.gmm_fwd_swiglu_fp8(*head, ctypes.byref(hop), _ptr(out), _ptr(ws), ws_n.value,
                                       _stream()), "gmm_fwd_swiglu_fp8")

@@ -178,14 +178,20 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                           const uint8_t* rhs, const float* rhs_scales,
                           const int32_t* group_sizes, void* out, void* workspace,
                           size_t workspace_bytes, hipStream_t st, bool swiglu = false,
-                          void* gu = nullptr, const gmm_operand_t* h_op = nullptr) {
+                          void* gu = nullptr, const gmm_operand_t* h_op = nullptr,
+                          float* h_scales = nullptr) {
   gmm_status_t s = check_operand(aop);
   if (s != GMM_OK) return s;
-  // SwiGLU with fp8 h: codes under a validated static per-tensor scale
+  // SwiGLU with fp8 h: codes under a validated static per-tensor scale, or (h_scales)
+  // under dynamic scales per row and 128-channel block
   if (h_op) {
     if ((s = check_operand(h_op)) != GMM_OK) return s;
-    if (h_op->kind != GMM_OPERAND_FP8 || h_op->scaling != GMM_SCALE_STATIC) return GMM_ERR_RECIPE;
+    if (h_op->kind != GMM_OPERAND_FP8 ||
+        (h_op->scaling != GMM_SCALE_STATIC && h_op->scaling != GMM_SCALE_DYNAMIC))
+      return GMM_ERR_RECIPE;
+    if (h_op->scaling == GMM_SCALE_DYNAMIC && M > 0 && !h_scales) return GMM_ERR_NULL;
   }
+  if (!h_op || h_op->scaling != GMM_SCALE_DYNAMIC) h_scales = nullptr;
   if (rhs_format != GMM_FP8_E4M3) return GMM_ERR_RECIPE;  // weights are e4m3 codes
   if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
   if ((s = check_shape(M, Kc, Nout, G_total)) != GMM_OK) return s;
@@ -241,6 +247,16 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                    overlaps(gu, gu_bytes, a_scales, as_bytes)))
     return GMM_ERR_ALIAS;
   if (gu && !aligned16(gu)) return GMM_ERR_ALIGN;
+  const size_t hs_bytes = h_scales ? (size_t)M * (Nout / 256) * 4 : 0;  // [M, I / 128]
+  if (hs_bytes && (overlaps(h_scales, hs_bytes, a, a_bytes) || overlaps(h_scales, hs_bytes, rhs, b_bytes) ||
+                   overlaps(h_scales, hs_bytes, rhs_scales, (size_t)G * Nout * 4) ||
+                   overlaps(h_scales, hs_bytes, group_sizes, (size_t)G_total * 4) ||
+                   overlaps(h_scales, hs_bytes, out, out_bytes) ||
+                   (gu_bytes && overlaps(h_scales, hs_bytes, gu, gu_bytes)) ||
+                   overlaps(h_scales, hs_bytes, workspace, ws_used) ||
+                   overlaps(h_scales, hs_bytes, a_scales, as_bytes)))
+    return GMM_ERR_ALIAS;
+  if (h_scales && !aligned16(h_scales)) return GMM_ERR_ALIGN;
   if ((s = check_group_sizes(group_sizes, G_total, M, st)) != GMM_OK) return s;
   trace(name, M, Kc, Nout, G);
   if (M == 0) return GMM_OK;
@@ -270,7 +286,9 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.split_ws = split ? (float*)((uint8_t*)workspace + ws_need) : nullptr;
   if (h_op) {
     p.h_codes = 1 + h_op->format;
-    p.h_inv = 1.0f / h_op->static_scale;  // IEEE division on the host: RNE(1/s)
+    // the static scale's inverse: IEEE division on the host, RNE(1/s)
+    p.h_inv = h_scales ? 0.0f : 1.0f / h_op->static_scale;
+    p.h_scales = h_scales;
   }
   Scaling sc;
   if ((s = resolve_scaling(aop, a, M, Kc, a_scales, workspace, st, sc)) != GMM_OK) return s;
@@ -402,6 +420,24 @@ gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int
                       group_sizes, h, workspace, workspace_bytes, (hipStream_t)stream, true, gu);
 }
 
+gmm_status_t gmm_fwd_swiglu_fp8_subchannel(const gmm_operand_t* lhs_op, int32_t rhs_format,
+                                           int32_t rhs_layout, int32_t gu_dtype, int64_t M,
+                                           int64_t K, int64_t I, int32_t G, const void* lhs,
+                                           float* lhs_scales, const uint8_t* rhs,
+                                           const float* rhs_scales, const int32_t* group_sizes,
+                                           void* gu, int32_t h_format, uint8_t* h_codes,
+                                           float* h_scales, void* workspace,
+                                           size_t workspace_bytes, gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  if (h_format != GMM_FP8_E4M3 && h_format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
+  const gmm_operand_t h_op{GMM_OPERAND_FP8, h_format, GMM_SCALE_DYNAMIC, 0.0f};
+  return grouped_gemm("gmm_fwd_swiglu_fp8_subchannel", lhs_op, rhs_format,
+                      rhs_layout == GMM_RHS_KN, gu_dtype, M, K, 2 * I, G, 0, G, lhs, lhs_scales,
+                      rhs, rhs_scales, group_sizes, h_codes, workspace, workspace_bytes,
+                      (hipStream_t)stream, true, gu, &h_op, h_scales);
+}
+
 gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
                                 int32_t rhs_layout, int32_t gu_dtype, int64_t M, int64_t K,
                                 int64_t I, int32_t G, const void* lhs, float* lhs_scales,
@@ -410,6 +446,7 @@ gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
                                 uint8_t* h_codes, void* workspace, size_t workspace_bytes,
                                 gmm_stream_t stream) {
   if (!h_op) return GMM_ERR_NULL;
+  if (h_op->scaling != GMM_SCALE_STATIC) return GMM_ERR_RECIPE;  // dynamic: the _subchannel call
   if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
   if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
   return grouped_gemm("gmm_fwd_swiglu_fp8", lhs_op, rhs_format, rhs_layout == GMM_RHS_KN,

@@ -379,6 +379,24 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
       }
       continue;
     }
+    // fp8 codes of h: under the static scale's inverse, or (h_scales) under one dynamic
+    // scale per row and 128-channel block.  This tile's 128 channels are one block: the
+    // lane holds 64 of its row's values and lane ^ 32 the other 64.
+    float h_inv = p.h_inv;
+    if (codes && p.h_scales) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(hv[j][r4][e]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const float sc = __fdiv_rn(amax, p.h_codes == 1 + FMT_E4M3 ? qmax<FMT_E4M3>() : qmax<FMT_E5M2>());
+      h_inv = inv_from_scale(sc);
+      const int m = mrow + frow;
+      if (fhalf == 0 && m < tc.row_end) p.h_scales[(int64_t)m * (I / 128) + c0 / 128] = sc;
+    }
     uint8_t* const st = wl + ii * 16384;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this half's reads are done
 #pragma unroll
@@ -387,9 +405,9 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
       for (int r4 = 0; r4 < 4; ++r4) {
         const v4f h = hv[j][r4];
         if (codes) {
-          // fp8 codes of h under a static scale, the lhs of the down projection
+          // the lhs of the down projection
           const uint32_t q =
-              p.h_codes == 1 + FMT_E4M3 ? quant4<FMT_E4M3>(h, p.h_inv) : quant4<FMT_E5M2>(h, p.h_inv);
+              p.h_codes == 1 + FMT_E4M3 ? quant4<FMT_E4M3>(h, h_inv) : quant4<FMT_E5M2>(h, h_inv);
           const int byte = j * 32 + 8 * r4 + 4 * fhalf;
           *reinterpret_cast<uint32_t*>(st + frow * 128 + ((((byte >> 4) ^ frow) & 7) << 4) + (byte & 15)) = q;
         } else {

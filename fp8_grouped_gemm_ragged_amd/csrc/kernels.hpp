@@ -31,9 +31,11 @@ struct GemmParams {
   // SwiGLU epilogue (gmm_fwd_swiglu): B holds the merged [W0 | W1] channels (Nout = 2 I),
   // out is h [M, I], gu (optional) the product itself [M, 2 I]
   void* gu;
-  // h as fp8 codes (1 + format; 0: h in the output dtype) under a static scale's inverse
+  // h as fp8 codes (1 + format; 0: h in the output dtype) under a static scale's inverse,
+  // or under dynamic scales per row and 128-channel block, written to h_scales [M, I/128]
   int32_t h_codes;
   float h_inv;
+  float* h_scales;
   // workspace of SPLIT_SLOTS partial tiles (the tail split of gmm_kernel), or null: no split
   float* split_ws;
 };

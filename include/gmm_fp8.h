@@ -13,8 +13,9 @@
  *
  * and the steps around them in the same MoE layer:
  *
- *   gmm_fwd_swiglu / gmm_fwd_swiglu_fp8 / gmm_swiglu_bwd   SwiGLU of the merged
- *              gate|up product in the forward's epilogue (h in bf16/f32 or fp8 codes),
+ *   gmm_fwd_swiglu / gmm_fwd_swiglu_fp8 / gmm_fwd_swiglu_fp8_subchannel /
+ *   gmm_swiglu_bwd   SwiGLU of the merged gate|up product in the forward's epilogue (h in
+ *              bf16/f32, or fp8 codes under a static or per-row-and-block dynamic scale),
  *              and its backward
  *   gmm_fwd_local / gmm_dlhs_local / tgmm_drhs_local   the products over a window of
  *              local experts (group_offset)
@@ -303,8 +304,7 @@ gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int
  * h_codes      uint8 [M, I]; rows outside every group are not written.
  * gu, gu_dtype the optional product [M, 2I] as in gmm_fwd_swiglu (gu_dtype bf16 or f32).
  * Everything else, the workspace (GMM_OP_FWD_SWIGLU) included, is as gmm_fwd_swiglu's.
- * A dynamic per-block scale for h would need the abs-max over all I channels of 128
- * rows, which spans many output tiles: that route stores h in bf16 and runs gmm_quantize.
+ * h_op->scaling must be GMM_SCALE_STATIC; dynamic scales are gmm_fwd_swiglu_fp8_subchannel's.
  */
 gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
                                 int32_t rhs_layout, int32_t gu_dtype, int64_t M, int64_t K,
@@ -313,6 +313,34 @@ gmm_status_t gmm_fwd_swiglu_fp8(const gmm_operand_t* lhs_op, int32_t rhs_format,
                                 const int32_t* group_sizes, void* gu, const gmm_operand_t* h_op,
                                 uint8_t* h_codes, void* workspace, size_t workspace_bytes,
                                 gmm_stream_t stream);
+
+/*
+ * gmm_fwd_swiglu_fp8_subchannel - gmm_fwd_swiglu with h written as fp8 codes under dynamic
+ * scales, one per row and block of 128 channels ("add static LHS scaling support for GMM
+ * v2 FWD", review thread on the lhs docstring: lhs scales of shape [M, num_blocks];
+ * "FP8 Megablox for batch split", Description (1)):
+ *
+ *   h_scales[m, b] = RNE_f32(max_{c in block b} |h[m, c]| / qmax),
+ *   h_codes[m, c]  = fp8(clamp(RNE_f32(h[m, c] * inv), -qmax, qmax)),
+ *   inv = 0 if h_scales[m, b] is 0 or its inverse overflows, else RNE_f32(1 / h_scales[m, b]),
+ *
+ * with h the fp32 value gmm_fwd_swiglu computes.  Each output tile of the merged product
+ * holds the 128 gate and 128 up channels of one block of h, so the block's abs-max is
+ * taken inside the tile's epilogue and h never leaves the registers in a wider type.
+ * h_format     e4m3 or e5m2 (else GMM_ERR_RECIPE).
+ * h_codes      uint8 [M, I]; h_scales f32 [M, I / 128] (NULL only when M = 0); rows
+ *              outside every group are not written.  The pair is the sub-channel lhs of
+ *              gmm_fwd_blockwise with bk = 128: the down projection on these codes.
+ * Everything else (gu, gu_dtype, workspace GMM_OP_FWD_SWIGLU) is as gmm_fwd_swiglu_fp8's.
+ */
+gmm_status_t gmm_fwd_swiglu_fp8_subchannel(const gmm_operand_t* lhs_op, int32_t rhs_format,
+                                           int32_t rhs_layout, int32_t gu_dtype, int64_t M,
+                                           int64_t K, int64_t I, int32_t G, const void* lhs,
+                                           float* lhs_scales, const uint8_t* rhs,
+                                           const float* rhs_scales, const int32_t* group_sizes,
+                                           void* gu, int32_t h_format, uint8_t* h_codes,
+                                           float* h_scales, void* workspace,
+                                           size_t workspace_bytes, gmm_stream_t stream);
 
 /*
  * gmm_swiglu_bwd - the SwiGLU backward between the down projection's dlhs and the merged

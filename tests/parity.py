@@ -150,12 +150,15 @@ def swiglu_h_bound(R, absR, K, I, mfma=True):
 
 def assert_fp8_codes_in_band(codes, h, dh, s, fmt, ref_codes, min_exact=0.95):
     """Every code lies between the codes of (h - dh) / s and (h + dh) / s (quantized as the
-    oracle does, widened by an fp32 rounding), and most equal the oracle's codes.  Returns
+    oracle does, widened by an fp32 rounding), and most equal the oracle's codes.  s is
+    one scale or one per element (a zero scale quantizes with inverse 0).  Returns
     (fraction not equal to ref_codes, fraction of elements whose band spans two codes)."""
     from oracle.fp8 import encode_fp8
     from oracle.quant import qmax_of
 
-    inv = np.float64(np.float32(1.0) / np.float32(s))
+    s32 = np.asarray(s, np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(s32 == 0, 0.0, (np.float32(1.0) / s32).astype(np.float64))
     q = qmax_of(fmt)
 
     def code_of(y):

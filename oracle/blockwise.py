@@ -24,13 +24,18 @@ lhs, a column's bk elements of one expert for the weights.
 
 The dlhs can also run on the forward's weight copy, whose per-channel scales s[g, n]
 lie on the dlhs contraction: they are folded into the gradient before it is quantized
-(``quantize_folded``), and the product then takes unit output-channel scales.
+(``quantize_folded``), and the product then takes unit output-channel scales.  With
+block-wise scales the dlhs is the same block-wise product on the transposed weight: the
+gradient gets sub-channel scales [M, N/bk] and the weight's dlhs copy one scale per
+expert, output channel k and block of bk columns n ([G, K, N/bk]).
 
 Parity: pinned by brute force with exact rationals on tiny inputs, by the one-block
 reduction to the per-channel forward, by block-constant scales factoring out, and by the
 quantizers' brute-force block abs-max; the fold by unit and power-of-two scales
 (identical codes, scales multiplied exactly) and by the folded dlhs against the float64
-definition within the quantization bound (``tests/test_oracle_blockwise.py``).
+definition within the quantization bound; the block-wise dlhs by brute force with exact
+rationals and by its one-block reduction to the per-channel dlhs
+(``tests/test_oracle_blockwise.py``).
 """
 
 import numpy as np
@@ -98,6 +103,28 @@ def gmm_fwd_blockwise_ref(a_codes, a_fmt, a_scale_kb, b_codes, b_fmt, b_scale_kb
             acc = (acc + v.astype(np.float32)).astype(np.float32)
         out[r0:r1] = acc
     return _finish(out, out_dtype)
+
+
+def quantize_rhs_blockwise_dlhs(w_bits, fmt, bk):
+    """bf16 bits [G, K, N] -> (codes [G, K, N], scales [G, K, N/bk]): the weight copy of the
+    block-wise dlhs, whose contraction is n: one dynamic scale per expert, output channel
+    k and block of bk columns n (the sub-channel recipe on the rows of w)."""
+    w = np.asarray(w_bits, np.uint16)
+    G, K, N = w.shape
+    codes, s = quantize_subchannel(w.reshape(G * K, N), fmt, bk)
+    return codes.reshape(G, K, N), s.reshape(G, K, N // bk)
+
+
+def gmm_dlhs_blockwise_ref(g_codes, g_fmt, g_scale_kb, w_codes, w_fmt, w_scale_kb, group_sizes,
+                           bk, out_dtype="f32"):
+    """dlhs[m, k] = sum_nb RNE(RNE(partial_nb[m, k] * sG[m, nb]) * sW[g, k, nb]) for m in
+    group g, partial_nb[m, k] = sum_{n in block nb} dq(grad[m, n]) dq(w[g, k, n]): the gmm
+    against the transposed weight, with scales that vary along its contraction n.
+
+    g_codes [M, N], g_scale_kb [M, N/bk]; w_codes [G, K, N], w_scale_kb [G, K, N/bk]."""
+    return gmm_fwd_blockwise_ref(g_codes, g_fmt, g_scale_kb, np.transpose(w_codes, (0, 2, 1)),
+                                 w_fmt, np.transpose(w_scale_kb, (0, 2, 1)), group_sizes, bk,
+                                 out_dtype)
 
 
 def quantize_folded(grad_bits, col_scales, group_sizes, fmt, block_rows=128):

@@ -7,9 +7,10 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle.blockwise import gmm_fwd_blockwise_ref, quantize_rhs_blockwise, quantize_subchannel
+from oracle.blockwise import (gmm_dlhs_blockwise_ref, gmm_fwd_blockwise_ref, quantize_rhs_blockwise,
+                              quantize_rhs_blockwise_dlhs, quantize_subchannel)
 from oracle.fp8 import bf16_bits_to_f32
-from oracle.gmm import gmm_fwd_ref
+from oracle.gmm import gmm_dlhs_ref, gmm_fwd_ref
 from oracle.quant import quantize_rhs_per_channel, quantize_with_inv
 from tests.test_oracle_gmm import gamma, random_codes, random_scales, tdec
 
@@ -147,3 +148,48 @@ def test_folded_dlhs_matches_the_definition():
     # e5m2 relative rounding 2^-3 per gradient element (plus its subnormal floor)
     assert np.all(np.abs(R - exact) <= absum * 2.0 ** -3 + 1e-12)
     assert np.abs(R - exact).max() < 0.1 * np.abs(exact).max()
+
+
+@pytest.mark.parametrize("bk", [4, 8])
+def test_blockwise_dlhs_brute_force(bk):
+    """dlhs[m, k] against exact rationals: the sum over n of grad[m, n] w[g, k, n], each
+    block of bk columns n scaled by sG[m, nb] sW[g, k, nb]."""
+    rng = np.random.default_rng(33)
+    M, G, K, N = 7, 3, 5, 16
+    gs = np.array([3, 0, 4], np.int32)
+    gq = random_codes(rng, (M, N), "e5m2")
+    wq = random_codes(rng, (G, K, N), "e4m3")
+    sg = random_scales(rng, (M, N // bk))
+    sw = random_scales(rng, (G, K, N // bk))
+    R = gmm_dlhs_blockwise_ref(gq, "e5m2", sg, wq, "e4m3", sw, gs, bk)
+    A, W = tdec(gq, "e5m2"), tdec(wq, "e4m3")
+    gid = np.repeat(np.arange(G), gs)
+    for m in range(M):
+        for k in range(K):
+            g = gid[m]
+            ex = Fraction(0)
+            ab = Fraction(0)
+            for nb in range(N // bk):
+                sc = Fraction(float(sg[m, nb])) * Fraction(float(sw[g, k, nb]))
+                terms = [Fraction(A[m, n]) * Fraction(W[g, k, n]) for n in range(nb * bk, (nb + 1) * bk)]
+                ex += sum(terms) * sc
+                ab += sum(abs(t) for t in terms) * sc
+            err = abs(Fraction(float(R[m, k])) - ex)
+            lim = ab * Fraction(1.01 * gamma(bk + 3 + N // bk)) + Fraction(2.0 ** -140)
+            assert err <= lim, (m, k, float(err), float(lim))
+
+
+def test_one_block_dlhs_is_the_per_channel_dlhs():
+    """With one block (bk = N) the weight's dlhs copy is the per-output-channel-k
+    quantization and the block-wise dlhs is the per-channel dlhs, bit for bit."""
+    rng = np.random.default_rng(34)
+    M, G, K, N = 300, 4, 96, 256
+    gs = np.array([100, 0, 150, 50], np.int32)
+    gb, wb = bits(rng, (M, N), 1e-3), bits(rng, (G, K, N), 0.02)
+    gq, sg = quantize_subchannel(gb, "e5m2", N)
+    wq, sw = quantize_rhs_blockwise_dlhs(wb, "e4m3", N)
+    wq2, sw2 = quantize_rhs_per_channel(wb, "e4m3", "k")
+    assert np.array_equal(wq, wq2) and np.array_equal(sw[:, :, 0], sw2)
+    R = gmm_dlhs_blockwise_ref(gq, "e5m2", sg, wq, "e4m3", sw, gs, N)
+    R2 = gmm_dlhs_ref(gq, "e5m2", sg[:, 0], wq2, "e4m3", sw2, gs)
+    assert np.array_equal(R, R2)

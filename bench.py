@@ -12,11 +12,11 @@ N=2x14336=28672, M=16384 rows = 8192 tokens x top-2, Zipf(1.1) routing):
   4. gmm_dlhs  dlhs[M, K]      = q(grad) . rhs[g]^T       (hybrid: the codes of step 3)
   5. tgmm_drhs drhs[G, K, N]   = q(lhs)_g^T . q(grad)_g   (the codes of steps 1 and 3)
 
-value = 3 * 2*M*K*N / step time (TFLOP/s), with steps 4 and 5 (independent of each other)
-on two HIP streams so that tgmm fills the CUs dlhs leaves idle in its short last round of
-tiles.  The per-op figures come from the same step on one stream, every call timed with HIP
-events on the stream it runs on.  The slowest product is reported against the dense FP8
-MFMA peak (5.0 PFLOP/s).
+value = 3 * 2*M*K*N / step time (TFLOP/s), the step on one HIP stream; the per-op figures
+come from the same steps, every call timed with HIP events on that stream, and each
+product gets the workspace gmm_workspace_size reports (for dlhs: its tail split).  The
+slowest product is reported against the dense FP8 MFMA peak (5.0 PFLOP/s).  The step with
+steps 4 and 5 (independent of each other) on two streams is timed beside it.
 
 Also reported (each timed with HIP events on the current stream):
   * protocol: per op and for the whole step, the median and the minimum of `--reps` runs
@@ -105,7 +105,7 @@ def parse():
     p.add_argument("--reps", type=int, default=50, help="timed runs per op for median / min")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-overlap", action="store_true",
-                   help="time the step on one stream only (ms_per_step is then the serial step)")
+                   help="skip the extra timing of the step with dlhs and tgmm on two streams")
     p.add_argument("--no-extras", action="store_true",
                    help="only the timed steps: no protocol, static/dynamic, FFN chain or blocks")
     p.add_argument("--no-clock", action="store_true", help="skip the GFX clock reading")
@@ -662,9 +662,10 @@ def blockwise_block(g, reps=10):
     """The forward with block-wise scales at the Mixtral gate|up shape (G=8, M=16384,
     K=4096, N=28672): gmm_fwd_blockwise on sub-channel e4m3 lhs codes ([M, K/bk] scales)
     and block-scaled e4m3 weights ([G, K/bk, N] scales) for bk 128 and 512, against the
-    fp8 MFMA peak; the lhs quantization timed apart; and the one-weight-copy dlhs (the
+    fp8 MFMA peak; the lhs quantization timed apart; the one-weight-copy dlhs (the
     gradient folded with the forward's scales, then the fp8-A dlhs on the forward's
-    codes).  HIP events on the current stream."""
+    codes); and the dlhs with block-wise scales (bk 512).  HIP events on the current
+    stream."""
     import torch
 
     from synth.workloads import WORKLOADS, normal_bf16
@@ -702,7 +703,15 @@ def blockwise_block(g, reps=10):
                                   rhs_layout="kn", out=dl))
     res["folded_dlhs"] = {"quantize_ms": round(tq, 4), "dlhs_ms": round(td, 4),
                           "dlhs_TFLOP/s": round(flop / td / 1e9, 1)}
-    del x, w, out, grad, wq, ws, ones, dl, codes, s
+    del wq, ws, ones, codes, s
+    # the dlhs with block-wise scales along its contraction n (bk 512): sub-channel grad
+    # codes and the weight's dlhs copy with one scale per expert, channel k and n-block
+    gq, gsc = g.gmm_quantize_subchannel(grad, 512, "e5m2")
+    wq, ws = g.gmm_quantize_rhs_blockwise_dlhs(w, 512)
+    tb = timed(lambda: g.gmm_dlhs_blockwise(gq, gsc, wq, ws, gs, 512, out=dl))
+    res["dlhs_bk512"] = {"ms": round(tb, 4), "TFLOP/s": round(flop / tb / 1e9, 1),
+                         "frac_peak": round(flop / tb / 1e9 / FP8_PEAK_TFLOPS, 4)}
+    del x, w, out, grad, wq, ws, dl, gq, gsc
     torch.cuda.empty_cache()
     return res
 
@@ -786,8 +795,11 @@ def main():
     per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
            for j, n in enumerate(names)}
     ms_serial = wall * 1000.0 / args.steps
-    # The same steps with dlhs and tgmm on two streams: value and ms_per_step.
+    # The step on one stream gives value and ms_per_step.  The same steps with dlhs and tgmm
+    # on two streams are timed beside it (context: with its tail split, dlhs no longer
+    # leaves CUs idle for tgmm to take).
     ms_step = ms_serial
+    ms_two = None
     if not args.no_overlap:
         s2 = torch.cuda.Stream()
         forks = [(torch.cuda.Event(), torch.cuda.Event()) for _ in range(args.steps)]
@@ -798,7 +810,7 @@ def main():
         for i in range(args.steps):
             step.run_overlapped(stream, s2, *forks[i])
         torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
+        ms_two = (time.perf_counter() - t0) * 1000.0 / args.steps
     # the GFX clock the chip holds under this load (FP8 MFMA work draws enough power to
     # keep it well below the 2.4 GHz the published peak assumes)
     clock_mhz = None if args.no_clock else gfx_clock_during(lambda: [step.run(s) for _ in range(8)])
@@ -827,11 +839,9 @@ def main():
                    "rhs": "e4m3 per-channel", "out": "bf16",
                    "step": "lhs quantize + fwd + grad quantize + hybrid dlhs + tgmm; each tensor "
                            "quantized once, its codes used by every product"},
-        "serial_ms_per_step": round(ms_serial, 4),
-        "overlap": None if args.no_overlap else
-                   "the backward products dlhs and tgmm run on two HIP streams (ms_per_step, "
-                   "value); ops, prep_ms and roofline come from the same step run on one stream "
-                   "(serial_ms_per_step)",
+        "schedule": "one HIP stream: value, ms_per_step, ops, prep_ms and roofline come from "
+                    "the same timed steps",
+        "two_stream_ms_per_step": None if ms_two is None else round(ms_two, 4),
         "ops": ops,
         "prep_ms": {"lhs_quantize": round(per["quantize_lhs"], 4),
                     "grad_quantize": round(per["quantize_grad"], 4)},

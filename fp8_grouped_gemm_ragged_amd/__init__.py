@@ -21,7 +21,8 @@ __all__ = [
     "gmm_dynamic_scales", "gmm_fwd_swiglu", "gmm_fwd_swiglu_fp8",
     "gmm_fwd_swiglu_fp8_subchannel", "gmm_swiglu_bwd",
     "gmm_permute", "gmm_unpermute", "gmm_fwd_local", "gmm_dlhs_local", "tgmm_drhs_local",
-    "gmm_fwd_blockwise", "gmm_quantize_subchannel", "gmm_quantize_rhs_blockwise",
+    "gmm_fwd_blockwise", "gmm_dlhs_blockwise", "gmm_quantize_subchannel",
+    "gmm_quantize_rhs_blockwise", "gmm_quantize_rhs_blockwise_dlhs",
     "gmm_quantize_folded",
     "gmm_quantize_rhs", "gmm_static_scale_from_bound", "gmm_workspace_size",
     "gmm_status_string", "gmm_version", "E4M3", "E5M2", "STATIC", "DYNAMIC", "BLOCK_ROWS",
@@ -76,6 +77,7 @@ _SIGNATURES = {
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
     "gmm_permute_workspace_size": [_I64, _I32, _I32],
     "gmm_fwd_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
+    "gmm_dlhs_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
     "gmm_quantize_subchannel": [_I32, _I64, _I64, _I64, _P, _P, _P, _P],
     "gmm_quantize_rhs_blockwise": [_I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _P],
     "gmm_quantize_folded": [_I32, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -716,6 +718,51 @@ def gmm_quantize_rhs_blockwise(w, bk=128, fmt="e4m3", layout="nk"):
     _check(lib.gmm_quantize_rhs_blockwise(_FMT[fmt], lay, G, K, N, int(bk), _ptr(w), _ptr(codes),
                                           _ptr(scales), _stream()), "gmm_quantize_rhs_blockwise")
     return codes, scales
+
+
+def gmm_quantize_rhs_blockwise_dlhs(w, bk=128, fmt="e4m3"):
+    """bf16 w [G, K, N] -> (uint8 codes [G, K, N], f32 scales [G, K, N / bk]): the weight copy
+    of gmm_dlhs_blockwise, one dynamic scale per expert, output channel k and block of bk
+    columns n (gmm_quantize_subchannel of w viewed as [G * K, N])."""
+    import torch
+
+    _need(w, torch.bfloat16, "w", 3)
+    G, K, N = w.shape
+    codes, scales = gmm_quantize_subchannel(w.reshape(G * K, N), bk, fmt)
+    return codes.view(G, K, N), scales.view(G, K, N // bk)
+
+
+def gmm_dlhs_blockwise(grad, grad_scales, rhs, rhs_scales, group_sizes, bk=128, *,
+                       grad_format="e5m2", out_dtype=None, out=None):
+    """lhs gradient with block-wise scales along its contraction: grad uint8 codes [M, N]
+    with grad_scales f32 [M, N / bk], rhs uint8 codes [G, K, N] with rhs_scales f32
+    [G, K, N / bk] (gmm_quantize_rhs_blockwise_dlhs); returns dlhs [M, K]."""
+    import torch
+
+    lib = load()
+    _need(grad, torch.uint8, "grad", 2)
+    _need(rhs, torch.uint8, "rhs", 3)
+    _need(grad_scales, torch.float32, "grad_scales", 2)
+    _need(rhs_scales, torch.float32, "rhs_scales", 3)
+    _need(group_sizes, torch.int32, "group_sizes", 1)
+    M, N = grad.shape
+    G, K = rhs.shape[0], rhs.shape[1]
+    if rhs.shape[2] != N or N % bk:
+        raise ValueError("rhs must be [G, K, N] codes matching the grad width, N a multiple of bk")
+    _shape(grad_scales, (M, N // bk), "grad_scales")
+    _shape(rhs_scales, (G, K, N // bk), "rhs_scales")
+    _group_sizes(group_sizes, G)
+    odt = torch.float32 if out_dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, K), dtype=odt, device=grad.device)
+    else:
+        _need(out, odt, "out", 2)
+        _shape(out, (M, K), "out")
+    _check(lib.gmm_dlhs_blockwise(_FMT[grad_format], OUT_F32 if odt == torch.float32 else OUT_BF16,
+                                  M, K, N, G, bk, _ptr(grad), _ptr(grad_scales), _ptr(rhs),
+                                  _ptr(rhs_scales), _ptr(group_sizes), _ptr(out), _stream()),
+           "gmm_dlhs_blockwise")
+    return out
 
 
 def gmm_fwd_blockwise(lhs, lhs_scales, rhs, rhs_scales, group_sizes, bk=128, *,

@@ -337,6 +337,52 @@ gmm_status_t noalloc_scratch(void** out) {
   return GMM_OK;
 }
 
+// Shared body of gmm_fwd_blockwise and gmm_dlhs_blockwise: out[M, N] from lhs codes
+// [M, K] (scales [M, K / bk]) and rhs codes [G, N, K] (contraction contiguous) with scales
+// [G, K / bk, N] or, n_major, [G, N, K / bk].
+gmm_status_t blockwise_gemm(const char* name, int32_t lhs_format, int32_t out_dtype, int64_t M,
+                            int64_t K, int64_t N, int32_t G, int64_t bk, const uint8_t* lhs,
+                            const float* lhs_scales, const uint8_t* rhs, const float* rhs_scales,
+                            bool n_major, const int32_t* group_sizes, void* out,
+                            hipStream_t stream) {
+  if (lhs_format != GMM_FP8_E4M3 && lhs_format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
+  if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
+  gmm_status_t s = check_shape(M, K, N, G);
+  if (s != GMM_OK) return s;
+  if (bk < 128 || bk % 128 || K % bk) return GMM_ERR_SHAPE;
+  if ((M / 128 + 1 + G) * (N / 128) >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
+  if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
+  if (M > 0 && (!lhs || !lhs_scales || !out)) return GMM_ERR_NULL;
+  for (const void* ptr : {(const void*)lhs, (const void*)lhs_scales, (const void*)rhs,
+                          (const void*)rhs_scales, (const void*)group_sizes, (const void*)out})
+    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
+  const int64_t nkb = K / bk;
+  const size_t ob = (size_t)M * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
+  if (overlaps(out, ob, lhs, (size_t)M * K) || overlaps(out, ob, lhs_scales, (size_t)M * nkb * 4) ||
+      overlaps(out, ob, rhs, (size_t)G * K * N) ||
+      overlaps(out, ob, rhs_scales, (size_t)G * nkb * N * 4) ||
+      overlaps(out, ob, group_sizes, (size_t)G * 4))
+    return GMM_ERR_ALIAS;
+  if ((s = check_group_sizes(group_sizes, G, M, stream)) != GMM_OK) return s;
+  trace(name, M, K, N, G);
+  if (M == 0) return GMM_OK;
+  BsParams p{};
+  p.a = lhs;
+  p.b = rhs;
+  p.a_scale = lhs_scales;
+  p.b_scale = rhs_scales;
+  p.group_sizes = group_sizes;
+  p.out = out;
+  p.M = M;
+  p.K = (int32_t)K;
+  p.N = (int32_t)N;
+  p.G = G;
+  p.bk = (int32_t)bk;
+  p.out_f32 = out_dtype == GMM_OUT_F32;
+  p.b_scale_nmajor = n_major;
+  return launch_gemm_blockwise(lhs_format, p, stream) == hipSuccess ? GMM_OK : GMM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -788,42 +834,21 @@ gmm_status_t gmm_fwd_blockwise(int32_t lhs_format, int32_t out_dtype, int64_t M,
                                const float* lhs_scales, const uint8_t* rhs,
                                const float* rhs_scales, const int32_t* group_sizes, void* out,
                                gmm_stream_t stream) {
-  if (lhs_format != GMM_FP8_E4M3 && lhs_format != GMM_FP8_E5M2) return GMM_ERR_RECIPE;
-  if (out_dtype != GMM_OUT_BF16 && out_dtype != GMM_OUT_F32) return GMM_ERR_RECIPE;
-  gmm_status_t s = check_shape(M, K, N, G);
-  if (s != GMM_OK) return s;
-  if (bk < 128 || bk % 128 || K % bk) return GMM_ERR_SHAPE;
-  if ((M / 128 + 1 + G) * (N / 128) >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
-  if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
-  if (M > 0 && (!lhs || !lhs_scales || !out)) return GMM_ERR_NULL;
-  for (const void* ptr : {(const void*)lhs, (const void*)lhs_scales, (const void*)rhs,
-                          (const void*)rhs_scales, (const void*)group_sizes, (const void*)out})
-    if (ptr && !aligned16(ptr)) return GMM_ERR_ALIGN;
-  const int64_t nkb = K / bk;
-  const size_t ob = (size_t)M * N * (out_dtype == GMM_OUT_F32 ? 4 : 2);
-  if (overlaps(out, ob, lhs, (size_t)M * K) || overlaps(out, ob, lhs_scales, (size_t)M * nkb * 4) ||
-      overlaps(out, ob, rhs, (size_t)G * K * N) ||
-      overlaps(out, ob, rhs_scales, (size_t)G * nkb * N * 4) ||
-      overlaps(out, ob, group_sizes, (size_t)G * 4))
-    return GMM_ERR_ALIAS;
-  if ((s = check_group_sizes(group_sizes, G, M, (hipStream_t)stream)) != GMM_OK) return s;
-  trace("gmm_fwd_blockwise", M, K, N, G);
-  if (M == 0) return GMM_OK;
-  BsParams p{};
-  p.a = lhs;
-  p.b = rhs;
-  p.a_scale = lhs_scales;
-  p.b_scale = rhs_scales;
-  p.group_sizes = group_sizes;
-  p.out = out;
-  p.M = M;
-  p.K = (int32_t)K;
-  p.N = (int32_t)N;
-  p.G = G;
-  p.bk = (int32_t)bk;
-  p.out_f32 = out_dtype == GMM_OUT_F32;
-  return launch_gemm_blockwise(lhs_format, p, (hipStream_t)stream) == hipSuccess ? GMM_OK
-                                                                                 : GMM_ERR_HIP;
+  return blockwise_gemm("gmm_fwd_blockwise", lhs_format, out_dtype, M, K, N, G, bk, lhs,
+                        lhs_scales, rhs, rhs_scales, false, group_sizes, out,
+                        (hipStream_t)stream);
+}
+
+gmm_status_t gmm_dlhs_blockwise(int32_t grad_format, int32_t out_dtype, int64_t M, int64_t K,
+                                int64_t N, int32_t G, int64_t bk, const uint8_t* grad,
+                                const float* grad_scales, const uint8_t* rhs,
+                                const float* rhs_scales, const int32_t* group_sizes, void* dlhs,
+                                gmm_stream_t stream) {
+  // the block-wise product with contraction N and output K: rhs [G, K, N] is already
+  // contraction-contiguous, its scales [G, K, N / bk] per output channel
+  return blockwise_gemm("gmm_dlhs_blockwise", grad_format, out_dtype, M, N, K, G, bk, grad,
+                        grad_scales, rhs, rhs_scales, true, group_sizes, dlhs,
+                        (hipStream_t)stream);
 }
 
 gmm_status_t gmm_static_scale_from_bound(float lo, float hi, int32_t format, float* scale) {

@@ -137,6 +137,8 @@ void gmm_bs_kernel(BsParams p) {
   for (int i = 0; i < 2; ++i)
     sa_row[i] = (int64_t)max(min(tc.row0 + 64 * wr + 32 * i + frow, tc.row_end - 1), 0) * nkb;
   const int64_t sb_base = (int64_t)tc.g * nkb * p.N + tc.n0 + 64 * wc + 4 * fhalf;
+  // b_scale_nmajor: scale of (column n, block kb) at (g N + n) nkb + kb
+  const int64_t sbt_base = ((int64_t)tc.g * p.N + tc.n0 + 64 * wc + 4 * fhalf) * nkb;
 
   // a block's scales are loaded at the start of its last step and used after that
   // step's MFMAs, so their latency hides behind the matrix core
@@ -148,8 +150,14 @@ void gmm_bs_kernel(BsParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        if (!p.b_scale_nmajor) {
+          sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sb[j][r4][e] = p.b_scale[sbt_base + (32 * j + 8 * r4 + e) * nkb + kb];
+        }
+      }
   };
   // total += partial * RNE(sA * sB): one fused multiply-add per value; the partial
   // restarts from zero

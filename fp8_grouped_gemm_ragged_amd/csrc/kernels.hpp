@@ -83,6 +83,9 @@ struct BsParams {
   int64_t M;
   int32_t K, N, G, bk;
   int32_t out_f32;
+  // b_scale layout: 0 = [G, K / bk, N] (the forward's), 1 = [G, N, K / bk] (per output
+  // channel, as the block-wise dlhs's weight copy comes out of the sub-channel quantizer)
+  int32_t b_scale_nmajor;
 };
 
 // plan words: off, cnt, seg (G + 1), wide, final scale per group, one any-wide flag

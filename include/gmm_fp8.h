@@ -19,9 +19,9 @@
  *              and its backward
  *   gmm_fwd_local / gmm_dlhs_local / tgmm_drhs_local   the products over a window of
  *              local experts (group_offset)
- *   gmm_fwd_blockwise, gmm_quantize_subchannel, gmm_quantize_rhs_blockwise,
- *   gmm_quantize_folded   block-wise weight scales, sub-channel lhs scales, and the
- *              dlhs on the forward's weight copy
+ *   gmm_fwd_blockwise, gmm_dlhs_blockwise, gmm_quantize_subchannel,
+ *   gmm_quantize_rhs_blockwise, gmm_quantize_folded   block-wise weight scales,
+ *              sub-channel lhs scales, and the dlhs on the forward's weight copy
  *   gmm_permute / gmm_unpermute   token routing: the sort of top-k choices by expert
  *              and the weighted combine back
  *
@@ -382,6 +382,32 @@ gmm_status_t gmm_fwd_blockwise(int32_t lhs_format, int32_t out_dtype, int64_t M,
                                const float* lhs_scales, const uint8_t* rhs,
                                const float* rhs_scales, const int32_t* group_sizes, void* out,
                                gmm_stream_t stream);
+
+/*
+ * gmm_dlhs_blockwise - the lhs gradient with block-wise scales along its contraction n
+ * (the dlhs is the gmm against the transposed weight: "Support quantization for tokamax
+ * gmm v2", the dlhs call with transpose_rhs flipped, and its review thread on 3-D,
+ * block-wise weight scales):
+ *
+ *   dlhs[m, k] = RNE_out( sum_nb partial_nb[m, k] * grad_scales[m, nb] * rhs_scales[g, k, nb] ),
+ *   partial_nb[m, k] = sum_{n in block nb} grad[m, n] * rhs[g, k, n]   (fp32),
+ *
+ * summed as gmm_fwd_blockwise sums (from +0 in increasing nb, one fused multiply-add per
+ * block by RNE(grad_scale * rhs_scale)).
+ * grad         fp8 codes [M, N] (grad_format), grad_scales f32 [M, N / bk]
+ *              (gmm_quantize_subchannel of the bf16 gradient).
+ * rhs          e4m3 codes [G, K, N] (the weight's own layout, GMM_RHS_KN), rhs_scales f32
+ *              [G, K, N / bk]: one scale per expert, output channel k and block of bk
+ *              columns n, which is gmm_quantize_subchannel of the bf16 weight viewed as
+ *              [G * K, N].
+ * dlhs         [M, K] bf16 or f32; rows outside every group are not written.
+ * bk           a multiple of 128 dividing N; M, K, N, G as for gmm_dlhs.  No workspace.
+ */
+gmm_status_t gmm_dlhs_blockwise(int32_t grad_format, int32_t out_dtype, int64_t M, int64_t K,
+                                int64_t N, int32_t G, int64_t bk, const uint8_t* grad,
+                                const float* grad_scales, const uint8_t* rhs,
+                                const float* rhs_scales, const int32_t* group_sizes, void* dlhs,
+                                gmm_stream_t stream);
 
 /*
  * gmm_quantize_folded - the gradient of the dlhs that runs on the forward's weight copy

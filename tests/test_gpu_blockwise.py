@@ -156,3 +156,39 @@ def test_folded_dlhs(lib, sizes):
     R = gmm_dlhs_ref(c_ref, "e5m2", row_scales(s_ref, M), wq_ref, "e4m3",
                      np.ones((G, K), np.float32), sizes)
     assert group_rel_err(to_np(out), R, group_row_ranges(sizes)) <= TOL
+
+
+@pytest.mark.parametrize("bk", [128, 256])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dlhs_blockwise_ragged(lib, bk, out_dtype):
+    """gmm_dlhs_blockwise: the gradient's sub-channel codes and the weight's dlhs copy
+    (one scale per expert, output channel k and n-block) byte for byte, then the product
+    against the oracle's block-wise dlhs (f32: per-group metric and elementwise bound)."""
+    from oracle.blockwise import gmm_dlhs_blockwise_ref, quantize_rhs_blockwise_dlhs
+    from tests.parity import assert_rounding_bound, magnitudes
+
+    sizes = [0, 260, 1, 0, 129, 300]
+    G, M, K, N = len(sizes), sum(sizes), 384, 1024
+    gr, grb = gen((M, N), 1e-3, 721)
+    w, wb = gen((G, K, N), 0.02, 722)
+    codes, s = lib.gmm_quantize_subchannel(gr, bk, "e5m2")
+    wq, ws = lib.gmm_quantize_rhs_blockwise_dlhs(w, bk)
+    out = lib.gmm_dlhs_blockwise(codes, s, wq, ws, gs_tensor(sizes), bk, out_dtype=out_dtype)
+    sync()
+    c_ref, s_ref = quantize_subchannel(grb, "e5m2", bk)
+    wc_ref, ws_ref = quantize_rhs_blockwise_dlhs(wb, "e4m3", bk)
+    assert np.array_equal(to_np(codes), c_ref)
+    assert np.array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(to_np(wq), wc_ref)
+    assert np.array_equal(to_np(ws).view(np.uint32), ws_ref.view(np.uint32))
+    R = gmm_dlhs_blockwise_ref(c_ref, "e5m2", s_ref, wc_ref, "e4m3", ws_ref, sizes, bk)
+    ranges = group_row_ranges(sizes)
+    if out_dtype == torch.float32:
+        err = group_rel_err(to_np(out), R, ranges)
+        print(f"dlhs bk {bk}: max group relative error {err:.3e}")
+        assert err <= TOL, err
+        absR = gmm_dlhs_blockwise_ref(magnitudes(c_ref), "e5m2", s_ref, magnitudes(wc_ref),
+                                      "e4m3", ws_ref, sizes, bk)
+        assert_rounding_bound(to_np(out), R, absR, N)
+    else:
+        assert_bf16_close(to_np(out), R, ranges)

@@ -403,7 +403,8 @@ void tgmm_main_kernel(TgmmCodesParams p) {
     v4u sa[4], sb[4];  // staging registers of step s + 2
     // Step x's loads into the staging registers: block c_lo + x's rows of the group;
     // past the group, or in a block whose scale product is zero, everything reads zero.
-    auto gload = [&](int x, bool live, int q) {
+    // which: 0 = the lhs chunk only, 1 = the grad chunk only
+    auto gload = [&](int x, bool live, int q, int which) {
       int lo, hi;
       block_rows(c_lo + x, off, cnt, lo, hi);
       live = live && x < nblk;
@@ -412,16 +413,30 @@ void tgmm_main_kernel(TgmmCodesParams p) {
       const __amdgpu_buffer_rsrc_t rb =
           make_rsrc(p.b + (int64_t)lo * N + n0, live ? (uint32_t)((hi - lo) * N - n0) : 0u);
       const int skip = lo - (c_lo + x) * BLOCK_ROWS;  // rows of the block before the group
-      sa[q] = buf_load16(ra, a_off[q] - (uint32_t)(skip * K));
-      sb[q] = buf_load16(rb, b_off[q] - (uint32_t)(skip * N));
+      if (which == 0) sa[q] = buf_load16(ra, a_off[q] - (uint32_t)(skip * K));
+      else sb[q] = buf_load16(rb, b_off[q] - (uint32_t)(skip * N));
     };
-    // whether block c_lo + x adds anything (read one step before its loads are issued)
-    auto live_of = [&](int x) -> bool {
-      return p.scprod[c_lo + min(x, nblk - 1)] != 0.0f;
+    // The steps' scalars, 64 steps at a time: lane i holds the ratio of the move into
+    // block w0 + i (see gratio) and a ballot mask whether that block adds anything, so a
+    // step reads them with readlane and a shift, not with a load it would wait for.
+    int w0 = 0;
+    float wratio = 1.0f;
+    uint64_t wlive = 0;
+    auto load_window = [&](int base) {
+      w0 = base;
+      const int x = base + lane;
+      wratio = gratio[min(x, nblk)];
+      wlive = __ballot(x < nblk && p.scprod[c_lo + min(x, nblk - 1)] != 0.0f);
+      // wait here, once per window, so that no step waits on these loads (vmcnt(0))
+      __builtin_amdgcn_s_waitcnt(0x0f70);
     };
-    auto lwrite = [&](uint8_t* at, uint8_t* bt, int q) {
-      *reinterpret_cast<v4u*>(at + q * 32 * ROWB + wofs) = sa[q];
-      *reinterpret_cast<v4u*>(bt + q * 32 * ROWB + wofs) = sb[q];
+    auto ratio_at = [&](int x) {  // w0 <= x < w0 + 64
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wratio), x - w0));
+    };
+    auto live_of = [&](int x) -> bool { return ((wlive >> (x - w0)) & 1u) != 0u; };
+    auto lwrite = [&](uint8_t* at, uint8_t* bt, int q, int which) {
+      if (which == 0) *reinterpret_cast<v4u*>(at + q * 32 * ROWB + wofs) = sa[q];
+      else *reinterpret_cast<v4u*>(bt + q * 32 * ROWB + wofs) = sb[q];
     };
     // fragment addresses: A operand rows wr 128 + 32 i (k), B operand rows wc 64 + 32 j (n)
     uint32_t fa[4], fb[2];
@@ -439,8 +454,9 @@ void tgmm_main_kernel(TgmmCodesParams p) {
     // Step s on stage (at, bt); (an, bn) is the next stage.  Unit u issues MFMA
     // (ks = u / 8, i = (u / 2) % 4, j = u % 2) on acc[2 i + j], with the A fragment of
     // linear index L = 4 ks + i in register slot L % 2.  Alongside:
-    //   * units 0..3: staging chunk q = u (step s + 1) is written to the next stage and
-    //     refilled with step s + 2's loads;
+    //   * units 0..7: staging chunk u / 2 of the lhs (u even) or the grad (u odd), step
+    //     s + 1, is written to the next stage and refilled with step s + 2's load (one
+    //     chunk per unit keeps the LDS writes and the loads from bunching up);
     //   * after odd unit u <= 11, A fragment L = (u + 3) / 2 is read into the slot unit u
     //     has just finished with (two MFMAs before its first use); the ks = 1 B
     //     fragments are read after unit 3;
@@ -467,11 +483,12 @@ void tgmm_main_kernel(TgmmCodesParams p) {
           af[0] = fragA(an, 0, 0);
         }
         acc[2 * i + j] = mfma32x32x64<B_FMT, A_FMT>(ks == 0 ? bf0[j] : bf1[j], af[i & 1], acc[2 * i + j]);
-        if (u < 4) {
-          // the chunk leaves its registers before they are reloaded (one staging set)
-          lwrite(an, bn, u);
+        if (u < 8) {
+          // the chunk leaves its registers before they are reloaded (one staging set);
+          // one chunk per unit, lhs and grad in turn
+          lwrite(an, bn, u >> 1, u & 1);
           __builtin_amdgcn_sched_barrier(0);
-          gload(s + 2, live2, u);
+          gload(s + 2, live2, u >> 1, u & 1);
         }
         if (u == 3) {
           bf1[0] = fragB(bt, 0, 1);
@@ -495,13 +512,14 @@ void tgmm_main_kernel(TgmmCodesParams p) {
 
     // prologue: step 0 into stage 0, step 1 into the staging registers, the first
     // fragments of stage 0
+    load_window(0);
     bool live0 = live_of(0), live1 = live_of(1), live2 = live_of(2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) gload(0, live0, q);
+    for (int q = 0; q < 8; ++q) gload(0, live0, q >> 1, q & 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lwrite(sA0, sB0, q);
+    for (int q = 0; q < 8; ++q) lwrite(sA0, sB0, q >> 1, q & 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) gload(1, live1, q);
+    for (int q = 0; q < 8; ++q) gload(1, live1, q >> 1, q & 1);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -509,17 +527,18 @@ void tgmm_main_kernel(TgmmCodesParams p) {
     bf0[1] = fragB(sB0, 1, 0);
     af[0] = fragA(sA0, 0, 0);
     af[1] = fragA(sA0, 1, 0);
-    float r_prev = 1.0f, r_next = gratio[min(1, nblk)];
+    float r_prev = 1.0f, r_next = ratio_at(min(1, nblk));
     int s = 0;
     for (; s + 1 < nblk; s += 2) {
+      if (s + 4 >= w0 + 64) load_window(s);  // the window holds steps s .. s + 4
       bool live3 = live_of(s + 3);
-      float r_n2 = gratio[min(s + 2, nblk)];
+      float r_n2 = ratio_at(s + 2);  // s + 2 <= nblk here
       step(s, sA0, sB0, sA1, sB1, r_prev, r_next, live2);
       r_prev = r_next;
       r_next = r_n2;
       live2 = live3;
       live3 = live_of(s + 4);
-      r_n2 = gratio[min(s + 3, nblk)];
+      r_n2 = ratio_at(min(s + 3, nblk));
       step(s + 1, sA1, sB1, sA0, sB0, r_prev, r_next, live2);
       r_prev = r_next;
       r_next = r_n2;
@@ -702,8 +721,10 @@ hipError_t launch_tgmm_fp8(const TgmmCodesParams& p, hipStream_t st) {
   hipLaunchKernelGGL((tgmm_main_kernel<A_FMT, B_FMT>), dim3((unsigned)tiles), dim3(MNT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // one workgroup per CU at most (a grid-stride loop): when no group is wide, every
+  // workgroup returns at once and one round of them costs next to nothing
   const int64_t ptiles = (int64_t)(p.Kout / PBK) * (p.Nout / PBK) * p.G;
-  hipLaunchKernelGGL((tgmm_promote_kernel<A_FMT, B_FMT>), dim3((unsigned)(ptiles < 1024 ? ptiles : 1024)),
+  hipLaunchKernelGGL((tgmm_promote_kernel<A_FMT, B_FMT>), dim3((unsigned)(ptiles < 256 ? ptiles : 256)),
                      dim3(PNT), 0, st, p);
   return hipGetLastError();
 }

@@ -76,7 +76,9 @@ __device__ inline bool bs_schedule(const int32_t* __restrict__ gs, int G, int64_
   return __builtin_amdgcn_readfirstlane((int)ok) != 0;
 }
 
-template <int A_FMT>
+// NMAJ: the weight scales are laid out [G, N, K / bk] (p.b_scale_nmajor) instead of
+// [G, K / bk, N]; a template parameter so that each instantiation holds one load path
+template <int A_FMT, bool NMAJ>
 __global__ __attribute__((amdgpu_flat_work_group_size(BS_NT, BS_NT), amdgpu_waves_per_eu(2, 2)))
 void gmm_bs_kernel(BsParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[BS_TILE];
@@ -136,9 +138,20 @@ void gmm_bs_kernel(BsParams p) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     sa_row[i] = (int64_t)max(min(tc.row0 + 64 * wr + 32 * i + frow, tc.row_end - 1), 0) * nkb;
-  const int64_t sb_base = (int64_t)tc.g * nkb * p.N + tc.n0 + 64 * wc + 4 * fhalf;
-  // b_scale_nmajor: scale of (column n, block kb) at (g N + n) nkb + kb
-  const int64_t sbt_base = ((int64_t)tc.g * p.N + tc.n0 + 64 * wc + 4 * fhalf) * nkb;
+  // NMAJ: scale of (column n, block kb) at (g N + n) nkb + kb, read through a resource
+  // over the tile's 128 columns: the lane's offset in a VGPR, the column's in an SGPR
+  // (otherwise: at (g nkb + kb) N + n, a resource from the tile's first column, the
+  // block's row offset in an SGPR)
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t sbt_lane;
+  if constexpr (NMAJ) {
+    rs = make_rsrc(p.b_scale + ((int64_t)tc.g * p.N + tc.n0) * nkb, (uint32_t)(BS_BN * nkb * 4));
+    sbt_lane = (uint32_t)((64 * wc + 4 * fhalf) * nkb) * 4u;
+  } else {
+    rs = make_rsrc(p.b_scale + (int64_t)tc.g * nkb * p.N + tc.n0,
+                   (uint32_t)((nkb * p.N - tc.n0) * 4));
+    sbt_lane = (uint32_t)(64 * wc + 4 * fhalf) * 4u;
+  }
 
   // a block's scales are loaded at the start of its last step and used after that
   // step's MFMAs, so their latency hides behind the matrix core
@@ -151,11 +164,14 @@ void gmm_bs_kernel(BsParams p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        if (!p.b_scale_nmajor) {
-          sb[j][r4] = *reinterpret_cast<const v4f*>(p.b_scale + sb_base + (int64_t)kb * p.N + 32 * j + 8 * r4);
+        if constexpr (!NMAJ) {
+          sb[j][r4] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+              rs, sbt_lane + (uint32_t)(32 * j + 8 * r4) * 4u, (uint32_t)(kb * p.N) * 4u, 0));
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sb[j][r4][e] = p.b_scale[sbt_base + (32 * j + 8 * r4 + e) * nkb + kb];
+          for (int e = 0; e < 4; ++e)
+            sb[j][r4][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rs, sbt_lane + (uint32_t)kb * 4u, (uint32_t)((32 * j + 8 * r4 + e) * nkb) * 4u, 0));
         }
       }
   };
@@ -437,12 +453,16 @@ hipError_t launch_gemm_blockwise(int a_fmt, const BsParams& p, hipStream_t st) {
   const int64_t max_mt = (p.M + BS_BM - 1) / BS_BM + p.G;
   const int64_t grid = max_mt * (p.N / BS_BN);
   if (grid == 0 || p.M == 0) return hipSuccess;
-  if (a_fmt == FMT_E4M3)
-    hipLaunchKernelGGL(gmm_bs_kernel<FMT_E4M3>, dim3((unsigned)grid), dim3(BS_NT), 0, st, p);
-  else if (a_fmt == FMT_E5M2)
-    hipLaunchKernelGGL(gmm_bs_kernel<FMT_E5M2>, dim3((unsigned)grid), dim3(BS_NT), 0, st, p);
+  const dim3 gd((unsigned)grid), bd(BS_NT);
+  if (a_fmt != FMT_E4M3 && a_fmt != FMT_E5M2) return hipErrorInvalidValue;
+  if (a_fmt == FMT_E4M3 && !p.b_scale_nmajor)
+    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, false>), gd, bd, 0, st, p);
+  else if (a_fmt == FMT_E4M3)
+    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, true>), gd, bd, 0, st, p);
+  else if (!p.b_scale_nmajor)
+    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, false>), gd, bd, 0, st, p);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, true>), gd, bd, 0, st, p);
   return hipGetLastError();
 }
 

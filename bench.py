@@ -109,6 +109,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true",
                    help="only the timed steps: no protocol, static/dynamic, FFN chain or blocks")
     p.add_argument("--no-clock", action="store_true", help="skip the GFX clock reading")
+    p.add_argument("--crossover", action="store_true",
+                   help="only the fused-vs-quantize-once table of the forward (crossover_block)")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=2048, help="at most 4096")
     p.add_argument("--copy-calibration", action="store_true",
@@ -716,6 +718,51 @@ def blockwise_block(g, reps=10):
     return res
 
 
+def crossover_block(g, reps=10):
+    """Where quantizing a bf16 lhs once beats the in-kernel ("fused") quantization: the
+    forward at a growing number of 256-column output tiles, dynamic lhs scaling, on the
+    Mixtral rows (G=8, M=16384, K=4096) and the 64-expert SwiGLU rows (G=64, M=65536,
+    K=2048).  Per width: the fused call alone (fused=True: every output tile quantizes
+    its rows in the kernel), gmm_quantize then the fp8-codes forward, and the call with
+    its full workspace (the library's own choice: quantize once from 4 tiles on).  HIP
+    events on the current stream, median of `reps`."""
+    import torch
+
+    from synth.workloads import WORKLOADS, normal_bf16
+
+    def timed(fn):
+        return float(np.median(event_times(fn, reps, warmup=3)))
+
+    res = {}
+    for name in ("mixtral_gate_up", "moe_swiglu"):
+        wl = WORKLOADS[name]
+        G, M, K = wl.G, wl.M, wl.K
+        gs = torch.tensor(wl.group_sizes(), dtype=torch.int32, device="cuda")
+        x = normal_bf16((M, K), 1.0, wl.seed * 100 + 21, "cuda")
+        rows = []
+        for tiles in (1, 2, 3, 4, 6, 8, 16):
+            N = 256 * tiles
+            w = normal_bf16((G, K, N), 0.02, wl.seed * 100 + 22, "cuda")
+            wq, ws = g.gmm_quantize_rhs(w, "e4m3", 0, "nk")
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            t_fused = timed(lambda: g.gmm_fwd(x, wq, ws, gs, fused=True, out=out))
+            t_lib = timed(lambda: g.gmm_fwd(x, wq, ws, gs, out=out))
+            codes, sc = g.gmm_quantize(x, "e4m3", "dynamic")
+            t_q = timed(lambda: g.gmm_quantize(x, "e4m3", "dynamic"))
+            t_f8 = timed(lambda: g.gmm_fwd(codes, wq, ws, gs, lhs_scaling="dynamic",
+                                           lhs_scales=sc, out=out))
+            rows.append({"tiles": tiles, "N": N, "fused_ms": round(t_fused, 4),
+                         "quantize_ms": round(t_q, 4), "fp8_ms": round(t_f8, 4),
+                         "quantize_then_fp8_ms": round(t_q + t_f8, 4),
+                         "library_ms": round(t_lib, 4),
+                         "fused_over_quantize_once": round(t_fused / (t_q + t_f8), 3)})
+            del w, wq, ws, out, codes, sc
+        res[name] = {"G": G, "M": M, "K": K, "rows": rows}
+        del x
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(step, rows, cols):
     """Time the CPU oracle on a bounded sample: the first `rows` rows (with their group
     split), all K, the first `cols` columns of the merged weight; fwd + dlhs + tgmm."""
@@ -770,6 +817,9 @@ def main():
     import fp8_grouped_gemm_ragged_amd as g
     from synth.workloads import WORKLOADS
 
+    if args.crossover:
+        print(json.dumps({"crossover_block": crossover_block(g)}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     step = Step(g, wl, seed=wl.seed * 100)
     if args.copy_calibration:

@@ -515,8 +515,10 @@ def gfx_clock_during(run, seconds=1.0):
             try:
                 m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
                 clks = m.get("current_gfxclks")
-                vals = [c for c in clks if isinstance(c, (int, float))] if isinstance(clks, list) else []
-                if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+                # entries of XCDs the table does not fill read 0 (or 0xFFFF): keep clocks
+                ok = lambda c: isinstance(c, (int, float)) and 100 <= c < 5000
+                vals = [c for c in clks if ok(c)] if isinstance(clks, list) else []
+                if not vals and ok(m.get("current_gfxclk")):
                     vals = [m["current_gfxclk"]]
                 if vals:
                     samples.append(sum(vals) / len(vals))

@@ -45,13 +45,15 @@
  * - Inputs are read-only; outputs must not overlap inputs.
  * - Errors are returned as gmm_status_t; argument validation happens before any work
  *   is enqueued, so an error return leaves every output untouched.
- * - The functions keep no global state and may be called concurrently on different
- *   streams with different buffers.
+ * - The functions keep no global state (apart from gmm_fwd_noalloc's device scratch
+ *   array, see there) and may be called concurrently on different streams with
+ *   different buffers.
  *
  * Quantization recipes
  * --------------------
- * An operand given as bf16 is quantized inside the kernel, in registers, right after
- * it is loaded:  code = fp8( clamp( RNE_f32(x * inv), -qmax, +qmax ) )  with
+ * An operand given as bf16 is quantized by the call, inside the product kernel right
+ * after it is loaded or, where the entry point says so, once into the workspace (the
+ * codes are the same bytes either way):  code = fp8( clamp( RNE_f32(x * inv), -qmax, +qmax ) )  with
  * round-to-nearest-even to fp8 (qmax = 448 for e4m3, 57344 for e5m2), and the fp32
  * product is multiplied back by the scale ("add static LHS scaling support for GMM v2
  * FWD", review thread on the lhs docstring: clip(lhs/scale), result multiplied back by

@@ -192,3 +192,44 @@ def test_dlhs_blockwise_ragged(lib, bk, out_dtype):
         assert_rounding_bound(to_np(out), R, absR, N)
     else:
         assert_bf16_close(to_np(out), R, ranges)
+
+
+def test_dlhs_blockwise_mixtral_full_size_sampled(lib):
+    """gmm_dlhs_blockwise at the Mixtral gate|up shape with bk = 512, as the benchmark
+    launches it: the gradient's sub-channel codes and the weight's dlhs copy, then the
+    product on sampled rows x sampled output channels k against the oracle (a row's grad
+    scales depend on that row only, and the dlhs copy's scales of channel k on row k of
+    each expert's weight only, so the samples quantize as in the whole)."""
+    from synth.workloads import WORKLOADS
+    from oracle.blockwise import gmm_dlhs_blockwise_ref, quantize_rhs_blockwise_dlhs
+    from tests.parity import assert_rounding_bound, magnitudes
+    from tests.test_gpu_full import sample_cols, sample_rows, sampled_sizes
+
+    wl = WORKLOADS["mixtral_gate_up"]
+    G, M, K, N, bk = wl.G, wl.M, wl.K, wl.N, 512
+    sizes = wl.group_sizes()
+    grad = normal_bf16((M, N), 1e-3, wl.seed * 100 + 13, DEV)
+    w = normal_bf16((G, K, N), 0.02, wl.seed * 100 + 12, DEV)
+    gq, gsc = lib.gmm_quantize_subchannel(grad, bk, "e5m2")
+    wq, ws = lib.gmm_quantize_rhs_blockwise_dlhs(w, bk)
+    out = lib.gmm_dlhs_blockwise(gq, gsc, wq, ws, gs_tensor(sizes), bk, out_dtype=torch.float32)
+    sync()
+    rng = np.random.default_rng(19)
+    rows = sample_rows(sizes, rng)
+    kc = sample_cols(K, rng, 40)
+    ri, ki = torch.as_tensor(rows, device=DEV), torch.as_tensor(kc, device=DEV)
+    c_ref, s_ref = quantize_subchannel(bf16_to_bits(grad[ri]), "e5m2", bk)
+    assert np.array_equal(to_np(gq[ri]), c_ref)
+    assert np.array_equal(to_np(gsc[ri]).view(np.uint32), s_ref.view(np.uint32))
+    wc_ref, ws_ref = quantize_rhs_blockwise_dlhs(bf16_to_bits(w[:, ki, :]), "e4m3", bk)
+    assert np.array_equal(to_np(ws[:, ki, :]).view(np.uint32), ws_ref.view(np.uint32))
+    sub = sampled_sizes(rows, sizes)
+    R = gmm_dlhs_blockwise_ref(c_ref, "e5m2", s_ref, wc_ref, "e4m3", ws_ref, sub, bk)
+    absR = gmm_dlhs_blockwise_ref(magnitudes(c_ref), "e5m2", s_ref, magnitudes(wc_ref), "e4m3",
+                                  ws_ref, sub, bk)
+    Y = to_np(out[ri][:, ki])
+    err = group_rel_err(Y, R, group_row_ranges(sub))
+    print(f"sampled max group relative error {err:.3e}", flush=True)
+    assert err <= TOL, err
+    assert_rounding_bound(Y, R, absR, N)
+

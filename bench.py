@@ -33,6 +33,7 @@ Also reported (each timed with HIP events on the current stream):
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
        [--no-cpu-baseline] [--no-overlap] [--no-extras] [--no-clock] [--reps 50]
+       python bench.py --crossover | --dense-only [--workload NAME] [--reps N]
 """
 
 import argparse
@@ -111,6 +112,9 @@ def parse():
     p.add_argument("--no-clock", action="store_true", help="skip the GFX clock reading")
     p.add_argument("--crossover", action="store_true",
                    help="only the fused-vs-quantize-once table of the forward (crossover_block)")
+    p.add_argument("--dense-only", action="store_true",
+                   help="only the vendor dense FP8 GEMM at the workload's shape (dense_ceiling), "
+                        "--reps timed calls: the comparison run for counter profiles")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=2048, help="at most 4096")
     p.add_argument("--copy-calibration", action="store_true",
@@ -823,6 +827,9 @@ def main():
         print(json.dumps({"crossover_block": crossover_block(g)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
+    if args.dense_only:
+        print(json.dumps({"dense_ceiling": dense_ceiling(wl, args.reps)}), flush=True)
+        return
     step = Step(g, wl, seed=wl.seed * 100)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -78,7 +78,7 @@ __device__ inline bool bs_schedule(const int32_t* __restrict__ gs, int G, int64_
 
 // NMAJ: the weight scales are laid out [G, N, K / bk] (p.b_scale_nmajor) instead of
 // [G, K / bk, N]; a template parameter so that each instantiation holds one load path
-template <int A_FMT, bool NMAJ>
+template <int A_FMT, bool NMAJ, bool ONE>
 __global__ __attribute__((amdgpu_flat_work_group_size(BS_NT, BS_NT), amdgpu_waves_per_eu(2, 2)))
 void gmm_bs_kernel(BsParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[BS_TILE];
@@ -176,7 +176,8 @@ void gmm_bs_kernel(BsParams p) {
       }
   };
   // total += partial * RNE(sA * sB): one fused multiply-add per value; the partial
-  // restarts from zero
+  // restarts from zero (ONE: every step is a whole block, whose first MFMAs take a zero
+  // accumulator operand instead)
   auto promote = [&]() {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -186,7 +187,7 @@ void gmm_bs_kernel(BsParams p) {
         for (int r = 0; r < 16; ++r)
           total[i][j][r] = __builtin_fmaf(part[i][j][r], mul_rn(sa[i], sb[j][r >> 2][r & 3]),
                                           total[i][j][r]);
-        part[i][j] = v16f{0};
+        if constexpr (!ONE) part[i][j] = v16f{0};
       }
   };
 
@@ -202,7 +203,8 @@ void gmm_bs_kernel(BsParams p) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          part[i][j] = mfma32x32x64<FMT_E4M3, A_FMT>(bf[j], af[i], part[i][j]);
+          part[i][j] = mfma32x32x64<FMT_E4M3, A_FMT>(bf[j], af[i],
+                                                     ONE && ks == 0 ? v16f{0} : part[i][j]);
     }
   };
 
@@ -455,14 +457,21 @@ hipError_t launch_gemm_blockwise(int a_fmt, const BsParams& p, hipStream_t st) {
   if (grid == 0 || p.M == 0) return hipSuccess;
   const dim3 gd((unsigned)grid), bd(BS_NT);
   if (a_fmt != FMT_E4M3 && a_fmt != FMT_E5M2) return hipErrorInvalidValue;
-  if (a_fmt == FMT_E4M3 && !p.b_scale_nmajor)
-    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, false>), gd, bd, 0, st, p);
-  else if (a_fmt == FMT_E4M3)
-    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, true>), gd, bd, 0, st, p);
-  else if (!p.b_scale_nmajor)
-    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, false>), gd, bd, 0, st, p);
-  else
-    hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, true>), gd, bd, 0, st, p);
+  // one contraction step per scale block (bk = 128) takes the variant without clearing
+  const bool one = p.bk == BS_BK;
+  if (a_fmt == FMT_E4M3 && !p.b_scale_nmajor) {
+    if (one) hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, false, true>), gd, bd, 0, st, p);
+    else hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, false, false>), gd, bd, 0, st, p);
+  } else if (a_fmt == FMT_E4M3) {
+    if (one) hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, true, true>), gd, bd, 0, st, p);
+    else hipLaunchKernelGGL((gmm_bs_kernel<FMT_E4M3, true, false>), gd, bd, 0, st, p);
+  } else if (!p.b_scale_nmajor) {
+    if (one) hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, false, true>), gd, bd, 0, st, p);
+    else hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, false, false>), gd, bd, 0, st, p);
+  } else {
+    if (one) hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, true, true>), gd, bd, 0, st, p);
+    else hipLaunchKernelGGL((gmm_bs_kernel<FMT_E5M2, true, false>), gd, bd, 0, st, p);
+  }
   return hipGetLastError();
 }
 

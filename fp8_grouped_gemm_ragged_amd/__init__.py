@@ -111,6 +111,10 @@ def load(path=None):
         raise RuntimeError(
             f"{p} is missing: build it with `python -m fp8_grouped_gemm_ragged_amd.build` "
             "(there is no fallback implementation)")
+    # torch first: the library then binds to the HIP runtime torch has loaded (the one its
+    # tensors and streams live in), not to a second copy that would reject torch's streams
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(p)
     for name, args in _SIGNATURES.items():
         fn = getattr(lib, name)

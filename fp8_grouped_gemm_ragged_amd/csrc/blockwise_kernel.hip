@@ -243,15 +243,23 @@ void gmm_bs_kernel(BsParams p) {
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // stores through a resource over the wave's 64 rows inside the group: rows past its
+    // end fall outside the range and are dropped (offsets below 2^30); all eight rows'
+    // LDS reads in flight before the stores
     const int c = lane & 7;
+    const int m0 = tc.row0 + 64 * wr;
+    const int rows_valid = max(min(tc.row_end - m0, 64), 0);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc((uint16_t*)p.out + (int64_t)m0 * p.N, (uint32_t)rows_valid * (uint32_t)p.N * 2u);
+    const uint32_t lane_off = ((uint32_t)(lane >> 3) * (uint32_t)p.N + (uint32_t)(tc.n0 + 64 * wc + c * 8)) * 2u;
+    v4u v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int row = q * 8 + (lane >> 3);
-      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 128 + ((c ^ (row & 7)) << 4));
-      const int m = tc.row0 + 64 * wr + row;
-      if (m < tc.row_end)
-        *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.N + tc.n0 + 64 * wc + c * 8) = v;
+      v[q] = *reinterpret_cast<const v4u*>(wl + row * 128 + ((c ^ (row & 7)) << 4));
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) buf_store16(ro, lane_off + (uint32_t)q * 16u * (uint32_t)p.N, v[q]);
     return;
   }
 #pragma unroll

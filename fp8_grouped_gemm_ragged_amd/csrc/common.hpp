@@ -40,6 +40,12 @@ __device__ inline v4u buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// A range-checked 16-byte store: a lane whose byte offset lies beyond num_records writes
+// nothing, which is how rows past the end of a group are left alone.
+__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------------------------
 // LDS tile layout: a tile is [rows][128 bytes] of fp8 codes, the contraction axis
 // contiguous.  16-byte chunk c of row r is stored at chunk position

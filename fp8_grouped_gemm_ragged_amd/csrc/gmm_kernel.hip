@@ -223,15 +223,29 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const TileCoord&
     }
     // this wave's LDS writes are done before its own reads (no other wave touches wl)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const bool cols_ok = tc.n0 + wc * 128 < p.Nout;  // N is a multiple of 128
+    // the wave's 128 columns lie all inside N or all outside it (N is a multiple of 128)
+    if (tc.n0 + wc * 128 >= p.Nout) return;
+    // Stores through a resource over the tile's rows of the group: rows past the group's
+    // end fall outside its range and are dropped, so no store needs a per-lane branch.
+    // Byte offsets stay below 2^31 (256 rows x N <= 2^22 columns x 2 bytes).
     const int c = lane & 15;
+    const int rows_here = min(tc.row_end - tc.row0, BM);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((uint16_t*)p.out + (int64_t)tc.row0 * p.Nout,
+                                                (uint32_t)rows_here * (uint32_t)p.Nout * 2u);
+    const uint32_t lane_off =
+        ((uint32_t)(wr * 128 + (lane >> 4)) * (uint32_t)p.Nout + (uint32_t)(tc.n0 + wc * 128 + c * 8)) * 2u;
+    const uint32_t q_stride = 8u * (uint32_t)p.Nout;  // 4 rows
+    // eight rows' LDS reads in flight before their stores
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const int row = q * 4 + (lane >> 4);
-      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 256 + ((c ^ (row & 15)) << 4));
-      const int m = tc.row0 + wr * 128 + row;
-      if (cols_ok && m < tc.row_end)
-        *reinterpret_cast<v4u*>((uint16_t*)p.out + (int64_t)m * p.Nout + tc.n0 + wc * 128 + c * 8) = v;
+    for (int q0 = 0; q0 < 32; q0 += 8) {
+      v4u v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = (q0 + t) * 4 + (lane >> 4);
+        v[t] = *reinterpret_cast<const v4u*>(wl + row * 256 + ((c ^ (row & 15)) << 4));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) buf_store16(ro, lane_off + (uint32_t)(q0 + t) * q_stride, v[t]);
     }
     return;
   }
@@ -418,12 +432,16 @@ __device__ inline void swiglu_epilogue(const GemmParams& p, const TileCoord& tc,
         }
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // stores through a resource over these 32 rows' part inside the group: rows past its
+    // end fall outside the range and are dropped (offsets below 2^27)
+    const uint32_t row_bytes = (uint32_t)I * (uint32_t)(RB / 128);
+    const int rows_valid = max(min(tc.row_end - mrow, 32), 0);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc((uint8_t*)p.out + ((int64_t)mrow * I + c0) * (RB / 128), (uint32_t)rows_valid * row_bytes);
     for (int q = 0; q < 32 / rows_per_op; ++q) {
       const int row = q * rows_per_op + lane / lanes_per_row;
       const v4u v = *reinterpret_cast<const v4u*>(st + row * RB + ((c ^ (row & swz)) << 4));
-      const int m = mrow + row;
-      if (m < tc.row_end)
-        *reinterpret_cast<v4u*>((uint8_t*)p.out + ((int64_t)m * I + c0) * (RB / 128) + c * 16) = v;
+      buf_store16(ro, (uint32_t)row * row_bytes + (uint32_t)c * 16u, v);
     }
   }
 }

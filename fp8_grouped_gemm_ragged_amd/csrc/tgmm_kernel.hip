@@ -570,14 +570,26 @@ void tgmm_main_kernel(TgmmCodesParams p) {
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's region only
-    const bool cols_ok = n0 + wc * 64 < p.Nout;
+    // K and N are multiples of 128: the wave's 128 k rows and 64 n columns lie all inside
+    // the output or all outside it
+    if (n0 + wc * 64 >= p.Nout || k0 + wr * 128 >= p.Kout) return;
+    // stores through a resource over the wave's 128 rows (offsets below 2^30), eight
+    // rows' LDS reads in flight before their stores
+    const int c = lane & 7;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc((uint16_t*)p.out + slab + (int64_t)(k0 + wr * 128) * p.Nout, 256u * (uint32_t)p.Nout);
+    const uint32_t lane_off = ((uint32_t)(lane >> 3) * (uint32_t)p.Nout + (uint32_t)(n0 + wc * 64 + c * 8)) * 2u;
+    const uint32_t q_stride = 16u * (uint32_t)p.Nout;  // 8 rows
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = q * 8 + (lane >> 3), c = lane & 7;
-      const v4u v = *reinterpret_cast<const v4u*>(wl + row * 128 + ((c ^ (row & 7)) << 4));
-      const int k = k0 + wr * 128 + row;
-      if (cols_ok && k < p.Kout)
-        *reinterpret_cast<v4u*>((uint16_t*)p.out + slab + (int64_t)k * p.Nout + n0 + wc * 64 + c * 8) = v;
+    for (int q0 = 0; q0 < 16; q0 += 8) {
+      v4u v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = (q0 + t) * 8 + (lane >> 3);
+        v[t] = *reinterpret_cast<const v4u*>(wl + row * 128 + ((c ^ (row & 7)) << 4));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) buf_store16(ro, lane_off + (uint32_t)(q0 + t) * q_stride, v[t]);
     }
     return;
   }

@@ -136,9 +136,49 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int g_befor
                                      int64_t M, int n_ntiles, int nk, bool split,
                                      int* s_tile_cum, int* s_row_off, TileCoord& tc, int& kb,
                                      int& ke, int& slot) {
-  group_prefix(gs, g_before, G, M, s_tile_cum, s_row_off);
-  __syncthreads();
-  const int total_mt = s_tile_cum[G];
+  // Up to 64 groups, every wave computes the prefix sums itself, lane g holding group g's
+  // (the same clamped sums as group_tiles_prefix), and finds its tile's group with a
+  // ballot: no LDS and no workgroup barrier before the prologue.  More groups take the
+  // prefix sums in LDS and a binary search.
+  const bool in_wave = G <= 64;
+  const int lane = threadIdx.x & 63;
+  uint32_t w_start = 0, w_end = 0;
+  int w_cum_ex = 0, total_mt;
+  if (in_wave) {
+    const uint32_t Mu = (uint32_t)M;  // M < 2^31
+    const uint32_t rb = rows_of_groups(gs, g_before, Mu);
+    const uint32_t m = lane < G ? (uint32_t)min(max(gs[g_before + lane], 0), (int)Mu) : 0u;
+    const uint32_t ir = wave_incl_scan_sat(m, lane, Mu);
+    const uint32_t up = (uint32_t)__shfl_up(ir, 1, 64);
+    w_end = min(rb + ir, Mu);
+    w_start = min(rb + (lane == 0 ? 0u : up), Mu);
+    const int tiles = (int)((w_end - w_start + BM - 1) / BM);
+    const int it = wave_incl_scan(tiles, lane);
+    w_cum_ex = it - tiles;
+    total_mt = __builtin_amdgcn_readlane(it, 63);  // lanes past G add no tile
+  } else {
+    group_prefix(gs, g_before, G, M, s_tile_cum, s_row_off);
+    __syncthreads();
+    total_mt = s_tile_cum[G];
+  }
+  // tile L of the order (tile_coord's arithmetic on the wave's sums)
+  auto coord = [&](int L) -> bool {
+    if (!in_wave) return tile_coord(L, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
+    const int band = L / (BAND * n_ntiles);
+    const int rem = L - band * BAND * n_ntiles;
+    const int mt0 = band * BAND;
+    const int gm = min(BAND, total_mt - mt0);
+    const int nt = rem / gm;
+    const int mt = mt0 + (rem - nt * gm);
+    // the last group whose first M-tile is at or before mt (lane 0's is 0)
+    const uint64_t below = __ballot(lane < G && w_cum_ex <= mt);
+    const int lo = 63 - __builtin_clzll(below);
+    tc.g = lo;
+    tc.row0 = (int)__builtin_amdgcn_readlane(w_start, lo) + (mt - __builtin_amdgcn_readlane(w_cum_ex, lo)) * BM;
+    tc.row_end = (int)__builtin_amdgcn_readlane(w_end, lo);
+    tc.n0 = nt * BN;
+    return tc.row0 < tc.row_end;
+  };
   const int total = total_mt * n_ntiles;
   // XCD-aware remap: workgroups of XCD x = wg % 8 take a contiguous range of tiles
   const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
@@ -148,14 +188,14 @@ __device__ inline bool schedule_tile(const int32_t* __restrict__ gs, int g_befor
   ke = nk;
   slot = -1;
   if (j < x.full) {
-    ok = tile_coord(x.lo + j, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
+    ok = coord(x.lo + j);
   } else if (j - x.full < x.tail * x.s) {
     const int t = j - x.full;
-    ok = tile_coord(x.lo + x.full + t / x.s, total_mt, n_ntiles, G, M, s_tile_cum, s_row_off, tc);
+    ok = coord(x.lo + x.full + t / x.s);
     slice_steps(t % x.s, x.s, nk, kb, ke);
     slot = xcd * SPLIT_CUS + t;
   }
-  __syncthreads();  // the scheduler arrays alias stage memory
+  if (!in_wave) __syncthreads();  // the scheduler arrays alias stage memory
   // every lane computed the same work: make that visible to the compiler, so the buffer
   // resources built from it live in scalar registers
   tc.g = __builtin_amdgcn_readfirstlane(tc.g);

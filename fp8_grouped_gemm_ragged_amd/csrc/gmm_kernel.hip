@@ -10,8 +10,9 @@
 //
 // Work decomposition (one workgroup = one 256 x 256 output tile, 4 waves):
 //   * expert-tile scheduler: every workgroup prefix-sums group_sizes into per-group
-//     M-tile counts ceil(m_g / 256) in LDS; a tile never spans two groups, empty groups
-//     own no tile, and workgroups past the real tile count exit at once;
+//     M-tile counts ceil(m_g / 256) (in each wave's registers for up to 64 groups, else in
+//     LDS); a tile never spans two groups, empty groups own no tile, and workgroups past
+//     the real tile count exit at once;
 //   * XCD-aware order: the hardware places workgroup i on XCD i % 8, so workgroup ids
 //     are remapped to give each XCD a contiguous range of tiles, ordered in bands of 8
 //     M-tiles sweeping the N-tiles: the 32 concurrent tiles of one XCD share A rows and

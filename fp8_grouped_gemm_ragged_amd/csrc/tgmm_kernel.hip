@@ -511,11 +511,18 @@ void tgmm_main_kernel(TgmmCodesParams p) {
     };
 
     // prologue: step 0 into stage 0, step 1 into the staging registers, the first
-    // fragments of stage 0
+    // fragments of stage 0.  Step 0's loads go out before the window's and share its
+    // wait (one memory round trip, not two): they read block 0 whatever its scale
+    // product, and a block that adds nothing has its registers cleared afterwards, as if
+    // it had been read as zeros.
+#pragma unroll
+    for (int q = 0; q < 8; ++q) gload(0, true, q >> 1, q & 1);
     load_window(0);
     bool live0 = live_of(0), live1 = live_of(1), live2 = live_of(2);
+    if (!live0) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) gload(0, live0, q >> 1, q & 1);
+      for (int q = 0; q < 4; ++q) sa[q] = sb[q] = v4u{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) lwrite(sA0, sB0, q >> 1, q & 1);
 #pragma unroll

@@ -28,7 +28,8 @@ Also reported (each timed with HIP events on the current stream):
   * ffn_chain: the MoE SwiGLU feed-forward block (G=64, M=65536, hidden 2048,
     intermediate 1408), forward and backward as one timed chain, in pure mode (every
     product quantizes its own bf16 operands) and hybrid mode (each gradient quantized once,
-    its codes feeding dlhs and tgmm), each with static and dynamic forward lhs scaling;
+    its codes feeding dlhs and tgmm), each with static and dynamic forward lhs scaling,
+    and the hybrid static chain with the SwiGLU backward in the down dlhs's epilogue;
   * the SwiGLU, routing and block-wise blocks, and the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload NAME]
@@ -373,7 +374,9 @@ def ffn_chain(g, reps=10):
     pure: every product takes bf16 operands and quantizes them itself.  hybrid: each
     gradient (grad_y, d_gu) is quantized once (e5m2, dynamic) and its codes feed both its
     dlhs and its tgmm.  static: the forward lhs (x, h) uses the static scale 4/448 (h comes
-    out of the gate|up epilogue as e4m3 codes); dynamic: 128-row block scales."""
+    out of the gate|up epilogue as e4m3 codes); dynamic: 128-row block scales.  Last, the
+    hybrid static chain once more with gmm_dlhs_swiglu_bwd in place of the down dlhs and
+    the SwiGLU backward (no dh)."""
     import torch
 
     from synth.workloads import WORKLOADS, normal_bf16
@@ -405,7 +408,7 @@ def ffn_chain(g, reps=10):
     names = ["fwd_gate_up_swiglu", "fwd_down", "dlhs_down", "swiglu_bwd", "dlhs_gate_up",
              "tgmm_down", "tgmm_gate_up"]
 
-    def chain(mode, scaling, ev=None):
+    def chain(mode, scaling, ev=None, fused_bwd=False):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         if scaling == "static":
@@ -423,9 +426,14 @@ def ffn_chain(g, reps=10):
         rec(2)
         if mode == "hybrid":
             gyq, sgy = g.gmm_quantize(grad_y, "e5m2", "dynamic")
-            g.gmm_dlhs(gyq, wdn_k, wdn_sk, gs, grad_scales=sgy, out=dh)
-            rec(3)
-            g.gmm_swiglu_bwd(dh, gu, out=d_gu)
+            if fused_bwd:
+                # the SwiGLU backward in the down projection's dlhs epilogue (no dh)
+                g.gmm_dlhs_swiglu_bwd(gyq, wdn_k, wdn_sk, gs, gu, grad_scales=sgy, out=d_gu)
+                rec(3)
+            else:
+                g.gmm_dlhs(gyq, wdn_k, wdn_sk, gs, grad_scales=sgy, out=dh)
+                rec(3)
+                g.gmm_swiglu_bwd(dh, gu, out=d_gu)
             rec(4)
             dgq, sdg = g.gmm_quantize(d_gu, "e5m2", "dynamic")
             g.gmm_dlhs(dgq, wgu_k, wgu_sk, gs, grad_scales=sdg, out=dx)
@@ -482,6 +490,24 @@ def ffn_chain(g, reps=10):
             res[f"{mode}_{scaling}"] = {"chain": mt,
                                         "TFLOP/s": round(total_flop / mt["median_ms"] / 1e9, 1),
                                         "ops": per}
+    # the hybrid static chain again with the SwiGLU backward in the down dlhs's epilogue
+    for _ in range(3):
+        chain("hybrid", "static", fused_bwd=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        chain("hybrid", "static", evs[i], fused_bwd=True)
+    torch.cuda.synchronize()
+    mt = _median_min([e[0].elapsed_time(e[7]) for e in evs])
+    t_fb = float(np.median([e[2].elapsed_time(e[4]) for e in evs]))
+    t_two = (res["hybrid_static"]["ops"]["dlhs_down"]["ms"] +
+             res["hybrid_static"]["ops"]["swiglu_bwd"]["ms"])
+    res["hybrid_static_fused_bwd"] = {
+        "chain": mt, "TFLOP/s": round(total_flop / mt["median_ms"] / 1e9, 1),
+        "dlhs_down_swiglu_bwd_ms": round(t_fb, 4),
+        "two_calls_ms": round(t_two, 4),
+        "what": "gmm_dlhs_swiglu_bwd (grad quantizer included) in place of gmm_dlhs + "
+                "gmm_swiglu_bwd; same d_gu bits"}
     res["hybrid_over_pure"] = {s: round(res[f"hybrid_{s}"]["chain"]["median_ms"] /
                                         res[f"pure_{s}"]["chain"]["median_ms"], 4)
                                for s in ("static", "dynamic")}

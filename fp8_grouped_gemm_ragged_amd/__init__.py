@@ -75,6 +75,8 @@ _SIGNATURES = {
     "gmm_fwd_swiglu_fp8_subchannel": [_OPP, _I32, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P,
                                       _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
+    "gmm_dlhs_swiglu_bwd": [_OPP, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
+                            _P, _SZ, _P],
     "gmm_permute_workspace_size": [_I64, _I32, _I32],
     "gmm_fwd_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
     "gmm_dlhs_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
@@ -219,7 +221,8 @@ def _nblocks(rows):
 
 
 def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_scales,
-          rhs_layout, out_dtype, out, contraction_dim, out_cols, fused, group_offset=None):
+          rhs_layout, out_dtype, out, contraction_dim, out_cols, fused, group_offset=None,
+          gu=None):
     import torch
 
     lib = load()
@@ -245,11 +248,19 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
         _group_sizes(group_sizes, G)
     elif not 0 <= int(group_offset) <= group_sizes.shape[0] - G:
         raise ValueError("the local window group_offset .. group_offset + G must lie inside group_sizes")
+    # with gu (the SwiGLU backward in the dlhs epilogue) the output is d_gu [M, 2 I], bf16
+    out_w = n_out
+    if gu is not None:
+        if odt != torch.bfloat16:
+            raise ValueError("the SwiGLU backward writes bf16")
+        _need(gu, torch.bfloat16, "gu", 2)
+        _shape(gu, (M, 2 * n_out), "gu")
+        out_w = 2 * n_out
     if out is None:
-        out = torch.empty((M, n_out), dtype=odt, device=a.device)
+        out = torch.empty((M, out_w), dtype=odt, device=a.device)
     else:
         _need(out, odt, "out", 2)
-        _shape(out, (M, n_out), "out")
+        _shape(out, (M, out_w), "out")
     op = _operand(KIND_FP8 if prequant else KIND_BF16, fmt, scaling, static_scale)
     mode = _SCALING[scaling]
     if mode != STATIC and a_scales is None:
@@ -267,7 +278,12 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
                                   G, ctypes.byref(ws_n)), "gmm_workspace_size")
     ws = _workspace(ws_n.value, a.device)
     odt_code = OUT_F32 if odt == torch.float32 else OUT_BF16
-    if group_offset is None:
+    if gu is not None:
+        _check(lib.gmm_dlhs_swiglu_bwd(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], M, K, N, G,
+                                       _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales),
+                                       _ptr(group_sizes), _ptr(gu), _ptr(out), _ptr(ws),
+                                       ws_n.value, _stream()), "gmm_dlhs_swiglu_bwd")
+    elif group_offset is None:
         _check(getattr(lib, cname)(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], odt_code, M, K, N,
                                    G, _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales),
                                    _ptr(group_sizes), _ptr(out), _ptr(ws), ws_n.value, _stream()),
@@ -370,6 +386,18 @@ def gmm_dlhs(grad, rhs, rhs_scales, group_sizes, *, grad_format="e5m2", grad_sca
     fused: as for gmm_fwd."""
     o, s = _gemm("gmm_dlhs", grad, rhs, rhs_scales, group_sizes, grad_format, grad_scaling,
                  static_scale, grad_scales, rhs_layout, out_dtype, out, "N", "K", fused)
+    return (o, s) if return_scales else o
+
+
+def gmm_dlhs_swiglu_bwd(grad, rhs, rhs_scales, group_sizes, gu, *, grad_format="e5m2",
+                        grad_scaling="dynamic", static_scale=None, grad_scales=None,
+                        rhs_layout="kn", out=None, return_scales=False, fused=False):
+    """The down projection's dlhs with the SwiGLU backward in its epilogue: d_gu [M, 2I]
+    bf16 = gmm_swiglu_bwd(gmm_dlhs(grad, rhs, ...) in bf16, gu), bit for bit, without the
+    [M, I] dh in between.  rhs: the down weight's dlhs copy ([G, I, H] for "kn"),
+    rhs_scales f32 [G, I]; gu bf16 [M, 2I] from gmm_fwd_swiglu."""
+    o, s = _gemm("gmm_dlhs", grad, rhs, rhs_scales, group_sizes, grad_format, grad_scaling,
+                 static_scale, grad_scales, rhs_layout, None, out, "N", "K", fused, gu=gu)
     return (o, s) if return_scales else o
 
 

@@ -179,7 +179,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                           const int32_t* group_sizes, void* out, void* workspace,
                           size_t workspace_bytes, hipStream_t st, bool swiglu = false,
                           void* gu = nullptr, const gmm_operand_t* h_op = nullptr,
-                          float* h_scales = nullptr) {
+                          float* h_scales = nullptr, const void* bwd_gu = nullptr) {
   gmm_status_t s = check_operand(aop);
   if (s != GMM_OK) return s;
   // SwiGLU with fp8 h: codes under a validated static per-tensor scale, or (h_scales)
@@ -199,6 +199,9 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   const bool window = G != G_total;
   // SwiGLU: Nout = 2 I channels, I a multiple of 128, contraction-contiguous weights
   if (swiglu && (Nout % 256 || b_trans)) return swiglu && b_trans ? GMM_ERR_RECIPE : GMM_ERR_SHAPE;
+  // SwiGLU backward in the dlhs epilogue: bf16 dh of Nout = I channels, d_gu [M, 2 I]
+  if (bwd_gu && (swiglu || h_op || out_dtype != GMM_OUT_BF16)) return GMM_ERR_RECIPE;
+  if (bwd_gu && (window || Nout > MAX_DIM / 2)) return GMM_ERR_SHAPE;
   // the kernels number output tiles with 32-bit integers
   if ((M / 256 + 1 + G) * ((Nout + 255) / 256) >= (int64_t(1) << 31)) return GMM_ERR_SHAPE;
   if (!rhs || !rhs_scales || !group_sizes) return GMM_ERR_NULL;
@@ -218,7 +221,8 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   // its room first, so that the sizes of both routes (GMM_OP_DLHS, GMM_OP_DLHS_FUSED)
   // give both the same split.
   const bool is_dlhs = std::strncmp(name, "gmm_dlhs", 8) == 0;
-  const size_t split_need = is_dlhs ? split_ws_bytes(M, Kc, Nout, G) : 0;
+  // (the fused SwiGLU backward has no tail split: its epilogue needs the whole sum)
+  const size_t split_need = is_dlhs && !bwd_gu ? split_ws_bytes(M, Kc, Nout, G) : 0;
   const bool split = split_need && workspace && workspace_bytes >= ws_need + split_need;
   const size_t ws_base = ws_need + (split ? split_need : 0);
   const bool quant_once = !a_fp8 && (swiglu || quant_once_applies(Nout)) && workspace &&
@@ -228,13 +232,15 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   const size_t ws_used = ws_base + (quant_once ? quant_once_bytes(M, Kc) : 0);
   const size_t a_bytes = (size_t)M * Kc * (a_fp8 ? 1 : 2);
   const size_t esize = out_dtype == GMM_OUT_F32 ? 4 : 2;
-  const size_t out_bytes = (size_t)M * (swiglu ? Nout / 2 : Nout) * (h_op ? 1 : esize);
+  const size_t out_bytes =
+      (size_t)M * (swiglu ? Nout / 2 : bwd_gu ? 2 * Nout : Nout) * (h_op ? 1 : esize);
   const size_t gu_bytes = swiglu && gu ? (size_t)M * Nout * esize : 0;
   const size_t b_bytes = (size_t)G * Kc * Nout;
   const size_t as_bytes = (size_t)nblocks(M) * 4;
   if (overlaps(out, out_bytes, a, a_bytes) || overlaps(out, out_bytes, rhs, b_bytes) ||
       overlaps(out, out_bytes, rhs_scales, (size_t)G * Nout * 4) ||
       overlaps(out, out_bytes, group_sizes, (size_t)G_total * 4) ||
+      (a_scales && overlaps(out, out_bytes, a_scales, as_bytes)) ||
       (needs_dyn_ws(aop) && overlaps(a_scales, as_bytes, a, a_bytes)) ||
       overlaps(workspace, ws_used, a, a_bytes) || overlaps(workspace, ws_used, out, out_bytes) ||
       overlaps(workspace, ws_used, a_scales, as_bytes))
@@ -247,6 +253,12 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                    overlaps(gu, gu_bytes, a_scales, as_bytes)))
     return GMM_ERR_ALIAS;
   if (gu && !aligned16(gu)) return GMM_ERR_ALIGN;
+  const size_t bg_bytes = bwd_gu ? (size_t)M * 2 * Nout * 2 : 0;
+  if (bg_bytes && (overlaps(bwd_gu, bg_bytes, out, out_bytes) ||
+                   overlaps(bwd_gu, bg_bytes, workspace, ws_used) ||
+                   overlaps(bwd_gu, bg_bytes, a_scales, as_bytes)))
+    return GMM_ERR_ALIAS;
+  if (bwd_gu && !aligned16(bwd_gu)) return GMM_ERR_ALIGN;
   const size_t hs_bytes = h_scales ? (size_t)M * (Nout / 256) * 4 : 0;  // [M, I / 128]
   if (hs_bytes && (overlaps(h_scales, hs_bytes, a, a_bytes) || overlaps(h_scales, hs_bytes, rhs, b_bytes) ||
                    overlaps(h_scales, hs_bytes, rhs_scales, (size_t)G * Nout * 4) ||
@@ -283,6 +295,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.g_before = g_before;
   p.out_f32 = out_dtype == GMM_OUT_F32;
   p.gu = gu;
+  p.bwd_gu = (const uint16_t*)bwd_gu;
   p.split_ws = split ? (float*)((uint8_t*)workspace + ws_need) : nullptr;
   if (h_op) {
     p.h_codes = 1 + h_op->format;
@@ -451,6 +464,22 @@ gmm_status_t gmm_dlhs_local(const gmm_operand_t* grad_op, int32_t rhs_format, in
                       out_dtype, M, N, K, G_total, group_offset, G_local, grad, grad_scales, rhs,
                       rhs_scales, group_sizes, dlhs, workspace, workspace_bytes,
                       (hipStream_t)stream);
+}
+
+gmm_status_t gmm_dlhs_swiglu_bwd(const gmm_operand_t* grad_op, int32_t rhs_format,
+                                 int32_t rhs_layout, int64_t M, int64_t I, int64_t N, int32_t G,
+                                 const void* grad, float* grad_scales, const uint8_t* rhs,
+                                 const float* rhs_scales, const int32_t* group_sizes,
+                                 const void* gu, void* d_gu, void* workspace,
+                                 size_t workspace_bytes, gmm_stream_t stream) {
+  if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
+  if (M > 0 && !gu) return GMM_ERR_NULL;
+  // dlhs of the down projection (contraction over its N = hidden columns, output I)
+  return grouped_gemm("gmm_dlhs_swiglu_bwd", grad_op, rhs_format, rhs_layout == GMM_RHS_NK,
+                      GMM_OUT_BF16, M, N, I, G, 0, G, grad, grad_scales, rhs, rhs_scales,
+                      group_sizes, d_gu, workspace, workspace_bytes, (hipStream_t)stream, false,
+                      nullptr, nullptr, nullptr, M > 0 ? gu : nullptr);
 }
 
 gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,

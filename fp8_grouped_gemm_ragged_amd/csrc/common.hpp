@@ -140,6 +140,33 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// SwiGLU backward of 8 channels of one row ("FP8 Megablox for batch split", Description
+// (2): gate and up projections merged): from bf16 dh (d), gate g and up u, with
+// s = sigmoid(g) through the hardware exp2 and reciprocal (about one ulp each) and every
+// other operation rounded to nearest in fp32,
+//   dL/dg = ((d * u) * s) * (1 + g * (1 - s)),   dL/du = d * (g * s),
+// returned as bf16 (RNE) in og and ou.  The elementwise kernel and the dlhs epilogue
+// that fuses this step both call it, so the two give the same bits.
+__device__ __forceinline__ void swiglu_bwd8(const v4u d, const v4u g8, const v4u u8, v4u& og,
+                                            v4u& ou) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float dg[2], du[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float g = h ? bf16_hi(g8[k]) : bf16_lo(g8[k]);
+      const float u = h ? bf16_hi(u8[k]) : bf16_lo(u8[k]);
+      const float dv = h ? bf16_hi(d[k]) : bf16_lo(d[k]);
+      const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+      const float grow = add_rn(1.0f, mul_rn(g, __fsub_rn(1.0f, s)));
+      dg[h] = __fmul_rn(__fmul_rn(__fmul_rn(dv, u), s), grow);
+      du[h] = __fmul_rn(dv, __fmul_rn(g, s));
+    }
+    og[k] = pack_bf16x2(dg[0], dg[1]);
+    ou[k] = pack_bf16x2(du[0], du[1]);
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // MFMA: D[32x32] += A[32x64] * B[64x32], fp8/bf8 operands, fp32 accumulation.  Lane l
 // holds row (l % 32) of A and column (l % 32) of B, 32 contraction bytes each; the

@@ -244,6 +244,31 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const TileCoord&
     for (int r4 = 0; r4 < 4; ++r4)
       sb[j][r4] = *reinterpret_cast<const v4f*>(s_sb + wc * 128 + j * 32 + 8 * r4 + 4 * fhalf);
   if (!p.out_f32) {
+    // SwiGLU backward in the epilogue: the first 8 rows' gate and up values are loaded
+    // now, so that their latency hides under the conversion below (the wave's columns lie
+    // all inside the output or all outside it)
+    const bool bwd = p.bwd_gu != nullptr && tc.n0 + wc * 128 < p.Nout;
+    const int c = lane & 15;
+    const int rows_here = min(tc.row_end - tc.row0, BM);
+    __amdgpu_buffer_rsrc_t rg = make_rsrc(nullptr, 0u);
+    uint32_t g_off = 0;
+    v4u gv[2][8], uv[2][8];
+    // gu rows of the tile inside the group: rows past its end read zeros (offsets below
+    // 2^31: 256 rows x 2 Nout <= 2^22 columns x 2 bytes)
+    const uint32_t two_i = 2u * (uint32_t)p.Nout;
+    auto bwd_load = [&](int set, int q0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t o = g_off + (uint32_t)(q0 + t) * 8u * two_i;
+        gv[set][t] = buf_load16(rg, o);
+        uv[set][t] = buf_load16(rg, o + 2u * (uint32_t)p.Nout);
+      }
+    };
+    if (bwd) {
+      rg = make_rsrc(p.bwd_gu + (int64_t)tc.row0 * two_i, (uint32_t)rows_here * two_i * 2u);
+      g_off = ((uint32_t)(wr * 128 + (lane >> 4)) * two_i + (uint32_t)(tc.n0 + wc * 128 + c * 8)) * 2u;
+      bwd_load(0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = i * 32 + frow;
@@ -266,11 +291,37 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const TileCoord&
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // the wave's 128 columns lie all inside N or all outside it (N is a multiple of 128)
     if (tc.n0 + wc * 128 >= p.Nout) return;
+    if (bwd) {
+      // d_gu rows through a resource over the tile's rows of the group (rows past its end
+      // are dropped), 4 rows per instruction, 16 lanes per row, 8 channels per lane; the
+      // next 8 rows' gate and up loads go out before this batch's stores (the
+      // vector-memory counter retires in order)
+      const __amdgpu_buffer_rsrc_t rd =
+          make_rsrc((uint16_t*)p.out + (int64_t)tc.row0 * two_i, (uint32_t)rows_here * two_i * 2u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int set = b & 1;
+        if (b < 3) bwd_load(set ^ 1, (b + 1) * 8);
+        v4u d[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = (b * 8 + t) * 4 + (lane >> 4);
+          d[t] = *reinterpret_cast<const v4u*>(wl + row * 256 + ((c ^ (row & 15)) << 4));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          v4u og, ou;
+          swiglu_bwd8(d[t], gv[set][t], uv[set][t], og, ou);
+          const uint32_t o = g_off + (uint32_t)(b * 8 + t) * 8u * two_i;
+          buf_store16(rd, o, og);
+          buf_store16(rd, o + 2u * (uint32_t)p.Nout, ou);
+        }
+      }
+      return;
+    }
     // Stores through a resource over the tile's rows of the group: rows past the group's
     // end fall outside its range and are dropped, so no store needs a per-lane branch.
     // Byte offsets stay below 2^31 (256 rows x N <= 2^22 columns x 2 bytes).
-    const int c = lane & 15;
-    const int rows_here = min(tc.row_end - tc.row0, BM);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc((uint16_t*)p.out + (int64_t)tc.row0 * p.Nout,
                                                 (uint32_t)rows_here * (uint32_t)p.Nout * 2u);
     const uint32_t lane_off =

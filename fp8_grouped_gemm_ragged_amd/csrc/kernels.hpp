@@ -38,6 +38,10 @@ struct GemmParams {
   float* h_scales;
   // workspace of SPLIT_SLOTS partial tiles (the tail split of gmm_kernel), or null: no split
   float* split_ws;
+  // dlhs of the down projection with the SwiGLU backward in its epilogue: gu = [g | u]
+  // bf16 [M, 2 Nout] of the forward; out is then d_gu bf16 [M, 2 Nout] (the product, dh,
+  // is rounded to bf16 and used in the epilogue only).  Null: out holds the product.
+  const uint16_t* bwd_gu;
 };
 
 // The tail split of the grouped GEMM: CUs per XCD that one round of tiles fills, the most

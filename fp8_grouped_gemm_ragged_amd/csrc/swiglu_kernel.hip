@@ -31,24 +31,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
     const v4u gv = *reinterpret_cast<const v4u*>(gu + m * 2 * I + c);
     const v4u uv = *reinterpret_cast<const v4u*>(gu + m * 2 * I + I + c);
     v4u og, ou;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float dg[2], du[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float g = h ? bf16_hi(gv[k]) : bf16_lo(gv[k]);
-        const float u = h ? bf16_hi(uv[k]) : bf16_lo(uv[k]);
-        const float d = h ? bf16_hi(dv[k]) : bf16_lo(dv[k]);
-        // sigmoid through the hardware exp2 and reciprocal, as in the forward epilogue
-        const float s =
-            __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
-        const float grow = add_rn(1.0f, mul_rn(g, __fsub_rn(1.0f, s)));
-        dg[h] = __fmul_rn(__fmul_rn(__fmul_rn(d, u), s), grow);
-        du[h] = __fmul_rn(d, __fmul_rn(g, s));
-      }
-      og[k] = pack_bf16x2(dg[0], dg[1]);
-      ou[k] = pack_bf16x2(du[0], du[1]);
-    }
+    swiglu_bwd8(dv, gv, uv, og, ou);
     *reinterpret_cast<v4u*>(d_gu + m * 2 * I + c) = og;
     *reinterpret_cast<v4u*>(d_gu + m * 2 * I + I + c) = ou;
   }

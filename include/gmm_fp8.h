@@ -14,9 +14,10 @@
  * and the steps around them in the same MoE layer:
  *
  *   gmm_fwd_swiglu / gmm_fwd_swiglu_fp8 / gmm_fwd_swiglu_fp8_subchannel /
- *   gmm_swiglu_bwd   SwiGLU of the merged gate|up product in the forward's epilogue (h in
- *              bf16/f32, or fp8 codes under a static or per-row-and-block dynamic scale),
- *              and its backward
+ *   gmm_swiglu_bwd / gmm_dlhs_swiglu_bwd   SwiGLU of the merged gate|up product in the
+ *              forward's epilogue (h in bf16/f32, or fp8 codes under a static or
+ *              per-row-and-block dynamic scale), and its backward, alone or in the
+ *              epilogue of the down projection's dlhs
  *   gmm_fwd_local / gmm_dlhs_local / tgmm_drhs_local   the products over a window of
  *              local experts (group_offset)
  *   gmm_fwd_blockwise, gmm_dlhs_blockwise, gmm_quantize_subchannel,
@@ -357,6 +358,31 @@ gmm_status_t gmm_fwd_swiglu_fp8_subchannel(const gmm_operand_t* lhs_op, int32_t 
  */
 gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu, void* d_gu,
                             gmm_stream_t stream);
+
+/*
+ * gmm_dlhs_swiglu_bwd - the down projection's dlhs with the SwiGLU backward in its
+ * epilogue ("FP8 Megablox for batch split", Description (2): gate and up projections
+ * merged, so the backward of h = silu(g) * u meets the merged gu in one pass):
+ *
+ *   dh   = gmm_dlhs(grad, rhs) in bf16 (the same bits gmm_dlhs returns),
+ *   d_gu = gmm_swiglu_bwd(dh, gu)          (the same bits as that call on dh),
+ *
+ * without dh leaving the product's epilogue: each tile reads gu's gate and up values for
+ * its rows and channels and writes both halves of d_gu.
+ * grad, grad_op, grad_scales, rhs (the down projection's weight as logical [G, I, N],
+ * quantized per output channel i), rhs_scales f32 [G, I], rhs_layout, group_sizes and
+ * the workspace are as in gmm_dlhs with K = I (GMM_OP_DLHS or GMM_OP_DLHS_FUSED sizes
+ * suffice; there is no tail split).  I is a positive multiple of 128, at most 2^21.
+ * gu           bf16 [M, 2I], the merged forward product [g | u] (gmm_fwd_swiglu's gu).
+ * d_gu         bf16 [M, 2I] = [dL/dg | dL/du]; rows outside every group are not written.
+ *              It must not overlap gu, the workspace or grad_scales (GMM_ERR_ALIAS).
+ */
+gmm_status_t gmm_dlhs_swiglu_bwd(const gmm_operand_t* grad_op, int32_t rhs_format,
+                                 int32_t rhs_layout, int64_t M, int64_t I, int64_t N, int32_t G,
+                                 const void* grad, float* grad_scales, const uint8_t* rhs,
+                                 const float* rhs_scales, const int32_t* group_sizes,
+                                 const void* gu, void* d_gu, void* workspace,
+                                 size_t workspace_bytes, gmm_stream_t stream);
 
 /*
  * Block-wise scales ("Support quantization for tokamax gmm v2", review thread on the

@@ -225,6 +225,21 @@ def test_swiglu_validation():
     assert lib.gmm_swiglu_bwd(256, 256, ptr(1), ptr(2), ptr(2), None) == 9
     assert lib.gmm_swiglu_bwd(0, 256, None, None, None, None) == 0
 
+    def dlhs_bwd(layout=0, M=256, I=256, N=256, gu=8, d_gu=9, ws=7):
+        P = lambda i: None if i is None else ptr(i)
+        return lib.gmm_dlhs_swiglu_bwd(ctypes.byref(op(kind=1, fmt=1)), 0, layout, M, I, N, 4,
+                                       ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), P(gu), P(d_gu),
+                                       P(ws), 1 << 20, None)
+
+    assert dlhs_bwd(M=0, gu=None, d_gu=None) == 0  # validated, nothing to enqueue
+    assert dlhs_bwd(layout=5) == 4
+    assert dlhs_bwd(I=0) == 2 and dlhs_bwd(I=192) == 2  # I a positive multiple of 128
+    assert dlhs_bwd(I=(1 << 21) + 128) == 2
+    assert dlhs_bwd(gu=None) == 1 and dlhs_bwd(d_gu=None) == 1
+    assert dlhs_bwd(d_gu=8) == 9  # d_gu over gu
+    assert dlhs_bwd(d_gu=1) == 9  # d_gu over the grad codes
+    assert dlhs_bwd(d_gu=2) == 9  # d_gu over the grad scales
+
 
 def test_route_validation():
     lib = g.load()

@@ -1,5 +1,6 @@
 """GPU parity of the SwiGLU steps: the merged gate|up forward with SwiGLU in its epilogue
-(gmm_fwd_swiglu) and the elementwise backward (gmm_swiglu_bwd)."""
+(gmm_fwd_swiglu), the elementwise backward (gmm_swiglu_bwd) and the backward in the
+epilogue of the down projection's dlhs (gmm_dlhs_swiglu_bwd)."""
 
 import numpy as np
 import pytest
@@ -9,6 +10,7 @@ import oracle.ops as ops
 from oracle.fp8 import bf16_bits_to_f32, decode_fp8, f32_to_bf16_bits
 from oracle.gmm import gmm_fwd_ref, row_scales
 from oracle.quant import qmax_of, quantize_rhs_per_channel
+from oracle.ops import dlhs as dlhs_oracle
 from oracle.swiglu import swiglu_bwd_ref, swiglu_fp8_ref, swiglu_ref
 from tests.gpu_util import gen, gs_tensor
 from tests.parity import (TOL, assert_bf16_close, assert_fp8_codes_in_band, group_rel_err,
@@ -88,6 +90,58 @@ def test_swiglu_backward(lib):
     exact = np.mean(to_np(d) == f32_to_bf16_bits(R))
     print(f"bf16 outputs equal to RNE of the exact value: {exact:.5f}")
     assert exact >= 0.99
+
+
+@pytest.mark.parametrize("grad_kind", ["codes", "bf16"])
+def test_dlhs_swiglu_bwd(lib, grad_kind):
+    """gmm_dlhs_swiglu_bwd: the same bits as gmm_dlhs (bf16 dh) followed by gmm_swiglu_bwd,
+    and within the parity metric of the SwiGLU backward of the oracle's dh.  Ragged groups
+    with empty and one-row ones over several 256-row tiles; I = 384, so the last 256-column
+    tile is half outside the output."""
+    sizes = [0, 300, 5, 0, 457, 130, 1]
+    G, M, H, I = len(sizes), sum(sizes), 512, 384
+    gy, gyb = gen((M, H), 1e-3, 541)
+    wd, wdb = gen((G, I, H), 0.02, 542)  # down projection [G, I, hidden]
+    gu, gub = gen((M, 2 * I), 2.0, 543)
+    wk, wks = lib.gmm_quantize_rhs(wd, "e4m3", 1, "kn")
+    gs = gs_tensor(sizes)
+    if grad_kind == "codes":
+        gq, sg = lib.gmm_quantize(gy, "e5m2", "dynamic")
+        grad, kw = gq, dict(grad_scales=sg)
+    else:
+        grad, kw = gy, {}
+    dh = lib.gmm_dlhs(grad, wk, wks, gs, **kw)
+    two_calls = lib.gmm_swiglu_bwd(dh, gu)
+    d = lib.gmm_dlhs_swiglu_bwd(grad, wk, wks, gs, gu, **kw)
+    assert torch.equal(d.view(torch.int16), two_calls.view(torch.int16))
+    # into a given output, twice: the same bits
+    out = torch.full_like(d, float("nan"))
+    lib.gmm_dlhs_swiglu_bwd(grad, wk, wks, gs, gu, out=out, **kw)
+    assert torch.equal(out.view(torch.int16), two_calls.view(torch.int16))
+    with pytest.raises(ValueError):
+        lib.gmm_dlhs_swiglu_bwd(grad, wk, wks, gs, gu[:, :I].contiguous(), **kw)
+    # oracle: dh from the oracle's dlhs, rounded to bf16 as the method hands it on, then
+    # the SwiGLU backward.  Both sides round dh to bf16; where the two fp32 sums lie on
+    # either side of a rounding boundary the dh differ by one bf16 ulp (2^-8 relative),
+    # which scales that row's d_gu values alike, and the GPU rounds d_gu once more
+    # (2^-9): so each element is held to 2^-7 of itself plus the parity metric's
+    # 1e-3 of its group's largest value (the fp32 sums' own difference).
+    c_ref, s_ref = quantize_rhs_per_channel(wdb, "e4m3", "k")
+    R_dh, _, _ = dlhs_oracle(gyb, c_ref, s_ref, sizes, "e5m2", "dynamic")
+    dh_ref = bf16_bits_to_f32(f32_to_bf16_bits(R_dh))
+    R = swiglu_bwd_ref(dh_ref, bf16_bits_to_f32(gub), I).astype(np.float64)
+    Y = bf16_bits_to_f32(to_np(d)).astype(np.float64)
+    worst = 0.0
+    for lo, hi in group_row_ranges(sizes):
+        if hi <= lo:
+            continue
+        r, y = R[lo:hi], Y[lo:hi]
+        bound = 2.0 ** -7 * np.abs(r) + TOL * np.abs(r).max()
+        worst = max(worst, float((np.abs(y - r) / bound).max()))
+    exact = float(np.mean(to_np(d) == f32_to_bf16_bits(R.astype(np.float32))))
+    print(f"{grad_kind}: worst error / bound {worst:.3f}; d_gu equal to RNE(oracle): {exact:.5f}")
+    assert worst <= 1.0
+    assert exact >= 0.95
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])

@@ -427,15 +427,19 @@ def ffn_chain(g, reps=10):
         if mode == "hybrid":
             gyq, sgy = g.gmm_quantize(grad_y, "e5m2", "dynamic")
             if fused_bwd:
-                # the SwiGLU backward in the down projection's dlhs epilogue (no dh)
-                g.gmm_dlhs_swiglu_bwd(gyq, wdn_k, wdn_sk, gs, gu, grad_scales=sgy, out=d_gu)
+                # the SwiGLU backward in the down projection's dlhs epilogue (no dh), which
+                # also gathers d_gu's block scales (its quantizer then has no prepass)
+                _, sdg = g.gmm_dlhs_swiglu_bwd(gyq, wdn_k, wdn_sk, gs, gu, grad_scales=sgy,
+                                               out=d_gu, d_gu_format="e5m2")
                 rec(3)
+                rec(4)
+                dgq, _ = g.gmm_quantize(d_gu, "e5m2", "dynamic_given", scales=sdg)
             else:
                 g.gmm_dlhs(gyq, wdn_k, wdn_sk, gs, grad_scales=sgy, out=dh)
                 rec(3)
                 g.gmm_swiglu_bwd(dh, gu, out=d_gu)
-            rec(4)
-            dgq, sdg = g.gmm_quantize(d_gu, "e5m2", "dynamic")
+                rec(4)
+                dgq, sdg = g.gmm_quantize(d_gu, "e5m2", "dynamic")
             g.gmm_dlhs(dgq, wgu_k, wgu_sk, gs, grad_scales=sdg, out=dx)
             rec(5)
             g.tgmm_drhs(h_lhs, gyq, gs, grad_scales=sgy, out=dwd, **h_kw)
@@ -506,8 +510,9 @@ def ffn_chain(g, reps=10):
         "chain": mt, "TFLOP/s": round(total_flop / mt["median_ms"] / 1e9, 1),
         "dlhs_down_swiglu_bwd_ms": round(t_fb, 4),
         "two_calls_ms": round(t_two, 4),
-        "what": "gmm_dlhs_swiglu_bwd (grad quantizer included) in place of gmm_dlhs + "
-                "gmm_swiglu_bwd; same d_gu bits"}
+        "what": "gmm_dlhs_swiglu_bwd with d_gu's block scales (grad quantizer included) in "
+                "place of gmm_dlhs + gmm_swiglu_bwd, and d_gu quantized on those scales "
+                "(no prepass); same d_gu bits and codes"}
     res["hybrid_over_pure"] = {s: round(res[f"hybrid_{s}"]["chain"]["median_ms"] /
                                         res[f"pure_{s}"]["chain"]["median_ms"], 4)
                                for s in ("static", "dynamic")}

@@ -76,7 +76,7 @@ _SIGNATURES = {
                                       _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "gmm_swiglu_bwd": [_I64, _I64, _P, _P, _P, _P],
     "gmm_dlhs_swiglu_bwd": [_OPP, _I32, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
-                            _P, _SZ, _P],
+                            _I32, _P, _P, _SZ, _P],
     "gmm_permute_workspace_size": [_I64, _I32, _I32],
     "gmm_fwd_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
     "gmm_dlhs_blockwise": [_I32, _I32, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P, _P, _P, _P],
@@ -222,7 +222,7 @@ def _nblocks(rows):
 
 def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_scales,
           rhs_layout, out_dtype, out, contraction_dim, out_cols, fused, group_offset=None,
-          gu=None):
+          gu=None, gu_scales=None, gu_fmt=0):
     import torch
 
     lib = load()
@@ -281,8 +281,9 @@ def _gemm(cname, a, rhs, rhs_scales, group_sizes, fmt, scaling, static_scale, a_
     if gu is not None:
         _check(lib.gmm_dlhs_swiglu_bwd(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], M, K, N, G,
                                        _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales),
-                                       _ptr(group_sizes), _ptr(gu), _ptr(out), _ptr(ws),
-                                       ws_n.value, _stream()), "gmm_dlhs_swiglu_bwd")
+                                       _ptr(group_sizes), _ptr(gu), _ptr(out), int(gu_fmt),
+                                       _ptr(gu_scales), _ptr(ws), ws_n.value, _stream()),
+               "gmm_dlhs_swiglu_bwd")
     elif group_offset is None:
         _check(getattr(lib, cname)(ctypes.byref(op), E4M3, _LAYOUT[rhs_layout], odt_code, M, K, N,
                                    G, _ptr(a), _ptr(a_scales), _ptr(rhs), _ptr(rhs_scales),
@@ -391,14 +392,27 @@ def gmm_dlhs(grad, rhs, rhs_scales, group_sizes, *, grad_format="e5m2", grad_sca
 
 def gmm_dlhs_swiglu_bwd(grad, rhs, rhs_scales, group_sizes, gu, *, grad_format="e5m2",
                         grad_scaling="dynamic", static_scale=None, grad_scales=None,
-                        rhs_layout="kn", out=None, return_scales=False, fused=False):
+                        rhs_layout="kn", out=None, return_scales=False, fused=False,
+                        d_gu_format=None):
     """The down projection's dlhs with the SwiGLU backward in its epilogue: d_gu [M, 2I]
     bf16 = gmm_swiglu_bwd(gmm_dlhs(grad, rhs, ...) in bf16, gu), bit for bit, without the
     [M, I] dh in between.  rhs: the down weight's dlhs copy ([G, I, H] for "kn"),
-    rhs_scales f32 [G, I]; gu bf16 [M, 2I] from gmm_fwd_swiglu."""
+    rhs_scales f32 [G, I]; gu bf16 [M, 2I] from gmm_fwd_swiglu.  With d_gu_format ("e4m3"
+    or "e5m2") the call also returns d_gu's dynamic 128-row block scales (those
+    gmm_dynamic_scales gives on d_gu): (d_gu, scales); return_scales appends the grad's."""
+    import torch
+
+    gsc, fmt = None, 0
+    if d_gu_format is not None:
+        fmt = _FMT[d_gu_format]
+        gsc = torch.empty(_nblocks(grad.shape[0]), dtype=torch.float32, device=grad.device)
     o, s = _gemm("gmm_dlhs", grad, rhs, rhs_scales, group_sizes, grad_format, grad_scaling,
-                 static_scale, grad_scales, rhs_layout, None, out, "N", "K", fused, gu=gu)
-    return (o, s) if return_scales else o
+                 static_scale, grad_scales, rhs_layout, None, out, "N", "K", fused, gu=gu,
+                 gu_scales=gsc, gu_fmt=fmt)
+    r = (o,) if gsc is None else (o, gsc)
+    if return_scales:
+        r = r + (s,)
+    return r[0] if len(r) == 1 else r
 
 
 def tgmm_drhs_local(lhs, grad, group_sizes, group_offset, num_local, **kw):

@@ -179,7 +179,8 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                           const int32_t* group_sizes, void* out, void* workspace,
                           size_t workspace_bytes, hipStream_t st, bool swiglu = false,
                           void* gu = nullptr, const gmm_operand_t* h_op = nullptr,
-                          float* h_scales = nullptr, const void* bwd_gu = nullptr) {
+                          float* h_scales = nullptr, const void* bwd_gu = nullptr,
+                          float* bwd_scales = nullptr, int32_t bwd_fmt = 0) {
   gmm_status_t s = check_operand(aop);
   if (s != GMM_OK) return s;
   // SwiGLU with fp8 h: codes under a validated static per-tensor scale, or (h_scales)
@@ -259,6 +260,18 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
                    overlaps(bwd_gu, bg_bytes, a_scales, as_bytes)))
     return GMM_ERR_ALIAS;
   if (bwd_gu && !aligned16(bwd_gu)) return GMM_ERR_ALIGN;
+  // d_gu's dynamic block scales, gathered in the same epilogue
+  if (!bwd_gu) bwd_scales = nullptr;
+  const size_t bs_bytes = bwd_scales ? (size_t)nblocks(M) * 4 : 0;
+  if (bs_bytes && (overlaps(bwd_scales, bs_bytes, out, out_bytes) ||
+                   overlaps(bwd_scales, bs_bytes, bwd_gu, bg_bytes) ||
+                   overlaps(bwd_scales, bs_bytes, a, a_bytes) ||
+                   overlaps(bwd_scales, bs_bytes, rhs_scales, (size_t)G * Nout * 4) ||
+                   overlaps(bwd_scales, bs_bytes, group_sizes, (size_t)G_total * 4) ||
+                   overlaps(bwd_scales, bs_bytes, workspace, ws_used) ||
+                   overlaps(bwd_scales, bs_bytes, a_scales, as_bytes)))
+    return GMM_ERR_ALIAS;
+  if (bwd_scales && !aligned16(bwd_scales)) return GMM_ERR_ALIGN;
   const size_t hs_bytes = h_scales ? (size_t)M * (Nout / 256) * 4 : 0;  // [M, I / 128]
   if (hs_bytes && (overlaps(h_scales, hs_bytes, a, a_bytes) || overlaps(h_scales, hs_bytes, rhs, b_bytes) ||
                    overlaps(h_scales, hs_bytes, rhs_scales, (size_t)G * Nout * 4) ||
@@ -296,6 +309,7 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
   p.out_f32 = out_dtype == GMM_OUT_F32;
   p.gu = gu;
   p.bwd_gu = (const uint16_t*)bwd_gu;
+  p.bwd_amax = (uint32_t*)bwd_scales;
   p.split_ws = split ? (float*)((uint8_t*)workspace + ws_need) : nullptr;
   if (h_op) {
     p.h_codes = 1 + h_op->format;
@@ -317,9 +331,13 @@ gmm_status_t grouped_gemm(const char* name, const gmm_operand_t* aop, int32_t rh
     p.a = codes;
     a_codes = true;
   }
+  if (bwd_scales && launch_zero_words(p.bwd_amax, nblocks(M), st) != hipSuccess) return GMM_ERR_HIP;
   const hipError_t e = swiglu ? launch_gemm_swiglu(aop->format, p, st)
                               : launch_gemm(aop->format, FMT_E4M3, a_codes, b_trans, p, st);
-  return e == hipSuccess ? GMM_OK : GMM_ERR_HIP;
+  if (e != hipSuccess) return GMM_ERR_HIP;
+  if (bwd_scales && launch_amax_bits_to_scales(bwd_fmt, p.bwd_amax, nblocks(M), st) != hipSuccess)
+    return GMM_ERR_HIP;
+  return GMM_OK;
 }
 
 // ---- the scratch array of gmm_fwd_noalloc ----
@@ -470,16 +488,20 @@ gmm_status_t gmm_dlhs_swiglu_bwd(const gmm_operand_t* grad_op, int32_t rhs_forma
                                  int32_t rhs_layout, int64_t M, int64_t I, int64_t N, int32_t G,
                                  const void* grad, float* grad_scales, const uint8_t* rhs,
                                  const float* rhs_scales, const int32_t* group_sizes,
-                                 const void* gu, void* d_gu, void* workspace,
-                                 size_t workspace_bytes, gmm_stream_t stream) {
+                                 const void* gu, void* d_gu, int32_t d_gu_format,
+                                 float* d_gu_scales, void* workspace, size_t workspace_bytes,
+                                 gmm_stream_t stream) {
   if (rhs_layout != GMM_RHS_KN && rhs_layout != GMM_RHS_NK) return GMM_ERR_RECIPE;
+  if (d_gu_scales && d_gu_format != GMM_FP8_E4M3 && d_gu_format != GMM_FP8_E5M2)
+    return GMM_ERR_RECIPE;
   if (I <= 0 || I > MAX_DIM / 2) return GMM_ERR_SHAPE;
   if (M > 0 && !gu) return GMM_ERR_NULL;
   // dlhs of the down projection (contraction over its N = hidden columns, output I)
   return grouped_gemm("gmm_dlhs_swiglu_bwd", grad_op, rhs_format, rhs_layout == GMM_RHS_NK,
                       GMM_OUT_BF16, M, N, I, G, 0, G, grad, grad_scales, rhs, rhs_scales,
                       group_sizes, d_gu, workspace, workspace_bytes, (hipStream_t)stream, false,
-                      nullptr, nullptr, nullptr, M > 0 ? gu : nullptr);
+                      nullptr, nullptr, nullptr, M > 0 ? gu : nullptr, d_gu_scales,
+                      d_gu_format == GMM_FP8_E5M2 ? FMT_E5M2 : FMT_E4M3);
 }
 
 gmm_status_t gmm_fwd_swiglu(const gmm_operand_t* lhs_op, int32_t rhs_format, int32_t rhs_layout,

@@ -298,6 +298,11 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const TileCoord&
       // vector-memory counter retires in order)
       const __amdgpu_buffer_rsrc_t rd =
           make_rsrc((uint16_t*)p.out + (int64_t)tc.row0 * two_i, (uint32_t)rows_here * two_i * 2u);
+      // block abs-max of the values written: the wave's 128 rows meet at most two
+      // 128-row blocks, blk0 and blk0 + 1 (rows past the group's end hold zeros)
+      const int wrow0 = tc.row0 + wr * 128;
+      const int blk0 = wrow0 >> 7;
+      uint32_t am0 = 0u, am1 = 0u;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int set = b & 1;
@@ -315,6 +320,21 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const TileCoord&
           const uint32_t o = g_off + (uint32_t)(b * 8 + t) * 8u * two_i;
           buf_store16(rd, o, og);
           buf_store16(rd, o + 2u * (uint32_t)p.Nout, ou);
+          const uint32_t mm = absmax_bits16(og, absmax_bits16(ou, 0u));
+          if (((wrow0 + (b * 8 + t) * 4 + (lane >> 4)) >> 7) == blk0) am0 = max(am0, mm);
+          else am1 = max(am1, mm);
+        }
+      }
+      if (p.bwd_amax) {
+#pragma unroll
+        for (int dd = 32; dd >= 1; dd >>= 1) {
+          am0 = max(am0, (uint32_t)__shfl_xor((int)am0, dd, 64));
+          am1 = max(am1, (uint32_t)__shfl_xor((int)am1, dd, 64));
+        }
+        // one vector atomic per block from lane 0; a zero maximum changes nothing
+        if (lane == 0) {
+          if (am0) atomicMax(p.bwd_amax + blk0, am0);
+          if (am1) atomicMax(p.bwd_amax + blk0 + 1, am1);
         }
       }
       return;

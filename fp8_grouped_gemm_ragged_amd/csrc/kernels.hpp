@@ -42,6 +42,10 @@ struct GemmParams {
   // bf16 [M, 2 Nout] of the forward; out is then d_gu bf16 [M, 2 Nout] (the product, dh,
   // is rounded to bf16 and used in the epilogue only).  Null: out holds the product.
   const uint16_t* bwd_gu;
+  // with bwd_gu, optionally: per 128-row block of d_gu (blocks aligned to row 0) the
+  // largest bf16 magnitude bits (absmax_bits16) of its values, by atomic max into words
+  // that start at zero; null: none
+  uint32_t* bwd_amax;
 };
 
 // The tail split of the grouped GEMM: CUs per XCD that one round of tiles fills, the most
@@ -102,6 +106,10 @@ hipError_t launch_gemm_swiglu(int a_fmt, const GemmParams& p, hipStream_t st);
 // d_gu [M, 2 I] from dh [M, I] and gu [M, 2 I], all bf16
 hipError_t launch_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, uint16_t* d_gu, int64_t M,
                              int64_t I, hipStream_t st);
+// words[0 .. n) = 0 (a fill kernel: no memset node where a caller captures a graph)
+hipError_t launch_zero_words(uint32_t* words, int64_t n, hipStream_t st);
+// in place: block magnitude bits (absmax_bits16) -> dynamic scales RNE_f32(amax / qmax)
+hipError_t launch_amax_bits_to_scales(int fmt, uint32_t* words, int64_t nb, hipStream_t st);
 // routing sort (workspace: counts, route_chunks(n) * (G + 1) ints, and dest_all, the row
 // of every slot, n ints) and the row gather
 int64_t route_chunks(int64_t n);

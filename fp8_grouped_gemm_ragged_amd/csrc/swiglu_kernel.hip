@@ -37,7 +37,37 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
   }
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ w, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    w[i] = 0u;
+}
+
+// the dynamic-scale rule of the quantizer's prepass: s = RNE_f32(amax / qmax)
+template <int FMT>
+__global__ __launch_bounds__(256) void amax_bits_to_scales_kernel(uint32_t* __restrict__ w,
+                                                                  int64_t nb) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b < nb) w[b] = __float_as_uint(__fdiv_rn(__uint_as_float(w[b] << 16), qmax<FMT>()));
+}
+
 }  // namespace
+
+hipError_t launch_zero_words(uint32_t* words, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, st, words, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bits_to_scales(int fmt, uint32_t* words, int64_t nb, hipStream_t st) {
+  if (nb <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((nb + 255) / 256));
+  if (fmt == FMT_E4M3)
+    hipLaunchKernelGGL(amax_bits_to_scales_kernel<FMT_E4M3>, grid, dim3(256), 0, st, words, nb);
+  else
+    hipLaunchKernelGGL(amax_bits_to_scales_kernel<FMT_E5M2>, grid, dim3(256), 0, st, words, nb);
+  return hipGetLastError();
+}
 
 hipError_t launch_swiglu_bwd(const uint16_t* dh, const uint16_t* gu, uint16_t* d_gu, int64_t M,
                              int64_t I, hipStream_t st) {

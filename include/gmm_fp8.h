@@ -376,13 +376,20 @@ gmm_status_t gmm_swiglu_bwd(int64_t M, int64_t I, const void* dh, const void* gu
  * gu           bf16 [M, 2I], the merged forward product [g | u] (gmm_fwd_swiglu's gu).
  * d_gu         bf16 [M, 2I] = [dL/dg | dL/du]; rows outside every group are not written.
  *              It must not overlap gu, the workspace or grad_scales (GMM_ERR_ALIAS).
+ * d_gu_scales  NULL, or f32 [ceil(M / 128)]: also the dynamic scales of d_gu for its
+ *              quantization as the next gradient, in d_gu_format (e4m3 or e5m2, else
+ *              GMM_ERR_RECIPE): per block of 128 rows over all 2I columns,
+ *              RNE_f32(max |d_gu| / qmax), the values gmm_dynamic_scales gives on d_gu,
+ *              gathered in the same epilogue (so a dynamic_given gmm_quantize of d_gu
+ *              needs no prepass).  It must not overlap any other buffer of the call.
  */
 gmm_status_t gmm_dlhs_swiglu_bwd(const gmm_operand_t* grad_op, int32_t rhs_format,
                                  int32_t rhs_layout, int64_t M, int64_t I, int64_t N, int32_t G,
                                  const void* grad, float* grad_scales, const uint8_t* rhs,
                                  const float* rhs_scales, const int32_t* group_sizes,
-                                 const void* gu, void* d_gu, void* workspace,
-                                 size_t workspace_bytes, gmm_stream_t stream);
+                                 const void* gu, void* d_gu, int32_t d_gu_format,
+                                 float* d_gu_scales, void* workspace, size_t workspace_bytes,
+                                 gmm_stream_t stream);
 
 /*
  * Block-wise scales ("Support quantization for tokamax gmm v2", review thread on the

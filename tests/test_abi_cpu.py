@@ -225,11 +225,11 @@ def test_swiglu_validation():
     assert lib.gmm_swiglu_bwd(256, 256, ptr(1), ptr(2), ptr(2), None) == 9
     assert lib.gmm_swiglu_bwd(0, 256, None, None, None, None) == 0
 
-    def dlhs_bwd(layout=0, M=256, I=256, N=256, gu=8, d_gu=9, ws=7):
+    def dlhs_bwd(layout=0, M=256, I=256, N=256, gu=8, d_gu=9, ws=7, fmt=1, sc=None):
         P = lambda i: None if i is None else ptr(i)
         return lib.gmm_dlhs_swiglu_bwd(ctypes.byref(op(kind=1, fmt=1)), 0, layout, M, I, N, 4,
                                        ptr(1), ptr(2), ptr(3), ptr(4), ptr(5), P(gu), P(d_gu),
-                                       P(ws), 1 << 20, None)
+                                       fmt, P(sc), P(ws), 1 << 20, None)
 
     assert dlhs_bwd(M=0, gu=None, d_gu=None) == 0  # validated, nothing to enqueue
     assert dlhs_bwd(layout=5) == 4
@@ -239,6 +239,9 @@ def test_swiglu_validation():
     assert dlhs_bwd(d_gu=8) == 9  # d_gu over gu
     assert dlhs_bwd(d_gu=1) == 9  # d_gu over the grad codes
     assert dlhs_bwd(d_gu=2) == 9  # d_gu over the grad scales
+    assert dlhs_bwd(sc=10, fmt=2) == 4  # d_gu's scales in e4m3 or e5m2 only
+    assert dlhs_bwd(sc=9) == 9 and dlhs_bwd(sc=8) == 9  # the scales over d_gu, over gu
+    assert dlhs_bwd(sc=2) == 9 and dlhs_bwd(sc=4) == 9  # over the grad scales, rhs_scales
 
 
 def test_route_validation():

@@ -120,6 +120,12 @@ def test_dlhs_swiglu_bwd(lib, grad_kind):
     assert torch.equal(out.view(torch.int16), two_calls.view(torch.int16))
     with pytest.raises(ValueError):
         lib.gmm_dlhs_swiglu_bwd(grad, wk, wks, gs, gu[:, :I].contiguous(), **kw)
+    # d_gu's dynamic block scales from the same epilogue: the prepass's values, bit for bit
+    for fmt in ("e5m2", "e4m3"):
+        d2, sc = lib.gmm_dlhs_swiglu_bwd(grad, wk, wks, gs, gu, d_gu_format=fmt, **kw)
+        assert torch.equal(d2.view(torch.int16), two_calls.view(torch.int16))
+        want = lib.gmm_dynamic_scales(two_calls, fmt)
+        assert torch.equal(sc.view(torch.int32), want.view(torch.int32)), fmt
     # oracle: dh from the oracle's dlhs, rounded to bf16 as the method hands it on, then
     # the SwiGLU backward.  Both sides round dh to bf16; where the two fp32 sums lie on
     # either side of a rounding boundary the dh differ by one bf16 ulp (2^-8 relative),
